@@ -1,0 +1,138 @@
+/*
+ * triroute.h -- C ABI of the MI355X (gfx950) library for TriRoute's inference hot path:
+ * routed attention over a KV cache whose precision varies per token.
+ *
+ * Source of the method: "TriRoute: Unified Learned Routing for Joint Adaptive Attention,
+ * Experts, and KV-Cache Allocation", paper-review page on xllm-io.github.io:
+ *   - Eq. (4), "(C) KV-cache bit width": each token's K and V are quantized asymmetrically,
+ *     per token, at a width b in {2, 4, 8, 16} chosen by the controller;
+ *     s = (max - min) / (2^b - 1), z = min, code = round((x - z) / s); b = 16 is native storage.
+ *   - Eq. (2), "(A) attention resolution": each (query token, head) runs in one of three
+ *     modes -- skip (output 0), local-w (keys t-w .. t) or full causal (keys <= t).
+ *   - the inference paragraph after Algorithm 1: hard decisions, skipped work never
+ *     materialized, each token's KV stored at its chosen width, one left-to-right pass,
+ *     compatible with batching and KV paging.
+ * The routing decisions (mode per query head, b per token) are inputs to every call, as in the
+ * page's problem statement; the controller that produces them is not part of this library.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory), owned by the caller, unless
+ *     a comment says otherwise.  bf16 tensors are passed as raw 16-bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call is
+ *     asynchronous on that stream; the caller keeps the inputs alive until the stream reaches
+ *     the call.  Calls on one cache must be ordered (one stream, or caller-side events).
+ *   - Host-side argument checks run first and synchronously; on failure the call returns an
+ *     error and launches nothing.  Element values that only the device sees (a width not in
+ *     {2,4,8,16}, a mode > 2) and pool exhaustion set sticky flags in the cache, read by
+ *     tr_kv_cache_status(); outputs touched by a bad element are unspecified.
+ *   - No call throws; no call allocates except tr_kv_cache_alloc.
+ *   - Inputs must be finite; for every quantized group max - min must be finite in fp32.
+ *   - Quantization is bit-exact: s = fl32(fl32(max - min) / (2^b - 1)) with a correctly
+ *     rounded divide, z = min (+0 for a zero minimum), code = rint(fl32(fl32(x - z) / s)),
+ *     codes 0 for a constant group.  Attention accumulates in fp32 and writes bf16 (RNE).
+ *   - Local windows are the inclusive range [max(0, t - w), t] (w + 1 keys); scores are
+ *     scaled by 1/sqrt(head_dim); the query attends to its own freshly written K/V.
+ */
+#ifndef TRIROUTE_H_
+#define TRIROUTE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TR_OK = 0,
+  TR_ERR_INVALID_ARG = 1,   /* a host-checked argument is out of range or NULL */
+  TR_ERR_CAPACITY = 2,      /* the write would exceed the per-sequence capacity max_tokens */
+  TR_ERR_OUT_OF_PAGES = 3,  /* sticky: the page pool ran out during a write */
+  TR_ERR_HIP = 4,           /* a HIP runtime call failed (allocation, launch, copy) */
+  TR_ERR_UNSUPPORTED = 5,   /* a valid but unsupported shape (head_dim not 64/128, ...) */
+  TR_ERR_BAD_VALUE = 6      /* sticky: a bits or mode element outside its domain was seen */
+} tr_status;
+
+/* Attention modes of Eq. (2): one uint8 per (sequence, query token, head). */
+enum { TR_MODE_SKIP = 0, TR_MODE_LOCAL = 1, TR_MODE_FULL = 2 };
+
+/* Cache shape.  Host struct, read only during tr_kv_cache_alloc. */
+typedef struct {
+  int32_t num_layers;       /* >= 1 */
+  int32_t batch;            /* sequences per layer, >= 1 */
+  int32_t num_heads;        /* KV heads = query heads (MHA), >= 1 */
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t max_tokens;       /* per-sequence capacity in positions, >= 1 */
+  int32_t page_code_bytes;  /* K (and V) code bytes of one head in one page; 0 -> 4096.
+                               A power of two in [1024, 65536].  A page of width b holds
+                               page_code_bytes * 8 / (head_dim * b) tokens. */
+  int64_t pool_pages;       /* pages in the pool; 0 -> enough for any mix of widths */
+} tr_kv_cache_desc;
+
+/* Opaque cache: per (layer, sequence, width class) a stream of pages of the pool, fp32
+ * (scale, zero) side arrays inside each page, per-position width-class prefix counts, and the
+ * scratch buffers of the attention calls.  Owned by the library. */
+typedef struct tr_kv_cache tr_kv_cache;
+
+/* Allocate and zero a cache (device memory via hipMalloc, on the current device).
+ * *out receives the handle; nothing is allocated on error. */
+tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* desc, tr_kv_cache** out);
+
+/* Free every device buffer of the cache.  Synchronizes the device first.  NULL is a no-op. */
+tr_status tr_kv_cache_free(tr_kv_cache* cache);
+
+/* Empty every layer (lengths 0, all pages returned, sticky flags cleared), on `stream`. */
+tr_status tr_kv_cache_reset(tr_kv_cache* cache, void* stream);
+
+/* Tokens written so far to `layer` (the same for every sequence).  -1 on a bad argument. */
+int32_t tr_kv_cache_length(const tr_kv_cache* cache, int32_t layer);
+
+/* Eq. (4) write: append n_new tokens to every sequence of `layer` at positions
+ * len .. len + n_new - 1, each quantized at its own width.
+ *   k, v:  bf16 [batch, n_new, num_heads, head_dim], row-major
+ *   bits:  uint8 [batch, n_new], values in {2, 4, 8, 16}; one width per token, shared by the
+ *          token's K, V and all heads (the page charges 2 * d_kv * b bits per token).
+ * Each (token, head) K vector and V vector is one quantization group of head_dim values. */
+tr_status tr_kv_quantize_write(tr_kv_cache* cache, int32_t layer, const void* k, const void* v,
+                               const uint8_t* bits, int32_t n_new, void* stream);
+
+/* Eq. (2) decode: one query per sequence at position t = len - 1 (its K/V must already be
+ * written with tr_kv_quantize_write), attending in its per-head mode to the cached K/V.
+ *   q:    bf16 [batch, num_heads, head_dim]
+ *   mode: uint8 [batch, num_heads] (TR_MODE_*)
+ *   window: w >= 0 for local heads
+ *   out:  bf16 [batch, num_heads, head_dim]; skip heads get zeros */
+tr_status tr_routed_attn_decode(tr_kv_cache* cache, int32_t layer, const void* q, const uint8_t* mode,
+                                int32_t window, void* out, void* stream);
+
+/* Prefill: write T new tokens with Eq. (4), then run Eq. (2) for all T queries (causal, each
+ * query at its own position len + i, reading the cache just written).
+ *   q, k, v: bf16 [batch, T, num_heads, head_dim];  bits: uint8 [batch, T]
+ *   mode:    uint8 [batch, T, num_heads];            out: bf16 [batch, T, num_heads, head_dim] */
+tr_status tr_routed_attn_prefill(tr_kv_cache* cache, int32_t layer, const void* q, const void* k,
+                                 const void* v, const uint8_t* bits, const uint8_t* mode, int32_t T,
+                                 int32_t window, void* out, void* stream);
+
+/* Diagnostic read-back of positions tok0 .. tok0 + n - 1 of every sequence of `layer`, in
+ * position order, into caller device buffers:
+ *   codes: uint16 [batch, n, 2, num_heads, head_dim]  (index 2: 0 = K, 1 = V); b < 16: the
+ *          code; b = 16: the stored bf16 bits
+ *   scale, zero: float [batch, n, 2, num_heads]; b = 16 tokens read (1, 0)
+ *   bits: uint8 [batch, n] */
+tr_status tr_kv_cache_export(const tr_kv_cache* cache, int32_t layer, int32_t tok0, int32_t n,
+                             uint16_t* codes, float* scale, float* zero, uint8_t* bits, void* stream);
+
+/* Synchronize `stream` and report the sticky device flags: TR_ERR_OUT_OF_PAGES, then
+ * TR_ERR_BAD_VALUE, else TR_OK. */
+tr_status tr_kv_cache_status(tr_kv_cache* cache, void* stream);
+
+/* Pages taken from the pool so far (synchronizes `stream`).  -1 on error. */
+int64_t tr_kv_cache_pages_used(tr_kv_cache* cache, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* tr_status_str(tr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRIROUTE_H_ */

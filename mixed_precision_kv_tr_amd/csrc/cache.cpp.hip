@@ -1,0 +1,489 @@
+// Cache allocation, the Eq. (4) write path and diagnostics.
+//
+// Write path of one tr_kv_quantize_write call (TriRoute review page, xllm-io.github.io,
+// Eq. (4) and the inference paragraph after Algorithm 1):
+//   k_assign_slots   one workgroup per sequence: block-wide scan of the new tokens' width
+//                    classes -> prefix counts (slot of each token in its class stream) and
+//                    deterministic page allocation from the shared pool (one atomic per
+//                    (sequence, class) that needs pages).
+//   k_quantize_write one (token, head, K|V) group of D values per D/8 lanes: 128-bit loads,
+//                    min/max across the group's lanes, fp32 s and z, correctly rounded
+//                    divides, round-half-to-even codes, packed stores into the class page.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// prefix[layer][seq][0][*] = 0 for every (layer, seq); allocator and flags reset.
+__global__ void k_reset(CacheLayout c) {
+  int64_t n = (int64_t)c.L * c.B;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    int32_t* row = c.prefix + i * (int64_t)(c.N + 1) * TR_NCLASS;
+    row[0] = row[1] = row[2] = row[3] = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *c.next_page = 0;
+    *c.err = 0;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// One workgroup per sequence.  Classes are counted in two 32-bit words of 16-bit fields
+// (classes 0|1 and 2|3); a 256-token chunk adds at most 256 to a field.
+__global__ __launch_bounds__(kBlock) void k_assign_slots(CacheLayout c, int layer, int p0, int n,
+                                                         const uint8_t* __restrict__ bits) {
+  __shared__ uint32_t wsum[2][kBlock / 64];
+  __shared__ int32_t base[TR_NCLASS];
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int32_t* pre0 = tr_prefix_row(c, layer, s, p0);
+  if (tid < TR_NCLASS) base[tid] = pre0[tid];
+  __syncthreads();
+  int32_t n0[TR_NCLASS];
+#pragma unroll
+  for (int k = 0; k < TR_NCLASS; ++k) n0[k] = base[k];
+
+  for (int chunk = 0; chunk < n; chunk += kBlock) {
+    const int i = chunk + tid;
+    uint32_t a = 0, b = 0;
+    if (i < n) {
+      int cls = tr_class_of_bits(bits[(int64_t)s * n + i]);
+      if (cls < 0) {
+        atomicOr(c.err, TR_ERRF_BAD_BITS);
+        cls = 3;                                     // stored as native; output unspecified
+      }
+      if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
+    }
+    uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    if (lane == 63) { wsum[0][wave] = ia; wsum[1][wave] = ib; }
+    __syncthreads();
+    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) {
+      if (w < wave) { pa += wsum[0][w]; pb += wsum[1][w]; }
+      ta += wsum[0][w]; tb += wsum[1][w];
+    }
+    ia += pa; ib += pb;
+    if (i < n) {
+      int32_t* row = const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + i + 1));
+      int4 v;
+      v.x = base[0] + (int)(ia & 0xffffu);
+      v.y = base[1] + (int)(ia >> 16);
+      v.z = base[2] + (int)(ib & 0xffffu);
+      v.w = base[3] + (int)(ib >> 16);
+      *reinterpret_cast<int4*>(row) = v;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      base[0] += (int)(ta & 0xffffu); base[1] += (int)(ta >> 16);
+      base[2] += (int)(tb & 0xffffu); base[3] += (int)(tb >> 16);
+    }
+    __syncthreads();
+  }
+  // Pages for the slots [n0, n1) of every class.
+  if (tid < TR_NCLASS) {
+    const int k = tid;
+    const int P = c.ptok[k];
+    const int first = (n0[k] + P - 1) / P, last = (base[k] + P - 1) / P;
+    const int need = last - first;
+    if (need > 0) {
+      int32_t* pt = tr_ptab(c, layer, s, k);
+      const int id0 = atomicAdd(c.next_page, need);
+      const bool ok = (int64_t)id0 + need <= c.pool_pages;
+      if (!ok) atomicOr(c.err, TR_ERRF_NO_PAGES);
+      for (int j = 0; j < need; ++j) pt[first + j] = ok ? id0 + j : -1;
+    }
+  }
+}
+
+// One group = one (token, head) K or V vector of D bf16 values, handled by D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int layer, int p0, int n,
+                                                           const uint16_t* __restrict__ kin,
+                                                           const uint16_t* __restrict__ vin,
+                                                           const uint8_t* __restrict__ bits) {
+#pragma clang fp contract(off)
+  constexpr int LPG = D / 8;
+  const int64_t ngroups = (int64_t)c.B * n * c.H * 2;
+  const int64_t gid = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / LPG;
+  const int part = threadIdx.x % LPG;
+  const bool live = gid < ngroups;
+  const int64_t g = live ? gid : 0;
+  const int kv = (int)(g & 1);
+  const int64_t th = g >> 1;
+  const int h = (int)(th % c.H);
+  const int64_t tok = th / c.H;
+  const int s = (int)(tok / n), i = (int)(tok % n);
+  const int p = p0 + i;
+
+  const uint16_t* src = (kv ? vin : kin) + ((tok * c.H + h) * D + part * 8);
+  uint4 raw = live ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+  float x[8];
+  x[0] = tr_bf16_lo(raw.x); x[1] = tr_bf16_hi(raw.x);
+  x[2] = tr_bf16_lo(raw.y); x[3] = tr_bf16_hi(raw.y);
+  x[4] = tr_bf16_lo(raw.z); x[5] = tr_bf16_hi(raw.z);
+  x[6] = tr_bf16_lo(raw.w); x[7] = tr_bf16_hi(raw.w);
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) { mn = fminf(mn, x[e]); mx = fmaxf(mx, x[e]); }
+#pragma unroll
+  for (int off = 1; off < LPG; off <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  if (!live) return;
+
+  int cls = tr_class_of_bits(bits[(int64_t)s * n + i]);
+  if (cls < 0) cls = 3;                                // flagged by k_assign_slots
+  const int32_t slot = tr_prefix_row(c, layer, s, p)[cls];
+  const int P = c.ptok[cls];
+  const int32_t page = tr_ptab(c, layer, s, cls)[slot / P];
+  if (page < 0) return;                                // pool exhausted (flagged)
+  const int j = slot % P;
+  uint8_t* base = c.pool + (int64_t)page * c.page_bytes;
+  uint8_t* row = base + (kv ? c.v_off[cls] : c.k_off[cls]) + (int64_t)h * c.cb + (int64_t)j * c.rowb[cls];
+  if (h == 0 && kv == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p;
+
+  if (cls == 3) {                                      // b = 16: native bf16 storage
+    reinterpret_cast<uint4*>(row)[part] = raw;
+    return;
+  }
+  const int b = 2 << cls;
+  const float nlev = (float)((1 << b) - 1);
+  const float z = mn + 0.0f;                           // -0 -> +0
+  const float R = mx - mn;
+  const float sc = R / nlev + 0.0f;                    // correctly rounded divide; -0 -> +0
+  uint32_t code[8];
+  if (sc == 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e] = 0;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = x[e] - z;
+      const float r = d / sc;
+      float cf = rintf(r);
+      cf = fminf(fmaxf(cf, 0.0f), nlev);
+      code[e] = (uint32_t)cf;
+    }
+  }
+  if (part == 0) {
+    float2* side = reinterpret_cast<float2*>(base + (kv ? c.sv_off[cls] : c.sk_off[cls]));
+    side[(int64_t)h * P + j] = make_float2(sc, z);
+  }
+  if (b == 2) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= code[e] << (2 * e);
+    reinterpret_cast<uint16_t*>(row)[part] = (uint16_t)w;
+  } else if (b == 4) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= code[e] << (4 * e);
+    reinterpret_cast<uint32_t*>(row)[part] = w;
+  } else {
+    uint2 w;
+    w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    reinterpret_cast<uint2*>(row)[part] = w;
+  }
+}
+
+// Read back positions tok0 .. tok0+n-1 of every sequence (position order).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_export(CacheLayout c, int layer, int tok0, int n,
+                                                   uint16_t* __restrict__ codes, float* __restrict__ scale,
+                                                   float* __restrict__ zero, uint8_t* __restrict__ bits) {
+  const int64_t total = (int64_t)c.B * n * 2 * c.H * D;
+  for (int64_t e = blockIdx.x * (int64_t)kBlock + threadIdx.x; e < total; e += (int64_t)gridDim.x * kBlock) {
+    const int d = (int)(e % D);
+    int64_t r = e / D;
+    const int h = (int)(r % c.H); r /= c.H;
+    const int kv = (int)(r % 2); r /= 2;
+    const int i = (int)(r % n);
+    const int s = (int)(r / n);
+    const int p = tok0 + i;
+    const int32_t* pa = tr_prefix_row(c, layer, s, p);
+    const int32_t* pb = tr_prefix_row(c, layer, s, p + 1);
+    int cls = 3;
+#pragma unroll
+    for (int k = 0; k < TR_NCLASS; ++k)
+      if (pb[k] != pa[k]) cls = k;
+    const int32_t slot = pa[cls];
+    const int P = c.ptok[cls];
+    const int32_t page = tr_ptab(c, layer, s, cls)[slot / P];
+    const int j = slot % P;
+    uint16_t val = 0;
+    float sv = 1.0f, zv = 0.0f;
+    if (page >= 0) {
+      const uint8_t* base = c.pool + (int64_t)page * c.page_bytes;
+      const uint8_t* row = base + (kv ? c.v_off[cls] : c.k_off[cls]) + (int64_t)h * c.cb + (int64_t)j * c.rowb[cls];
+      const int b = 2 << cls;
+      if (cls == 3) {
+        val = reinterpret_cast<const uint16_t*>(row)[d];
+      } else {
+        const int bit = d * b;
+        val = (uint16_t)((row[bit >> 3] >> (bit & 7)) & ((1u << b) - 1u));
+        const float2 sz = reinterpret_cast<const float2*>(base + (kv ? c.sv_off[cls] : c.sk_off[cls]))[(int64_t)h * P + j];
+        sv = sz.x;
+        zv = sz.y;
+      }
+    }
+    codes[e] = val;
+    if (d == 0) {
+      const int64_t si = (((int64_t)s * n + i) * 2 + kv) * c.H + h;
+      scale[si] = sv;
+      zero[si] = zv;
+      if (kv == 0 && h == 0) bits[(int64_t)s * n + i] = (uint8_t)(2 << cls);
+    }
+  }
+}
+
+int grid_for(int64_t items, int per_block) {
+  int64_t g = (items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > (1 << 20)) g = 1 << 20;
+  return (int)g;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+}  // namespace
+
+tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                          const uint8_t* bits, int n, hipStream_t stream) {
+  const CacheLayout& L = c->lay;
+  hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kBlock), 0, stream, L, layer, p0, n, bits);
+  TR_LAUNCH_CHECK();
+  const int64_t lanes = (int64_t)L.B * n * L.H * 2 * (L.D / 8);
+  const int grid = (int)((lanes + kBlock - 1) / kBlock);
+  if (L.D == 64)
+    hipLaunchKernelGGL(k_quantize_write<64>, dim3(grid), dim3(kBlock), 0, stream, L, layer, p0, n, k, v, bits);
+  else
+    hipLaunchKernelGGL(k_quantize_write<128>, dim3(grid), dim3(kBlock), 0, stream, L, layer, p0, n, k, v, bits);
+  TR_LAUNCH_CHECK();
+  return TR_OK;
+}
+
+extern "C" {
+
+const char* tr_status_str(tr_status s) {
+  switch (s) {
+    case TR_OK: return "ok";
+    case TR_ERR_INVALID_ARG: return "invalid argument";
+    case TR_ERR_CAPACITY: return "write exceeds the per-sequence capacity";
+    case TR_ERR_OUT_OF_PAGES: return "page pool exhausted";
+    case TR_ERR_HIP: return "HIP runtime error";
+    case TR_ERR_UNSUPPORTED: return "unsupported shape";
+    case TR_ERR_BAD_VALUE: return "a bits or mode element outside its domain";
+  }
+  return "unknown status";
+}
+
+static void free_all(tr_kv_cache* c) {
+  if (!c) return;
+  (void)hipFree(c->lay.pool);
+  (void)hipFree(c->lay.ptab);
+  (void)hipFree(c->lay.prefix);
+  (void)hipFree(c->lay.next_page);
+  (void)hipFree(c->lay.err);
+  (void)hipFree(c->partials);
+  (void)hipFree(c->rows);
+  (void)hipFree(c->row_counts);
+  (void)hipFree(c->done);
+  delete c;
+}
+
+tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
+  if (!d || !out) return TR_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (d->num_layers < 1 || d->batch < 1 || d->num_heads < 1 || d->max_tokens < 1 || d->pool_pages < 0)
+    return TR_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return TR_ERR_UNSUPPORTED;
+  const int cb = d->page_code_bytes ? d->page_code_bytes : 4096;
+  if (cb < 1024 || cb > 65536 || (cb & (cb - 1))) return TR_ERR_INVALID_ARG;
+
+  tr_kv_cache* c = new tr_kv_cache();
+  memset(&c->lay, 0, sizeof(c->lay));
+  c->partials = nullptr;
+  c->rows = c->row_counts = nullptr;
+  c->done = nullptr;
+  CacheLayout& L = c->lay;
+  L.L = d->num_layers; L.B = d->batch; L.H = d->num_heads; L.D = d->head_dim; L.N = d->max_tokens;
+  L.cb = cb;
+  int64_t page_bytes = 0;
+  L.pt_stride = 0;
+  for (int k = 0; k < TR_NCLASS; ++k) {
+    const int b = 2 << k;
+    L.rowb[k] = L.D * b / 8;
+    L.ptok[k] = cb / L.rowb[k];
+    int64_t off = align256(4LL * L.ptok[k]);
+    L.k_off[k] = (int32_t)off; off += (int64_t)L.H * cb;
+    L.v_off[k] = (int32_t)off; off += (int64_t)L.H * cb;
+    if (k < 3) {
+      L.sk_off[k] = (int32_t)off; off += align256((int64_t)L.H * L.ptok[k] * 8);
+      L.sv_off[k] = (int32_t)off; off += align256((int64_t)L.H * L.ptok[k] * 8);
+    } else {
+      L.sk_off[k] = L.sv_off[k] = 0;
+    }
+    if (off > page_bytes) page_bytes = off;
+    L.maxp[k] = (L.N + L.ptok[k] - 1) / L.ptok[k] + 1;
+    L.pt_off[k] = L.pt_stride;
+    L.pt_stride += L.maxp[k];
+  }
+  if (page_bytes > (1LL << 30)) { delete c; return TR_ERR_UNSUPPORTED; }
+  L.page_bytes = (int32_t)page_bytes;
+  // Worst case over any mix of widths: every token in the class with the fewest tokens per
+  // page, plus one partial page for each other class.
+  const int64_t worst = (int64_t)L.L * L.B * ((L.N + L.ptok[3] - 1) / L.ptok[3] + TR_NCLASS);
+  L.pool_pages = d->pool_pages ? d->pool_pages : worst;
+  if (L.pool_pages > 0x7fffffffLL) { delete c; return TR_ERR_UNSUPPORTED; }
+
+  c->len.assign(L.L, 0);
+  c->max_chunks = (L.N + 255) / 256 + 1;
+  (void)hipGetDevice(&c->device);
+  bool ok = true;
+  ok = ok && hipMalloc((void**)&L.pool, (size_t)(L.pool_pages * L.page_bytes)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&L.ptab, sizeof(int32_t) * (size_t)L.L * L.B * L.pt_stride) == hipSuccess;
+  ok = ok && hipMalloc((void**)&L.prefix, sizeof(int32_t) * TR_NCLASS * (size_t)L.L * L.B * (L.N + 1)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&L.next_page, sizeof(int32_t)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&L.err, sizeof(uint32_t)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->partials,
+                       sizeof(float) * (size_t)L.B * L.H * c->max_chunks * (L.D + 2)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * L.H * L.N) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * L.H * 4) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->done, sizeof(uint32_t) * (size_t)L.B * L.H) == hipSuccess;
+  if (!ok) {
+    hipGetLastError();
+    free_all(c);
+    return TR_ERR_HIP;
+  }
+  const int64_t npt = (int64_t)L.L * L.B * L.pt_stride;
+  hipLaunchKernelGGL(k_fill_i32, dim3(grid_for(npt, kBlock)), dim3(kBlock), 0, 0, L.ptab, npt, -1);
+  hipLaunchKernelGGL(k_fill_i32, dim3(grid_for((int64_t)L.B * L.H, kBlock)), dim3(kBlock), 0, 0,
+                     (int32_t*)c->done, (int64_t)L.B * L.H, 0);
+  hipLaunchKernelGGL(k_reset, dim3(grid_for((int64_t)L.L * L.B, kBlock)), dim3(kBlock), 0, 0, L);
+  if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    free_all(c);
+    return TR_ERR_HIP;
+  }
+  *out = c;
+  return TR_OK;
+}
+
+tr_status tr_kv_cache_free(tr_kv_cache* c) {
+  if (!c) return TR_OK;
+  hipDeviceSynchronize();
+  free_all(c);
+  return TR_OK;
+}
+
+tr_status tr_kv_cache_reset(tr_kv_cache* c, void* stream) {
+  if (!c) return TR_ERR_INVALID_ARG;
+  CacheLayout& L = c->lay;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t npt = (int64_t)L.L * L.B * L.pt_stride;
+  hipLaunchKernelGGL(k_fill_i32, dim3(grid_for(npt, kBlock)), dim3(kBlock), 0, st, L.ptab, npt, -1);
+  hipLaunchKernelGGL(k_reset, dim3(grid_for((int64_t)L.L * L.B, kBlock)), dim3(kBlock), 0, st, L);
+  TR_LAUNCH_CHECK();
+  for (auto& x : c->len) x = 0;
+  return TR_OK;
+}
+
+int32_t tr_kv_cache_length(const tr_kv_cache* c, int32_t layer) {
+  if (!c || layer < 0 || layer >= c->lay.L) return -1;
+  return c->len[layer];
+}
+
+tr_status tr_kv_quantize_write(tr_kv_cache* c, int32_t layer, const void* k, const void* v,
+                               const uint8_t* bits, int32_t n_new, void* stream) {
+  if (!c || layer < 0 || layer >= c->lay.L || n_new < 0) return TR_ERR_INVALID_ARG;
+  if (n_new == 0) return TR_OK;
+  if (!k || !v || !bits) return TR_ERR_INVALID_ARG;
+  if ((int64_t)c->len[layer] + n_new > c->lay.N) return TR_ERR_CAPACITY;
+  tr_status st = tr_write_launch(c, layer, c->len[layer], (const uint16_t*)k, (const uint16_t*)v, bits, n_new,
+                                 (hipStream_t)stream);
+  if (st == TR_OK) c->len[layer] += n_new;
+  return st;
+}
+
+tr_status tr_routed_attn_decode(tr_kv_cache* c, int32_t layer, const void* q, const uint8_t* mode,
+                                int32_t window, void* out, void* stream) {
+  if (!c || layer < 0 || layer >= c->lay.L || !q || !mode || !out || window < 0) return TR_ERR_INVALID_ARG;
+  if (c->len[layer] < 1) return TR_ERR_INVALID_ARG;
+  return tr_decode_launch(c, layer, (const uint16_t*)q, mode, window, (uint16_t*)out, (hipStream_t)stream);
+}
+
+tr_status tr_routed_attn_prefill(tr_kv_cache* c, int32_t layer, const void* q, const void* k, const void* v,
+                                 const uint8_t* bits, const uint8_t* mode, int32_t T, int32_t window, void* out,
+                                 void* stream) {
+  if (!c || layer < 0 || layer >= c->lay.L || T < 0 || window < 0) return TR_ERR_INVALID_ARG;
+  if (T == 0) return TR_OK;
+  if (!q || !k || !v || !bits || !mode || !out) return TR_ERR_INVALID_ARG;
+  if ((int64_t)c->len[layer] + T > c->lay.N) return TR_ERR_CAPACITY;
+  const int p0 = c->len[layer];
+  hipStream_t st = (hipStream_t)stream;
+  tr_status s = tr_write_launch(c, layer, p0, (const uint16_t*)k, (const uint16_t*)v, bits, T, st);
+  if (s != TR_OK) return s;
+  c->len[layer] += T;
+  return tr_prefill_launch(c, layer, p0, (const uint16_t*)q, mode, T, window, (uint16_t*)out, st);
+}
+
+tr_status tr_kv_cache_export(const tr_kv_cache* c, int32_t layer, int32_t tok0, int32_t n, uint16_t* codes,
+                             float* scale, float* zero, uint8_t* bits, void* stream) {
+  if (!c || layer < 0 || layer >= c->lay.L || tok0 < 0 || n < 0) return TR_ERR_INVALID_ARG;
+  if ((int64_t)tok0 + n > c->len[layer]) return TR_ERR_INVALID_ARG;
+  if (n == 0) return TR_OK;
+  if (!codes || !scale || !zero || !bits) return TR_ERR_INVALID_ARG;
+  const CacheLayout& L = c->lay;
+  const int64_t total = (int64_t)L.B * n * 2 * L.H * L.D;
+  const int grid = grid_for(total, kBlock);
+  if (L.D == 64)
+    hipLaunchKernelGGL(k_export<64>, dim3(grid), dim3(kBlock), 0, (hipStream_t)stream, L, layer, tok0, n, codes,
+                       scale, zero, bits);
+  else
+    hipLaunchKernelGGL(k_export<128>, dim3(grid), dim3(kBlock), 0, (hipStream_t)stream, L, layer, tok0, n, codes,
+                       scale, zero, bits);
+  TR_LAUNCH_CHECK();
+  return TR_OK;
+}
+
+tr_status tr_kv_cache_status(tr_kv_cache* c, void* stream) {
+  if (!c) return TR_ERR_INVALID_ARG;
+  uint32_t flags = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TR_ERR_HIP;
+  if (hipMemcpy(&flags, c->lay.err, sizeof(flags), hipMemcpyDeviceToHost) != hipSuccess) return TR_ERR_HIP;
+  if (flags & TR_ERRF_NO_PAGES) return TR_ERR_OUT_OF_PAGES;
+  if (flags & (TR_ERRF_BAD_BITS | TR_ERRF_BAD_MODE)) return TR_ERR_BAD_VALUE;
+  return TR_OK;
+}
+
+int64_t tr_kv_cache_pages_used(tr_kv_cache* c, void* stream) {
+  if (!c) return -1;
+  int32_t used = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
+  if (hipMemcpy(&used, c->lay.next_page, sizeof(used), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  return used < c->lay.pool_pages ? used : c->lay.pool_pages;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal declarations shared by the translation units of libtriroute.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "layout.h"
+#include "triroute.h"
+
+struct tr_kv_cache {
+  CacheLayout lay;
+  int device;
+  std::vector<int32_t> len;       // host mirror: tokens written per layer (same for every sequence)
+  // decode split-K partials: [B][H][max_chunks][D + 2] floats (o[D], m, l)
+  float* partials;
+  int32_t max_chunks;
+  // prefill scratch: compacted query rows per (seq, head) [B][H][N] and counts [B][H][2]
+  int32_t* rows;
+  int32_t* row_counts;
+  uint32_t* done;                 // decode completion counters per (seq, head)
+};
+
+// Every kernel launch goes through here so launch errors map to TR_ERR_HIP.
+#define TR_LAUNCH_CHECK()                                     \
+  do {                                                        \
+    if (hipGetLastError() != hipSuccess) return TR_ERR_HIP;   \
+  } while (0)
+
+// bf16 bits -> float (exact) and float -> bf16 bits (round to nearest even, finite input).
+__device__ __forceinline__ float tr_bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float tr_bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint16_t tr_f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Decode entry points implemented in decode.hip / prefill.hip.
+tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
+                           uint16_t* out, hipStream_t stream);
+tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint8_t* mode, int T,
+                            int window, uint16_t* out, hipStream_t stream);
+tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                          const uint8_t* bits, int n, hipStream_t stream);

@@ -14,7 +14,7 @@ round-to-nearest-even, done with numpy float32 arrays, in this order:
     mx, mn = max(x), min(x)          (exact)
     z      = mn + 0.0                (turns -0 into +0; otherwise exact)
     R      = fl32(mx - mn)
-    s      = fl32(R / n),  n = 2^b - 1
+    s      = fl32(R / n) + 0.0   n = 2^b - 1 (the + 0.0 turns a -0 range into +0)
     d      = fl32(x - z)
     r      = fl32(d / s)
     code   = rint(r)                 (round half to even; exact on a float32)
@@ -68,7 +68,7 @@ def quantize(x_bits: np.ndarray, b, group_size: int | None = None):
     z = mn + np.float32(0.0)
     R = mx - mn
     n = (np.left_shift(np.int64(1), bg) - 1).astype(np.float32)
-    s = R / n
+    s = R / n + np.float32(0.0)
 
     native = bg == 16
     degenerate = (s == np.float32(0.0)) & ~native
@@ -76,7 +76,7 @@ def quantize(x_bits: np.ndarray, b, group_size: int | None = None):
     d = x - z[..., None]
     r = d / safe_s[..., None]
     c = np.rint(r)
-    c = np.where(degenerate[..., None], np.float32(0.0), c)
+    c = np.where((degenerate | native)[..., None], np.float32(0.0), c)   # native rows keep bits
     quant = ~native
     if quant.any():
         cq = c[quant]

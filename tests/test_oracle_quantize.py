@@ -93,6 +93,15 @@ def test_negative_zero_becomes_positive_zero():
     assert codes.tolist() == [0, 3, 0] and float(s) == 1.0
 
 
+def test_signed_zero_range_gives_positive_zero_scale():
+    # a group of +0 and -0 has max - min = +-0 depending on which zero is taken as the max;
+    # the scale is canonicalised to +0 either way, so its bits are well defined
+    for pattern in ([0x0000, 0x8000], [0x8000, 0x0000], [0x8000, 0x8000, 0x0000]):
+        codes, s, z = oracle.quantize(np.array(pattern, dtype=np.uint16), 8)
+        assert np.float32(s).view(np.uint32) == 0 and np.float32(z).view(np.uint32) == 0
+        assert np.all(codes == 0)
+
+
 def test_rejects_other_widths():
     with pytest.raises(ValueError):
         oracle.quantize(bf16([1.0, 2.0]), 3)
