@@ -1,0 +1,345 @@
+"""Benchmark of the routed-attention hot path on one MI355X.
+
+Headline (``value``): mixed-bit KV decode bandwidth on the 1.3B-shaped decode workload --
+24 layers x 32 sequences x 16 heads x head_dim 128, cached context 8192, widths
+{2: .3, 4: .4, 8: .2, 16: .1}, modes {skip: .2, local: .4, full: .4}, w = 512.  One step =
+for every layer: quantize-write the new token of every sequence (Eq. 4) and run routed decode
+attention (Eq. 2) over the cache.  After each step the layers are truncated back to 8192
+cached tokens, so every step sees the same context.
+
+Second object (``prefill``): routed prefill on the 160M-shaped workload -- 12 layers x 4
+sequences x T = 2048 x 12 heads x head_dim 64, w = 256; one step = the 12 layer calls
+(quantize-write of the prompt, then causal routed attention), tokens/s = 4 * 2048 / step time.
+
+Accounting (algorithmic, from the realized seeded draws):
+  decode bytes  = per attended (key, head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
+                  4*D for b = 16; plus per non-skip (seq, head) 2*D (q); per (seq, head) 2*D
+                  (out); plus the new token's write: 4*D read + its stored bytes.
+  prefill flops = 4*D per attended (query, key, head) pair.
+
+Timing: warmup steps, then K steps between HIP events on the launch stream (torch's current
+stream), synchronized on both sides.  A second pass of the same steps with the library's
+per-kernel event timing enabled gives each kernel's average launch duration (roofline).
+The CPU oracle is timed on a bounded sample of the same inputs, on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, layer_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+METRIC = "mixed-bit KV decode GB/s (% HBM peak); routed prefill tokens/s (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def row_bytes(b: np.ndarray, D: int) -> np.ndarray:
+    """Stored bytes of one (token, head): K and V codes plus fp32 (s, z) pairs, or bf16."""
+    return np.where(b == 16, 4 * D, 2 * D * b // 8 + 16)
+
+
+def decode_layer_bytes(bits: np.ndarray, mode: np.ndarray, C: int, w: int, D: int):
+    """Algorithmic bytes of one decode layer: (split-kernel bytes, whole-layer bytes).
+
+    bits [B, C+1] (position C is the new token), mode [B, H]."""
+    B, H = mode.shape
+    rb = row_bytes(bits.astype(np.int64), D)               # [B, C+1]
+    csum = np.concatenate([np.zeros((B, 1), np.int64), np.cumsum(rb, axis=1)], axis=1)
+    attn = 0
+    for s in range(B):
+        for h in range(H):
+            m = int(mode[s, h])
+            if m == 0:
+                continue
+            lo = 0 if m == 2 else max(0, C - w)
+            attn += int(csum[s, C + 1] - csum[s, lo]) + 2 * D    # keys + q
+    out = B * H * 2 * D
+    write = int((4 * D + rb[:, C]).sum()) * H
+    return attn, attn + out + write
+
+
+def prefill_layer_flops(mode: np.ndarray, w: int, D: int) -> int:
+    """4*D per attended pair; mode [B, T, H]."""
+    B, T, H = mode.shape
+    t = np.arange(T)
+    keys = np.where(mode == 2, (t + 1)[None, :, None], np.where(mode == 1, (np.minimum(t, w) + 1)[None, :, None], 0))
+    return int(keys.sum()) * 4 * D
+
+
+def pool_pages_needed(bits_layers, P: dict, slack: int = 4) -> int:
+    total = 0
+    for bits in bits_layers:                               # [B, T] per layer
+        for b, p in P.items():
+            cnt = (bits == b).sum(axis=1)
+            total += int(np.ceil(cnt / p).sum())
+        total += slack * bits.shape[0]
+    return total
+
+
+def time_steps(step, K: int) -> float:
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(K):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K
+
+
+# --------------------------------------------------------------------------------------------
+# CPU oracle baseline (runs in worker processes on this host)
+
+def _oracle_decode_worker(args):
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    import oracle
+    q, k, v, bits, mode, C, w = args
+    t0 = time.perf_counter()
+    oracle.attend_cached(q[None], k, v, bits, mode[None], np.array([C]), w)
+    return time.perf_counter() - t0
+
+
+def _oracle_prefill_worker(args):
+    import oracle
+    q, k, v, bits, mode, w = args
+    t0 = time.perf_counter()
+    oracle.attend_cached(q, k, v, bits, mode, np.arange(k.shape[0]), w)
+    return time.perf_counter() - t0
+
+
+def run_pool(fn, jobs, workers):
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers, initializer=_pool_init) as pool:
+        t0 = time.perf_counter()
+        cpu_times = pool.map(fn, jobs)
+        wall = time.perf_counter() - t0
+    return wall, cpu_times
+
+
+def _pool_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    sys.path.insert(0, ROOT)
+
+
+def cpu_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------------------------
+
+def bench_decode(tr, args):
+    cfg = CONFIGS[3]
+    B, H, D, C, w, Lyr = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens, cfg.window, cfg.layers
+    dev = torch.device("cuda")
+    log(f"[decode] generating {Lyr} layers of {cfg.name}")
+    per_layer, samples = [], []
+    sample_seqs = list(range(args.cpu_sample_seqs))
+    ptok = {b: 4096 // (D * b // 8) for b in (2, 4, 8, 16)}
+    cache = None
+    acc_attn, acc_total = [], []
+    for layer in range(Lyr):
+        case = layer_inputs(cfg, layer, seed=args.seed, device=dev)
+        bits_np = case["bits"].cpu().numpy()
+        mode_np = case["mode"].cpu().numpy()
+        if cache is None:
+            # pool sized from layer 0's realized width mix, with 25% headroom for the others
+            pool_pages = int(pool_pages_needed([bits_np], ptok) * Lyr * 1.25) + 64
+            cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, C + 1, pool_pages=pool_pages)
+        tr.tr_kv_quantize_write(cache, layer, case["k"][:, :C].contiguous(), case["v"][:, :C].contiguous(),
+                                case["bits"][:, :C].contiguous())
+        a, t = decode_layer_bytes(bits_np, mode_np, C, w, D)
+        acc_attn.append(a)
+        acc_total.append(t)
+        per_layer.append({x: case[x][:, C:C + 1].contiguous() for x in ("k", "v", "bits")} |
+                         {"q": case["q"].contiguous(), "mode": case["mode"].contiguous()})
+        if layer == 0 and not args.no_cpu_baseline:
+            for s in sample_seqs:
+                samples.append((u16(case["q"][s]), u16(case["k"][s]), u16(case["v"][s]), bits_np[s],
+                                mode_np[s], C, w))
+        del case
+    torch.cuda.synchronize()
+    st = tr.tr_kv_cache_status(cache)
+    if st != 0:
+        raise RuntimeError(f"cache fill failed with status {st}")
+    outs = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(Lyr)]
+
+    def step():
+        for layer in range(Lyr):
+            p = per_layer[layer]
+            tr.tr_kv_quantize_write(cache, layer, p["k"], p["v"], p["bits"])
+            tr.tr_routed_attn_decode(cache, layer, p["q"], p["mode"], w, outs[layer])
+        for layer in range(Lyr):
+            tr.tr_kv_cache_truncate(cache, layer, C)
+
+    for _ in range(args.warmup):
+        step()
+    log(f"[decode] timing {args.steps} steps")
+    ms = time_steps(step, args.steps)
+    st = tr.tr_kv_cache_status(cache)
+    if st != 0:
+        raise RuntimeError(f"decode steps failed with status {st}")
+    step_bytes = float(sum(acc_total))
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+
+    # per-kernel durations: same steps with event timing inside the library
+    tr.tr_profile_read(cache)
+    tr.tr_profile_enable(cache, True)
+    for _ in range(args.steps):
+        step()
+    prof = tr.tr_profile_read(cache)
+    tr.tr_profile_enable(cache, False)
+    n_split, ms_split = prof["decode_split"]
+    avg_split_ms = ms_split / max(1, n_split)
+    bytes_per_launch = float(np.mean(acc_attn))
+    achieved = bytes_per_launch / (avg_split_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": "k_decode_split", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_us": round(avg_split_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch),
+            "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
+
+    cpu = None
+    if samples:
+        workers = min(cpu_workers(), len(samples))
+        log(f"[decode] oracle on {len(samples)} sampled sequences, {workers} worker processes")
+        wall, _ = run_pool(_oracle_decode_worker, samples, workers)
+        s_bytes = 0
+        for (q, k, v, bits, mode, C_, w_) in samples:
+            a, t = decode_layer_bytes(bits[None], mode[None], C_, w_, D)
+            s_bytes += t
+        cpu = {"value": round(s_bytes / wall / 1e9, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
+               "sample": f"layer 0, sequences {sample_seqs[0]}..{sample_seqs[-1]} of {cfg.name}: quantize the "
+                         f"{C + 1}-token cache of each sequence and attend its one query per head; "
+                         f"{wall:.2f} s wall"}
+    cache.close()
+    return {"ms": ms, "gbs": gbs, "bytes": step_bytes, "roofline": roof, "cpu": cpu, "cfg": cfg}
+
+
+def bench_prefill(tr, args):
+    cfg = CONFIGS[2]
+    B, H, D, T, w, Lyr = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens, cfg.window, cfg.layers
+    dev = torch.device("cuda")
+    log(f"[prefill] generating {Lyr} layers of {cfg.name}")
+    cases = [layer_inputs(cfg, layer, seed=args.seed, device=dev) for layer in range(Lyr)]
+    flops = [prefill_layer_flops(c["mode"].cpu().numpy(), w, D) for c in cases]
+    cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, T)
+    outs = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(Lyr)]
+
+    def step():
+        for layer in range(Lyr):
+            c = cases[layer]
+            tr.tr_kv_cache_truncate(cache, layer, 0)
+            tr.tr_routed_attn_prefill(cache, layer, c["q"], c["k"], c["v"], c["bits"], c["mode"], T, w, outs[layer])
+
+    for _ in range(args.warmup):
+        step()
+    log(f"[prefill] timing {args.steps} steps")
+    ms = time_steps(step, args.steps)
+    st = tr.tr_kv_cache_status(cache)
+    if st != 0:
+        raise RuntimeError(f"prefill steps failed with status {st}")
+    tok_s = B * T / (ms * 1e-3)
+    tflops = sum(flops) / (ms * 1e-3) / 1e12
+
+    tr.tr_profile_read(cache)
+    tr.tr_profile_enable(cache, True)
+    for _ in range(args.steps):
+        step()
+    prof = tr.tr_profile_read(cache)
+    tr.tr_profile_enable(cache, False)
+    n_attn, ms_attn = prof["prefill_attn"]
+    avg_ms = ms_attn / max(1, n_attn)
+    fl_per_launch = float(np.mean(flops))
+    achieved = fl_per_launch / (avg_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "k_prefill_attn", "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": int(fl_per_launch),
+            "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        c0 = cases[0]
+        job = (u16(c0["q"][0]), u16(c0["k"][0]), u16(c0["v"][0]), c0["bits"][0].cpu().numpy(),
+               c0["mode"][0].cpu().numpy(), w)
+        log("[prefill] oracle on layer 0, sequence 0")
+        wall, _ = run_pool(_oracle_prefill_worker, [job], 1)
+        cpu = {"value": round(T / (wall * Lyr), 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"layer 0, sequence 0 of {cfg.name} ({T} tokens, {H} heads): quantize-write and "
+                         f"attend every query; {wall:.2f} s wall, scaled to {Lyr} layers"}
+    cache.close()
+    return {"ms": ms, "tok_s": tok_s, "tflops": tflops, "roofline": roof, "cpu": cpu, "cfg": cfg}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=8)
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (decode and prefill shard by "
+              "(sequence, head) with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import mixed_precision_kv_tr_amd as tr
+
+    dec = bench_decode(tr, args) if args.only in (None, "decode") else None
+    pre = bench_prefill(tr, args) if args.only in (None, "prefill") else None
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    if dec:
+        cfg = dec["cfg"]
+        line.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 4),
+                     "dtype": "fp32", "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+                     "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch,
+                                "context": cfg.tokens, "heads": cfg.heads, "head_dim": cfg.head_dim,
+                                "window": cfg.window, "bytes_per_step": int(dec["bytes"])},
+                     "roofline": dec["roofline"], "cpu_baseline": dec["cpu"]})
+    if pre:
+        cfg = pre["cfg"]
+        pobj = {"workload": cfg.name, "value": round(pre["tok_s"], 1), "unit": "tokens/s",
+                "ms_per_step": round(pre["ms"], 4), "dtype": "bf16 QK / fp16 PV MFMA, fp32 softmax",
+                "tflops": round(pre["tflops"], 2), "mfma_frac": round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                "roofline": pre["roofline"], "cpu_baseline": pre["cpu"]}
+        if dec:
+            line["prefill"] = pobj
+        else:
+            line.update({"value": pobj["value"], "unit": "tokens/s", "ms_per_step": pobj["ms_per_step"],
+                         "dtype": "bf16", "config": {"workload": cfg.name}, "roofline": pobj["roofline"],
+                         "cpu_baseline": pobj["cpu_baseline"]})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

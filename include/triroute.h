@@ -83,6 +83,11 @@ tr_status tr_kv_cache_free(tr_kv_cache* cache);
 /* Empty every layer (lengths 0, all pages returned, sticky flags cleared), on `stream`. */
 tr_status tr_kv_cache_reset(tr_kv_cache* cache, void* stream);
 
+/* Roll `layer` back to its first new_len positions (0 <= new_len <= length), e.g. to discard
+ * rejected speculative tokens.  Host-side only; the pages of the dropped positions stay
+ * attached to their class streams and are reused by the next write. */
+tr_status tr_kv_cache_truncate(tr_kv_cache* cache, int32_t layer, int32_t new_len);
+
 /* Tokens written so far to `layer` (the same for every sequence).  -1 on a bad argument. */
 int32_t tr_kv_cache_length(const tr_kv_cache* cache, int32_t layer);
 
@@ -127,6 +132,15 @@ tr_status tr_kv_cache_status(tr_kv_cache* cache, void* stream);
 
 /* Pages taken from the pool so far (synchronizes `stream`).  -1 on error. */
 int64_t tr_kv_cache_pages_used(tr_kv_cache* cache, void* stream);
+
+/* Diagnostics: while enabled, the library's kernel launches on this cache are bracketed by HIP
+ * events on the call's stream.  tr_profile_read synchronizes on them, returns per kernel family
+ * the number of launches and their summed duration in milliseconds since the last read, and
+ * clears the record.  Families (array index): 0 quantize-write (slot assignment + quantize),
+ * 1 decode split-K, 2 decode combine, 3 prefill mode compaction, 4 prefill attention.
+ * launches and total_ms are HOST arrays of 5 elements. */
+tr_status tr_profile_enable(tr_kv_cache* cache, int32_t enable);
+tr_status tr_profile_read(tr_kv_cache* cache, int64_t* launches, double* total_ms);
 
 /* Static description of a status code (never NULL). */
 const char* tr_status_str(tr_status status);

@@ -47,6 +47,10 @@ _export = _sig("tr_kv_cache_export", ctypes.c_int, _vp, _i32, _i32, _i32, _vp, _
 _status = _sig("tr_kv_cache_status", ctypes.c_int, _vp, _vp)
 _pages = _sig("tr_kv_cache_pages_used", _i64, _vp, _vp)
 _status_str = _sig("tr_status_str", ctypes.c_char_p, ctypes.c_int)
+_truncate = _sig("tr_kv_cache_truncate", ctypes.c_int, _vp, _i32, _i32)
+_prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
+_prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
+PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_compact", "prefill_attn")
 
 STATUS_NAMES = {0: "TR_OK", 1: "TR_ERR_INVALID_ARG", 2: "TR_ERR_CAPACITY", 3: "TR_ERR_OUT_OF_PAGES",
                 4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE"}
@@ -156,3 +160,19 @@ def tr_kv_cache_status(cache: KVCache, stream=None) -> int:
 
 def tr_kv_cache_pages_used(cache: KVCache, stream=None) -> int:
     return int(_pages(cache.handle, _stream(stream)))
+
+
+def tr_kv_cache_truncate(cache: KVCache, layer: int, new_len: int):
+    _check(_truncate(cache.handle, layer, new_len), "tr_kv_cache_truncate")
+
+
+def tr_profile_enable(cache: KVCache, enable: bool = True):
+    _check(_prof_enable(cache.handle, 1 if enable else 0), "tr_profile_enable")
+
+
+def tr_profile_read(cache: KVCache) -> dict:
+    """{family: (launches, total_ms)} since the last read (synchronizes)."""
+    n = (_i64 * 5)()
+    ms = (ctypes.c_double * 5)()
+    _check(_prof_read(cache.handle, n, ms), "tr_profile_read")
+    return {name: (int(n[i]), float(ms[i])) for i, name in enumerate(PROFILE_FAMILIES)}

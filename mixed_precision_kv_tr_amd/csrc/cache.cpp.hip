@@ -100,18 +100,21 @@ __global__ __launch_bounds__(kBlock) void k_assign_slots(CacheLayout c, int laye
     }
     __syncthreads();
   }
-  // Pages for the slots [n0, n1) of every class.
+  // Pages for the slots [n0, n1) of every class.  Pages kept from before a truncation are
+  // reused; only the page-table entries still empty take new pages from the pool.
   if (tid < TR_NCLASS) {
     const int k = tid;
     const int P = c.ptok[k];
     const int first = (n0[k] + P - 1) / P, last = (base[k] + P - 1) / P;
-    const int need = last - first;
+    int32_t* pt = tr_ptab(c, layer, s, k);
+    int reuse = first;
+    while (reuse < last && pt[reuse] >= 0) ++reuse;
+    const int need = last - reuse;
     if (need > 0) {
-      int32_t* pt = tr_ptab(c, layer, s, k);
       const int id0 = atomicAdd(c.next_page, need);
       const bool ok = (int64_t)id0 + need <= c.pool_pages;
       if (!ok) atomicOr(c.err, TR_ERRF_NO_PAGES);
-      for (int j = 0; j < need; ++j) pt[first + j] = ok ? id0 + j : -1;
+      for (int j = 0; j < need; ++j) pt[reuse + j] = ok ? id0 + j : -1;
     }
   }
 }
@@ -273,6 +276,7 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                           const uint8_t* bits, int n, hipStream_t stream) {
   const CacheLayout& L = c->lay;
+  TrProfScope prof(c, TR_PROF_WRITE, stream);
   hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kBlock), 0, stream, L, layer, p0, n, bits);
   TR_LAUNCH_CHECK();
   const int64_t lanes = (int64_t)L.B * n * L.H * 2 * (L.D / 8);
@@ -302,6 +306,11 @@ const char* tr_status_str(tr_status s) {
 
 static void free_all(tr_kv_cache* c) {
   if (!c) return;
+  for (auto& r : c->prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (auto e : c->ev_free) (void)hipEventDestroy(e);
   (void)hipFree(c->lay.pool);
   (void)hipFree(c->lay.ptab);
   (void)hipFree(c->lay.prefix);
@@ -328,6 +337,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   c->partials = nullptr;
   c->rows = c->row_counts = nullptr;
   c->done = nullptr;
+  c->prof_on = false;
   CacheLayout& L = c->lay;
   L.L = d->num_layers; L.B = d->batch; L.H = d->num_heads; L.D = d->head_dim; L.N = d->max_tokens;
   L.cb = cb;
@@ -410,6 +420,12 @@ tr_status tr_kv_cache_reset(tr_kv_cache* c, void* stream) {
   return TR_OK;
 }
 
+tr_status tr_kv_cache_truncate(tr_kv_cache* c, int32_t layer, int32_t new_len) {
+  if (!c || layer < 0 || layer >= c->lay.L || new_len < 0 || new_len > c->len[layer]) return TR_ERR_INVALID_ARG;
+  c->len[layer] = new_len;
+  return TR_OK;
+}
+
 int32_t tr_kv_cache_length(const tr_kv_cache* c, int32_t layer) {
   if (!c || layer < 0 || layer >= c->lay.L) return -1;
   return c->len[layer];
@@ -476,6 +492,34 @@ tr_status tr_kv_cache_status(tr_kv_cache* c, void* stream) {
   if (flags & TR_ERRF_NO_PAGES) return TR_ERR_OUT_OF_PAGES;
   if (flags & (TR_ERRF_BAD_BITS | TR_ERRF_BAD_MODE)) return TR_ERR_BAD_VALUE;
   return TR_OK;
+}
+
+tr_status tr_profile_enable(tr_kv_cache* c, int32_t enable) {
+  if (!c) return TR_ERR_INVALID_ARG;
+  c->prof_on = enable != 0;
+  return TR_OK;
+}
+
+tr_status tr_profile_read(tr_kv_cache* c, int64_t* launches, double* total_ms) {
+  if (!c || !launches || !total_ms) return TR_ERR_INVALID_ARG;
+  for (int f = 0; f < TR_PROF_NFAM; ++f) {
+    launches[f] = 0;
+    total_ms[f] = 0.0;
+  }
+  tr_status st = TR_OK;
+  for (auto& r : c->prof) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = TR_ERR_HIP;
+    } else {
+      launches[r.fam] += 1;
+      total_ms[r.fam] += ms;
+    }
+    c->ev_free.push_back(r.a);
+    c->ev_free.push_back(r.b);
+  }
+  c->prof.clear();
+  return st;
 }
 
 int64_t tr_kv_cache_pages_used(tr_kv_cache* c, void* stream) {

@@ -20,6 +20,43 @@ struct tr_kv_cache {
   int32_t* rows;
   int32_t* row_counts;
   uint32_t* done;                 // decode completion counters per (seq, head)
+  // optional kernel timing (tr_profile_enable): HIP events around each kernel launch
+  bool prof_on;
+  struct ProfRec { int fam; hipEvent_t a, b; };
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> ev_free;
+};
+
+// Kernel families reported by tr_profile_read.
+enum { TR_PROF_WRITE = 0, TR_PROF_DECODE_SPLIT = 1, TR_PROF_DECODE_COMBINE = 2, TR_PROF_PREFILL_COMPACT = 3,
+       TR_PROF_PREFILL_ATTN = 4, TR_PROF_NFAM = 5 };
+
+// Brackets the kernel launches of its scope with events when timing is on.
+struct TrProfScope {
+  tr_kv_cache* c;
+  int fam;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  static hipEvent_t take(tr_kv_cache* c) {
+    if (!c->ev_free.empty()) {
+      hipEvent_t e = c->ev_free.back();
+      c->ev_free.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  TrProfScope(tr_kv_cache* c_, int fam_, hipStream_t st_) : c(c_), fam(fam_), st(st_) {
+    if (c->prof_on && (a = take(c))) (void)hipEventRecord(a, st);
+  }
+  ~TrProfScope() {
+    if (!c->prof_on || !a) return;
+    hipEvent_t b = take(c);
+    if (!b) return;
+    (void)hipEventRecord(b, st);
+    c->prof.push_back({fam, a, b});
+  }
 };
 
 // Every kernel launch goes through here so launch errors map to TR_ERR_HIP.

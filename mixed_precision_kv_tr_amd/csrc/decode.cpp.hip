@@ -301,18 +301,24 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
   const size_t lds = sizeof(float) * (size_t)CH;
   const int grid = BH * nch;
-  if (L.D == 64) {
-    hipLaunchKernelGGL(k_decode_split<64>, dim3(grid), dim3(kBlock), lds, stream, L, layer, t, window, CH, nch,
-                       c->max_chunks, kscale, q, mode, c->partials);
+  {
+    TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
+    if (L.D == 64)
+      hipLaunchKernelGGL(k_decode_split<64>, dim3(grid), dim3(kBlock), lds, stream, L, layer, t, window, CH, nch,
+                         c->max_chunks, kscale, q, mode, c->partials);
+    else
+      hipLaunchKernelGGL(k_decode_split<128>, dim3(grid), dim3(kBlock), lds, stream, L, layer, t, window, CH, nch,
+                         c->max_chunks, kscale, q, mode, c->partials);
     TR_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, L.H, t, window, CH, c->max_chunks, mode,
-                       c->partials, out);
-  } else {
-    hipLaunchKernelGGL(k_decode_split<128>, dim3(grid), dim3(kBlock), lds, stream, L, layer, t, window, CH, nch,
-                       c->max_chunks, kscale, q, mode, c->partials);
-    TR_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, L.H, t, window, CH, c->max_chunks,
-                       mode, c->partials, out);
+  }
+  {
+    TrProfScope prof(c, TR_PROF_DECODE_COMBINE, stream);
+    if (L.D == 64)
+      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, L.H, t, window, CH, c->max_chunks,
+                         mode, c->partials, out);
+    else
+      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, L.H, t, window, CH, c->max_chunks,
+                         mode, c->partials, out);
   }
   TR_LAUNCH_CHECK();
   return TR_OK;

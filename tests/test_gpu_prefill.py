@@ -1,0 +1,162 @@
+"""GPU parity of prefill routed attention (Eq. 2 for every prompt query over the cache that
+Eq. 4 just wrote): |gpu - oracle| <= 2e-3 + 1e-2 |oracle| element-wise; cache contents
+bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import bf16_to_f64, check_codes, compare_out, export_layer, say, u16
+from workloads import CONFIGS, layer_inputs, random_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tr():
+    import mixed_precision_kv_tr_amd as tr
+    return tr
+
+
+def run_prefill(tr, case, window, cuts=None, page_code_bytes=0, layers=1, layer=0):
+    """Prefill positions 0..T-1 in one call, or in pieces split at `cuts` (chunked prefill)."""
+    q, k, v, bits, mode = (case[x] for x in ("q", "k", "v", "bits", "mode"))
+    B, T, H, D = k.shape
+    cache = tr.tr_kv_cache_alloc(layers, B, H, D, T, page_code_bytes=page_code_bytes)
+    out = torch.full((B, T, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    edges = [0] + (cuts or []) + [T]
+    for a, b in zip(edges[:-1], edges[1:]):
+        piece = torch.empty((B, b - a, H, D), dtype=torch.bfloat16, device="cuda")
+        tr.tr_routed_attn_prefill(cache, layer, q[:, a:b].contiguous(), k[:, a:b].contiguous(),
+                                  v[:, a:b].contiguous(), bits[:, a:b].contiguous(), mode[:, a:b].contiguous(),
+                                  b - a, window, piece)
+        out[:, a:b] = piece
+    status = tr.tr_kv_cache_status(cache)
+    return cache, out, status
+
+
+def oracle_prefill(case, window, seqs):
+    kb, vb, qb = u16(case["k"]), u16(case["v"]), u16(case["q"])
+    bb, mb = case["bits"].cpu().numpy(), case["mode"].cpu().numpy()
+    T = kb.shape[1]
+    return {s: oracle.attend_cached(qb[s], kb[s], vb[s], bb[s], mb[s], np.arange(T), window)["out"] for s in seqs}
+
+
+def check(case, out, window, seqs, where):
+    got = bf16_to_f64(out)
+    refs = oracle_prefill(case, window, seqs)
+    for s in seqs:
+        compare_out(got[s], refs[s], f"{where} seq {s}")
+
+
+def test_prefill_config0(tr):
+    cfg = CONFIGS[0]
+    say(f"prefill {cfg.name}")
+    case = layer_inputs(cfg, 0, device="cuda")
+    cache, out, status = run_prefill(tr, case, cfg.window)
+    assert status == 0
+    B, T, H, D = case["k"].shape
+    check_codes(export_layer(tr, cache, 0, 0, T, B, H, D), case["k"], case["v"], case["bits"], where=cfg.name)
+    cache.close()
+    check(case, out, cfg.window, [0], cfg.name)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 5, 31, 32, 33, 127, 128, 129, 300])
+def test_prefill_ragged(tr, D, T):
+    say(f"prefill ragged D={D} T={T}")
+    case = random_case(2, T, 3, D, window=11, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.2, "local": 0.4, "full": 0.4}, seed=T * 7 + D, device="cuda")
+    cache, out, status = run_prefill(tr, case, 11)
+    cache.close()
+    assert status == 0
+    check(case, out, 11, range(2), f"D={D} T={T}")
+
+
+@pytest.mark.parametrize("bw", [2, 4, 8, 16])
+@pytest.mark.parametrize("window", [0, 3, 1000])
+def test_prefill_single_width_windows(tr, bw, window):
+    say(f"prefill b={bw} w={window}")
+    case = random_case(1, 200, 2, 64, window=window, bit_weights={bw: 1.0},
+                       mode_weights={"local": 0.5, "full": 0.5}, seed=bw * 31 + window, device="cuda")
+    cache, out, status = run_prefill(tr, case, window)
+    cache.close()
+    assert status == 0
+    check(case, out, window, [0], f"b={bw} w={window}")
+
+
+def test_prefill_all_skip_zero_and_own_value(tr):
+    case = random_case(1, 70, 2, 64, window=0, bit_weights={4: 1.0}, mode_weights={"skip": 1.0},
+                       seed=3, device="cuda")
+    cache, out, status = run_prefill(tr, case, 0)
+    cache.close()
+    assert status == 0 and torch.count_nonzero(out.float()) == 0
+    case["mode"].fill_(1)                                        # local with w = 0: own v_hat
+    cache, out, status = run_prefill(tr, case, 0)
+    cache.close()
+    check(case, out, 0, [0], "local w=0")
+
+
+def test_prefill_chunked_matches_oracle(tr):
+    say("prefill in three chunks (later queries read earlier chunks)")
+    case = random_case(2, 400, 3, 64, window=50, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.1, "local": 0.4, "full": 0.5}, seed=12, device="cuda")
+    cache, out, status = run_prefill(tr, case, 50, cuts=[97, 256])
+    cache.close()
+    assert status == 0
+    check(case, out, 50, range(2), "chunked")
+
+
+def test_prefill_then_decode_agree(tr):
+    say("decode after prefill equals the last prefill row")
+    B, T, H, D, w = 2, 257, 4, 128, 40
+    case = random_case(B, T, H, D, window=w, bit_weights={2: 0.3, 4: 0.4, 8: 0.2, 16: 0.1},
+                       mode_weights={"local": 0.5, "full": 0.5}, seed=21, device="cuda")
+    _, out_full, _ = run_prefill(tr, case, w)
+    cache = tr.tr_kv_cache_alloc(1, B, H, D, T)
+    part = torch.empty((B, T - 1, H, D), dtype=torch.bfloat16, device="cuda")
+    sl = lambda x, a, b: case[x][:, a:b].contiguous()
+    tr.tr_routed_attn_prefill(cache, 0, sl("q", 0, T - 1), sl("k", 0, T - 1), sl("v", 0, T - 1),
+                              sl("bits", 0, T - 1), sl("mode", 0, T - 1), T - 1, w, part)
+    tr.tr_kv_quantize_write(cache, 0, sl("k", T - 1, T), sl("v", T - 1, T), sl("bits", T - 1, T))
+    dec = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    tr.tr_routed_attn_decode(cache, 0, case["q"][:, T - 1].contiguous(), case["mode"][:, T - 1].contiguous(), w, dec)
+    assert tr.tr_kv_cache_status(cache) == 0
+    cache.close()
+    a, b = bf16_to_f64(out_full[:, T - 1]), bf16_to_f64(dec)
+    refs = oracle_prefill(case, w, range(B))
+    for s in range(B):
+        compare_out(a[s], refs[s][T - 1], f"prefill last row seq {s}")
+        compare_out(b[s], refs[s][T - 1], f"decode seq {s}")
+
+
+def test_prefill_page_size_invariance(tr):
+    case = random_case(1, 300, 2, 64, window=30, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.2, "local": 0.4, "full": 0.4}, seed=5, device="cuda")
+    outs = []
+    for pcb in (1024, 4096, 32768):
+        cache, out, _ = run_prefill(tr, case, 30, page_code_bytes=pcb)
+        cache.close()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_prefill_config2_layer_full_size(tr):
+    cfg = CONFIGS[2]
+    say(f"prefill {cfg.name}, layer 5 of a 12-layer workload, all sequences")
+    case = layer_inputs(cfg, 5, device="cuda")
+    cache, out, status = run_prefill(tr, case, cfg.window, layers=2, layer=1)
+    cache.close()
+    assert status == 0
+    check(case, out, cfg.window, range(cfg.batch), cfg.name)
+
+
+def test_prefill_bad_mode_is_flagged(tr):
+    case = random_case(1, 40, 2, 64, window=3, bit_weights={4: 1.0}, mode_weights={"full": 1.0},
+                       seed=2, device="cuda")
+    case["mode"][0, 7, 1] = 5
+    cache, out, status = run_prefill(tr, case, 3)
+    cache.close()
+    assert status == 6
+    assert torch.count_nonzero(out[0, 7, 1].float()) == 0
