@@ -19,6 +19,7 @@
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kAssignBlock = 1024;
 
 __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -49,10 +50,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 }
 
 // One workgroup per sequence.  Classes are counted in two 32-bit words of 16-bit fields
-// (classes 0|1 and 2|3); a 256-token chunk adds at most 256 to a field.
-__global__ __launch_bounds__(kBlock) void k_assign_slots(CacheLayout c, int layer, int p0, int n,
-                                                         const uint8_t* __restrict__ bits) {
-  __shared__ uint32_t wsum[2][kBlock / 64];
+// (classes 0|1 and 2|3); a chunk of kAssignBlock tokens adds at most 1024 to a field.
+__global__ __launch_bounds__(kAssignBlock) void k_assign_slots(CacheLayout c, int layer, int p0, int n,
+                                                               const uint8_t* __restrict__ bits) {
+  __shared__ uint32_t wsum[2][kAssignBlock / 64];
   __shared__ int32_t base[TR_NCLASS];
   const int s = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void k_assign_slots(CacheLayout c, int laye
 #pragma unroll
   for (int k = 0; k < TR_NCLASS; ++k) n0[k] = base[k];
 
-  for (int chunk = 0; chunk < n; chunk += kBlock) {
+  for (int chunk = 0; chunk < n; chunk += kAssignBlock) {
     const int i = chunk + tid;
     uint32_t a = 0, b = 0;
     if (i < n) {
@@ -79,9 +80,10 @@ __global__ __launch_bounds__(kBlock) void k_assign_slots(CacheLayout c, int laye
     __syncthreads();
     uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
-      if (w < wave) { pa += wsum[0][w]; pb += wsum[1][w]; }
-      ta += wsum[0][w]; tb += wsum[1][w];
+    for (int w = 0; w < kAssignBlock / 64; ++w) {
+      const uint32_t xa = wsum[0][w], xb = wsum[1][w];
+      if (w < wave) { pa += xa; pb += xb; }
+      ta += xa; tb += xb;
     }
     ia += pa; ib += pb;
     if (i < n) {
@@ -119,28 +121,15 @@ __global__ __launch_bounds__(kBlock) void k_assign_slots(CacheLayout c, int laye
   }
 }
 
-// One group = one (token, head) K or V vector of D bf16 values, handled by D/8 lanes.
+// Eq. (4) on one group = one (token, head) K or V vector of D bf16 values, held by the D/8
+// lanes that call this together (8 values each, one 128-bit load); the lanes shuffle, so every
+// lane of the group must call it, `live` or not.
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int layer, int p0, int n,
-                                                           const uint16_t* __restrict__ kin,
-                                                           const uint16_t* __restrict__ vin,
-                                                           const uint8_t* __restrict__ bits) {
+__device__ __forceinline__ void quantize_group(const CacheLayout& c, int layer, int s, int p, int h, int kv, int part,
+                                               bool live, const uint16_t* src, int bval) {
 #pragma clang fp contract(off)
   constexpr int LPG = D / 8;
-  const int64_t ngroups = (int64_t)c.B * n * c.H * 2;
-  const int64_t gid = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / LPG;
-  const int part = threadIdx.x % LPG;
-  const bool live = gid < ngroups;
-  const int64_t g = live ? gid : 0;
-  const int kv = (int)(g & 1);
-  const int64_t th = g >> 1;
-  const int h = (int)(th % c.H);
-  const int64_t tok = th / c.H;
-  const int s = (int)(tok / n), i = (int)(tok % n);
-  const int p = p0 + i;
-
-  const uint16_t* src = (kv ? vin : kin) + ((tok * c.H + h) * D + part * 8);
-  uint4 raw = live ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+  uint4 raw = live ? *reinterpret_cast<const uint4*>(src + part * 8) : make_uint4(0, 0, 0, 0);
   float x[8];
   x[0] = tr_bf16_lo(raw.x); x[1] = tr_bf16_hi(raw.x);
   x[2] = tr_bf16_lo(raw.y); x[3] = tr_bf16_hi(raw.y);
@@ -156,8 +145,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int la
   }
   if (!live) return;
 
-  int cls = tr_class_of_bits(bits[(int64_t)s * n + i]);
-  if (cls < 0) cls = 3;                                // flagged by k_assign_slots
+  int cls = tr_class_of_bits(bval);
+  if (cls < 0) cls = 3;                                // flagged by the slot assignment
   const int32_t slot = tr_prefix_row(c, layer, s, p)[cls];
   const int P = c.ptok[cls];
   const int32_t page = tr_ptab(c, layer, s, cls)[slot / P];
@@ -209,6 +198,90 @@ __global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int la
     w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
     w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
     reinterpret_cast<uint2*>(row)[part] = w;
+  }
+}
+
+// Grid-wide quantize of n tokens per sequence (after k_assign_slots).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int layer, int p0, int n,
+                                                           const uint16_t* __restrict__ kin,
+                                                           const uint16_t* __restrict__ vin,
+                                                           const uint8_t* __restrict__ bits) {
+  constexpr int LPG = D / 8;
+  const int64_t ngroups = (int64_t)c.B * n * c.H * 2;
+  const int64_t gid = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / LPG;
+  const int part = threadIdx.x % LPG;
+  const bool live = gid < ngroups;
+  const int64_t g = live ? gid : 0;
+  const int kv = (int)(g & 1);
+  const int64_t th = g >> 1;
+  const int h = (int)(th % c.H);
+  const int64_t tok = th / c.H;
+  const int s = (int)(tok / n), i = (int)(tok % n);
+  const uint16_t* src = (kv ? vin : kin) + (tok * c.H + h) * D;
+  quantize_group<D>(c, layer, s, p0 + i, h, kv, part, live, src, live ? bits[(int64_t)s * n + i] : 16);
+}
+
+// Small appends (n <= 64 tokens per sequence, e.g. one decode step): slot assignment, page
+// allocation and quantization of one sequence in one workgroup -- a single launch.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_write_small(CacheLayout c, int layer, int p0, int n,
+                                                        const uint16_t* __restrict__ kin,
+                                                        const uint16_t* __restrict__ vin,
+                                                        const uint8_t* __restrict__ bits) {
+  constexpr int LPG = D / 8;
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    uint32_t a = 0, b = 0;
+    if (lane < n) {
+      int cls = tr_class_of_bits(bits[(int64_t)s * n + lane]);
+      if (cls < 0) {
+        atomicOr(c.err, TR_ERRF_BAD_BITS);
+        cls = 3;
+      }
+      if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
+    }
+    const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    const int32_t* pre0 = tr_prefix_row(c, layer, s, p0);
+    const int n0[4] = {pre0[0], pre0[1], pre0[2], pre0[3]};
+    if (lane < n) {
+      int4 v;
+      v.x = n0[0] + (int)(ia & 0xffffu);
+      v.y = n0[1] + (int)(ia >> 16);
+      v.z = n0[2] + (int)(ib & 0xffffu);
+      v.w = n0[3] + (int)(ib >> 16);
+      *reinterpret_cast<int4*>(const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + lane + 1))) = v;
+    }
+    const uint32_t ta = __shfl(ia, 63, 64), tb = __shfl(ib, 63, 64);
+    if (lane < TR_NCLASS) {
+      const int k = lane;
+      const int tot = k == 0 ? (int)(ta & 0xffffu) : k == 1 ? (int)(ta >> 16) : k == 2 ? (int)(tb & 0xffffu) : (int)(tb >> 16);
+      const int P = c.ptok[k];
+      const int first = (n0[k] + P - 1) / P, last = (n0[k] + tot + P - 1) / P;
+      int32_t* pt = tr_ptab(c, layer, s, k);
+      int reuse = first;
+      while (reuse < last && pt[reuse] >= 0) ++reuse;
+      const int need = last - reuse;
+      if (need > 0) {
+        const int id0 = atomicAdd(c.next_page, need);
+        const bool ok = (int64_t)id0 + need <= c.pool_pages;
+        if (!ok) atomicOr(c.err, TR_ERRF_NO_PAGES);
+        for (int j = 0; j < need; ++j) pt[reuse + j] = ok ? id0 + j : -1;
+      }
+    }
+  }
+  __syncthreads();
+  const int ngroups = n * c.H * 2;
+  const int part = tid % LPG;
+  for (int g0 = 0; g0 < ngroups; g0 += kBlock / LPG) {
+    const int gid = g0 + tid / LPG;
+    const bool live = gid < ngroups;
+    const int g = live ? gid : 0;
+    const int kv = g & 1, th = g >> 1;
+    const int h = th % c.H, i = th / c.H;
+    const uint16_t* src = (kv ? vin : kin) + (((int64_t)s * n + i) * c.H + h) * D;
+    quantize_group<D>(c, layer, s, p0 + i, h, kv, part, live, src, live ? bits[(int64_t)s * n + i] : 16);
   }
 }
 
@@ -277,7 +350,15 @@ tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, 
                           const uint8_t* bits, int n, hipStream_t stream) {
   const CacheLayout& L = c->lay;
   TrProfScope prof(c, TR_PROF_WRITE, stream);
-  hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kBlock), 0, stream, L, layer, p0, n, bits);
+  if (n <= 64) {
+    if (L.D == 64)
+      hipLaunchKernelGGL(k_write_small<64>, dim3(L.B), dim3(kBlock), 0, stream, L, layer, p0, n, k, v, bits);
+    else
+      hipLaunchKernelGGL(k_write_small<128>, dim3(L.B), dim3(kBlock), 0, stream, L, layer, p0, n, k, v, bits);
+    TR_LAUNCH_CHECK();
+    return TR_OK;
+  }
+  hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kAssignBlock), 0, stream, L, layer, p0, n, bits);
   TR_LAUNCH_CHECK();
   const int64_t lanes = (int64_t)L.B * n * L.H * 2 * (L.D / 8);
   const int grid = (int)((lanes + kBlock - 1) / kBlock);
@@ -347,6 +428,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
     const int b = 2 << k;
     L.rowb[k] = L.D * b / 8;
     L.ptok[k] = cb / L.rowb[k];
+    L.ptok_log2[k] = 0;
+    while ((1 << L.ptok_log2[k]) < L.ptok[k]) ++L.ptok_log2[k];
     int64_t off = align256(4LL * L.ptok[k]);
     L.k_off[k] = (int32_t)off; off += (int64_t)L.H * cb;
     L.v_off[k] = (int32_t)off; off += (int64_t)L.H * cb;
@@ -370,7 +453,10 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   if (L.pool_pages > 0x7fffffffLL) { delete c; return TR_ERR_UNSUPPORTED; }
 
   c->len.assign(L.L, 0);
-  c->max_chunks = (L.N + 255) / 256 + 1;
+  {
+    const int min_chunk = tr_decode_max_chunk(L) < TR_DECODE_MIN_CHUNK ? tr_decode_max_chunk(L) : TR_DECODE_MIN_CHUNK;
+    c->max_chunks = (L.N + min_chunk - 1) / min_chunk + 1;
+  }
   (void)hipGetDevice(&c->device);
   bool ok = true;
   ok = ok && hipMalloc((void**)&L.pool, (size_t)(L.pool_pages * L.page_bytes)) == hipSuccess;

@@ -27,6 +27,19 @@ struct tr_kv_cache {
   std::vector<hipEvent_t> ev_free;
 };
 
+// Decode work items: at most TR_DECODE_ITEM_MAX positions (LDS score buffer) and at most
+// TR_DECODE_PG_MAX page ids per width class (LDS page list); the host never picks chunks below
+// TR_DECODE_MIN_CHUNK positions unless those limits force it.
+#define TR_DECODE_ITEM_MAX 512
+#define TR_DECODE_PG_MAX 34
+#define TR_DECODE_MIN_CHUNK 256
+
+// Largest decode chunk (positions) this layout allows.
+inline int tr_decode_max_chunk(const CacheLayout& L) {
+  const int by_pages = (TR_DECODE_PG_MAX - 2) * L.ptok[3];
+  return by_pages < TR_DECODE_ITEM_MAX ? by_pages : TR_DECODE_ITEM_MAX;
+}
+
 // Kernel families reported by tr_profile_read.
 enum { TR_PROF_WRITE = 0, TR_PROF_DECODE_SPLIT = 1, TR_PROF_DECODE_COMBINE = 2, TR_PROF_PREFILL_COMPACT = 3,
        TR_PROF_PREFILL_ATTN = 4, TR_PROF_NFAM = 5 };

@@ -7,17 +7,24 @@
 // prefix counts, to one contiguous slot range per width class, so out-of-window keys are
 // never read and each inner loop runs over a single width (wave-uniform unpacking).
 //
-// k_decode_split (one workgroup per (seq, head, chunk)):
-//   phase 1  K codes -> scores in LDS: 8/16-byte loads per lane, codes unpacked in
-//            registers, dot with q in fp32, reduced across the lanes of a key; the zero
-//            point folds in as s * (q . c) + z * sum(q) (exact identity of Eq. (4)'s
-//            reconstruction), scaled into the log2 domain.
+// k_decode: one wavefront = one workgroup = one (seq, head, chunk) work item, with no
+// cross-wave synchronization, so every wave streams independently.
+//   prologue the chunk's page ids of every class and q -> LDS.
+//   phase 1  K codes -> scores in LDS.  Each lane takes a 16/32-byte slice of a key row;
+//            batches of keys are software-pipelined (the next batch is in flight while the
+//            current one is computed).  2- and 4-bit codes become bf16 (128 + c) by an OR
+//            into the mantissa and go through v_dot2_f32_bf16 with bf16 q pairs; 8-bit codes
+//            use byte converts and fp32 FMA; bf16 keys use v_dot2 directly.  Partial dots are
+//            reduced across the lanes of the key.  The zero point folds out as
+//            s * (q . c) + z * sum(q) (an exact identity of Eq. (4)'s reconstruction); scores
+//            are kept in the log2 domain.
 //   softmax  chunk max m, p = 2^(score - m), l = sum p (fp32).
-//   phase 2  V codes: every lane owns 16 fixed channels of a key, so all width classes
-//            accumulate into the same 16 fp32 registers: acc += (p * s_v) * c,
-//            plus sum(p * z_v) once per key.
-//   output   partial (o[D], m, l) per chunk.
-// k_decode_combine: log-sum-exp merge of the chunks -> bf16; zeros for skip heads.
+//   phase 2  V codes, pipelined the same way: each lane owns 32 fixed channels of a key, so
+//            all width classes accumulate into the same 32 fp32 registers:
+//            acc += (p * s_v) * c, plus sum(p * z_v) once per key.
+//   epilogue a one-chunk window writes bf16 out directly; otherwise the chunk writes
+//            (o[D], m, l).  Skip heads: chunk 0 writes zeros.
+// k_decode_combine: log-sum-exp merge of multi-chunk windows -> bf16.
 #include <math.h>
 #include <stdlib.h>
 
@@ -25,157 +32,261 @@
 
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kMaxChunkPositions = 4096;
+constexpr int kWave = 64;
+constexpr int kItemMax = TR_DECODE_ITEM_MAX;
+constexpr int kPgMax = TR_DECODE_PG_MAX;
+constexpr int kMinChunk = TR_DECODE_MIN_CHUNK;
 
-template <int B>
-__device__ __forceinline__ uint32_t code_at(const uint32_t* w, int k) {
-  return (w[(k * B) >> 5] >> ((k * B) & 31)) & ((1u << B) - 1u);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+// bf16 bit pattern of a float that holds a bf16 value (q is bf16 on input, so this is exact).
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return __float_as_uint(x) >> 16; }
+
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return v;
 }
 
-__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  return v;
+}
+
+// Codes of b bits, element e of a little-endian packed slice, as floats, in groups that map to
+// byte converts: for b = 2 the mask (w >> 2k) & 0x03030303 holds elements 4i + k in byte i;
+// b = 4: (w >> 4k) & 0x0f0f0f0f holds 2i + k; b = 8: byte i is element i.
+template <int B, int NW>
+__device__ __forceinline__ void unpack_codes(const uint32_t* w, float* out) {
+#pragma unroll
+  for (int d = 0; d < NW; ++d) {
+    if constexpr (B == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t m = (w[d] >> (2 * k)) & 0x03030303u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[16 * d + 4 * i + k] = (float)((m >> (8 * i)) & 0xffu);
+      }
+    } else if constexpr (B == 4) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t m = (w[d] >> (4 * k)) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[8 * d + 2 * i + k] = (float)((m >> (8 * i)) & 0xffu);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[4 * d + i] = (float)((w[d] >> (8 * i)) & 0xffu);
+    }
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
+  if constexpr (NW == 1) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (NW == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    w[0] = t.x; w[1] = t.y;
+  } else {
+#pragma unroll
+    for (int x = 0; x < NW / 4; ++x) {
+      const uint4 t = reinterpret_cast<const uint4*>(p)[x];
+      w[4 * x] = t.x; w[4 * x + 1] = t.y; w[4 * x + 2] = t.z; w[4 * x + 3] = t.w;
+    }
+  }
+}
+
+// One batch of U keys (one sub-iteration of KPW keys per u) of class C: codes and (s, z).
+template <int U, int NW, bool SIDE>
+struct Batch {
+  uint32_t w[U][NW];
+  float2 sz[U];
+};
+
+template <int U, int NW, bool SIDE, int LPK>
+__device__ __forceinline__ void load_batch(Batch<U, NW, SIDE>& bt, const CacheLayout& c, const int32_t* pg, int first,
+                                           int lp, int pm, int base, int e, int kslot, int64_t code_off,
+                                           int64_t side_off, int rowb) {
+  constexpr int KPW = kWave / LPK;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = min(base + u * KPW + kslot, e - 1);    // clamped: loads never branch
+    const int page = pg[(j >> lp) - first];
+    const int slot = j & pm;
+    const uint8_t* pb = c.pool + (int64_t)page * c.page_bytes;
+    load_words<NW>(pb + code_off + (int64_t)slot * rowb, bt.w[u]);
+    if constexpr (SIDE) bt.sz[u] = reinterpret_cast<const float2*>(pb + side_off)[slot];
+  }
 }
 
 // Phase 1 for width class C over class slots [a, e): scores into sc[off + (j - a)].
+// Lane slices: 16 bytes (b = 2, 4, 8) or 32 bytes (b = 16) of one key row.
+//   b = 2, 4: code pairs are ORed into bf16 mantissas (value 128 + c, exact) and dotted with
+//             bf16 q pairs by v_dot2_f32_bf16; the 128 * sum(q) offset is removed with the
+//             zero point: score = s * dot + (z - 128 s) * sum(q).
+//   b = 8:    byte converts and fp32 FMA.
+//   b = 16:   native bf16 pairs straight into v_dot2_f32_bf16.
 template <int D, int C>
-__device__ __forceinline__ void score_phase(const CacheLayout& c, int layer, int s, int h, int a, int e, int off,
-                                            const float* qs, float sigma, float kscale, float* sc) {
+__device__ __forceinline__ void score_phase(const CacheLayout& c, const int32_t* pg, int first, int h, int a, int e,
+                                            int off, const float* qs, float sigma, float kscale, float* sc) {
   constexpr int b = 2 << C;
-  constexpr int KBL = (C == 0) ? 8 : 16;           // bytes per lane per key
-  constexpr int E = KBL * 8 / b;                   // elements per lane
-  constexpr int LPK = D * b / 8 / KBL;             // lanes per key
-  constexpr int KPI = kBlock / LPK;                // keys per block iteration
-  constexpr int W = KBL / 4;
-  const int tid = threadIdx.x;
-  const int part = tid % LPK;
-  float qr[E];
+  constexpr int SB = (C == 3) ? 32 : 16;           // slice bytes per lane per key
+  constexpr int E = SB * 8 / b;                    // elements per lane
+  constexpr int LPK = D * b / 8 / SB;              // lanes per key
+  constexpr int KPW = kWave / LPK;                 // keys per wave sub-iteration
+  constexpr int NW = SB / 4;
+#ifndef TR_DECODE_U1
+#define TR_DECODE_U1 4
+#endif
+  constexpr int U = (C == 3) ? 1 : TR_DECODE_U1;   // sub-iterations per batch
+  constexpr int NQ = (C == 2) ? 1 : E / 2;
+  const int lane = threadIdx.x;
+  const int part = lane % LPK, kslot = lane / LPK;
+  const float* qv = qs + part * E;
+  uint32_t qp[NQ];
+  float qf[(C == 2) ? E : 1];
+  if constexpr (C == 0) {
 #pragma unroll
-  for (int k = 0; k < E; ++k) qr[k] = qs[part * E + k];
-  const int32_t* pt = tr_ptab(c, layer, s, C);
-  const int P = c.ptok[C];
-  const int64_t hoff = (int64_t)h * c.cb + part * KBL;
-  for (int base = a; base < e; base += KPI) {
-    const int j = base + tid / LPK;
-    const bool valid = j < e;
-    float dot = 0.0f, sK = 1.0f, zK = 0.0f;
-    if (valid) {
-      const int page = pt[j / P];
-      const int slot = j % P;
-      const uint8_t* pb = c.pool + (int64_t)page * c.page_bytes;
-      const uint8_t* row = pb + c.k_off[C] + hoff + (int64_t)slot * (D * b / 8);
-      uint32_t w[W];
-      if constexpr (W == 2) {
-        const uint2 t = *reinterpret_cast<const uint2*>(row);
-        w[0] = t.x; w[1] = t.y;
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qp[8 * d + k] = bf16_bits(qv[16 * d + k]) | (bf16_bits(qv[16 * d + k + 8]) << 16);
+  } else if constexpr (C == 1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qp[4 * d + k] = bf16_bits(qv[8 * d + k]) | (bf16_bits(qv[8 * d + k + 4]) << 16);
+  } else if constexpr (C == 2) {
+#pragma unroll
+    for (int k = 0; k < E; ++k) qf[k] = qv[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) qp[k] = bf16_bits(qv[2 * k]) | (bf16_bits(qv[2 * k + 1]) << 16);
+  }
+  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1;
+  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + part * SB;
+  const int64_t side_off = c.sk_off[C] + (int64_t)h * c.ptok[C] * 8;
+  constexpr int RB = D * b / 8;
+  constexpr int STEP = KPW * U;
+  Batch<U, NW, (C < 3)> cur, nxt;
+  load_batch<U, NW, (C < 3), LPK>(cur, c, pg, first, lp, pm, a, e, kslot, code_off, side_off, RB);
+  for (int base = a; base < e; base += STEP) {
+    if (base + STEP < e) load_batch<U, NW, (C < 3), LPK>(nxt, c, pg, first, lp, pm, base + STEP, e, kslot, code_off,
+                                                        side_off, RB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.0f;
+      if constexpr (C == 0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            dot = dot2(((cur.w[u][d] >> (2 * k)) & 0x00030003u) | 0x43004300u, qp[8 * d + k], dot);
+      } else if constexpr (C == 1) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            dot = dot2(((cur.w[u][d] >> (4 * k)) & 0x000f000fu) | 0x43004300u, qp[4 * d + k], dot);
+      } else if constexpr (C == 2) {
+        float cf[E];
+        unpack_codes<8, NW>(cur.w[u], cf);
+#pragma unroll
+        for (int k = 0; k < E; ++k) dot = fmaf(qf[k], cf[k], dot);
       } else {
-        const uint4 t = *reinterpret_cast<const uint4*>(row);
-        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) dot = dot2(cur.w[u][k], qp[k], dot);
       }
-      if constexpr (C < 3) {
-        const float2 sz = reinterpret_cast<const float2*>(pb + c.sk_off[C])[(int64_t)h * P + slot];
-        sK = sz.x;
-        zK = sz.y;
 #pragma unroll
-        for (int k = 0; k < E; ++k) dot = fmaf(qr[k], (float)code_at<b>(w, k), dot);
+      for (int o = 1; o < LPK; o <<= 1) dot += __shfl_xor(dot, o, 64);
+      const int j = base + u * KPW + kslot;
+      if (j < e && part == 0) {
+        float x;
+        if constexpr (C < 2) x = fmaf(cur.sz[u].x, dot, fmaf(-128.0f, cur.sz[u].x, cur.sz[u].y) * sigma);
+        else if constexpr (C == 2) x = fmaf(cur.sz[u].x, dot, cur.sz[u].y * sigma);
+        else x = dot;
+        sc[off + (j - a)] = x * kscale;
+      }
+    }
+    cur = nxt;
+  }
+}
+
+// Phase 2 for width class C: acc[32] (channels 32*part ..) += p * v_hat.
+template <int D, int C>
+__device__ __forceinline__ void value_phase(const CacheLayout& c, const int32_t* pg, int first, int h, int a, int e,
+                                            int off, const float* pw, float* acc, float& zacc) {
+  constexpr int b = 2 << C;
+  constexpr int VLPK = D / 32;                     // lanes per key
+  constexpr int KPW = kWave / VLPK;
+  constexpr int NW = b;                            // 32 codes of b bits = b words
+#ifndef TR_DECODE_U2
+#define TR_DECODE_U2 2
+#endif
+  constexpr int U = (C == 0) ? TR_DECODE_U2 : 1;
+  constexpr int RB = D * b / 8;
+  constexpr int STEP = KPW * U;
+  const int lane = threadIdx.x;
+  const int part = lane % VLPK, kslot = lane / VLPK;
+  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1;
+  const int64_t code_off = c.v_off[C] + (int64_t)h * c.cb + part * (4 * b);
+  const int64_t side_off = c.sv_off[C] + (int64_t)h * c.ptok[C] * 8;
+  Batch<U, NW, (C < 3)> cur, nxt;
+  load_batch<U, NW, (C < 3), VLPK>(cur, c, pg, first, lp, pm, a, e, kslot, code_off, side_off, RB);
+  for (int base = a; base < e; base += STEP) {
+    if (base + STEP < e) load_batch<U, NW, (C < 3), VLPK>(nxt, c, pg, first, lp, pm, base + STEP, e, kslot,
+                                                         code_off, side_off, RB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jr = base + u * KPW + kslot;
+      const float p = (jr < e) ? pw[off + (min(jr, e - 1) - a)] : 0.0f;
+      if constexpr (C < 3) {
+        const float ps = p * cur.sz[u].x;
+        if (part == 0) zacc = fmaf(p, cur.sz[u].y, zacc);
+        float cf[32];
+        unpack_codes<b, NW>(cur.w[u], cf);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) acc[k] = fmaf(ps, cf[k], acc[k]);
       } else {
 #pragma unroll
-        for (int k = 0; k < E / 2; ++k) {
-          dot = fmaf(qr[2 * k], tr_bf16_lo(w[k]), dot);
-          dot = fmaf(qr[2 * k + 1], tr_bf16_hi(w[k]), dot);
+        for (int k = 0; k < 16; ++k) {
+          acc[2 * k] = fmaf(p, tr_bf16_lo(cur.w[u][k]), acc[2 * k]);
+          acc[2 * k + 1] = fmaf(p, tr_bf16_hi(cur.w[u][k]), acc[2 * k + 1]);
         }
       }
     }
-#pragma unroll
-    for (int o = 1; o < LPK; o <<= 1) dot += __shfl_xor(dot, o, 64);
-    if (valid && part == 0) sc[off + (j - a)] = fmaf(sK, dot, zK * sigma) * kscale;
+    cur = nxt;
   }
 }
 
-// Phase 2 for width class C: acc[16] (channels 16*part ..) += p * v_hat.
-template <int D, int C>
-__device__ __forceinline__ void value_phase(const CacheLayout& c, int layer, int s, int h, int a, int e, int off,
-                                            const float* pw, float* acc, float& zacc) {
-  constexpr int b = 2 << C;
-  constexpr int VLPK = D / 16;
-  constexpr int KPI = kBlock / VLPK;
-  constexpr int BYTES = 2 * b;                     // 16 codes of b bits
-  const int tid = threadIdx.x;
-  const int part = tid % VLPK;
-  const int32_t* pt = tr_ptab(c, layer, s, C);
-  const int P = c.ptok[C];
-  const int64_t hoff = (int64_t)h * c.cb + part * BYTES;
-  for (int base = a; base < e; base += KPI) {
-    const int j = base + tid / VLPK;
-    if (j >= e) continue;
-    const int page = pt[j / P];
-    const int slot = j % P;
-    const uint8_t* pb = c.pool + (int64_t)page * c.page_bytes;
-    const uint8_t* row = pb + c.v_off[C] + hoff + (int64_t)slot * (D * b / 8);
-    const float p = pw[off + (j - a)];
-    if constexpr (C < 3) {
-      const float2 sz = reinterpret_cast<const float2*>(pb + c.sv_off[C])[(int64_t)h * P + slot];
-      const float ps = p * sz.x;
-      if (part == 0) zacc = fmaf(p, sz.y, zacc);
-      uint32_t w[4];
-      if constexpr (b == 2) {
-        w[0] = *reinterpret_cast<const uint32_t*>(row);
-      } else if constexpr (b == 4) {
-        const uint2 t = *reinterpret_cast<const uint2*>(row);
-        w[0] = t.x; w[1] = t.y;
-      } else {
-        const uint4 t = *reinterpret_cast<const uint4*>(row);
-        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k) acc[k] = fmaf(ps, (float)code_at<b>(w, k), acc[k]);
-    } else {
-      const uint4 t0 = reinterpret_cast<const uint4*>(row)[0];
-      const uint4 t1 = reinterpret_cast<const uint4*>(row)[1];
-      const uint32_t w[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[2 * k] = fmaf(p, tr_bf16_lo(w[k]), acc[2 * k]);
-        acc[2 * k + 1] = fmaf(p, tr_bf16_hi(w[k]), acc[2 * k + 1]);
-      }
-    }
-  }
-}
-
+#ifndef TR_DECODE_WAVES
+#define TR_DECODE_WAVES 5
+#endif
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_decode_split(CacheLayout c, int layer, int t, int window, int CH, int nch_grid,
-                                                         int max_chunks, float kscale,
-                                                         const uint16_t* __restrict__ q,
-                                                         const uint8_t* __restrict__ mode,
-                                                         float* __restrict__ part) {
-  extern __shared__ float sc[];                    // [CH] scores, then weights
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_WAVES, 8))) void k_decode(CacheLayout c, int layer, int t, int window, int CH, int nch_grid,
+                                                  int max_chunks, float kscale, const uint16_t* __restrict__ q,
+                                                  const uint8_t* __restrict__ mode, float* __restrict__ part,
+                                                  uint16_t* __restrict__ out) {
   __shared__ float qs[D];
-  __shared__ float red[4];
-  __shared__ float ored[4][D + 1];
-  const int tid = threadIdx.x;
+  __shared__ float sc[kItemMax];
+  __shared__ int32_t pg[TR_NCLASS][kPgMax];
+  const int lane = threadIdx.x;
   const int k = blockIdx.x % nch_grid;
   const int sh = blockIdx.x / nch_grid;
   const int h = sh % c.H, s = sh / c.H;
   const int m = mode[sh];
-  if (m == TR_MODE_SKIP) return;
+  uint16_t* o = out + (int64_t)sh * D;
   if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) {
-    if (k == 0 && tid == 0) atomicOr(c.err, TR_ERRF_BAD_MODE);
+    if (k == 0) {
+#pragma unroll
+      for (int d = lane; d < D; d += kWave) o[d] = 0;
+      if (lane == 0 && m != TR_MODE_SKIP) atomicOr(c.err, TR_ERRF_BAD_MODE);
+    }
     return;
   }
   const int lo = (m == TR_MODE_FULL) ? 0 : max(0, t - window);
@@ -187,7 +298,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_split(CacheLayout c, int laye
 
   const int32_t* pa = tr_prefix_row(c, layer, s, p0);
   const int32_t* pe = tr_prefix_row(c, layer, s, p1);
-  int a[4], e[4], off[4];
+  int a[4], e[4], off[4], first[4];
   int nk = 0;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -195,80 +306,100 @@ __global__ __launch_bounds__(kBlock) void k_decode_split(CacheLayout c, int laye
     e[x] = pe[x];
     off[x] = nk;
     nk += e[x] - a[x];
+    first[x] = a[x] >> c.ptok_log2[x];
   }
-  if (tid < D) qs[tid] = tr_bf16_lo((uint32_t)q[(int64_t)sh * D + tid]);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    if (e[x] > a[x]) {
+      const int np = ((e[x] - 1) >> c.ptok_log2[x]) - first[x] + 1;
+      const int32_t* pt = tr_ptab(c, layer, s, x) + first[x];
+      for (int i = lane; i < np; i += kWave) pg[x][i] = pt[i];
+    }
+  }
+  float qpart = 0.0f;
+#pragma unroll
+  for (int d = lane; d < D; d += kWave) {
+    const float v = tr_bf16_lo((uint32_t)q[(int64_t)sh * D + d]);
+    qs[d] = v;
+    qpart += v;
+  }
+  const float sigma = wave_sum(qpart);
   __syncthreads();
-  float sigma = 0.0f;
-  for (int d = 0; d < D; ++d) sigma += qs[d];      // same order in every thread
 
-  if (e[0] > a[0]) score_phase<D, 0>(c, layer, s, h, a[0], e[0], off[0], qs, sigma, kscale, sc);
-  if (e[1] > a[1]) score_phase<D, 1>(c, layer, s, h, a[1], e[1], off[1], qs, sigma, kscale, sc);
-  if (e[2] > a[2]) score_phase<D, 2>(c, layer, s, h, a[2], e[2], off[2], qs, sigma, kscale, sc);
-  if (e[3] > a[3]) score_phase<D, 3>(c, layer, s, h, a[3], e[3], off[3], qs, sigma, kscale, sc);
+  if (e[0] > a[0]) score_phase<D, 0>(c, pg[0], first[0], h, a[0], e[0], off[0], qs, sigma, kscale, sc);
+  if (e[1] > a[1]) score_phase<D, 1>(c, pg[1], first[1], h, a[1], e[1], off[1], qs, sigma, kscale, sc);
+  if (e[2] > a[2]) score_phase<D, 2>(c, pg[2], first[2], h, a[2], e[2], off[2], qs, sigma, kscale, sc);
+  if (e[3] > a[3]) score_phase<D, 3>(c, pg[3], first[3], h, a[3], e[3], off[3], qs, sigma, kscale, sc);
   __syncthreads();
 
   float mx = -INFINITY;
-  for (int i = tid; i < nk; i += kBlock) mx = fmaxf(mx, sc[i]);
-  mx = block_reduce_max(mx, red);
+  for (int i = lane; i < nk; i += kWave) mx = fmaxf(mx, sc[i]);
+  mx = wave_max(mx);
   float lsum = 0.0f;
-  for (int i = tid; i < nk; i += kBlock) {
+  for (int i = lane; i < nk; i += kWave) {
     const float p = exp2f(sc[i] - mx);
     sc[i] = p;
     lsum += p;
   }
-  lsum = block_reduce_sum(lsum, red);              // contains the barrier before phase 2
+  lsum = wave_sum(lsum);
+  __syncthreads();
 
-  float acc[16];
+  float acc[32];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
+  for (int x = 0; x < 32; ++x) acc[x] = 0.0f;
   float zacc = 0.0f;
-  if (e[0] > a[0]) value_phase<D, 0>(c, layer, s, h, a[0], e[0], off[0], sc, acc, zacc);
-  if (e[1] > a[1]) value_phase<D, 1>(c, layer, s, h, a[1], e[1], off[1], sc, acc, zacc);
-  if (e[2] > a[2]) value_phase<D, 2>(c, layer, s, h, a[2], e[2], off[2], sc, acc, zacc);
-  if (e[3] > a[3]) value_phase<D, 3>(c, layer, s, h, a[3], e[3], off[3], sc, acc, zacc);
+  if (e[0] > a[0]) value_phase<D, 0>(c, pg[0], first[0], h, a[0], e[0], off[0], sc, acc, zacc);
+  if (e[1] > a[1]) value_phase<D, 1>(c, pg[1], first[1], h, a[1], e[1], off[1], sc, acc, zacc);
+  if (e[2] > a[2]) value_phase<D, 2>(c, pg[2], first[2], h, a[2], e[2], off[2], sc, acc, zacc);
+  if (e[3] > a[3]) value_phase<D, 3>(c, pg[3], first[3], h, a[3], e[3], off[3], sc, acc, zacc);
 
-  // Reduce over the key slots of the wave (lanes with the same channel group), then waves.
-  constexpr int VLPK = D / 16;
+  // Sum over the key slots (lanes with the same channel group); lane p < VLPK then holds
+  // channels [32 p, 32 p + 32).
+  constexpr int VLPK = D / 32;
 #pragma unroll
-  for (int o = VLPK; o < 64; o <<= 1) {
+  for (int o2 = VLPK; o2 < kWave; o2 <<= 1) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) acc[x] += __shfl_xor(acc[x], o, 64);
+    for (int x = 0; x < 32; ++x) acc[x] += __shfl_xor(acc[x], o2, 64);
   }
+  zacc = wave_sum(zacc);
+  if (nch == 1) {                                  // whole window in this chunk
+    if (lane < VLPK) {
+      const float inv = 1.0f / lsum;
+      uint32_t pk[16];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) zacc += __shfl_xor(zacc, o, 64);
-  const int wave = tid >> 6, lane = tid & 63;
+      for (int x = 0; x < 16; ++x)
+        pk[x] = (uint32_t)tr_f32_to_bf16((acc[2 * x] + zacc) * inv) |
+                ((uint32_t)tr_f32_to_bf16((acc[2 * x + 1] + zacc) * inv) << 16);
+      uint4* dst = reinterpret_cast<uint4*>(o + 32 * lane);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) dst[x] = make_uint4(pk[4 * x], pk[4 * x + 1], pk[4 * x + 2], pk[4 * x + 3]);
+    }
+    return;
+  }
+  float* dst = part + ((int64_t)sh * max_chunks + k) * (D + 2);
   if (lane < VLPK) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) ored[wave][lane * 16 + x] = acc[x];
+    for (int x = 0; x < 32; ++x) dst[32 * lane + x] = acc[x] + zacc;
   }
-  if (lane == 0) ored[wave][D] = zacc;
-  __syncthreads();
-  float* dst = part + ((int64_t)sh * max_chunks + k) * (D + 2);
-  if (tid < D) {
-    const float z = (ored[0][D] + ored[1][D]) + (ored[2][D] + ored[3][D]);
-    dst[tid] = (ored[0][tid] + ored[1][tid]) + (ored[2][tid] + ored[3][tid]) + z;
-  }
-  if (tid == 0) {
+  if (lane == 0) {
     dst[D] = mx;
     dst[D + 1] = lsum;
   }
 }
 
+// Log-sum-exp merge of the chunks of windows that span more than one chunk.
 template <int D>
-__global__ __launch_bounds__(D) void k_decode_combine(int H, int t, int window, int CH, int max_chunks,
+__global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH, int max_chunks,
                                                       const uint8_t* __restrict__ mode,
                                                       const float* __restrict__ part, uint16_t* __restrict__ out) {
   const int sh = blockIdx.x;
   const int d = threadIdx.x;
   const int m = mode[sh];
-  uint16_t* o = out + (int64_t)sh * D;
-  if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) {
-    o[d] = 0;
-    return;
-  }
+  if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) return;
   const int lo = (m == TR_MODE_FULL) ? 0 : max(0, t - window);
   const int L = t + 1 - lo;
   const int nch = (L + CH - 1) / CH;
+  if (nch == 1) return;                            // written by k_decode
   const float* base = part + (int64_t)sh * max_chunks * (D + 2);
   float M = -INFINITY;
   for (int k = 0; k < nch; ++k) M = fmaxf(M, base[(int64_t)k * (D + 2) + D]);
@@ -279,7 +410,7 @@ __global__ __launch_bounds__(D) void k_decode_combine(int H, int t, int window, 
     num = fmaf(wgt, pk[d], num);
     den = fmaf(wgt, pk[D + 1], den);
   }
-  o[d] = tr_f32_to_bf16(num / den);
+  out[(int64_t)sh * D + d] = tr_f32_to_bf16(num / den);
 }
 
 }  // namespace
@@ -290,36 +421,38 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
   const int t = c->len[layer] - 1;
   const int n = t + 1;
   const int BH = L.B * L.H;
-  int nch = (4096 + BH - 1) / BH;
+  const int max_ch = tr_decode_max_chunk(L);
+  // About 8192 work items if every head were full (a few times the waves the chip holds at
+  // once), but no chunk below kMinChunk positions.
+  int nch = (8192 + BH - 1) / BH;
   if (const char* env = getenv("TR_DECODE_NCH")) nch = atoi(env);
-  if (nch > (n + 63) / 64) nch = (n + 63) / 64;
-  if (nch < (n + kMaxChunkPositions - 1) / kMaxChunkPositions) nch = (n + kMaxChunkPositions - 1) / kMaxChunkPositions;
+  if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
+  if (nch < (n + max_ch - 1) / max_ch) nch = (n + max_ch - 1) / max_ch;
   if (nch > c->max_chunks) nch = c->max_chunks;
   if (nch < 1) nch = 1;
   const int CH = (n + nch - 1) / nch;
-  if (CH > kMaxChunkPositions) return TR_ERR_UNSUPPORTED;
+  if (CH > max_ch) return TR_ERR_UNSUPPORTED;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
-  const size_t lds = sizeof(float) * (size_t)CH;
   const int grid = BH * nch;
   {
     TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
     if (L.D == 64)
-      hipLaunchKernelGGL(k_decode_split<64>, dim3(grid), dim3(kBlock), lds, stream, L, layer, t, window, CH, nch,
-                         c->max_chunks, kscale, q, mode, c->partials);
+      hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
+                         c->max_chunks, kscale, q, mode, c->partials, out);
     else
-      hipLaunchKernelGGL(k_decode_split<128>, dim3(grid), dim3(kBlock), lds, stream, L, layer, t, window, CH, nch,
-                         c->max_chunks, kscale, q, mode, c->partials);
+      hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
+                         c->max_chunks, kscale, q, mode, c->partials, out);
     TR_LAUNCH_CHECK();
   }
-  {
+  if (nch > 1) {
     TrProfScope prof(c, TR_PROF_DECODE_COMBINE, stream);
     if (L.D == 64)
-      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, L.H, t, window, CH, c->max_chunks,
-                         mode, c->partials, out);
+      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, c->max_chunks, mode,
+                         c->partials, out);
     else
-      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, L.H, t, window, CH, c->max_chunks,
-                         mode, c->partials, out);
+      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, t, window, CH, c->max_chunks, mode,
+                         c->partials, out);
+    TR_LAUNCH_CHECK();
   }
-  TR_LAUNCH_CHECK();
   return TR_OK;
 }

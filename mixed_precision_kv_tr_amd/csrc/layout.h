@@ -34,7 +34,8 @@ struct CacheLayout {
   int32_t L, B, H, D, N;          // layers, batch, heads, head_dim, max_tokens
   int32_t cb;                     // code bytes per head per page (K or V)
   int32_t page_bytes;
-  int32_t ptok[TR_NCLASS];        // tokens per page
+  int32_t ptok[TR_NCLASS];        // tokens per page (a power of two)
+  int32_t ptok_log2[TR_NCLASS];
   int32_t rowb[TR_NCLASS];        // code bytes per (token, head): D * b / 8
   int32_t k_off[TR_NCLASS], v_off[TR_NCLASS], sk_off[TR_NCLASS], sv_off[TR_NCLASS];
   int32_t maxp[TR_NCLASS];        // page-table entries per (layer, seq, class)
