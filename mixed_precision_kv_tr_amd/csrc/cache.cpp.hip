@@ -400,7 +400,9 @@ static void free_all(tr_kv_cache* c) {
   (void)hipFree(c->partials);
   (void)hipFree(c->rows);
   (void)hipFree(c->row_counts);
-  (void)hipFree(c->done);
+  (void)hipFree(c->dk);
+  (void)hipFree(c->dv);
+  (void)hipFree(c->dsz);
   delete c;
 }
 
@@ -417,7 +419,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   memset(&c->lay, 0, sizeof(c->lay));
   c->partials = nullptr;
   c->rows = c->row_counts = nullptr;
-  c->done = nullptr;
+  c->dk = c->dv = nullptr;
+  c->dsz = nullptr;
   c->prof_on = false;
   CacheLayout& L = c->lay;
   L.L = d->num_layers; L.B = d->batch; L.H = d->num_heads; L.D = d->head_dim; L.N = d->max_tokens;
@@ -468,7 +471,10 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
                        sizeof(float) * (size_t)L.B * L.H * c->max_chunks * (L.D + 2)) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * L.H * L.N) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * L.H * 4) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->done, sizeof(uint32_t) * (size_t)L.B * L.H) == hipSuccess;
+  c->np = (L.N + 31) / 32 * 32;
+  ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->dsz, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;
   if (!ok) {
     hipGetLastError();
     free_all(c);
@@ -476,8 +482,6 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   }
   const int64_t npt = (int64_t)L.L * L.B * L.pt_stride;
   hipLaunchKernelGGL(k_fill_i32, dim3(grid_for(npt, kBlock)), dim3(kBlock), 0, 0, L.ptab, npt, -1);
-  hipLaunchKernelGGL(k_fill_i32, dim3(grid_for((int64_t)L.B * L.H, kBlock)), dim3(kBlock), 0, 0,
-                     (int32_t*)c->done, (int64_t)L.B * L.H, 0);
   hipLaunchKernelGGL(k_reset, dim3(grid_for((int64_t)L.L * L.B, kBlock)), dim3(kBlock), 0, 0, L);
   if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     free_all(c);

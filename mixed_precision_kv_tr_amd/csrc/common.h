@@ -19,7 +19,14 @@ struct tr_kv_cache {
   // prefill scratch: compacted query rows per (seq, head) [B][H][N] and counts [B][H][2]
   int32_t* rows;
   int32_t* row_counts;
-  uint32_t* done;                 // decode completion counters per (seq, head)
+  // prefill scratch: the cache range a prefill call reads, dequantized once, position order
+  //   dk [B][H][NP][D] uint16: K code as a bf16 integer (exact), or the stored bf16 (b = 16)
+  //   dv [B][H][D][NP] uint16: v_hat = s * c + z as fp16, channel-major
+  //   dsz [B][H][NP] float2:   (s_K, z_K) * log2(e) / sqrt(D); (log2(e)/sqrt(D), 0) for b = 16
+  int32_t np;                     // N rounded up to a multiple of 32
+  uint16_t* dk;
+  uint16_t* dv;
+  float2* dsz;
   // optional kernel timing (tr_profile_enable): HIP events around each kernel launch
   bool prof_on;
   struct ProfRec { int fam; hipEvent_t a, b; };

@@ -5,19 +5,22 @@
 // k_prefill_compact (one workgroup per (seq, head)): stable partition of the T query rows
 //   by mode -- full rows, then local rows -- so that a 128-row tile holds one mode and its
 //   key range is tight; skip rows (and rows with an invalid mode) get zeros right here.
-// k_prefill_attn (one workgroup = 4 waves = one 128-row tile):
-//   key range of the tile = union of its rows' windows, mapped through the class prefix
-//   counts to one slot range per width class; the four ranges are walked as one virtual
-//   stream in 32-key tiles.  Per tile:
-//     staging   K codes -> LDS as bf16 integers (exact; b = 16 keeps its bf16 bits), key-major;
-//               V -> v_hat = s*c + z in fp32 -> fp16, channel-major (transposed);
-//               per key alpha = s_K * log2(e)/sqrt(D), beta = z_K * log2(e)/sqrt(D), position.
+// k_prefill_dense (one workgroup per (seq, head, 32 positions)): the cache range the call's
+//   queries read, dequantized once into position-ordered scratch: K as its code in bf16
+//   (an exact integer <= 255, or the stored bf16 for b = 16) plus per-key
+//   (s_K, z_K) * log2(e)/sqrt(D); V as v_hat = s * c + z (fp32) rounded to fp16, stored
+//   channel-major.  Every 128-row tile of a (seq, head) then reads this instead of
+//   re-unpacking the pages (a (seq, head) stays on one XCD, so the re-reads hit its L2).
+// k_prefill_attn (one workgroup = 4 waves = one 128-row tile), per 32-key tile:
+//     staging   16-byte copies of K rows and V^T rows into double-buffered LDS, the next
+//               tile's copies in flight in registers while the current one is computed.
 //     QK^T      S^T[32 keys x 32 queries] per wave = v_mfma_f32_32x32x16_bf16 over D/16 steps;
 //               the score is alpha * (q . c) + beta * sum(q) -- Eq. (4)'s reconstruction
 //               folded out of the product, so K stays exact in the matrix cores.
-//     softmax   fp32 in registers, each lane holds 16 keys of one query; running max with a
-//               lazy rescale (only when the max grows by more than 2^8), mask only on tiles
-//               that cross a row's window edge; waves skip tiles outside their own window.
+//     softmax   fp32 in registers, each lane holds 16 keys of one query; running reference
+//               max with a lazy rescale (only when a row's max grows by more than 2^8);
+//               masks only on tiles that cross a row's window edge; waves skip tiles outside
+//               their own windows.
 //     PV        O^T[D x 32 queries] += V^T P^T with v_mfma_f32_32x32x16_f16; P is the lane's
 //               own scores (the key order of the S^T layout is mirrored in the V^T read).
 //   epilogue  O / l -> bf16, scattered back to the rows' original positions.
@@ -120,57 +123,141 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int e) {
   return (w[(e * NB) >> 5] >> ((e * NB) & 31)) & ((1u << NB) - 1u);
 }
 
-// Load the DPT codes (or bf16 values) of one thread's channel slice of a key row.
-template <int DPT>
-__device__ __forceinline__ void load_slice(const uint8_t* p, int b, uint32_t* w) {
-  const int bytes = DPT * b / 8;
-  if (bytes == 2) {
+template <int BYTES>
+__device__ __forceinline__ void load_slice_c(const uint8_t* p, uint32_t* w) {
+  if constexpr (BYTES == 2) {
     w[0] = *reinterpret_cast<const uint16_t*>(p);
-  } else if (bytes == 4) {
+  } else if constexpr (BYTES == 4) {
     w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if (bytes == 8) {
+  } else if constexpr (BYTES == 8) {
     const uint2 t = *reinterpret_cast<const uint2*>(p);
     w[0] = t.x; w[1] = t.y;
-  } else if (bytes == 16) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
-    w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
   } else {
-    const uint4 t0 = reinterpret_cast<const uint4*>(p)[0];
-    const uint4 t1 = reinterpret_cast<const uint4*>(p)[1];
-    w[0] = t0.x; w[1] = t0.y; w[2] = t0.z; w[3] = t0.w;
-    w[4] = t1.x; w[5] = t1.y; w[6] = t1.z; w[7] = t1.w;
+#pragma unroll
+    for (int x = 0; x < BYTES / 16; ++x) {
+      const uint4 t = reinterpret_cast<const uint4*>(p)[x];
+      w[4 * x] = t.x; w[4 * x + 1] = t.y; w[4 * x + 2] = t.z; w[4 * x + 3] = t.w;
+    }
   }
 }
 
-template <int DPT>
-__device__ __forceinline__ float code_f(const uint32_t* w, int b, int e) {
-  switch (b) {
-    case 2: return (float)code_at<2>(w, e);
-    case 4: return (float)code_at<4>(w, e);
-    default: return (float)code_at<8>(w, e);
+__device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// Dequantize DPL channels of one (token, head) K/V pair of width class C into the dense
+// scratch (K row slice) and the LDS V^T tile.
+template <int D, int C>
+__device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout& c, int h, int j, int part,
+                                            uint16_t* krow, _Float16 (*vt)[40], int tk, float2* szk_out) {
+  constexpr int DPL = D / 8;
+  constexpr int b = 2 << C;
+  constexpr int SLB = DPL * b / 8;                 // slice bytes
+  uint32_t wk[8], wv[8];
+  const int64_t off = (int64_t)h * c.cb + (int64_t)j * (D * b / 8) + part * SLB;
+  load_slice_c<SLB>(pb + c.k_off[C] + off, wk);
+  load_slice_c<SLB>(pb + c.v_off[C] + off, wv);
+  uint32_t ko[DPL / 2];
+  if constexpr (C == 3) {
+#pragma unroll
+    for (int e = 0; e < DPL / 2; ++e) {
+      ko[e] = wk[e];
+      vt[part * DPL + 2 * e][tk] = (_Float16)tr_bf16_lo(wv[e]);
+      vt[part * DPL + 2 * e + 1][tk] = (_Float16)tr_bf16_hi(wv[e]);
+    }
+    *szk_out = make_float2(1.0f, 0.0f);
+  } else {
+    const int P = c.ptok[C];
+    const float2 szk = reinterpret_cast<const float2*>(pb + c.sk_off[C])[(int64_t)h * P + j];
+    const float2 szv = reinterpret_cast<const float2*>(pb + c.sv_off[C])[(int64_t)h * P + j];
+#pragma unroll
+    for (int e = 0; e < DPL; e += 2) {
+      const float k0 = (float)code_at<b>(wk, e), k1 = (float)code_at<b>(wk, e + 1);
+      ko[e / 2] = (__float_as_uint(k0) >> 16) | (__float_as_uint(k1) & 0xffff0000u);
+      vt[part * DPL + e][tk] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
+      vt[part * DPL + e + 1][tk] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
+    }
+    *szk_out = szk;
+  }
+#pragma unroll
+  for (int x = 0; x < DPL / 8; ++x)
+    reinterpret_cast<uint4*>(krow)[x] = make_uint4(ko[4 * x], ko[4 * x + 1], ko[4 * x + 2], ko[4 * x + 3]);
+}
+
+// Positions [32 * tile0, 32 * tile0 + 32 * ntile) of every (seq, head); positions >= pend
+// are written as zeros (they are only ever read masked).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int layer, int tile0, int ntile, int pend,
+                                                          int np, float kscale, uint16_t* __restrict__ dk,
+                                                          uint16_t* __restrict__ dv, float2* __restrict__ dsz) {
+  constexpr int DPL = D / 8;
+  __shared__ _Float16 vt[D][40];                   // v_hat tile, channel-major (row = 80 B)
+  const int tile = tile0 + blockIdx.x % ntile, sh = blockIdx.x / ntile;
+  const int s = sh / c.H, h = sh % c.H;
+  const int tid = threadIdx.x, tk = tid / 8, part = tid % 8;
+  const int p = tile * 32 + tk;
+  uint16_t* krow = dk + ((int64_t)sh * np + p) * D + part * DPL;
+  float2 szk = make_float2(0.0f, 0.0f);
+  if (p < pend) {
+    const int32_t* pr0 = tr_prefix_row(c, layer, s, p);
+    const int32_t* pr1 = tr_prefix_row(c, layer, s, p + 1);
+    int cls = 3;
+#pragma unroll
+    for (int x = 0; x < TR_NCLASS; ++x)
+      if (pr1[x] != pr0[x]) cls = x;
+    const int32_t slot = pr0[cls];
+    const int32_t page = tr_ptab(c, layer, s, cls)[slot >> c.ptok_log2[cls]];
+    const int j = slot & (c.ptok[cls] - 1);
+    const uint8_t* pb = c.pool + (int64_t)(page < 0 ? 0 : page) * c.page_bytes;
+    switch (cls) {
+      case 0: dense_token<D, 0>(pb, c, h, j, part, krow, vt, tk, &szk); break;
+      case 1: dense_token<D, 1>(pb, c, h, j, part, krow, vt, tk, &szk); break;
+      case 2: dense_token<D, 2>(pb, c, h, j, part, krow, vt, tk, &szk); break;
+      default: dense_token<D, 3>(pb, c, h, j, part, krow, vt, tk, &szk); break;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < DPL / 8; ++x) reinterpret_cast<uint4*>(krow)[x] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vt[part * DPL + e][tk] = (_Float16)0.0f;
+  }
+  if (part == 0) dsz[(int64_t)sh * np + p] = make_float2(szk.x * kscale, szk.y * kscale);
+  __syncthreads();
+  // V^T rows: D rows x 32 positions (64 bytes each), 16 bytes per thread.
+  for (int x = tid; x < D * 4; x += kBlock) {
+    const int d = x >> 2, seg = x & 3;
+    const uint4 v = *reinterpret_cast<const uint4*>(&vt[d][seg * 8]);
+    *reinterpret_cast<uint4*>(dv + ((int64_t)sh * D + d) * np + tile * 32 + seg * 8) = v;
   }
 }
 
 template <int D>
-struct PrefillSmem {
-  uint16_t ks[BN][D + 8];      // K codes / bf16 values, key-major
-  _Float16 vt[D][BN + 8];      // v_hat, channel-major
-  float alpha[BN];
-  float beta[BN];
-  int32_t kpos[BN];
-  int32_t wrange[4][4];        // per wave: lo, hi, tmin, lomax
+struct PrefillTile {
+  uint16_t ks[BN][D + 8];      // K codes as bf16 integers / stored bf16, key-major
+  uint16_t vt[D][BN + 8];      // v_hat fp16, channel-major
+  float alpha[BN];             // s_K * log2(e) / sqrt(D)
+  float beta[BN];              // z_K * log2(e) / sqrt(D)
 };
 
-template <int D>
-__global__ __launch_bounds__(kBlock) void k_prefill_attn(CacheLayout c, int layer, int p0, int T, int window,
-                                                         float kscale, const uint16_t* __restrict__ q,
-                                                         const int32_t* __restrict__ rows,
-                                                         const int32_t* __restrict__ counts,
-                                                         uint16_t* __restrict__ out) {
-  constexpr int DPT = D / 8;           // channels per thread when staging a key
+template <int D, int G>
+struct PrefillSmem {
+  PrefillTile<D> tile[G][2];   // per key group: double buffer
+  int32_t wrange[4][4];        // per row wave: lo, hi, tmin, lomax
+};
+
+#ifndef TR_PREFILL_GROUPS
+#define TR_PREFILL_GROUPS 2
+#endif
+// G groups of 4 waves share the same 128 query rows and split the key tiles round-robin;
+// their (max, sum, O) states merge through LDS at the end.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
+    CacheLayout c, int p0, int T, int window, int np, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const uint16_t* __restrict__ dk,
+    const uint16_t* __restrict__ dv, const float2* __restrict__ dsz, uint16_t* __restrict__ out) {
   constexpr int KS = D / 16;           // MFMA k-steps for QK^T
   constexpr int MT = D / 32;           // 32-channel tiles of O^T
-  __shared__ PrefillSmem<D> sm;
+  constexpr int KPT = D / 64;          // 16-byte K pieces per thread per tile
+  constexpr int VPT = D / 64;          // 16-byte V^T pieces per thread per tile
+  __shared__ PrefillSmem<D, G> sm;
 
   const int BH = c.B * c.H;
   const int rank = blockIdx.x / BH, sh = blockIdx.x % BH;
@@ -188,7 +275,8 @@ __global__ __launch_bounds__(kBlock) void k_prefill_attn(CacheLayout c, int laye
     r0 = nf + (rank - ftiles) * BM;
     rend = min(r0 + BM, nf + nl);
   }
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = threadIdx.x / kBlock;              // key group
+  const int tid = threadIdx.x % kBlock, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int ri = r0 + wave * 32 + n;
   const bool row_ok = ri < rend;
@@ -218,7 +306,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_attn(CacheLayout c, int laye
     tmin = min(tmin, __shfl_xor(tmin, o, 64));
     lomax = max(lomax, __shfl_xor(lomax, o, 64));
   }
-  if (lane == 0) {
+  if (lane == 0 && grp == 0) {
     sm.wrange[wave][0] = wlo;
     sm.wrange[wave][1] = whi;
     sm.wrange[wave][2] = tmin;
@@ -232,17 +320,45 @@ __global__ __launch_bounds__(kBlock) void k_prefill_attn(CacheLayout c, int laye
     bhi = max(bhi, sm.wrange[w][1]);
   }
   const bool wave_live = whi > 0;
+  const int kb0 = blo & ~31;
+  const int ntiles = (bhi - kb0 + 31) >> 5;
 
-  const int32_t* pa = tr_prefix_row(c, layer, s, blo);
-  const int32_t* pe = tr_prefix_row(c, layer, s, bhi);
-  int A[4], voff[5];
-  voff[0] = 0;
+  // Staging: thread -> K row (tid / 8), 16-byte piece (tid % 8); V^T row (tid / 4), piece
+  // (tid % 4); for D = 128 every thread moves two pieces of each.
+  const uint16_t* kbase = dk + (int64_t)sh * np * D;
+  const uint16_t* vbase = dv + (int64_t)sh * D * np;
+  const float2* sbase = dsz + (int64_t)sh * np;
+  uint4 rk[KPT], rv[VPT];
+  float2 rs = make_float2(0.0f, 0.0f);
+  auto load_tile = [&](int kb) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    A[x] = pa[x];
-    voff[x + 1] = voff[x] + (pe[x] - pa[x]);
-  }
-  const int total = voff[4];
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * kBlock;                  // 16-byte piece index in the K tile
+      rk[x] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(kb + (e * 8) / D) * D + (e * 8) % D);
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * kBlock;
+      rv[x] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(e >> 2) * np + kb + (e & 3) * 8);
+    }
+    if (tid < BN) rs = sbase[kb + tid];
+  };
+  auto store_tile = [&](PrefillTile<D>& tl) {
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * kBlock;
+      *reinterpret_cast<uint4*>(&tl.ks[(e * 8) / D][(e * 8) % D]) = rk[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * kBlock;
+      *reinterpret_cast<uint4*>(&tl.vt[e >> 2][(e & 3) * 8]) = rv[x];
+    }
+    if (tid < BN) {
+      tl.alpha[tid] = rs.x;
+      tl.beta[tid] = rs.y;
+    }
+  };
 
   f32x16 o[MT];
 #pragma unroll
@@ -251,136 +367,126 @@ __global__ __launch_bounds__(kBlock) void k_prefill_attn(CacheLayout c, int laye
     for (int r = 0; r < 16; ++r) o[mt][r] = 0.0f;
   float mref = -INFINITY, lsum = 0.0f;
 
-  const int kk = tid / 8, sub = tid % 8;
-  for (int tb = 0; tb < total; tb += BN) {
-    __syncthreads();
-    // ---- stage one 32-key tile ----
-    {
-      const int vi = tb + kk;
-      if (vi < total) {
-        int cls = 0;
-        while (cls < 3 && vi >= voff[cls + 1]) ++cls;
-        const int slot = A[cls] + (vi - voff[cls]);
-        const int P = c.ptok[cls];
-        const int page = tr_ptab(c, layer, s, cls)[slot / P];
-        const int j = slot % P;
-        const uint8_t* pb = c.pool + (int64_t)page * c.page_bytes;
-        const int b = 2 << cls;
-        const int rowb = D * b / 8;
-        const int64_t hoff = (int64_t)h * c.cb + (int64_t)j * rowb + sub * (DPT * b / 8);
-        uint32_t wk[8], wv[8];
-        load_slice<DPT>(pb + c.k_off[cls] + hoff, b, wk);
-        load_slice<DPT>(pb + c.v_off[cls] + hoff, b, wv);
-        if (cls == 3) {
-#pragma unroll
-          for (int e = 0; e < DPT / 2; ++e) {
-            sm.ks[kk][sub * DPT + 2 * e] = (uint16_t)(wk[e] & 0xffffu);
-            sm.ks[kk][sub * DPT + 2 * e + 1] = (uint16_t)(wk[e] >> 16);
-            sm.vt[sub * DPT + 2 * e][kk] = (_Float16)tr_bf16_lo(wv[e]);
-            sm.vt[sub * DPT + 2 * e + 1][kk] = (_Float16)tr_bf16_hi(wv[e]);
-          }
-          if (sub == 0) {
-            sm.alpha[kk] = kscale;
-            sm.beta[kk] = 0.0f;
-          }
-        } else {
-          const float2 szv = reinterpret_cast<const float2*>(pb + c.sv_off[cls])[(int64_t)h * P + j];
-#pragma unroll
-          for (int e = 0; e < DPT; ++e) {
-            const float ck = code_f<DPT>(wk, b, e);
-            sm.ks[kk][sub * DPT + e] = (uint16_t)(__float_as_uint(ck) >> 16);
-            sm.vt[sub * DPT + e][kk] = (_Float16)fmaf(szv.x, code_f<DPT>(wv, b, e), szv.y);
-          }
-          if (sub == 0) {
-            const float2 szk = reinterpret_cast<const float2*>(pb + c.sk_off[cls])[(int64_t)h * P + j];
-            sm.alpha[kk] = szk.x * kscale;
-            sm.beta[kk] = szk.y * kscale;
-          }
-        }
-        if (sub == 0) sm.kpos[kk] = reinterpret_cast<const int32_t*>(pb)[j];
-      } else {
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) {
-          sm.ks[kk][sub * DPT + e] = 0;
-          sm.vt[sub * DPT + e][kk] = (_Float16)0.0f;
-        }
-        if (sub == 0) {
-          sm.alpha[kk] = 0.0f;
-          sm.beta[kk] = 0.0f;
-          sm.kpos[kk] = 0x7fffffff;
-        }
-      }
-    }
-    __syncthreads();
-    if (!wave_live) continue;
-    // ---- does this tile touch the wave's windows? ----
-    const int mypos = sm.kpos[n];
-    int kmin = mypos, kmax_raw = mypos, kmax_real = (mypos == 0x7fffffff) ? -1 : mypos;
-#pragma unroll
-    for (int o2 = 16; o2 > 0; o2 >>= 1) {
-      kmin = min(kmin, __shfl_xor(kmin, o2, 64));
-      kmax_raw = max(kmax_raw, __shfl_xor(kmax_raw, o2, 64));
-      kmax_real = max(kmax_real, __shfl_xor(kmax_real, o2, 64));
-    }
-    if (kmin >= whi || kmax_real < wlo) continue;
-    const bool needmask = !(kmax_raw <= tmin && kmin >= lomax);
+  // Group grp handles key tiles grp, grp + G, grp + 2G, ...; every group runs the same number
+  // of rounds so the block barrier stays uniform.
+  const int rounds = (ntiles + G - 1) / G;
+  if (grp < ntiles) load_tile(kb0 + grp * BN);
+  if (grp < ntiles) store_tile(sm.tile[grp][0]);
+  if (grp + G < ntiles) load_tile(kb0 + (grp + G) * BN);
+  __syncthreads();
 
-    // ---- S^T = K Q^T ----
-    f32x16 sacc;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int it = rd * G + grp;
+    const PrefillTile<D>& tl = sm.tile[grp][rd & 1];
+    const int kb = kb0 + it * BN;
+    // ---- compute tile it (waves outside their windows skip it) ----
+    if (it < ntiles && wave_live && kb < whi && kb + BN - 1 >= wlo) {
+      const bool needmask = !(kb + BN - 1 <= tmin && kb >= lomax);
+      f32x16 sacc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.ks[n][16 * ks + 8 * g]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
-    }
-    // ---- scores, mask, running max ----
-    float sv[16];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      float x = fmaf(sm.alpha[key], sacc[r], sm.beta[key] * qsum);
-      if (needmask) {
-        const int kp = sm.kpos[key];
-        if (!(kp <= t && kp >= lo)) x = -INFINITY;
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&tl.ks[n][16 * ks + 8 * g]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
       }
-      sv[r] = x;
-      tmax = fmaxf(tmax, x);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    if (__any(tmax > mref + kRescale)) {
-      const float mnew = fmaxf(mref, tmax);
-      const float corr = (mref == -INFINITY) ? 0.0f : exp2f(mref - mnew);
+      // x = score - mref = alpha * S + (beta * sum(q) - mref): two fused multiply-adds.
+      float sv[16];
+      float tmax = -INFINITY;
+      const float nm = (mref == -INFINITY) ? 0.0f : -mref;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int k0 = 8 * r4 + 4 * g;
+        const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[k0]);
+        const float4 be = *reinterpret_cast<const float4*>(&tl.beta[k0]);
+        const float alv[4] = {al.x, al.y, al.z, al.w}, bev[4] = {be.x, be.y, be.z, be.w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[mt][r] *= corr;
-      lsum *= corr;
-      mref = mnew;
-    }
-    f16x8 pk[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = (sv[r] == -INFINITY) ? 0.0f : exp2f(sv[r] - mref);
-      lsum += p;
-      pk[r >> 3][r & 7] = (_Float16)p;
-    }
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const _Float16* vrow = &sm.vt[32 * mt + n][16 * kh + 4 * g];
-        f16x8 a;
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
-        a = __builtin_bit_cast(f16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pk[kh], o[mt], 0, 0, 0);
+        for (int x = 0; x < 4; ++x) {
+          float v = fmaf(alv[x], sacc[4 * r4 + x], fmaf(bev[x], qsum, nm));
+          if (needmask) {
+            const int kp = kb + k0 + x;
+            if (!(kp <= t && kp >= lo)) v = -INFINITY;
+          }
+          sv[4 * r4 + x] = v;
+          tmax = fmaxf(tmax, v);
+        }
       }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // Lazy rescale: x is relative to the running reference mref; it moves only when some
+      // row's maximum exceeds it by more than kRescale (so p <= 2^kRescale in fp16), or on the
+      // first visible key of a row.
+      const bool first = (mref == -INFINITY);
+      const bool need = first ? (tmax > -INFINITY) : (tmax > kRescale);
+      if (__any(need)) {
+        const float shift = first ? ((tmax > -INFINITY) ? tmax : 0.0f) : fmaxf(tmax, 0.0f);
+        const float corr = first ? 0.0f : exp2f(-shift);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[mt][r] *= corr;
+        lsum *= corr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] -= shift;
+        if (!first) mref += shift;
+        else if (tmax > -INFINITY) mref = tmax;
+      }
+      f16x8 pk[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sv[r]);
+        lsum += p;
+        pk[r >> 3][r & 7] = (_Float16)p;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const uint16_t* vrow = &tl.vt[32 * mt + n][16 * kh + 4 * g];
+          const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
+          const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kh], o[mt], 0, 0, 0);
+        }
+      }
+    }
+    // ---- stage this group's next tile into its other buffer, issue loads for the one after ----
+    if (it + G < ntiles) store_tile(sm.tile[grp][(rd + 1) & 1]);
+    if (it + 2 * G < ntiles) load_tile(kb0 + (it + 2 * G) * BN);
+    __syncthreads();
+  }
+  // ---- merge the groups' (mref, lsum, O) -- same (row, channel) mapping in every group ----
+  if constexpr (G > 1) {
+    float* st = reinterpret_cast<float*>(&sm.tile[0][0]);   // tile buffers are free now
+    constexpr int NS = MT * 16 + 2;
+    static_assert(sizeof(PrefillTile<D>) * 2 * G >= sizeof(float) * NS * kBlock * (G > 1 ? 1 : 0), "merge space");
+    for (int src = G - 1; src >= 1; --src) {
+      if (grp == src) {
+        float* my = st + tid * NS;
+        my[0] = mref;
+        my[1] = lsum;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) my[2 + mt * 16 + r] = o[mt][r];
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float* ot = st + tid * NS;
+        const float m2 = ot[0];
+        const float mnew = fmaxf(mref, m2);
+        const float a1 = (mref == -INFINITY) ? 0.0f : exp2f(mref - mnew);
+        const float a2 = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - mnew);
+        lsum = lsum * a1 + ot[1] * a2;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[mt][r] = o[mt][r] * a1 + ot[2 + mt * 16 + r] * a2;
+        mref = mnew;
+      }
+      __syncthreads();
     }
   }
-  if (!row_ok) return;
+  if (grp != 0 || !row_ok) return;
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = 1.0f / ltot;
   uint16_t* orow = out + (((int64_t)s * T + i) * c.H + h) * D;
@@ -405,23 +511,32 @@ tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q
   const int BH = L.B * L.H;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
   const int ranks = (T + BM - 1) / BM + 1;
+  const int pend = p0 + T;                          // dense range [0, pend), 32-aligned tiles
+  const int ntile = (pend + 31) / 32;
   {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
-    if (L.D == 64)
+    if (L.D == 64) {
       hipLaunchKernelGGL(k_prefill_compact<64>, dim3(BH), dim3(kBlock), 0, stream, L, T, mode, c->rows,
                          c->row_counts, out);
-    else
+      TR_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_prefill_dense<64>, dim3(BH * ntile), dim3(kBlock), 0, stream, L, layer, 0, ntile, pend,
+                         c->np, kscale, c->dk, c->dv, c->dsz);
+    } else {
       hipLaunchKernelGGL(k_prefill_compact<128>, dim3(BH), dim3(kBlock), 0, stream, L, T, mode, c->rows,
                          c->row_counts, out);
+      TR_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_prefill_dense<128>, dim3(BH * ntile), dim3(kBlock), 0, stream, L, layer, 0, ntile, pend,
+                         c->np, kscale, c->dk, c->dv, c->dsz);
+    }
     TR_LAUNCH_CHECK();
   }
   TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
   if (L.D == 64)
-    hipLaunchKernelGGL(k_prefill_attn<64>, dim3(BH * ranks), dim3(kBlock), 0, stream, L, layer, p0, T, window,
-                       kscale, q, c->rows, c->row_counts, out);
+    hipLaunchKernelGGL((k_prefill_attn<64, TR_PREFILL_GROUPS>), dim3(BH * ranks), dim3(kBlock * TR_PREFILL_GROUPS), 0, stream, L, p0, T, window, c->np, q,
+                       c->rows, c->row_counts, c->dk, c->dv, c->dsz, out);
   else
-    hipLaunchKernelGGL(k_prefill_attn<128>, dim3(BH * ranks), dim3(kBlock), 0, stream, L, layer, p0, T, window,
-                       kscale, q, c->rows, c->row_counts, out);
+    hipLaunchKernelGGL((k_prefill_attn<128, TR_PREFILL_GROUPS>), dim3(BH * ranks), dim3(kBlock * TR_PREFILL_GROUPS), 0, stream, L, p0, T, window, c->np, q,
+                       c->rows, c->row_counts, c->dk, c->dv, c->dsz, out);
   TR_LAUNCH_CHECK();
   return TR_OK;
 }
