@@ -41,6 +41,34 @@ sys.path.insert(0, ROOT)
 from workloads import CONFIGS, layer_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+
+# HBM traffic of the dominant kernels from rocprofv3 PMC passes (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch, averaged over the timed launches), each divided by what the same counter
+# read per byte of a plain 1 GiB device-to-device copy in the same run (``--calib-copy-mib``).
+# ``sources`` lists the files the kernel is built from and their sha256 when the counters were
+# taken: once any of them changes the figures no longer describe the kernel and the bench
+# reports traffic as null.
+TRAFFIC = {
+    "k_decode": {
+        "fetch_kib": 169362.9, "write_kib": 3097.1, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "sources": {
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip":
+                "7ed929ac13da511781b11ce96e571a17df834d00dc4e2daf4e6d8ae1b398f0b2",
+            "mixed_precision_kv_tr_amd/csrc/common.h":
+                "54bd8db721150d71b7a243f1fe0ffd7a85065e875b9990cf48cf5b3e1e2d3718",
+            "mixed_precision_kv_tr_amd/csrc/layout.h":
+                "deccfa7c21582ee2fb81b10673d54efc556bbce562ffa21c31648783721cf4ba"}},
+    "k_prefill_attn": {
+        "fetch_kib": 18126.6, "write_kib": 10438.6, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "sources": {
+            "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip":
+                "db3e31706351f29b4ac3edf2f8fa0e7e46f9e133b6403a386f4433ed7f8dfba4",
+            "mixed_precision_kv_tr_amd/csrc/common.h":
+                "54bd8db721150d71b7a243f1fe0ffd7a85065e875b9990cf48cf5b3e1e2d3718",
+            "mixed_precision_kv_tr_amd/csrc/layout.h":
+                "deccfa7c21582ee2fb81b10673d54efc556bbce562ffa21c31648783721cf4ba"}},
+}
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, TFLOP/s
 METRIC = "mixed-bit KV decode GB/s (% HBM peak); routed prefill tokens/s (% MFMA peak)"
 
@@ -90,6 +118,35 @@ def pool_pages_needed(bits_layers, P: dict, slack: int = 4) -> int:
             total += int(np.ceil(cnt / p).sum())
         total += slack * bits.shape[0]
     return total
+
+
+def _sha256(path: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """Calibrated HBM bytes per launch of ``kernel`` if its sources are unchanged, else None."""
+    t = TRAFFIC.get(kernel)
+    if not t or any(_sha256(f) != h for f, h in t["sources"].items()):
+        return None
+    return int(t["fetch_kib"] * 1024 / t["fetch_per_byte"] + t["write_kib"] * 1024 / t["write_per_byte"])
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """Plain device-to-device copies of a known size, for scaling the PMC byte counters.
+
+    uint8 -> int8, so torch runs its elementwise copy kernel (n bytes read, n written) rather
+    than a DMA blit that the counters would not see."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.int8, device="cuda")
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[calib] {reps} copies of {n} bytes")
+    del src, dst
 
 
 def time_steps(step, K: int) -> float:
@@ -218,8 +275,8 @@ def bench_decode(tr, args):
     avg_split_ms = ms_split / max(1, n_split)
     bytes_per_launch = float(np.mean(acc_attn))
     achieved = bytes_per_launch / (avg_split_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "kernel": "k_decode_split", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+    roof = {"bound": "hbm", "kernel": "k_decode", "traffic_unit": "bytes per launch", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_decode"),
             "avg_launch_us": round(avg_split_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch),
             "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
 
@@ -278,7 +335,8 @@ def bench_prefill(tr, args):
     achieved = fl_per_launch / (avg_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": "k_prefill_attn", "achieved": round(achieved, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": int(fl_per_launch),
+            "traffic": measured_traffic("k_prefill_attn"), "traffic_unit": "bytes per launch",
+            "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": int(fl_per_launch),
             "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
     cpu = None
     if not args.no_cpu_baseline:
@@ -303,6 +361,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run plain copies of this many MiB (PMC counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (decode and prefill shard by "
@@ -312,6 +372,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import mixed_precision_kv_tr_amd as tr
+
+    if args.calib_copy_mib:
+        copy_calibration(args.calib_copy_mib)
 
     dec = bench_decode(tr, args) if args.only in (None, "decode") else None
     pre = bench_prefill(tr, args) if args.only in (None, "prefill") else None
