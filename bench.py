@@ -217,7 +217,8 @@ def bench_decode(tr, args):
     log(f"[decode] generating {Lyr} layers of {cfg.name}")
     per_layer, samples = [], []
     sample_seqs = list(range(args.cpu_sample_seqs))
-    ptok = {b: 4096 // (D * b // 8) for b in (2, 4, 8, 16)}
+    pcb = args.page_code_bytes or 4096
+    ptok = {b: pcb * 8 // (D * b) for b in (2, 4, 8, 16)}
     cache = None
     acc_attn, acc_total = [], []
     for layer in range(Lyr):
@@ -227,7 +228,8 @@ def bench_decode(tr, args):
         if cache is None:
             # pool sized from layer 0's realized width mix, with 25% headroom for the others
             pool_pages = int(pool_pages_needed([bits_np], ptok) * Lyr * 1.25) + 64
-            cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, C + 1, pool_pages=pool_pages)
+            cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, C + 1, page_code_bytes=args.page_code_bytes,
+                                         pool_pages=pool_pages)
         tr.tr_kv_quantize_write(cache, layer, case["k"][:, :C].contiguous(), case["v"][:, :C].contiguous(),
                                 case["bits"][:, :C].contiguous())
         a, t = decode_layer_bytes(bits_np, mode_np, C, w, D)
@@ -304,7 +306,7 @@ def bench_prefill(tr, args):
     log(f"[prefill] generating {Lyr} layers of {cfg.name}")
     cases = [layer_inputs(cfg, layer, seed=args.seed, device=dev) for layer in range(Lyr)]
     flops = [prefill_layer_flops(c["mode"].cpu().numpy(), w, D) for c in cases]
-    cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, T)
+    cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, T, page_code_bytes=args.page_code_bytes)
     outs = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(Lyr)]
 
     def step():
@@ -361,6 +363,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--page-code-bytes", type=int, default=0,
+                    help="cache page size: K (and V) code bytes per head per page; 0 = the library default")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run plain copies of this many MiB (PMC counter calibration)")
     args = ap.parse_args()
