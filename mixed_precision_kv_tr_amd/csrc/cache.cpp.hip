@@ -403,6 +403,9 @@ static void free_all(tr_kv_cache* c) {
   (void)hipFree(c->dk);
   (void)hipFree(c->dv);
   (void)hipFree(c->dsz);
+  (void)hipFree(c->pf_units);
+  (void)hipFree(c->pf_merges);
+  (void)hipFree(c->pf_part);
   delete c;
 }
 
@@ -421,6 +424,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   c->rows = c->row_counts = nullptr;
   c->dk = c->dv = nullptr;
   c->dsz = nullptr;
+  c->pf_units = c->pf_merges = nullptr;
+  c->pf_part = nullptr;
   c->prof_on = false;
   CacheLayout& L = c->lay;
   L.L = d->num_layers; L.B = d->batch; L.H = d->num_heads; L.D = d->head_dim; L.N = d->max_tokens;
@@ -475,6 +480,11 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dsz, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;
+  c->pf_uph = tr_prefill_units_per_head(L.N);
+  ok = ok && hipMalloc((void**)&c->pf_units, sizeof(int4) * (size_t)L.B * L.H * c->pf_uph) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->pf_merges, sizeof(int4) * (size_t)L.B * L.H * (TR_PREFILL_SLOTS / 2)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->pf_part,
+                       sizeof(float) * (size_t)L.B * L.H * TR_PREFILL_SLOTS * 128 * (L.D + 4)) == hipSuccess;
   if (!ok) {
     hipGetLastError();
     free_all(c);

@@ -21,8 +21,16 @@ struct tr_kv_cache {
   int32_t* row_counts;
   // prefill scratch: the cache range a prefill call reads, dequantized once, position order
   //   dk [B][H][NP][D] uint16: K code as a bf16 integer (exact), or the stored bf16 (b = 16)
-  //   dv [B][H][D][NP] uint16: v_hat = s * c + z as fp16, channel-major
+  //   dv [B][H][D][NP] uint16: v_hat = s * c + z as fp16, channel-major; within each group of
+  //                            16 positions, bits 2 and 3 of the position are swapped
   //   dsz [B][H][NP] float2:   (s_K, z_K) * log2(e) / sqrt(D); (log2(e)/sqrt(D), 0) for b = 16
+  // prefill attention work: units (128-row tile, key-tile chunk) [B][H][pf_uph] int4, merges of
+  // split tiles [B][H][TR_PREFILL_SLOTS / 2] int4, partial results of split tiles
+  // [B][H][TR_PREFILL_SLOTS][128][D + 4] floats (O, max, sum, padding)
+  int4* pf_units;
+  int4* pf_merges;
+  float* pf_part;
+  int32_t pf_uph;
   int32_t np;                     // N rounded up to a multiple of 32
   uint16_t* dk;
   uint16_t* dv;
@@ -46,6 +54,14 @@ inline int tr_decode_max_chunk(const CacheLayout& L) {
   const int by_pages = (TR_DECODE_PG_MAX - 2) * L.ptok[3];
   return by_pages < TR_DECODE_ITEM_MAX ? by_pages : TR_DECODE_ITEM_MAX;
 }
+
+// Prefill: partial-result slots per (seq, head) for key-split row tiles, and the work units of a
+// prefill of T tokens per (seq, head): one per 128-row tile (full and local rows fill separate
+// tiles) plus the extra chunks of split tiles.
+#ifndef TR_PREFILL_SLOTS
+#define TR_PREFILL_SLOTS 16
+#endif
+inline int tr_prefill_units_per_head(int T) { return (T + 127) / 128 + 1 + TR_PREFILL_SLOTS; }
 
 // Kernel families reported by tr_profile_read.
 enum { TR_PROF_WRITE = 0, TR_PROF_DECODE_SPLIT = 1, TR_PROF_DECODE_COMBINE = 2, TR_PROF_PREFILL_COMPACT = 3,

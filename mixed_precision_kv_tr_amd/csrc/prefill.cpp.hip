@@ -22,10 +22,13 @@
 //               masks only on tiles that cross a row's window edge; waves skip tiles outside
 //               their own windows.
 //     PV        O^T[D x 32 queries] += V^T P^T with v_mfma_f32_32x32x16_f16; P is the lane's
-//               own scores (the key order of the S^T layout is mirrored in the V^T read).
+//               own scores; the dense V^T rows store keys in the S^T accumulator's order
+//               (vt_pos), so each V^T operand is one 16-byte LDS read.
 //   epilogue  O / l -> bf16, scattered back to the rows' original positions.
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -39,6 +42,7 @@ constexpr int kBlock = 256;
 constexpr int BM = 128;       // query rows per workgroup (4 waves x 32)
 constexpr int BN = 32;        // keys per tile
 constexpr float kRescale = 8.0f;
+constexpr int kSlotsPerHead = TR_PREFILL_SLOTS;   // partial-result slots of one (seq, head)
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   const int lane = threadIdx.x & 63;
@@ -50,11 +54,129 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// Max / sum of a value and its copy 32 lanes away, with v_permlane32_swap (no LDS traffic): the
+// swap hands lanes 0-31 the upper half's value in its second result and lanes 32-63 the lower
+// half's in its first, so max(first, second) is the pairwise max in every lane.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Work units of the attention kernel for one (seq, head), after the row compaction: one per
+// 128-row tile, except that a tile whose key range spans more than kch key tiles is cut into
+// chunks of kch key tiles that run as separate units, write partial (max, sum, O) rows, and are
+// merged by k_prefill_merge.  kch is the smallest of 16, 32, 64, ... key tiles for which the
+// head's partial results fit its kSlotsPerHead slots (no split if none does).
+//   unit  = (r0 | full << 31, rend, kt0 | kt1 << 16, partial slot or -1)
+//   merge = (r0, rend, first slot, chunks)
+// Units are listed heaviest first: full tiles from the last (longest key range), then local.
+__device__ __forceinline__ void build_units(int sh, int p0, int window, int nfull, int nl, const int32_t* rl,
+                                            int32_t* counts, int4* units, int4* merges) {
+  constexpr int NC = 8;                            // candidate chunk sizes 16 << j key tiles
+  __shared__ int32_t red[kBlock / 64][NC];
+  __shared__ int32_t scan[kBlock / 64][3];
+  __shared__ int32_t kch_s, base_s[3];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nft = (nfull + BM - 1) / BM, nlt = (nl + BM - 1) / BM, ntl = nft + nlt;
+  auto tile_range = [&](int k, int& r0, int& rend, int& full, int& klo, int& khi) {
+    full = k < nft;
+    const int ft = nft - 1 - k;                    // full tiles from the last
+    r0 = full ? ft * BM : nfull + (k - nft) * BM;
+    rend = full ? min(r0 + BM, nfull) : min(r0 + BM, nfull + nl);
+    const int tmin = p0 + rl[r0], tmax = p0 + rl[rend - 1];   // rows are in position order
+    const int blo = full ? 0 : max(0, tmin - window);
+    klo = blo >> 5;
+    khi = (tmax + 1 + 31) >> 5;
+  };
+  // pass A: partial slots each candidate chunk size would need
+  int want[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) want[j] = 0;
+  for (int k = tid; k < ntl; k += kBlock) {
+    int r0, rend, full, klo, khi;
+    tile_range(k, r0, rend, full, klo, khi);
+    const int nkt = khi - klo;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int kc = 16 << j;
+      want[j] += (nkt > kc) ? (nkt + kc - 1) / kc : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) want[j] += __shfl_xor(want[j], o, 64);
+    if (lane == 0) red[wave][j] = want[j];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int kch = 1 << 30;                             // no split
+    for (int j = NC - 1; j >= 0; --j) {
+      int tot = 0;
+      for (int w = 0; w < kBlock / 64; ++w) tot += red[w][j];
+      if (tot <= kSlotsPerHead) kch = 16 << j;
+    }
+    kch_s = kch;
+    base_s[0] = base_s[1] = base_s[2] = 0;
+  }
+  __syncthreads();
+  const int kch = kch_s;
+  // pass B: units, slots and merges in tile order (exclusive scans carried across chunks)
+  for (int k0 = 0; k0 < ntl; k0 += kBlock) {
+    const int k = k0 + tid;
+    int r0 = 0, rend = 0, full = 0, klo = 0, khi = 0, nch = 0;
+    if (k < ntl) {
+      tile_range(k, r0, rend, full, klo, khi);
+      nch = (khi - klo > kch) ? (khi - klo + kch - 1) / kch : 1;
+    }
+    const int v[3] = {nch, nch > 1 ? nch : 0, nch > 1 ? 1 : 0};
+    int incl[3];
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      incl[x] = (int)wave_incl_scan((uint32_t)v[x]);
+      if (lane == 63) scan[wave][x] = incl[x];
+    }
+    __syncthreads();
+    int pos[3];
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      pos[x] = base_s[x] + incl[x] - v[x];
+      for (int w = 0; w < wave; ++w) pos[x] += scan[w][x];
+    }
+    if (k < ntl) {
+      for (int cc = 0; cc < nch; ++cc) {
+        const int kt0 = klo + cc * kch, kt1 = min(khi, kt0 + kch);
+        units[pos[0] + cc] = make_int4(r0 | (full << 31), rend, kt0 | (kt1 << 16), nch > 1 ? pos[1] + cc : -1);
+      }
+      if (nch > 1) merges[pos[2]] = make_int4(r0, rend, pos[1], nch);
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+        for (int w = 0; w < kBlock / 64; ++w) base_s[x] += scan[w][x];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    counts[sh * 4 + 0] = nfull;
+    counts[sh * 4 + 1] = nl;
+    counts[sh * 4 + 2] = base_s[0];
+    counts[sh * 4 + 3] = base_s[2];
+  }
+}
+
 // Stable partition of the query rows of one (seq, head) by mode.
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_prefill_compact(CacheLayout c, int T, const uint8_t* __restrict__ mode,
+__global__ __launch_bounds__(kBlock) void k_prefill_compact(CacheLayout c, int p0, int T, int window,
+                                                            const uint8_t* __restrict__ mode,
                                                             int32_t* __restrict__ rows, int32_t* __restrict__ counts,
-                                                            uint16_t* __restrict__ out) {
+                                                            int4* __restrict__ units, int4* __restrict__ merges,
+                                                            int uph, uint16_t* __restrict__ out) {
   __shared__ uint32_t wsum[kBlock / 64];
   __shared__ int32_t nfull_s, run_f, run_l;
   const int sh = blockIdx.x;
@@ -112,10 +234,9 @@ __global__ __launch_bounds__(kBlock) void k_prefill_compact(CacheLayout c, int T
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    counts[sh * 4 + 0] = nfull;
-    counts[sh * 4 + 1] = run_l;
-  }
+  const int nl = run_l;
+  build_units(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph,
+              merges + (int64_t)sh * (kSlotsPerHead / 2));
 }
 
 template <int NB>
@@ -145,6 +266,11 @@ __device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cas
 
 // Dequantize DPL channels of one (token, head) K/V pair of width class C into the dense
 // scratch (K row slice) and the LDS V^T tile.
+// Position of key k (0..31) of a tile inside a V^T row: bits 2 and 3 swapped within each group
+// of 16, so that the 8 keys one lane of the PV product needs (4g .. 4g+3 and 8+4g .. 8+4g+3 of a
+// 16-key step, the key order of the S^T accumulator) are contiguous.
+__device__ __forceinline__ int vt_pos(int k) { return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
 template <int D, int C>
 __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout& c, int h, int j, int part,
                                             uint16_t* krow, _Float16 (*vt)[40], int tk, float2* szk_out) {
@@ -160,8 +286,8 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
 #pragma unroll
     for (int e = 0; e < DPL / 2; ++e) {
       ko[e] = wk[e];
-      vt[part * DPL + 2 * e][tk] = (_Float16)tr_bf16_lo(wv[e]);
-      vt[part * DPL + 2 * e + 1][tk] = (_Float16)tr_bf16_hi(wv[e]);
+      vt[part * DPL + 2 * e][vt_pos(tk)] = (_Float16)tr_bf16_lo(wv[e]);
+      vt[part * DPL + 2 * e + 1][vt_pos(tk)] = (_Float16)tr_bf16_hi(wv[e]);
     }
     *szk_out = make_float2(1.0f, 0.0f);
   } else {
@@ -172,8 +298,8 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
     for (int e = 0; e < DPL; e += 2) {
       const float k0 = (float)code_at<b>(wk, e), k1 = (float)code_at<b>(wk, e + 1);
       ko[e / 2] = (__float_as_uint(k0) >> 16) | (__float_as_uint(k1) & 0xffff0000u);
-      vt[part * DPL + e][tk] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
-      vt[part * DPL + e + 1][tk] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
+      vt[part * DPL + e][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
+      vt[part * DPL + e + 1][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
     }
     *szk_out = szk;
   }
@@ -217,7 +343,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 #pragma unroll
     for (int x = 0; x < DPL / 8; ++x) reinterpret_cast<uint4*>(krow)[x] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) vt[part * DPL + e][tk] = (_Float16)0.0f;
+    for (int e = 0; e < DPL; ++e) vt[part * DPL + e][vt_pos(tk)] = (_Float16)0.0f;
   }
   if (part == 0) dsz[(int64_t)sh * np + p] = make_float2(szk.x * kscale, szk.y * kscale);
   __syncthreads();
@@ -230,11 +356,11 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 }
 
 template <int D>
-struct PrefillTile {
+struct alignas(16) PrefillTile {
   uint16_t ks[BN][D + 8];      // K codes as bf16 integers / stored bf16, key-major
-  uint16_t vt[D][BN + 8];      // v_hat fp16, channel-major
-  float alpha[BN];             // s_K * log2(e) / sqrt(D)
-  float beta[BN];              // z_K * log2(e) / sqrt(D)
+  uint16_t vt[D][BN + 8];      // v_hat fp16, channel-major, keys in vt_pos order
+  alignas(16) float alpha[BN]; // s_K * log2(e) / sqrt(D)
+  alignas(16) float beta[BN];  // z_K * log2(e) / sqrt(D)
 };
 
 template <int D, int G>
@@ -244,15 +370,19 @@ struct PrefillSmem {
 };
 
 #ifndef TR_PREFILL_GROUPS
-#define TR_PREFILL_GROUPS 2
+#define TR_PREFILL_GROUPS 1
 #endif
 // G groups of 4 waves share the same 128 query rows and split the key tiles round-robin;
 // their (max, sum, O) states merge through LDS at the end.
+#ifndef TR_PREFILL_WAVES
+#define TR_PREFILL_WAVES 4
+#endif
 template <int D, int G>
-__global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
+__global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D == 64 ? TR_PREFILL_WAVES : 2))) void k_prefill_attn(
     CacheLayout c, int p0, int T, int window, int np, const uint16_t* __restrict__ q,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const uint16_t* __restrict__ dk,
-    const uint16_t* __restrict__ dv, const float2* __restrict__ dsz, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const int4* __restrict__ units, int uph,
+    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, const float2* __restrict__ dsz,
+    float* __restrict__ part, uint16_t* __restrict__ out) {
   constexpr int KS = D / 16;           // MFMA k-steps for QK^T
   constexpr int MT = D / 32;           // 32-channel tiles of O^T
   constexpr int KPT = D / 64;          // 16-byte K pieces per thread per tile
@@ -260,21 +390,13 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
   __shared__ PrefillSmem<D, G> sm;
 
   const int BH = c.B * c.H;
-  const int rank = blockIdx.x / BH, sh = blockIdx.x % BH;
+  const int u = blockIdx.x / BH, sh = blockIdx.x % BH;
   const int s = sh / c.H, h = sh % c.H;
-  const int nf = counts[sh * 4 + 0], nl = counts[sh * 4 + 1];
-  const int ftiles = (nf + BM - 1) / BM, ltiles = (nl + BM - 1) / BM;
-  if (rank >= ftiles + ltiles) return;
-  const bool full = rank < ftiles;
-  int r0, rend;
-  if (full) {                                   // heaviest full tiles first
-    const int ft = ftiles - 1 - rank;
-    r0 = ft * BM;
-    rend = min(r0 + BM, nf);
-  } else {
-    r0 = nf + (rank - ftiles) * BM;
-    rend = min(r0 + BM, nf + nl);
-  }
+  if (u >= counts[sh * 4 + 2]) return;
+  const int4 unit = units[(int64_t)sh * uph + u];
+  const bool full = unit.x < 0;
+  const int r0 = unit.x & 0x7fffffff, rend = unit.y;
+  const int kt0 = unit.z & 0xffff, kt1 = unit.z >> 16, slot = unit.w;
   const int grp = threadIdx.x / kBlock;              // key group
   const int tid = threadIdx.x % kBlock, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
@@ -295,7 +417,7 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
     qsum += (tr_bf16_lo(raw.x) + tr_bf16_hi(raw.x)) + (tr_bf16_lo(raw.y) + tr_bf16_hi(raw.y)) +
             (tr_bf16_lo(raw.z) + tr_bf16_hi(raw.z)) + (tr_bf16_lo(raw.w) + tr_bf16_hi(raw.w));
   }
-  qsum += __shfl_xor(qsum, 32, 64);
+  qsum = xor32_sum(qsum);
 
   // Wave and workgroup key-position ranges.
   int wlo = lo, whi = row_ok ? t + 1 : -1, tmin = row_ok ? t : 0x7fffffff, lomax = row_ok ? lo : -1;
@@ -320,8 +442,10 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
     bhi = max(bhi, sm.wrange[w][1]);
   }
   const bool wave_live = whi > 0;
-  const int kb0 = blo & ~31;
-  const int ntiles = (bhi - kb0 + 31) >> 5;
+  (void)blo;
+  (void)bhi;
+  const int kb0 = kt0 * BN;                        // this unit's key tiles [kt0, kt1)
+  const int ntiles = kt1 - kt0;
 
   // Staging: thread -> K row (tid / 8), 16-byte piece (tid % 8); V^T row (tid / 4), piece
   // (tid % 4); for D = 128 every thread moves two pieces of each.
@@ -381,7 +505,6 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
     const int kb = kb0 + it * BN;
     // ---- compute tile it (waves outside their windows skip it) ----
     if (it < ntiles && wave_live && kb < whi && kb + BN - 1 >= wlo) {
-      const bool needmask = !(kb + BN - 1 <= tmin && kb >= lomax);
       f32x16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
@@ -390,28 +513,37 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&tl.ks[n][16 * ks + 8 * g]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
       }
-      // x = score - mref = alpha * S + (beta * sum(q) - mref): two fused multiply-adds.
+      // x = score - mref = alpha * S + (beta * sum(q) - mref): two fused multiply-adds.  Only tiles
+      // that cross a row's window edge are masked (a wave-uniform choice between two versions):
+      // key kb + 4g + off (off = 8 * r4 + x) is visible iff lo <= key <= t, i.e. iff
+      // (unsigned)(off - dlo) <= (unsigned)(t - lo) with dlo = lo - kb - 4g.
       float sv[16];
       float tmax = -INFINITY;
       const float nm = (mref == -INFINITY) ? 0.0f : -mref;
+      auto scores = [&](auto masked) {
+        const int dlo = row_ok ? lo - kb - 4 * g : 0x40000000;   // rows past the tile's end: all masked
+        const uint32_t span = row_ok ? (uint32_t)(t - lo) : 0u;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int k0 = 8 * r4 + 4 * g;
-        const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[k0]);
-        const float4 be = *reinterpret_cast<const float4*>(&tl.beta[k0]);
-        const float alv[4] = {al.x, al.y, al.z, al.w}, bev[4] = {be.x, be.y, be.z, be.w};
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int k0 = 8 * r4 + 4 * g;
+          const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[k0]);
+          const float4 be = *reinterpret_cast<const float4*>(&tl.beta[k0]);
+          const float alv[4] = {al.x, al.y, al.z, al.w}, bev[4] = {be.x, be.y, be.z, be.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          float v = fmaf(alv[x], sacc[4 * r4 + x], fmaf(bev[x], qsum, nm));
-          if (needmask) {
-            const int kp = kb + k0 + x;
-            if (!(kp <= t && kp >= lo)) v = -INFINITY;
+          for (int x = 0; x < 4; ++x) {
+            float v = fmaf(alv[x], sacc[4 * r4 + x], fmaf(bev[x], qsum, nm));
+            if constexpr (decltype(masked)::value) {
+              if ((uint32_t)(8 * r4 + x - dlo) > span) v = -INFINITY;
+            }
+            sv[4 * r4 + x] = v;
           }
-          sv[4 * r4 + x] = v;
-          tmax = fmaxf(tmax, v);
         }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      };
+      if (!(kb + BN - 1 <= tmin && kb >= lomax)) scores(std::true_type());
+      else scores(std::false_type());
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(sv[r], sv[r + 1]));
+      tmax = xor32_max(tmax);
       // Lazy rescale: x is relative to the running reference mref; it moves only when some
       // row's maximum exceeds it by more than kRescale (so p <= 2^kRescale in fp16), or on the
       // first visible key of a row.
@@ -441,10 +573,7 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          const uint16_t* vrow = &tl.vt[32 * mt + n][16 * kh + 4 * g];
-          const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
-          const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+          const f16x8 av = *reinterpret_cast<const f16x8*>(&tl.vt[32 * mt + n][16 * kh + 8 * g]);
           o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kh], o[mt], 0, 0, 0);
         }
       }
@@ -486,8 +615,24 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
       __syncthreads();
     }
   }
-  if (grp != 0 || !row_ok) return;
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  if (grp != 0) return;
+  const float ltot = xor32_sum(lsum);
+  if (!row_ok) return;
+  if (slot >= 0) {
+    // one chunk of a split tile: unnormalized O, reference max and sum of this row
+    float* pr = part + (((int64_t)sh * kSlotsPerHead + slot) * BM + (ri - r0)) * (D + 4);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * mt + 8 * j + 4 * g;
+        *reinterpret_cast<float4*>(pr + d0) = make_float4(o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2],
+                                                          o[mt][4 * j + 3]);
+      }
+    }
+    if (g == 0) *reinterpret_cast<float2*>(pr + D) = make_float2(mref, ltot);
+    return;
+  }
   const float inv = 1.0f / ltot;
   uint16_t* orow = out + (((int64_t)s * T + i) * c.H + h) * D;
 #pragma unroll
@@ -503,6 +648,58 @@ __global__ __launch_bounds__(kBlock * G) void k_prefill_attn(
   }
 }
 
+// Merge of the chunks of split tiles: per row, out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// A partial row is D + 4 floats: O[D], then the reference max and the sum (16-byte aligned rows).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, const int32_t* __restrict__ rows,
+                                                          const int32_t* __restrict__ counts,
+                                                          const int4* __restrict__ merges, const float* __restrict__ part,
+                                                          uint16_t* __restrict__ out) {
+  constexpr int MPH = kSlotsPerHead / 2;
+  constexpr int TPR = kBlock / BM;                 // threads per row
+  constexpr int CPT = D / TPR;                     // channels per thread
+  const int BH = c.B * c.H;
+  const int mi = blockIdx.x / BH, sh = blockIdx.x % BH;
+  if (mi >= counts[sh * 4 + 3]) return;
+  const int4 mg = merges[(int64_t)sh * MPH + mi];
+  const int r = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * CPT;
+  const int ri = mg.x + r;
+  if (ri >= mg.y) return;
+  const int s = sh / c.H, h = sh % c.H;
+  const float* base = part + ((int64_t)sh * kSlotsPerHead + mg.z) * BM * (D + 4) + (int64_t)r * (D + 4);
+  constexpr int64_t SLOT = (int64_t)BM * (D + 4);
+  float M = -INFINITY;
+  for (int k = 0; k < mg.w; ++k) M = fmaxf(M, base[k * SLOT + D]);
+  float acc[CPT];
+#pragma unroll
+  for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
+  float den = 0.0f;
+  for (int k = 0; k < mg.w; ++k) {
+    const float* pk = base + k * SLOT;
+    const float m = pk[D];
+    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+    den = fmaf(w, pk[D + 1], den);
+#pragma unroll
+    for (int x = 0; x < CPT; x += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(pk + d0 + x);
+      acc[x] = fmaf(w, v.x, acc[x]);
+      acc[x + 1] = fmaf(w, v.y, acc[x + 1]);
+      acc[x + 2] = fmaf(w, v.z, acc[x + 2]);
+      acc[x + 3] = fmaf(w, v.w, acc[x + 3]);
+    }
+  }
+  const float inv = 1.0f / den;
+  const int i = rows[(int64_t)sh * c.N + ri];
+  uint16_t* orow = out + (((int64_t)s * T + i) * c.H + h) * D + d0;
+#pragma unroll
+  for (int x = 0; x < CPT; x += 4) {
+    uint2 w;
+    w.x = (uint32_t)tr_f32_to_bf16(acc[x] * inv) | ((uint32_t)tr_f32_to_bf16(acc[x + 1] * inv) << 16);
+    w.y = (uint32_t)tr_f32_to_bf16(acc[x + 2] * inv) | ((uint32_t)tr_f32_to_bf16(acc[x + 3] * inv) << 16);
+    *reinterpret_cast<uint2*>(orow + x) = w;
+  }
+}
+
 }  // namespace
 
 tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint8_t* mode, int T,
@@ -510,20 +707,21 @@ tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q
   const CacheLayout& L = c->lay;
   const int BH = L.B * L.H;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
-  const int ranks = (T + BM - 1) / BM + 1;
+  const int uph = tr_prefill_units_per_head(T);
+  if (uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
   const int pend = p0 + T;                          // dense range [0, pend), 32-aligned tiles
   const int ntile = (pend + 31) / 32;
   {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
     if (L.D == 64) {
-      hipLaunchKernelGGL(k_prefill_compact<64>, dim3(BH), dim3(kBlock), 0, stream, L, T, mode, c->rows,
-                         c->row_counts, out);
+      hipLaunchKernelGGL(k_prefill_compact<64>, dim3(BH), dim3(kBlock), 0, stream, L, p0, T, window, mode, c->rows,
+                         c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
       TR_LAUNCH_CHECK();
       hipLaunchKernelGGL(k_prefill_dense<64>, dim3(BH * ntile), dim3(kBlock), 0, stream, L, layer, 0, ntile, pend,
                          c->np, kscale, c->dk, c->dv, c->dsz);
     } else {
-      hipLaunchKernelGGL(k_prefill_compact<128>, dim3(BH), dim3(kBlock), 0, stream, L, T, mode, c->rows,
-                         c->row_counts, out);
+      hipLaunchKernelGGL(k_prefill_compact<128>, dim3(BH), dim3(kBlock), 0, stream, L, p0, T, window, mode, c->rows,
+                         c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
       TR_LAUNCH_CHECK();
       hipLaunchKernelGGL(k_prefill_dense<128>, dim3(BH * ntile), dim3(kBlock), 0, stream, L, layer, 0, ntile, pend,
                          c->np, kscale, c->dk, c->dv, c->dsz);
@@ -531,12 +729,21 @@ tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q
     TR_LAUNCH_CHECK();
   }
   TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
-  if (L.D == 64)
-    hipLaunchKernelGGL((k_prefill_attn<64, TR_PREFILL_GROUPS>), dim3(BH * ranks), dim3(kBlock * TR_PREFILL_GROUPS), 0, stream, L, p0, T, window, c->np, q,
-                       c->rows, c->row_counts, c->dk, c->dv, c->dsz, out);
-  else
-    hipLaunchKernelGGL((k_prefill_attn<128, TR_PREFILL_GROUPS>), dim3(BH * ranks), dim3(kBlock * TR_PREFILL_GROUPS), 0, stream, L, p0, T, window, c->np, q,
-                       c->rows, c->row_counts, c->dk, c->dv, c->dsz, out);
+  if (L.D == 64) {
+    hipLaunchKernelGGL((k_prefill_attn<64, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
+                       stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk,
+                       c->dv, c->dsz, c->pf_part, out);
+    TR_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_prefill_merge<64>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
+                       c->row_counts, c->pf_merges, c->pf_part, out);
+  } else {
+    hipLaunchKernelGGL((k_prefill_attn<128, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
+                       stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk,
+                       c->dv, c->dsz, c->pf_part, out);
+    TR_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_prefill_merge<128>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
+                       c->row_counts, c->pf_merges, c->pf_part, out);
+  }
   TR_LAUNCH_CHECK();
   return TR_OK;
 }
