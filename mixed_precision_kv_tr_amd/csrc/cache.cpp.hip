@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "quant.h"
 
 namespace {
 
@@ -122,83 +123,14 @@ __global__ __launch_bounds__(kAssignBlock) void k_assign_slots(CacheLayout c, in
 }
 
 // Eq. (4) on one group = one (token, head) K or V vector of D bf16 values, held by the D/8
-// lanes that call this together (8 values each, one 128-bit load); the lanes shuffle, so every
-// lane of the group must call it, `live` or not.
+// lanes that call this together (8 values each); the lanes shuffle, so every lane of the group
+// must call it, `live` or not.
 template <int D>
 __device__ __forceinline__ void quantize_group(const CacheLayout& c, int layer, int s, int p, int h, int kv, int part,
                                                bool live, const uint16_t* src, int bval) {
-#pragma clang fp contract(off)
-  constexpr int LPG = D / 8;
-  uint4 raw = live ? *reinterpret_cast<const uint4*>(src + part * 8) : make_uint4(0, 0, 0, 0);
-  float x[8];
-  x[0] = tr_bf16_lo(raw.x); x[1] = tr_bf16_hi(raw.x);
-  x[2] = tr_bf16_lo(raw.y); x[3] = tr_bf16_hi(raw.y);
-  x[4] = tr_bf16_lo(raw.z); x[5] = tr_bf16_hi(raw.z);
-  x[6] = tr_bf16_lo(raw.w); x[7] = tr_bf16_hi(raw.w);
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) { mn = fminf(mn, x[e]); mx = fmaxf(mx, x[e]); }
-#pragma unroll
-  for (int off = 1; off < LPG; off <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  }
-  if (!live) return;
-
-  int cls = tr_class_of_bits(bval);
-  if (cls < 0) cls = 3;                                // flagged by the slot assignment
-  const int32_t slot = tr_prefix_row(c, layer, s, p)[cls];
-  const int P = c.ptok[cls];
-  const int32_t page = tr_ptab(c, layer, s, cls)[slot / P];
-  if (page < 0) return;                                // pool exhausted (flagged)
-  const int j = slot % P;
-  uint8_t* base = c.pool + (int64_t)page * c.page_bytes;
-  uint8_t* row = base + (kv ? c.v_off[cls] : c.k_off[cls]) + (int64_t)h * c.cb + (int64_t)j * c.rowb[cls];
-  if (h == 0 && kv == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p;
-
-  if (cls == 3) {                                      // b = 16: native bf16 storage
-    reinterpret_cast<uint4*>(row)[part] = raw;
-    return;
-  }
-  const int b = 2 << cls;
-  const float nlev = (float)((1 << b) - 1);
-  const float z = mn + 0.0f;                           // -0 -> +0
-  const float R = mx - mn;
-  const float sc = R / nlev + 0.0f;                    // correctly rounded divide; -0 -> +0
-  uint32_t code[8];
-  if (sc == 0.0f) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) code[e] = 0;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float d = x[e] - z;
-      const float r = d / sc;
-      float cf = rintf(r);
-      cf = fminf(fmaxf(cf, 0.0f), nlev);
-      code[e] = (uint32_t)cf;
-    }
-  }
-  if (part == 0) {
-    float2* side = reinterpret_cast<float2*>(base + (kv ? c.sv_off[cls] : c.sk_off[cls]));
-    side[(int64_t)h * P + j] = make_float2(sc, z);
-  }
-  if (b == 2) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= code[e] << (2 * e);
-    reinterpret_cast<uint16_t*>(row)[part] = (uint16_t)w;
-  } else if (b == 4) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= code[e] << (4 * e);
-    reinterpret_cast<uint32_t*>(row)[part] = w;
-  } else {
-    uint2 w;
-    w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-    reinterpret_cast<uint2*>(row)[part] = w;
-  }
+  QPiece qp;
+  eq4_piece<D>(qp, src, part, live, bval);
+  if (live) store_piece(c, layer, s, p, h, kv, part, qp);
 }
 
 // Grid-wide quantize of n tokens per sequence (after k_assign_slots).
@@ -346,6 +278,12 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 }  // namespace
 
+tr_status tr_assign_launch(tr_kv_cache* c, int layer, int p0, const uint8_t* bits, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(k_assign_slots, dim3(c->lay.B), dim3(kAssignBlock), 0, stream, c->lay, layer, p0, n, bits);
+  TR_LAUNCH_CHECK();
+  return TR_OK;
+}
+
 tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                           const uint8_t* bits, int n, hipStream_t stream) {
   const CacheLayout& L = c->lay;
@@ -358,8 +296,8 @@ tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, 
     TR_LAUNCH_CHECK();
     return TR_OK;
   }
-  hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kAssignBlock), 0, stream, L, layer, p0, n, bits);
-  TR_LAUNCH_CHECK();
+  const tr_status st = tr_assign_launch(c, layer, p0, bits, n, stream);
+  if (st != TR_OK) return st;
   const int64_t lanes = (int64_t)L.B * n * L.H * 2 * (L.D / 8);
   const int grid = (int)((lanes + kBlock - 1) / kBlock);
   if (L.D == 64)
@@ -559,10 +497,20 @@ tr_status tr_routed_attn_prefill(tr_kv_cache* c, int32_t layer, const void* q, c
   if ((int64_t)c->len[layer] + T > c->lay.N) return TR_ERR_CAPACITY;
   const int p0 = c->len[layer];
   hipStream_t st = (hipStream_t)stream;
-  tr_status s = tr_write_launch(c, layer, p0, (const uint16_t*)k, (const uint16_t*)v, bits, T, st);
+  // Short calls take the one-launch append and stage every dense tile from the pages; longer
+  // ones quantize and stage their own positions in one pass.
+  tr_status s;
+  int dense_to;
+  if (T <= 64) {
+    s = tr_write_launch(c, layer, p0, (const uint16_t*)k, (const uint16_t*)v, bits, T, st);
+    dense_to = (p0 + T + 31) / 32;
+  } else {
+    s = tr_prefill_write_launch(c, layer, p0, (const uint16_t*)k, (const uint16_t*)v, bits, T, st);
+    dense_to = (p0 + 31) / 32;
+  }
   if (s != TR_OK) return s;
   c->len[layer] += T;
-  return tr_prefill_launch(c, layer, p0, (const uint16_t*)q, mode, T, window, (uint16_t*)out, st);
+  return tr_prefill_launch(c, layer, p0, (const uint16_t*)q, mode, T, window, dense_to, (uint16_t*)out, st);
 }
 
 tr_status tr_kv_cache_export(const tr_kv_cache* c, int32_t layer, int32_t tok0, int32_t n, uint16_t* codes,

@@ -113,7 +113,14 @@ __device__ __forceinline__ uint16_t tr_f32_to_bf16(float f) {
 // Decode entry points implemented in decode.hip / prefill.hip.
 tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
                            uint16_t* out, hipStream_t stream);
+// tr_prefill_launch stages the dense tiles [0, dense_to) from the pages; the tiles above were
+// staged by tr_prefill_write_launch.
 tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint8_t* mode, int T,
-                            int window, uint16_t* out, hipStream_t stream);
+                            int window, int dense_to, uint16_t* out, hipStream_t stream);
 tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                           const uint8_t* bits, int n, hipStream_t stream);
+tr_status tr_assign_launch(tr_kv_cache* c, int layer, int p0, const uint8_t* bits, int n, hipStream_t stream);
+// Slot assignment, Eq. (4) quantize-write of positions [p0, p0 + T) and their dense staging for
+// the prefill attention (tiles from ceil(p0 / 32) on).
+tr_status tr_prefill_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                                  const uint8_t* bits, int T, hipStream_t stream);

@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "quant.h"
 
 namespace {
 
@@ -349,6 +350,79 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
   __syncthreads();
   // V^T rows: D rows x 32 positions (64 bytes each), 16 bytes per thread.
   for (int x = tid; x < D * 4; x += kBlock) {
+    const int d = x >> 2, seg = x & 3;
+    const uint4 v = *reinterpret_cast<const uint4*>(&vt[d][seg * 8]);
+    *reinterpret_cast<uint4*>(dv + ((int64_t)sh * D + d) * np + tile * 32 + seg * 8) = v;
+  }
+}
+
+// Eq. (4) quantize-write of a prefill call's positions [p0, p0 + T), fused with their dense
+// staging: one workgroup per (seq, head, 32 positions) of tiles [tile0, tile0 + ntile), D/8 lanes
+// per position doing its K and then its V group.  Codes, scales and page stores are the ones the
+// plain write path makes (the same Eq. (4) helpers); tiles from dense_from on also get their
+// dk / dsz rows and V^T columns from the values in registers, without re-reading the pages, and
+// zeros at positions >= p0 + T.  Runs after the slot assignment of the same positions.
+template <int D>
+__global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int layer, int p0, int T, int tile0,
+                                                         int ntile, int dense_from, int np, float kscale,
+                                                         const uint16_t* __restrict__ kin,
+                                                         const uint16_t* __restrict__ vin,
+                                                         const uint8_t* __restrict__ bits, uint16_t* __restrict__ dk,
+                                                         uint16_t* __restrict__ dv, float2* __restrict__ dsz) {
+  constexpr int LPG = D / 8;
+  constexpr int NT = 4 * D;
+  __shared__ _Float16 vt[D][40];
+  const int tile = tile0 + blockIdx.x % ntile, sh = blockIdx.x / ntile;
+  const int s = sh / c.H, h = sh % c.H;
+  const int tid = threadIdx.x, tk = tid / LPG, part = tid % LPG;
+  const int p = tile * 32 + tk, i = p - p0;
+  const bool live = i >= 0 && i < T;
+  const int64_t tok = (int64_t)s * T + (live ? i : 0);
+  const int bval = live ? bits[tok] : 16;
+  QPiece qk, qv;
+  eq4_piece<D>(qk, kin + (tok * c.H + h) * D, part, live, bval);
+  eq4_piece<D>(qv, vin + (tok * c.H + h) * D, part, live, bval);
+  if (live) {
+    store_piece(c, layer, s, p, h, 0, part, qk);
+    store_piece(c, layer, s, p, h, 1, part, qv);
+  }
+  if (tile < dense_from) return;                   // the tile also holds earlier positions
+  uint4 ko = make_uint4(0, 0, 0, 0);
+  float2 szk = make_float2(0.0f, 0.0f);
+  _Float16 vh[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vh[e] = (_Float16)0.0f;
+  if (live) {
+    if (qk.cls == 3) {
+      ko = qk.raw;
+      szk = make_float2(kscale, 0.0f);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (__float_as_uint((float)qk.code[2 * e]) >> 16) | (__float_as_uint((float)qk.code[2 * e + 1]) & 0xffff0000u);
+      ko = make_uint4(w[0], w[1], w[2], w[3]);
+      szk = make_float2(qk.s * kscale, qk.z * kscale);
+    }
+    if (qv.cls == 3) {
+      const uint32_t r[4] = {qv.raw.x, qv.raw.y, qv.raw.z, qv.raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vh[2 * e] = (_Float16)tr_bf16_lo(r[e]);
+        vh[2 * e + 1] = (_Float16)tr_bf16_hi(r[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vh[e] = (_Float16)fmaf(qv.s, (float)qv.code[e], qv.z);
+    }
+  }
+  *reinterpret_cast<uint4*>(dk + ((int64_t)sh * np + p) * D + part * 8) = ko;
+  if (part == 0) dsz[(int64_t)sh * np + p] = szk;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vt[part * 8 + e][vt_pos(tk)] = vh[e];
+  __syncthreads();
+  // V^T rows: D rows x 32 positions (64 bytes each), 16 bytes per thread.
+  for (int x = tid; x < D * 4; x += NT) {
     const int d = x >> 2, seg = x & 3;
     const uint4 v = *reinterpret_cast<const uint4*>(&vt[d][seg * 8]);
     *reinterpret_cast<uint4*>(dv + ((int64_t)sh * D + d) * np + tile * 32 + seg * 8) = v;
@@ -702,29 +776,52 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
 
 }  // namespace
 
+namespace {
+float prefill_kscale(int D) { return (float)(1.4426950408889634 / sqrt((double)D)); }
+}  // namespace
+
+tr_status tr_prefill_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                                  const uint8_t* bits, int T, hipStream_t stream) {
+  const CacheLayout& L = c->lay;
+  TrProfScope prof(c, TR_PROF_WRITE, stream);
+  const tr_status st = tr_assign_launch(c, layer, p0, bits, T, stream);
+  if (st != TR_OK) return st;
+  const int tile0 = p0 / 32, ntile = (p0 + T + 31) / 32 - tile0, dense_from = (p0 + 31) / 32;
+  const dim3 grid(L.B * L.H * ntile);
+  if (L.D == 64)
+    hipLaunchKernelGGL(k_prefill_write<64>, grid, dim3(4 * 64), 0, stream, L, layer, p0, T, tile0, ntile, dense_from,
+                       c->np, prefill_kscale(64), k, v, bits, c->dk, c->dv, c->dsz);
+  else
+    hipLaunchKernelGGL(k_prefill_write<128>, grid, dim3(4 * 128), 0, stream, L, layer, p0, T, tile0, ntile,
+                       dense_from, c->np, prefill_kscale(128), k, v, bits, c->dk, c->dv, c->dsz);
+  TR_LAUNCH_CHECK();
+  return TR_OK;
+}
+
 tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint8_t* mode, int T,
-                            int window, uint16_t* out, hipStream_t stream) {
+                            int window, int dense_to, uint16_t* out, hipStream_t stream) {
   const CacheLayout& L = c->lay;
   const int BH = L.B * L.H;
-  const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
+  const float kscale = prefill_kscale(L.D);
   const int uph = tr_prefill_units_per_head(T);
   if (uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
   const int pend = p0 + T;                          // dense range [0, pend), 32-aligned tiles
-  const int ntile = (pend + 31) / 32;
   {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
     if (L.D == 64) {
       hipLaunchKernelGGL(k_prefill_compact<64>, dim3(BH), dim3(kBlock), 0, stream, L, p0, T, window, mode, c->rows,
                          c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
       TR_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_prefill_dense<64>, dim3(BH * ntile), dim3(kBlock), 0, stream, L, layer, 0, ntile, pend,
-                         c->np, kscale, c->dk, c->dv, c->dsz);
+      if (dense_to > 0)
+        hipLaunchKernelGGL(k_prefill_dense<64>, dim3(BH * dense_to), dim3(kBlock), 0, stream, L, layer, 0, dense_to,
+                           pend, c->np, kscale, c->dk, c->dv, c->dsz);
     } else {
       hipLaunchKernelGGL(k_prefill_compact<128>, dim3(BH), dim3(kBlock), 0, stream, L, p0, T, window, mode, c->rows,
                          c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
       TR_LAUNCH_CHECK();
-      hipLaunchKernelGGL(k_prefill_dense<128>, dim3(BH * ntile), dim3(kBlock), 0, stream, L, layer, 0, ntile, pend,
-                         c->np, kscale, c->dk, c->dv, c->dsz);
+      if (dense_to > 0)
+        hipLaunchKernelGGL(k_prefill_dense<128>, dim3(BH * dense_to), dim3(kBlock), 0, stream, L, layer, 0, dense_to,
+                           pend, c->np, kscale, c->dk, c->dv, c->dsz);
     }
     TR_LAUNCH_CHECK();
   }

@@ -170,3 +170,24 @@ def test_capacity_is_checked_on_the_host(tr):
     assert err.value.status == 2
     assert tr.tr_kv_cache_length(cache, 0) == 0
     cache.close()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_write_bit_exact(tr, D):
+    """The prefill call quantizes its own K/V (fused with staging them for its attention): the
+    stored codes, scales and zeros must be the write path's, also for chunks that start inside a
+    32-position tile."""
+    say(f"prefill quantize-on-write bit-exact D={D}")
+    B, T, H = 2, 333, 3
+    case = random_case(B, T, H, D, window=8, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"full": 0.5, "local": 0.3, "skip": 0.2}, seed=40 + D, device="cuda")
+    cache = tr.tr_kv_cache_alloc(1, B, H, D, T)
+    cuts = [0, 70, 97, 200, T]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = lambda x: case[x][:, a:b].contiguous()
+        out = torch.empty((B, b - a, H, D), dtype=torch.bfloat16, device="cuda")
+        tr.tr_routed_attn_prefill(cache, 0, sl("q"), sl("k"), sl("v"), sl("bits"), sl("mode"), b - a, 8, out)
+    assert tr.tr_kv_cache_status(cache) == 0
+    exp = export_layer(tr, cache, 0, 0, T, B, H, D)
+    check_codes(exp, case["k"], case["v"], case["bits"], where=f"prefill D={D}")
+    cache.close()
