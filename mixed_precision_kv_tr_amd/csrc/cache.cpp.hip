@@ -15,12 +15,12 @@
 #include <string.h>
 
 #include "common.h"
-#include "quant.h"
+#include "kv_write.h"
 
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kAssignBlock = 1024;
+constexpr int kAssignBlock = TR_ASSIGN_THREADS;
 
 __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -40,86 +40,9 @@ __global__ void k_reset(CacheLayout c) {
   }
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
-
-// One workgroup per sequence.  Classes are counted in two 32-bit words of 16-bit fields
-// (classes 0|1 and 2|3); a chunk of kAssignBlock tokens adds at most 1024 to a field.
 __global__ __launch_bounds__(kAssignBlock) void k_assign_slots(CacheLayout c, int layer, int p0, int n,
                                                                const uint8_t* __restrict__ bits) {
-  __shared__ uint32_t wsum[2][kAssignBlock / 64];
-  __shared__ int32_t base[TR_NCLASS];
-  const int s = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int32_t* pre0 = tr_prefix_row(c, layer, s, p0);
-  if (tid < TR_NCLASS) base[tid] = pre0[tid];
-  __syncthreads();
-  int32_t n0[TR_NCLASS];
-#pragma unroll
-  for (int k = 0; k < TR_NCLASS; ++k) n0[k] = base[k];
-
-  for (int chunk = 0; chunk < n; chunk += kAssignBlock) {
-    const int i = chunk + tid;
-    uint32_t a = 0, b = 0;
-    if (i < n) {
-      int cls = tr_class_of_bits(bits[(int64_t)s * n + i]);
-      if (cls < 0) {
-        atomicOr(c.err, TR_ERRF_BAD_BITS);
-        cls = 3;                                     // stored as native; output unspecified
-      }
-      if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
-    }
-    uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
-    if (lane == 63) { wsum[0][wave] = ia; wsum[1][wave] = ib; }
-    __syncthreads();
-    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
-#pragma unroll
-    for (int w = 0; w < kAssignBlock / 64; ++w) {
-      const uint32_t xa = wsum[0][w], xb = wsum[1][w];
-      if (w < wave) { pa += xa; pb += xb; }
-      ta += xa; tb += xb;
-    }
-    ia += pa; ib += pb;
-    if (i < n) {
-      int32_t* row = const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + i + 1));
-      int4 v;
-      v.x = base[0] + (int)(ia & 0xffffu);
-      v.y = base[1] + (int)(ia >> 16);
-      v.z = base[2] + (int)(ib & 0xffffu);
-      v.w = base[3] + (int)(ib >> 16);
-      *reinterpret_cast<int4*>(row) = v;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      base[0] += (int)(ta & 0xffffu); base[1] += (int)(ta >> 16);
-      base[2] += (int)(tb & 0xffffu); base[3] += (int)(tb >> 16);
-    }
-    __syncthreads();
-  }
-  // Pages for the slots [n0, n1) of every class.  Pages kept from before a truncation are
-  // reused; only the page-table entries still empty take new pages from the pool.
-  if (tid < TR_NCLASS) {
-    const int k = tid;
-    const int P = c.ptok[k];
-    const int first = (n0[k] + P - 1) / P, last = (base[k] + P - 1) / P;
-    int32_t* pt = tr_ptab(c, layer, s, k);
-    int reuse = first;
-    while (reuse < last && pt[reuse] >= 0) ++reuse;
-    const int need = last - reuse;
-    if (need > 0) {
-      const int id0 = atomicAdd(c.next_page, need);
-      const bool ok = (int64_t)id0 + need <= c.pool_pages;
-      if (!ok) atomicOr(c.err, TR_ERRF_NO_PAGES);
-      for (int j = 0; j < need; ++j) pt[reuse + j] = ok ? id0 + j : -1;
-    }
-  }
+  tr_assign_slots_seq(c, layer, p0, n, bits, blockIdx.x);
 }
 
 // Eq. (4) on one group = one (token, head) K or V vector of D bf16 values, held by the D/8
@@ -174,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void k_write_small(CacheLayout c, int layer
       }
       if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
     }
-    const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    const uint32_t ia = tr_wave_incl_scan(a), ib = tr_wave_incl_scan(b);
     const int32_t* pre0 = tr_prefix_row(c, layer, s, p0);
     const int n0[4] = {pre0[0], pre0[1], pre0[2], pre0[3]};
     if (lane < n) {
@@ -278,12 +201,6 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 }  // namespace
 
-tr_status tr_assign_launch(tr_kv_cache* c, int layer, int p0, const uint8_t* bits, int n, hipStream_t stream) {
-  hipLaunchKernelGGL(k_assign_slots, dim3(c->lay.B), dim3(kAssignBlock), 0, stream, c->lay, layer, p0, n, bits);
-  TR_LAUNCH_CHECK();
-  return TR_OK;
-}
-
 tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                           const uint8_t* bits, int n, hipStream_t stream) {
   const CacheLayout& L = c->lay;
@@ -296,8 +213,8 @@ tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, 
     TR_LAUNCH_CHECK();
     return TR_OK;
   }
-  const tr_status st = tr_assign_launch(c, layer, p0, bits, n, stream);
-  if (st != TR_OK) return st;
+  hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kAssignBlock), 0, stream, L, layer, p0, n, bits);
+  TR_LAUNCH_CHECK();
   const int64_t lanes = (int64_t)L.B * n * L.H * 2 * (L.D / 8);
   const int grid = (int)((lanes + kBlock - 1) / kBlock);
   if (L.D == 64)
@@ -497,20 +414,10 @@ tr_status tr_routed_attn_prefill(tr_kv_cache* c, int32_t layer, const void* q, c
   if ((int64_t)c->len[layer] + T > c->lay.N) return TR_ERR_CAPACITY;
   const int p0 = c->len[layer];
   hipStream_t st = (hipStream_t)stream;
-  // Short calls take the one-launch append and stage every dense tile from the pages; longer
-  // ones quantize and stage their own positions in one pass.
-  tr_status s;
-  int dense_to;
-  if (T <= 64) {
-    s = tr_write_launch(c, layer, p0, (const uint16_t*)k, (const uint16_t*)v, bits, T, st);
-    dense_to = (p0 + T + 31) / 32;
-  } else {
-    s = tr_prefill_write_launch(c, layer, p0, (const uint16_t*)k, (const uint16_t*)v, bits, T, st);
-    dense_to = (p0 + 31) / 32;
-  }
-  if (s != TR_OK) return s;
-  c->len[layer] += T;
-  return tr_prefill_launch(c, layer, p0, (const uint16_t*)q, mode, T, window, dense_to, (uint16_t*)out, st);
+  const tr_status s = tr_prefill_launch(c, layer, p0, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                       bits, mode, T, window, (uint16_t*)out, st);
+  if (s == TR_OK) c->len[layer] += T;
+  return s;
 }
 
 tr_status tr_kv_cache_export(const tr_kv_cache* c, int32_t layer, int32_t tok0, int32_t n, uint16_t* codes,

@@ -110,17 +110,24 @@ __device__ __forceinline__ uint16_t tr_f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t tr_wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
 // Decode entry points implemented in decode.hip / prefill.hip.
 tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
                            uint16_t* out, hipStream_t stream);
-// tr_prefill_launch stages the dense tiles [0, dense_to) from the pages; the tiles above were
-// staged by tr_prefill_write_launch.
-tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint8_t* mode, int T,
-                            int window, int dense_to, uint16_t* out, hipStream_t stream);
+// The whole prefill call: Eq. (4) write of positions [p0, p0 + T), then routed attention of their
+// queries over [0, p0 + T).
+tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const uint8_t* bits, const uint8_t* mode, int T, int window,
+                            uint16_t* out, hipStream_t stream);
 tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                           const uint8_t* bits, int n, hipStream_t stream);
-tr_status tr_assign_launch(tr_kv_cache* c, int layer, int p0, const uint8_t* bits, int n, hipStream_t stream);
-// Slot assignment, Eq. (4) quantize-write of positions [p0, p0 + T) and their dense staging for
-// the prefill attention (tiles from ceil(p0 / 32) on).
-tr_status tr_prefill_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
-                                  const uint8_t* bits, int T, hipStream_t stream);

@@ -2,15 +2,19 @@
 // xllm-io.github.io: Eq. (2) for every query of the prompt, reading the K/V that Eq. (4) has
 // just written -- the inference paragraph after Algorithm 1).
 //
-// k_prefill_compact (one workgroup per (seq, head)): stable partition of the T query rows
-//   by mode -- full rows, then local rows -- so that a 128-row tile holds one mode and its
-//   key range is tight; skip rows (and rows with an invalid mode) get zeros right here.
-// k_prefill_dense (one workgroup per (seq, head, 32 positions)): the cache range the call's
-//   queries read, dequantized once into position-ordered scratch: K as its code in bf16
-//   (an exact integer <= 255, or the stored bf16 for b = 16) plus per-key
-//   (s_K, z_K) * log2(e)/sqrt(D); V as v_hat = s * c + z (fp32) rounded to fp16, stored
-//   channel-major.  Every 128-row tile of a (seq, head) then reads this instead of
-//   re-unpacking the pages (a (seq, head) stays on one XCD, so the re-reads hit its L2).
+// k_prefill_prep (one workgroup per (seq, head), plus one per sequence for the slot
+//   assignment of the call's positions): stable partition of the T query rows by mode -- full
+//   rows, then local rows -- so that a 128-row tile holds one mode and its key range is tight;
+//   skip rows (and rows with an invalid mode) get zeros right here.  Then the attention work
+//   units of the (seq, head).
+// Dense staging: the cache range the call's queries read, dequantized once into
+//   position-ordered scratch: K as its code in bf16 (an exact integer <= 255, or the stored
+//   bf16 for b = 16) plus per-key (s_K, z_K) * log2(e)/sqrt(D); V as v_hat = s * c + z (fp32)
+//   rounded to fp16, stored channel-major.  Every 128-row tile of a (seq, head) then reads this
+//   instead of re-unpacking the pages (a (seq, head) stays on one XCD, so the re-reads hit its
+//   L2).  k_prefill_write (one workgroup per (seq, head, 32 positions)) quantizes the call's
+//   own K/V into the pages and stages them from registers; k_prefill_dense stages the tiles
+//   holding earlier calls' positions from the pages.
 // k_prefill_attn (one workgroup = 4 waves = one 128-row tile), per 32-key tile:
 //     staging   16-byte copies of K rows and V^T rows into double-buffered LDS, the next
 //               tile's copies in flight in registers while the current one is computed.
@@ -31,7 +35,7 @@
 #include <type_traits>
 
 #include "common.h"
-#include "quant.h"
+#include "kv_write.h"
 
 namespace {
 
@@ -44,16 +48,6 @@ constexpr int BM = 128;       // query rows per workgroup (4 waves x 32)
 constexpr int BN = 32;        // keys per tile
 constexpr float kRescale = 8.0f;
 constexpr int kSlotsPerHead = TR_PREFILL_SLOTS;   // partial-result slots of one (seq, head)
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
 
 // Max / sum of a value and its copy 32 lanes away, with v_permlane32_swap (no LDS traffic): the
 // swap hands lanes 0-31 the upper half's value in its second result and lanes 32-63 the lower
@@ -75,11 +69,13 @@ __device__ __forceinline__ float xor32_sum(float v) {
 //   unit  = (r0 | full << 31, rend, kt0 | kt1 << 16, partial slot or -1)
 //   merge = (r0, rend, first slot, chunks)
 // Units are listed heaviest first: full tiles from the last (longest key range), then local.
+template <int NT>
 __device__ __forceinline__ void build_units(int sh, int p0, int window, int nfull, int nl, const int32_t* rl,
                                             int32_t* counts, int4* units, int4* merges) {
   constexpr int NC = 8;                            // candidate chunk sizes 16 << j key tiles
-  __shared__ int32_t red[kBlock / 64][NC];
-  __shared__ int32_t scan[kBlock / 64][3];
+  constexpr int NW = NT / 64;
+  __shared__ int32_t red[NW][NC];
+  __shared__ int32_t scan[NW][3];
   __shared__ int32_t kch_s, base_s[3];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nft = (nfull + BM - 1) / BM, nlt = (nl + BM - 1) / BM, ntl = nft + nlt;
@@ -97,7 +93,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
   int want[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) want[j] = 0;
-  for (int k = tid; k < ntl; k += kBlock) {
+  for (int k = tid; k < ntl; k += NT) {
     int r0, rend, full, klo, khi;
     tile_range(k, r0, rend, full, klo, khi);
     const int nkt = khi - klo;
@@ -118,7 +114,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
     int kch = 1 << 30;                             // no split
     for (int j = NC - 1; j >= 0; --j) {
       int tot = 0;
-      for (int w = 0; w < kBlock / 64; ++w) tot += red[w][j];
+      for (int w = 0; w < NW; ++w) tot += red[w][j];
       if (tot <= kSlotsPerHead) kch = 16 << j;
     }
     kch_s = kch;
@@ -127,7 +123,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
   __syncthreads();
   const int kch = kch_s;
   // pass B: units, slots and merges in tile order (exclusive scans carried across chunks)
-  for (int k0 = 0; k0 < ntl; k0 += kBlock) {
+  for (int k0 = 0; k0 < ntl; k0 += NT) {
     const int k = k0 + tid;
     int r0 = 0, rend = 0, full = 0, klo = 0, khi = 0, nch = 0;
     if (k < ntl) {
@@ -138,7 +134,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
     int incl[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      incl[x] = (int)wave_incl_scan((uint32_t)v[x]);
+      incl[x] = (int)tr_wave_incl_scan((uint32_t)v[x]);
       if (lane == 63) scan[wave][x] = incl[x];
     }
     __syncthreads();
@@ -159,7 +155,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
     if (tid == 0) {
 #pragma unroll
       for (int x = 0; x < 3; ++x)
-        for (int w = 0; w < kBlock / 64; ++w) base_s[x] += scan[w][x];
+        for (int w = 0; w < NW; ++w) base_s[x] += scan[w][x];
     }
     __syncthreads();
   }
@@ -171,74 +167,95 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
   }
 }
 
-// Stable partition of the query rows of one (seq, head) by mode.
-template <int D>
-__global__ __launch_bounds__(kBlock) void k_prefill_compact(CacheLayout c, int p0, int T, int window,
-                                                            const uint8_t* __restrict__ mode,
-                                                            int32_t* __restrict__ rows, int32_t* __restrict__ counts,
-                                                            int4* __restrict__ units, int4* __restrict__ merges,
-                                                            int uph, uint16_t* __restrict__ out) {
-  __shared__ uint32_t wsum[kBlock / 64];
-  __shared__ int32_t nfull_s, run_f, run_l;
-  const int sh = blockIdx.x;
+// Stable partition of the query rows of one (seq, head) by mode, NT threads: thread t takes
+// the contiguous rows [t R, t R + R), counts its full and local rows, one block-wide scan gives
+// every thread its output offsets, and a second pass over its rows writes them.
+template <int D, int NT>
+__device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p0, int T, int window,
+                                             const uint8_t* __restrict__ mode, int32_t* __restrict__ rows,
+                                             int32_t* __restrict__ counts, int4* __restrict__ units,
+                                             int4* __restrict__ merges, int uph, uint16_t* __restrict__ out) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t wf[NW], wl[NW];
   const int s = sh / c.H, h = sh % c.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int32_t* rl = rows + (int64_t)sh * c.N;
-  // pass 1: number of full rows
-  uint32_t nf = 0;
-  for (int i = tid; i < T; i += kBlock) nf += mode[((int64_t)s * T + i) * c.H + h] == TR_MODE_FULL;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o, 64);
-  if (lane == 0) wsum[wave] = nf;
-  __syncthreads();
-  if (tid == 0) {
-    nfull_s = (int)(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
-    run_f = 0;
-    run_l = 0;
+  const uint8_t* mcol = mode + (int64_t)s * T * c.H + h;
+  const int R = (T + NT - 1) / NT;
+  const int i0 = min(T, tid * R), i1 = min(T, i0 + R);
+  uint32_t nf = 0, nlc = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int m = mcol[(int64_t)i * c.H];
+    nf += m == TR_MODE_FULL;
+    nlc += m == TR_MODE_LOCAL;
+  }
+  const uint32_t incf = tr_wave_incl_scan(nf), incl = tr_wave_incl_scan(nlc);
+  if (lane == 63) {
+    wf[wave] = incf;
+    wl[wave] = incl;
   }
   __syncthreads();
-  const int nfull = nfull_s;
-  // pass 2: ordered positions; full and local counters packed in 16-bit halves
-  for (int chunk = 0; chunk < T; chunk += kBlock) {
-    const int i = chunk + tid;
-    int m = TR_MODE_SKIP;
-    if (i < T) {
-      m = mode[((int64_t)s * T + i) * c.H + h];
-      if (m > TR_MODE_FULL) {
-        atomicOr(c.err, TR_ERRF_BAD_MODE);
-        m = TR_MODE_SKIP;
-      }
-      if (m == TR_MODE_SKIP) {
-        uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * c.H + h) * D);
+  uint32_t bf = incf - nf, bl = incl - nlc, tf = 0, tl = 0;
 #pragma unroll
-        for (int x = 0; x < D / 8; ++x) o[x] = make_uint4(0, 0, 0, 0);
-      }
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) {
+      bf += wf[w];
+      bl += wl[w];
     }
-    const uint32_t one = (m == TR_MODE_FULL) ? 1u : (m == TR_MODE_LOCAL) ? (1u << 16) : 0u;
-    uint32_t incl = wave_incl_scan(one);
-    __syncthreads();
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
+    tf += wf[w];
+    tl += wl[w];
+  }
+  const int nfull = (int)tf, nl = (int)tl;
+  for (int i = i0; i < i1; ++i) {
+    int m = mcol[(int64_t)i * c.H];
+    if (m > TR_MODE_FULL) {
+      atomicOr(c.err, TR_ERRF_BAD_MODE);
+      m = TR_MODE_SKIP;
+    }
+    if (m == TR_MODE_FULL) {
+      rl[bf++] = i;
+    } else if (m == TR_MODE_LOCAL) {
+      rl[nfull + bl++] = i;
+    } else {
+      uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * c.H + h) * D);
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
-      if (w < wave) before += wsum[w];
-      total += wsum[w];
-    }
-    const uint32_t excl = incl - one + before;
-    if (m == TR_MODE_FULL) rl[run_f + (int)(excl & 0xffffu)] = i;
-    if (m == TR_MODE_LOCAL) rl[nfull + run_l + (int)(excl >> 16)] = i;
-    __syncthreads();
-    if (tid == 0) {
-      run_f += (int)(total & 0xffffu);
-      run_l += (int)(total >> 16);
+      for (int x = 0; x < D / 8; ++x) o[x] = make_uint4(0, 0, 0, 0);
     }
   }
+  __threadfence_block();
   __syncthreads();
-  const int nl = run_l;
-  build_units(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph,
-              merges + (int64_t)sh * (kSlotsPerHead / 2));
+  build_units<NT>(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph,
+                  merges + (int64_t)sh * (kSlotsPerHead / 2));
 }
+
+// Preparation of a prefill call, one launch: workgroups [0, B*H) compact the query rows of one
+// (seq, head) each and list its attention work units; with assign set, workgroups [B*H, B*H + B)
+// assign the slots and pages of the call's positions, one sequence each (independent work that
+// the quantize-write needs, so it overlaps the compaction instead of taking a launch of its own).
+template <int D>
+__global__ __launch_bounds__(TR_ASSIGN_THREADS) void k_prefill_prep(CacheLayout c, int layer, int p0, int T,
+                                                                    int window, const uint8_t* __restrict__ mode,
+                                                                    const uint8_t* __restrict__ bits, int32_t* rows,
+                                                                    int32_t* counts, int4* units, int4* merges,
+                                                                    int uph, uint16_t* __restrict__ out) {
+  const int BH = c.B * c.H;
+  if ((int)blockIdx.x >= BH) {
+    tr_assign_slots_seq(c, layer, p0, T, bits, blockIdx.x - BH);
+    return;
+  }
+  compact_rows<D, TR_ASSIGN_THREADS>(c, blockIdx.x, p0, T, window, mode, rows, counts, units, merges, uph, out);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin by id; this gives XCD x the contiguous run
+// [x * per, (x + 1) * per) of the n work items (grid = 8 * per, per = ceil(n / 8)), so that
+// neighbouring tiles -- which share cache lines of the dense scratch and of the class pages --
+// are written through the same L2.  -1 for the padding workgroups.
+__device__ __forceinline__ int xcd_linear(int n) {
+  const int per = (n + 7) >> 3;
+  const int lin = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  return lin < n ? lin : -1;
+}
+inline int xcd_grid(int n) { return ((n + 7) >> 3) << 3; }
 
 template <int NB>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int e) {
@@ -317,7 +334,9 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
                                                           uint16_t* __restrict__ dv, float2* __restrict__ dsz) {
   constexpr int DPL = D / 8;
   __shared__ _Float16 vt[D][40];                   // v_hat tile, channel-major (row = 80 B)
-  const int tile = tile0 + blockIdx.x % ntile, sh = blockIdx.x / ntile;
+  const int lin = xcd_linear(c.B * c.H * ntile);
+  if (lin < 0) return;
+  const int tile = tile0 + lin % ntile, sh = lin / ntile;
   const int s = sh / c.H, h = sh % c.H;
   const int tid = threadIdx.x, tk = tid / 8, part = tid % 8;
   const int p = tile * 32 + tk;
@@ -372,20 +391,20 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
   constexpr int LPG = D / 8;
   constexpr int NT = 4 * D;
   __shared__ _Float16 vt[D][40];
-  const int tile = tile0 + blockIdx.x % ntile, sh = blockIdx.x / ntile;
+  const int lin = xcd_linear(c.B * c.H * ntile);
+  if (lin < 0) return;
+  const int tile = tile0 + lin % ntile, sh = lin / ntile;
   const int s = sh / c.H, h = sh % c.H;
   const int tid = threadIdx.x, tk = tid / LPG, part = tid % LPG;
   const int p = tile * 32 + tk, i = p - p0;
   const bool live = i >= 0 && i < T;
   const int64_t tok = (int64_t)s * T + (live ? i : 0);
   const int bval = live ? bits[tok] : 16;
+  const int4 prefix = live ? *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, p)) : make_int4(0, 0, 0, 0);
   QPiece qk, qv;
   eq4_piece<D>(qk, kin + (tok * c.H + h) * D, part, live, bval);
   eq4_piece<D>(qv, vin + (tok * c.H + h) * D, part, live, bval);
-  if (live) {
-    store_piece(c, layer, s, p, h, 0, part, qk);
-    store_piece(c, layer, s, p, h, 1, part, qv);
-  }
+  if (live) store_pair(c, layer, s, p, h, part, qk, qv, prefix);
   if (tile < dense_from) return;                   // the tile also holds earlier positions
   uint4 ko = make_uint4(0, 0, 0, 0);
   float2 szk = make_float2(0.0f, 0.0f);
@@ -777,70 +796,61 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
 }  // namespace
 
 namespace {
-float prefill_kscale(int D) { return (float)(1.4426950408889634 / sqrt((double)D)); }
-}  // namespace
 
-tr_status tr_prefill_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
-                                  const uint8_t* bits, int T, hipStream_t stream) {
+template <int D>
+tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint8_t* bits, const uint8_t* mode, int T, int window,
+                           uint16_t* out, hipStream_t stream) {
   const CacheLayout& L = c->lay;
-  TrProfScope prof(c, TR_PROF_WRITE, stream);
-  const tr_status st = tr_assign_launch(c, layer, p0, bits, T, stream);
-  if (st != TR_OK) return st;
-  const int tile0 = p0 / 32, ntile = (p0 + T + 31) / 32 - tile0, dense_from = (p0 + 31) / 32;
-  const dim3 grid(L.B * L.H * ntile);
-  if (L.D == 64)
-    hipLaunchKernelGGL(k_prefill_write<64>, grid, dim3(4 * 64), 0, stream, L, layer, p0, T, tile0, ntile, dense_from,
-                       c->np, prefill_kscale(64), k, v, bits, c->dk, c->dv, c->dsz);
-  else
-    hipLaunchKernelGGL(k_prefill_write<128>, grid, dim3(4 * 128), 0, stream, L, layer, p0, T, tile0, ntile,
-                       dense_from, c->np, prefill_kscale(128), k, v, bits, c->dk, c->dv, c->dsz);
+  const int BH = L.B * L.H;
+  const float kscale = (float)(1.4426950408889634 / sqrt((double)D));
+  const int uph = tr_prefill_units_per_head(T);
+  if (uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
+  const int pend = p0 + T;
+  // Short calls take the one-launch append and stage every dense tile from the pages; longer
+  // ones assign their slots beside the row compaction, then quantize and stage their own
+  // positions in one pass (the dense pass keeps the tiles that hold earlier positions).
+  const bool fused = T > 64;
+  const int dense_to = fused ? (p0 + 31) / 32 : (pend + 31) / 32;
+  if (!fused) {
+    const tr_status st = tr_write_launch(c, layer, p0, k, v, bits, T, stream);
+    if (st != TR_OK) return st;
+  }
+  {
+    TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
+    hipLaunchKernelGGL(k_prefill_prep<D>, dim3(BH + (fused ? L.B : 0)), dim3(TR_ASSIGN_THREADS), 0, stream, L, layer,
+                       p0, T, window, mode, bits, c->rows, c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
+    TR_LAUNCH_CHECK();
+  }
+  if (fused) {
+    TrProfScope prof(c, TR_PROF_WRITE, stream);
+    const int tile0 = p0 / 32, ntile = (pend + 31) / 32 - tile0;
+    hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid(BH * ntile)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0, ntile,
+                       dense_to, c->np, kscale, k, v, bits, c->dk, c->dv, c->dsz);
+    TR_LAUNCH_CHECK();
+  }
+  if (dense_to > 0) {
+    TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
+    hipLaunchKernelGGL(k_prefill_dense<D>, dim3(xcd_grid(BH * dense_to)), dim3(kBlock), 0, stream, L, layer, 0, dense_to, pend,
+                       c->np, kscale, c->dk, c->dv, c->dsz);
+    TR_LAUNCH_CHECK();
+  }
+  TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
+  hipLaunchKernelGGL((k_prefill_attn<D, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
+                     stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
+                     c->dsz, c->pf_part, out);
+  TR_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_prefill_merge<D>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
+                     c->row_counts, c->pf_merges, c->pf_part, out);
   TR_LAUNCH_CHECK();
   return TR_OK;
 }
 
-tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint8_t* mode, int T,
-                            int window, int dense_to, uint16_t* out, hipStream_t stream) {
-  const CacheLayout& L = c->lay;
-  const int BH = L.B * L.H;
-  const float kscale = prefill_kscale(L.D);
-  const int uph = tr_prefill_units_per_head(T);
-  if (uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
-  const int pend = p0 + T;                          // dense range [0, pend), 32-aligned tiles
-  {
-    TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
-    if (L.D == 64) {
-      hipLaunchKernelGGL(k_prefill_compact<64>, dim3(BH), dim3(kBlock), 0, stream, L, p0, T, window, mode, c->rows,
-                         c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
-      TR_LAUNCH_CHECK();
-      if (dense_to > 0)
-        hipLaunchKernelGGL(k_prefill_dense<64>, dim3(BH * dense_to), dim3(kBlock), 0, stream, L, layer, 0, dense_to,
-                           pend, c->np, kscale, c->dk, c->dv, c->dsz);
-    } else {
-      hipLaunchKernelGGL(k_prefill_compact<128>, dim3(BH), dim3(kBlock), 0, stream, L, p0, T, window, mode, c->rows,
-                         c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
-      TR_LAUNCH_CHECK();
-      if (dense_to > 0)
-        hipLaunchKernelGGL(k_prefill_dense<128>, dim3(BH * dense_to), dim3(kBlock), 0, stream, L, layer, 0, dense_to,
-                           pend, c->np, kscale, c->dk, c->dv, c->dsz);
-    }
-    TR_LAUNCH_CHECK();
-  }
-  TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
-  if (L.D == 64) {
-    hipLaunchKernelGGL((k_prefill_attn<64, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
-                       stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk,
-                       c->dv, c->dsz, c->pf_part, out);
-    TR_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_prefill_merge<64>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
-                       c->row_counts, c->pf_merges, c->pf_part, out);
-  } else {
-    hipLaunchKernelGGL((k_prefill_attn<128, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
-                       stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk,
-                       c->dv, c->dsz, c->pf_part, out);
-    TR_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_prefill_merge<128>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
-                       c->row_counts, c->pf_merges, c->pf_part, out);
-  }
-  TR_LAUNCH_CHECK();
-  return TR_OK;
+}  // namespace
+
+tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const uint8_t* bits, const uint8_t* mode, int T, int window,
+                            uint16_t* out, hipStream_t stream) {
+  if (c->lay.D == 64) return prefill_launch_d<64>(c, layer, p0, q, k, v, bits, mode, T, window, out, stream);
+  return prefill_launch_d<128>(c, layer, p0, q, k, v, bits, mode, T, window, out, stream);
 }
