@@ -51,9 +51,12 @@ __global__ __launch_bounds__(kAssignBlock) void k_assign_slots(CacheLayout c, in
 template <int D>
 __device__ __forceinline__ void quantize_group(const CacheLayout& c, int layer, int s, int p, int h, int kv, int part,
                                                bool live, const uint16_t* src, int bval) {
-  QPiece qp;
-  eq4_piece<D>(qp, src, part, live, bval);
-  if (live) store_piece(c, layer, s, p, h, kv, part, qp);
+  const uint4 raw = *reinterpret_cast<const uint4*>(src + part * 8);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  const int cls = eq4_class(bval);
+  QVec<8> q;
+  eq4_quant<D, 8>(q, w, cls);
+  if (live) store_piece<8>(c, layer, s, p, h, kv, part, cls, q);
 }
 
 // Grid-wide quantize of n tokens per sequence (after k_assign_slots).
@@ -331,7 +334,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
                        sizeof(float) * (size_t)L.B * L.H * c->max_chunks * (L.D + 2)) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * L.H * L.N) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * L.H * 4) == hipSuccess;
-  c->np = (L.N + 31) / 32 * 32;
+  c->np = (L.N + 63) / 64 * 64;
   ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dsz, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;

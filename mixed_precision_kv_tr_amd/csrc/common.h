@@ -31,7 +31,7 @@ struct tr_kv_cache {
   int4* pf_merges;
   float* pf_part;
   int32_t pf_uph;
-  int32_t np;                     // N rounded up to a multiple of 32
+  int32_t np;                     // N rounded up to a multiple of 64 (the write tile)
   uint16_t* dk;
   uint16_t* dv;
   float2* dsz;

@@ -8,8 +8,8 @@
 // class) that needs pages), pages kept from before a truncation being reused first.
 //
 // Eq. (4): one token's K or V vector of one head quantized asymmetrically at its width b.
-// A group is the D bf16 values of one (token, head, K or V); D/8 consecutive lanes hold it, 8
-// values each (one 128-bit load).  In binary32, in this order: mx, mn exact; z = mn + 0 (no
+// A group is the D bf16 values of one (token, head, K or V); D/NV consecutive lanes hold it, NV
+// values each (8 or 16: one or two 128-bit loads).  In binary32, in this order: mx, mn exact; z = mn + 0 (no
 // -0); R = fl(mx - mn); s = fl(R / (2^b - 1)) + 0 with a correctly rounded divide;
 // code = rint(fl(fl(x - z) / s)), 0 for every value when s = 0.  b = 16 stores the bf16 input.
 #pragma once
@@ -101,123 +101,211 @@ __device__ __forceinline__ void tr_assign_slots_seq(const CacheLayout& c, int la
   }
 }
 
-struct QPiece {
-  uint4 raw;                  // this lane's 8 input values (bf16 bits)
-  int cls;                    // width class; 3 = native bf16
-  float s, z;                 // scale and zero point ((1, 0) for native storage)
-  uint32_t code[8];           // codes (b < 16)
-};
-
-// Loads and quantizes this lane's piece.  Every lane of the group must call it (the min/max are
-// reduced across the group's lanes); lanes with live = false contribute nothing.
-template <int D>
-__device__ __forceinline__ void eq4_piece(QPiece& qp, const uint16_t* src, int part, bool live, int bval) {
-#pragma clang fp contract(off)
-  constexpr int LPG = D / 8;
-  qp.raw = live ? *reinterpret_cast<const uint4*>(src + part * 8) : make_uint4(0, 0, 0, 0);
-  float x[8];
-  x[0] = tr_bf16_lo(qp.raw.x); x[1] = tr_bf16_hi(qp.raw.x);
-  x[2] = tr_bf16_lo(qp.raw.y); x[3] = tr_bf16_hi(qp.raw.y);
-  x[4] = tr_bf16_lo(qp.raw.z); x[5] = tr_bf16_hi(qp.raw.z);
-  x[6] = tr_bf16_lo(qp.raw.w); x[7] = tr_bf16_hi(qp.raw.w);
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) { mn = fminf(mn, x[e]); mx = fmaxf(mx, x[e]); }
-#pragma unroll
-  for (int off = 1; off < LPG; off <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+// Value of lane (lane ^ 1), (lane ^ 2), or of the mirrored lane within 8 / 16 lanes (DPP, no
+// LDS traffic).  After the two quad steps every lane holds its quad's result, and the mirror
+// within 8 (16) lanes pairs it with the other quad (half-row), so a min / max over a group of 4,
+// 8 or 16 lanes takes 2, 3 or 4 steps.
+template <int CTRL>
+__device__ __forceinline__ float tr_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// min / max that do not quiet NaNs first (v_minimum / v_maximum): the same result as fminf /
+// fmaxf for the finite values the cache stores, without a canonicalizing op per input.
+__device__ __forceinline__ float tr_min(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ float tr_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+template <int LPG>
+__device__ __forceinline__ void tr_group_minmax(float& mn, float& mx) {
+  static_assert(LPG == 4 || LPG == 8 || LPG == 16, "groups of 4, 8 or 16 lanes");
+  mn = tr_min(mn, tr_dpp<0xB1>(mn)); mx = tr_max(mx, tr_dpp<0xB1>(mx));     // quad_perm 1,0,3,2
+  mn = tr_min(mn, tr_dpp<0x4E>(mn)); mx = tr_max(mx, tr_dpp<0x4E>(mx));     // quad_perm 2,3,0,1
+  if constexpr (LPG >= 8) {
+    mn = tr_min(mn, tr_dpp<0x141>(mn)); mx = tr_max(mx, tr_dpp<0x141>(mx)); // row_half_mirror
   }
-  int cls = tr_class_of_bits(bval);
-  if (cls < 0) cls = 3;                                // flagged by the slot assignment
-  qp.cls = cls;
-  if (cls == 3) {
-    qp.s = 1.0f;
-    qp.z = 0.0f;
-    return;
-  }
-  const int b = 2 << cls;
-  const float nlev = (float)((1 << b) - 1);
-  const float z = mn + 0.0f;                           // -0 -> +0
-  const float R = mx - mn;
-  const float sc = R / nlev + 0.0f;                    // correctly rounded divide; -0 -> +0
-  qp.s = sc;
-  qp.z = z;
-  if (sc == 0.0f) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qp.code[e] = 0;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float d = x[e] - z;
-      const float r = d / sc;
-      float cf = rintf(r);
-      cf = fminf(fmaxf(cf, 0.0f), nlev);
-      qp.code[e] = (uint32_t)cf;
-    }
+  if constexpr (LPG == 16) {
+    mn = tr_min(mn, tr_dpp<0x140>(mn)); mx = tr_max(mx, tr_dpp<0x140>(mx)); // row_mirror
   }
 }
 
-// Stores this lane's piece into row j of a class page (base): head h, kv = 0 for K and 1 for V.
-__device__ __forceinline__ void put_piece(const CacheLayout& c, uint8_t* base, int j, int h, int kv, int part,
-                                          const QPiece& qp) {
-  const int cls = qp.cls;
-  uint8_t* row = base + (kv ? c.v_off[cls] : c.k_off[cls]) + (int64_t)h * c.cb + (int64_t)j * c.rowb[cls];
-  if (cls == 3) {                                      // b = 16: native bf16 storage
-    reinterpret_cast<uint4*>(row)[part] = qp.raw;
+// One of four per-class layout values for a lane's own class.  The values are pinned in
+// registers first: a select between loads of the kernel-argument array would otherwise become
+// one load with a lane-dependent index, a memory round trip on the store path.
+__device__ __forceinline__ int tr_sel4(int cls, const int32_t (&a)[TR_NCLASS]) {
+  int a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+  asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+  const int lo = (cls & 1) ? a1 : a0, hi = (cls & 1) ? a3 : a2;   // bit tests: selects, not a branch tree
+  return (cls & 2) ? hi : lo;
+}
+
+// Width class of a position (a bits value outside {2, 4, 8, 16} is flagged by the slot
+// assignment and stored natively).
+__device__ __forceinline__ int eq4_class(int bval) {
+  const int c = tr_class_of_bits(bval);
+  return c < 0 ? 3 : c;
+}
+
+// NV values of one group held by one lane (the group's D values are spread over D / NV lanes).
+template <int NV>
+struct QVec {
+  float f[NV];                // b < 16: the codes (exact small integers); b = 16: the input values
+  float s, z;                 // scale and zero point ((1, 0) for native storage)
+};
+
+// Quantizes this lane's NV values (w: NV/2 words of bf16 pairs, in channel order) at width
+// class cls.  Every lane of the group must call it (the min/max are reduced across the group's
+// D / NV lanes).
+//
+// The codes are rint(fl(d / s)), d = fl(x - z).  Each quotient is first taken as q = fl(d * r)
+// with r = v_rcp_f32(s) (1 ulp): |q - fl(d / s)| <= 2^-22 q <= 2^-14 for q <= 255, so when every
+// q of the lane lies more than 2^-12 from the nearest half-integer, rint(q) = rint(fl(d / s))
+// exactly.  Lanes that miss this (or with s = 0, or s outside [2^-100, 2^100]) redo their values
+// with the correctly rounded divide; the codes are the same either way.  On the fast path the
+// codes already lie in [0, 2^b - 1]: 0 <= d <= R and r ~ (2^b - 1) / R to within 2^-22.
+template <int D, int NV>
+__device__ __forceinline__ void eq4_quant(QVec<NV>& q, const uint32_t* w, int cls) {
+#pragma clang fp contract(off)
+  constexpr int LPG = D / NV;
+  float x[NV];
+#pragma unroll
+  for (int e = 0; e < NV / 2; ++e) {
+    x[2 * e] = tr_bf16_lo(w[e]);
+    x[2 * e + 1] = tr_bf16_hi(w[e]);
+  }
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < NV; ++e) {
+    mn = tr_min(mn, x[e]);
+    mx = tr_max(mx, x[e]);
+  }
+  tr_group_minmax<LPG>(mn, mx);
+  q.s = 1.0f;
+  q.z = 0.0f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) q.f[e] = x[e];
+  if (cls == 3) return;
+  const float nlev = (float)((1 << (2 << cls)) - 1);
+  const float z = mn + 0.0f;                           // -0 -> +0
+  const float R = mx - mn;
+  const float sc = R / nlev + 0.0f;                    // correctly rounded divide; -0 -> +0
+  q.s = sc;
+  q.z = z;
+  const float r = __builtin_amdgcn_rcpf(sc);
+  float dist = 0.0f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const float qq = (x[e] - z) * r;
+    const float cf = rintf(qq);
+    dist = fmaxf(dist, fabsf(qq - cf));
+    q.f[e] = cf;
+  }
+  if (!(dist < 0.5f - 0x1p-12f && sc >= 0x1p-100f && sc <= 0x1p100f)) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e)
+      q.f[e] = sc == 0.0f ? 0.0f : __builtin_amdgcn_fmed3f(rintf((x[e] - z) / sc), 0.0f, nlev);
+  }
+}
+
+// f as bf16 words (exact: codes are integers <= 255, b = 16 values were bf16): NV / 2 words.
+template <int NV>
+__device__ __forceinline__ void bf16_words(const QVec<NV>& q, uint32_t* out) {
+#pragma unroll
+  for (int e = 0; e < NV / 2; ++e)
+    out[e] = __builtin_amdgcn_perm(__float_as_uint(q.f[2 * e + 1]), __float_as_uint(q.f[2 * e]), 0x07060302u);
+}
+
+// Codes packed from the low bit up (code e at bit e * b) for b = 2, 4, 8: NV * b / 32 words of
+// out[NV / 4] are meaningful.  Branch-free over the three widths.
+template <int NV>
+__device__ __forceinline__ void code_words(const QVec<NV>& q, int cls, uint32_t* out) {
+  const int b = 2 << cls;
+  uint32_t A[NV / 4];                                  // 4 codes each, in the low 4b bits
+#pragma unroll
+  for (int k = 0; k < NV / 4; ++k) {
+    const uint32_t u0 = (uint32_t)q.f[4 * k], u1 = (uint32_t)q.f[4 * k + 1];
+    const uint32_t u2 = (uint32_t)q.f[4 * k + 2], u3 = (uint32_t)q.f[4 * k + 3];
+    A[k] = u0 | (u1 << b) | (u2 << (2 * b)) | (u3 << (3 * b));
+  }
+#pragma unroll
+  for (int k = 0; k < NV / 4; ++k) {
+    uint32_t v = A[k];                                 // b = 8
+    if (2 * k + 1 < NV / 4) {
+      const uint32_t v4 = A[2 * k] | (A[2 * k + 1] << 16);
+      v = cls == 1 ? v4 : v;
+    }
+    if (4 * k + 3 < NV / 4) {
+      const uint32_t v2 = A[4 * k] | (A[4 * k + 1] << 8) | (A[4 * k + 2] << 16) | (A[4 * k + 3] << 24);
+      v = cls == 0 ? v2 : v;
+    } else if (NV == 8 && k == 0) {
+      v = cls == 0 ? (A[0] | (A[1] << 8)) : v;         // b = 2, 8 codes: 16 bits
+    }
+    out[k] = v;
+  }
+}
+
+// Stores this lane's share of a page row (row = the row's first byte): NV * b / 8 bytes at
+// part * NV * b / 8.
+template <int NV>
+__device__ __forceinline__ void put_row(uint8_t* row, int part, int cls, const QVec<NV>& q) {
+  if (cls == 3) {
+    uint32_t w[NV / 2];
+    bf16_words<NV>(q, w);
+#pragma unroll
+    for (int x = 0; x < NV / 8; ++x)
+      reinterpret_cast<uint4*>(row)[part * (NV / 8) + x] = make_uint4(w[4 * x], w[4 * x + 1], w[4 * x + 2], w[4 * x + 3]);
     return;
   }
-  if (part == 0) {
-    float2* side = reinterpret_cast<float2*>(base + (kv ? c.sv_off[cls] : c.sk_off[cls]));
-    side[(int64_t)h * c.ptok[cls] + j] = make_float2(qp.s, qp.z);
-  }
-  if (cls == 0) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= qp.code[e] << (2 * e);
-    reinterpret_cast<uint16_t*>(row)[part] = (uint16_t)w;
-  } else if (cls == 1) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= qp.code[e] << (4 * e);
-    reinterpret_cast<uint32_t*>(row)[part] = w;
+  uint32_t w[NV / 4];
+  code_words<NV>(q, cls, w);
+  if constexpr (NV == 8) {
+    if (cls == 0) reinterpret_cast<uint16_t*>(row)[part] = (uint16_t)w[0];
+    else if (cls == 1) reinterpret_cast<uint32_t*>(row)[part] = w[0];
+    else reinterpret_cast<uint2*>(row)[part] = make_uint2(w[0], w[1]);
   } else {
-    uint2 w;
-    w.x = qp.code[0] | (qp.code[1] << 8) | (qp.code[2] << 16) | (qp.code[3] << 24);
-    w.y = qp.code[4] | (qp.code[5] << 8) | (qp.code[6] << 16) | (qp.code[7] << 24);
-    reinterpret_cast<uint2*>(row)[part] = w;
+    if (cls == 0) reinterpret_cast<uint32_t*>(row)[part] = w[0];
+    else if (cls == 1) reinterpret_cast<uint2*>(row)[part] = make_uint2(w[0], w[1]);
+    else reinterpret_cast<uint4*>(row)[part] = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+// Row of position slot-index j, head h, kv = 0 for K and 1 for V, in a page of class cls, and
+// its group's (s, z) entry (b < 16).
+__device__ __forceinline__ uint8_t* page_row(const CacheLayout& c, uint8_t* base, int j, int h, int kv, int cls) {
+  return base + tr_sel4(cls, kv ? c.v_off : c.k_off) + (int64_t)h * c.cb + (int64_t)j * tr_sel4(cls, c.rowb);
+}
+__device__ __forceinline__ float2* page_side(const CacheLayout& c, uint8_t* base, int j, int h, int kv, int cls) {
+  return reinterpret_cast<float2*>(base + tr_sel4(cls, kv ? c.sv_off : c.sk_off)) + (int64_t)h * tr_sel4(cls, c.ptok) + j;
+}
+
+// Stores this lane's piece (and, from the group's first lane, its (s, z) for b < 16).
+template <int NV>
+__device__ __forceinline__ void put_piece(const CacheLayout& c, uint8_t* base, int j, int h, int kv, int part, int cls,
+                                          const QVec<NV>& q) {
+  put_row<NV>(page_row(c, base, j, h, kv, cls), part, cls, q);
+  if (cls != 3 && part == 0) *page_side(c, base, j, h, kv, cls) = make_float2(q.s, q.z);
 }
 
 // Page of slot `slot` of class cls (nullptr when the pool was exhausted, which is flagged) and the
 // row within it.
 __device__ __forceinline__ uint8_t* slot_page(const CacheLayout& c, int layer, int s, int cls, int32_t slot, int& j) {
-  const int32_t page = tr_ptab(c, layer, s, cls)[slot >> c.ptok_log2[cls]];
-  j = slot & (c.ptok[cls] - 1);
-  return page < 0 ? nullptr : c.pool + (int64_t)page * c.page_bytes;
+  const int32_t* pt = c.ptab + ((int64_t)layer * c.B + s) * c.pt_stride + tr_sel4(cls, c.pt_off);
+  const int32_t page = pt[slot >> tr_sel4(cls, c.ptok_log2)];
+  j = slot & (tr_sel4(cls, c.ptok) - 1);
+  uint8_t* base = c.pool + (int64_t)max(page, 0) * c.page_bytes;
+  return page < 0 ? nullptr : base;
 }
 
 // Stores this lane's piece into its slot: position p of sequence s, head h, kv = 0 for K and 1 for
 // V.  The slot assignment must have run (prefix counts and page tables of position p).
+template <int NV>
 __device__ __forceinline__ void store_piece(const CacheLayout& c, int layer, int s, int p, int h, int kv, int part,
-                                            const QPiece& qp) {
+                                            int cls, const QVec<NV>& q) {
   int j;
-  uint8_t* base = slot_page(c, layer, s, qp.cls, tr_prefix_row(c, layer, s, p)[qp.cls], j);
+  uint8_t* base = slot_page(c, layer, s, cls, tr_prefix_row(c, layer, s, p)[cls], j);
   if (!base) return;
   if (h == 0 && kv == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p;
-  put_piece(c, base, j, h, kv, part, qp);
+  put_piece<NV>(c, base, j, h, kv, part, cls, q);
 }
 
-// Both pieces of position p, head h (K and V share the width class and so the slot), given the
-// position's prefix-count row.
-__device__ __forceinline__ void store_pair(const CacheLayout& c, int layer, int s, int p, int h, int part,
-                                           const QPiece& qk, const QPiece& qv, int4 prefix) {
-  const int cls = qk.cls;
-  const int32_t slot = cls == 0 ? prefix.x : cls == 1 ? prefix.y : cls == 2 ? prefix.z : prefix.w;
-  int j;
-  uint8_t* base = slot_page(c, layer, s, cls, slot, j);
-  if (!base) return;
-  if (h == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p;
-  put_piece(c, base, j, h, 0, part, qk);
-  put_piece(c, base, j, h, 1, part, qv);
+__device__ __forceinline__ int32_t slot_of(int cls, int4 prefix) {
+  const int lo = (cls & 1) ? prefix.y : prefix.x, hi = (cls & 1) ? prefix.w : prefix.z;
+  return (cls & 2) ? hi : lo;
 }

@@ -53,7 +53,9 @@ __host__ __device__ inline int tr_bits_of_class(int c) { return 2 << c; }
 
 // Class of a width value; -1 if the value is not one of 2, 4, 8, 16.
 __host__ __device__ inline int tr_class_of_bits(int b) {
-  return b == 2 ? 0 : b == 4 ? 1 : b == 8 ? 2 : b == 16 ? 3 : -1;
+  // b = 2^(c+1) for c in 0..3: a power of two in [2, 16] (branch-free: no compare tree on GPUs)
+  const bool ok = b >= 2 && b <= 16 && (b & (b - 1)) == 0;
+  return ok ? __builtin_ctz((unsigned)b) - 1 : -1;
 }
 
 __host__ __device__ inline const int32_t* tr_prefix_row(const CacheLayout& c, int layer, int seq, int p) {

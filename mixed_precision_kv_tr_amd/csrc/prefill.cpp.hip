@@ -376,11 +376,16 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 }
 
 // Eq. (4) quantize-write of a prefill call's positions [p0, p0 + T), fused with their dense
-// staging: one workgroup per (seq, head, 32 positions) of tiles [tile0, tile0 + ntile), D/8 lanes
-// per position doing its K and then its V group.  Codes, scales and page stores are the ones the
-// plain write path makes (the same Eq. (4) helpers); tiles from dense_from on also get their
-// dk / dsz rows and V^T columns from the values in registers, without re-reading the pages, and
-// zeros at positions >= p0 + T.  Runs after the slot assignment of the same positions.
+// staging: one workgroup of 4D threads per (seq, head, 64 positions) of tiles [tile0, tile0 +
+// ntile); D/16 lanes per position, 16 channels of K and of V each.  A lane issues all its loads
+// (bits, prefix counts, K, V), then the page-table lookup of its slot, and quantizes while that
+// lookup is in flight.  Codes, scales and page stores are the plain write path's (the same Eq. (4)
+// helpers); tiles from dense_from on also get their dk / dsz rows and V^T columns from the values
+// in registers, without re-reading the pages, and zeros at positions >= p0 + T.  Runs after the
+// slot assignment of the same positions.
+constexpr int kWriteTile = 64;
+constexpr int kWriteNV = 16;                       // channels per lane
+
 template <int D>
 __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int layer, int p0, int T, int tile0,
                                                          int ntile, int dense_from, int np, float kscale,
@@ -388,63 +393,66 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
                                                          const uint16_t* __restrict__ vin,
                                                          const uint8_t* __restrict__ bits, uint16_t* __restrict__ dk,
                                                          uint16_t* __restrict__ dv, float2* __restrict__ dsz) {
-  constexpr int LPG = D / 8;
+  constexpr int NV = kWriteNV;
+  constexpr int LPG = D / NV;
   constexpr int NT = 4 * D;
-  __shared__ _Float16 vt[D][40];
+  constexpr int TP = kWriteTile;
+  static_assert(NT / LPG == TP, "one position per lane group");
+  __shared__ _Float16 vt[D][TP + 8];               // v_hat tile, channel-major (row = 144 B)
   const int lin = xcd_linear(c.B * c.H * ntile);
   if (lin < 0) return;
   const int tile = tile0 + lin % ntile, sh = lin / ntile;
   const int s = sh / c.H, h = sh % c.H;
   const int tid = threadIdx.x, tk = tid / LPG, part = tid % LPG;
-  const int p = tile * 32 + tk, i = p - p0;
+  const int p = tile * TP + tk, i = p - p0;
   const bool live = i >= 0 && i < T;
+  // positions outside the call read the call's first position and store nothing
   const int64_t tok = (int64_t)s * T + (live ? i : 0);
-  const int bval = live ? bits[tok] : 16;
-  const int4 prefix = live ? *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, p)) : make_int4(0, 0, 0, 0);
-  QPiece qk, qv;
-  eq4_piece<D>(qk, kin + (tok * c.H + h) * D, part, live, bval);
-  eq4_piece<D>(qv, vin + (tok * c.H + h) * D, part, live, bval);
-  if (live) store_pair(c, layer, s, p, h, part, qk, qv, prefix);
-  if (tile < dense_from) return;                   // the tile also holds earlier positions
-  uint4 ko = make_uint4(0, 0, 0, 0);
-  float2 szk = make_float2(0.0f, 0.0f);
-  _Float16 vh[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vh[e] = (_Float16)0.0f;
-  if (live) {
-    if (qk.cls == 3) {
-      ko = qk.raw;
-      szk = make_float2(kscale, 0.0f);
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (__float_as_uint((float)qk.code[2 * e]) >> 16) | (__float_as_uint((float)qk.code[2 * e + 1]) & 0xffff0000u);
-      ko = make_uint4(w[0], w[1], w[2], w[3]);
-      szk = make_float2(qk.s * kscale, qk.z * kscale);
-    }
-    if (qv.cls == 3) {
-      const uint32_t r[4] = {qv.raw.x, qv.raw.y, qv.raw.z, qv.raw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vh[2 * e] = (_Float16)tr_bf16_lo(r[e]);
-        vh[2 * e + 1] = (_Float16)tr_bf16_hi(r[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vh[e] = (_Float16)fmaf(qv.s, (float)qv.code[e], qv.z);
-    }
+  const int bval = bits[tok];
+  const int4 prefix = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, live ? p : p0));
+  const uint4* ksrc = reinterpret_cast<const uint4*>(kin + (tok * c.H + h) * D + part * NV);
+  const uint4* vsrc = reinterpret_cast<const uint4*>(vin + (tok * c.H + h) * D + part * NV);
+  const uint4 k0 = ksrc[0], k1 = ksrc[1], v0 = vsrc[0], v1 = vsrc[1];
+  const int cls = eq4_class(bval);
+  int j;
+  uint8_t* base = slot_page(c, layer, s, cls, slot_of(cls, prefix), j);
+  QVec<NV> qk, qv;
+  {
+    const uint32_t w[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    eq4_quant<D, NV>(qk, w, cls);
   }
-  *reinterpret_cast<uint4*>(dk + ((int64_t)sh * np + p) * D + part * 8) = ko;
-  if (part == 0) dsz[(int64_t)sh * np + p] = szk;
+  {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    eq4_quant<D, NV>(qv, w, cls);
+  }
+  const bool dense = tile >= dense_from;           // else the tile also holds earlier positions
+  if (dense) {
+    uint32_t kw[NV / 2];
+    bf16_words<NV>(qk, kw);
+    uint4* krow = reinterpret_cast<uint4*>(dk + ((int64_t)sh * np + p) * D + part * NV);
+    krow[0] = live ? make_uint4(kw[0], kw[1], kw[2], kw[3]) : make_uint4(0, 0, 0, 0);
+    krow[1] = live ? make_uint4(kw[4], kw[5], kw[6], kw[7]) : make_uint4(0, 0, 0, 0);
+    if (part == 0)
+      dsz[(int64_t)sh * np + p] = live ? make_float2(qk.s * kscale, qk.z * kscale) : make_float2(0.0f, 0.0f);
+    // v_hat = fp16(s * f + z); b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's sign
+    const float zv = cls == 3 ? -0.0f : qv.z;
+    const int tpos = vt_pos(tk);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vt[part * 8 + e][vt_pos(tk)] = vh[e];
+    for (int e = 0; e < NV; ++e) vt[part * NV + e][tpos] = live ? (_Float16)fmaf(qv.s, qv.f[e], zv) : (_Float16)0.0f;
+  }
+  if (live && base) {
+    if (h == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p;
+    put_piece<NV>(c, base, j, h, 0, part, cls, qk);
+    put_piece<NV>(c, base, j, h, 1, part, cls, qv);
+  }
+  if (!dense) return;
   __syncthreads();
-  // V^T rows: D rows x 32 positions (64 bytes each), 16 bytes per thread.
-  for (int x = tid; x < D * 4; x += NT) {
-    const int d = x >> 2, seg = x & 3;
+  // V^T rows: D rows x TP positions (128 bytes each), 16 bytes per thread.
+  constexpr int SEGS = TP / 8;
+  for (int x = tid; x < D * SEGS; x += NT) {
+    const int d = x / SEGS, seg = x % SEGS;
     const uint4 v = *reinterpret_cast<const uint4*>(&vt[d][seg * 8]);
-    *reinterpret_cast<uint4*>(dv + ((int64_t)sh * D + d) * np + tile * 32 + seg * 8) = v;
+    *reinterpret_cast<uint4*>(dv + ((int64_t)sh * D + d) * np + tile * TP + seg * 8) = v;
   }
 }
 
@@ -811,7 +819,8 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   // ones assign their slots beside the row compaction, then quantize and stage their own
   // positions in one pass (the dense pass keeps the tiles that hold earlier positions).
   const bool fused = T > 64;
-  const int dense_to = fused ? (p0 + 31) / 32 : (pend + 31) / 32;
+  const int write_from = (p0 + kWriteTile - 1) / kWriteTile;      // first tile k_prefill_write stages
+  const int dense_to = fused ? min((pend + 31) / 32, write_from * (kWriteTile / 32)) : (pend + 31) / 32;
   if (!fused) {
     const tr_status st = tr_write_launch(c, layer, p0, k, v, bits, T, stream);
     if (st != TR_OK) return st;
@@ -824,9 +833,9 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   }
   if (fused) {
     TrProfScope prof(c, TR_PROF_WRITE, stream);
-    const int tile0 = p0 / 32, ntile = (pend + 31) / 32 - tile0;
-    hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid(BH * ntile)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0, ntile,
-                       dense_to, c->np, kscale, k, v, bits, c->dk, c->dv, c->dsz);
+    const int tile0 = p0 / kWriteTile, ntile = (pend + kWriteTile - 1) / kWriteTile - tile0;
+    hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid(BH * ntile)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
+                       ntile, write_from, c->np, kscale, k, v, bits, c->dk, c->dv, c->dsz);
     TR_LAUNCH_CHECK();
   }
   if (dense_to > 0) {
