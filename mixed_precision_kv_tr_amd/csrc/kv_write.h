@@ -19,58 +19,88 @@
 #define TR_ASSIGN_THREADS 1024
 
 // Slots and pages of positions [p0, p0 + n) of sequence s; blockDim.x must be TR_ASSIGN_THREADS.
-// Classes are counted in two 32-bit words of 16-bit fields (classes 0|1 and 2|3); a chunk of
-// TR_ASSIGN_THREADS positions adds at most that many to a field.
+// Thread t takes the contiguous positions [t R, t R + R): it counts their classes, one block-wide
+// scan of the four counts gives its slots, and a second pass writes the prefix rows.  The bits
+// are loaded 4 positions at a time (addresses clamped into the row, so the loads go out
+// together) and, for R <= 16, kept as 2-bit classes for the second pass.
 __device__ __forceinline__ void tr_assign_slots_seq(const CacheLayout& c, int layer, int p0, int n,
                                                     const uint8_t* __restrict__ bits, int s) {
-  constexpr int NW = TR_ASSIGN_THREADS / 64;
-  __shared__ uint32_t wsum[2][NW];
+  constexpr int NT = TR_ASSIGN_THREADS;
+  constexpr int NW = NT / 64;
+  __shared__ int32_t wsum[TR_NCLASS][NW];
   __shared__ int32_t base[TR_NCLASS];
+  if (n <= 0) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int32_t* pre0 = tr_prefix_row(c, layer, s, p0);
+  const uint8_t* brow = bits + (int64_t)s * n;
+  const int R = (n + NT - 1) / NT;
+  const int i0 = min(n, tid * R), i1 = min(n, i0 + R);
+  bool bad = false;
+  auto load4 = [&](int r0, int (&k)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + r0 + u;
+      const int cl = tr_class_of_bits(brow[min(i, n - 1)]);
+      bad |= i < i1 && cl < 0;
+      k[u] = cl < 0 ? 3 : cl;                        // stored as native; output unspecified
+    }
+  };
+  const bool cached = R <= 16;
+  uint32_t cp = 0;
+  int cnt[TR_NCLASS] = {0, 0, 0, 0};
+  for (int r0 = 0; r0 < R; r0 += 4) {
+    int k[4];
+    load4(r0, k);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + r0 + u >= i1) break;
+#pragma unroll
+      for (int x = 0; x < TR_NCLASS; ++x) cnt[x] += k[u] == x;
+      if (cached) cp |= (uint32_t)k[u] << (2 * (r0 + u));
+    }
+  }
+  if (bad) atomicOr(c.err, TR_ERRF_BAD_BITS);
+  int excl[TR_NCLASS];
+#pragma unroll
+  for (int x = 0; x < TR_NCLASS; ++x) {
+    const int incl = (int)tr_wave_incl_scan((uint32_t)cnt[x]);
+    excl[x] = incl - cnt[x];
+    if (lane == 63) wsum[x][wave] = incl;
+  }
   if (tid < TR_NCLASS) base[tid] = pre0[tid];
   __syncthreads();
-  int32_t n0[TR_NCLASS];
+  int32_t n0[TR_NCLASS], run[TR_NCLASS], tot[TR_NCLASS];
 #pragma unroll
-  for (int k = 0; k < TR_NCLASS; ++k) n0[k] = base[k];
-
-  for (int chunk = 0; chunk < n; chunk += TR_ASSIGN_THREADS) {
-    const int i = chunk + tid;
-    uint32_t a = 0, b = 0;
-    if (i < n) {
-      int cls = tr_class_of_bits(bits[(int64_t)s * n + i]);
-      if (cls < 0) {
-        atomicOr(c.err, TR_ERRF_BAD_BITS);
-        cls = 3;                                     // stored as native; output unspecified
-      }
-      if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
-    }
-    uint32_t ia = tr_wave_incl_scan(a), ib = tr_wave_incl_scan(b);
-    if (lane == 63) { wsum[0][wave] = ia; wsum[1][wave] = ib; }
-    __syncthreads();
-    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
+  for (int x = 0; x < TR_NCLASS; ++x) {
+    n0[x] = base[x];
+    int before = 0, all = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const uint32_t xa = wsum[0][w], xb = wsum[1][w];
-      if (w < wave) { pa += xa; pb += xb; }
-      ta += xa; tb += xb;
+      const int v = wsum[x][w];
+      before += w < wave ? v : 0;
+      all += v;
     }
-    ia += pa; ib += pb;
-    if (i < n) {
-      int32_t* row = const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + i + 1));
-      int4 v;
-      v.x = base[0] + (int)(ia & 0xffffu);
-      v.y = base[1] + (int)(ia >> 16);
-      v.z = base[2] + (int)(ib & 0xffffu);
-      v.w = base[3] + (int)(ib >> 16);
-      *reinterpret_cast<int4*>(row) = v;
+    run[x] = n0[x] + before + excl[x];
+    tot[x] = n0[x] + all;
+  }
+  // prefix row of position p0 + i + 1 = slots used up to and including position p0 + i
+  for (int r0 = 0; r0 < R; r0 += 4) {
+    int k[4];
+    if (cached) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) k[u] = (int)((cp >> (2 * (r0 + u))) & 3u);
+    } else {
+      load4(r0, k);
     }
-    __syncthreads();
-    if (tid == 0) {
-      base[0] += (int)(ta & 0xffffu); base[1] += (int)(ta >> 16);
-      base[2] += (int)(tb & 0xffffu); base[3] += (int)(tb >> 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + r0 + u;
+      if (i >= i1) break;
+#pragma unroll
+      for (int x = 0; x < TR_NCLASS; ++x) run[x] += k[u] == x;
+      *reinterpret_cast<int4*>(const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + i + 1))) =
+          make_int4(run[0], run[1], run[2], run[3]);
     }
-    __syncthreads();
   }
   // Pages for the slots [n0, n1) of class k = wave k.  Entries of the page table that are still
   // set (pages kept from before a truncation) are reused up to the first empty one; the rest
@@ -78,7 +108,9 @@ __device__ __forceinline__ void tr_assign_slots_seq(const CacheLayout& c, int la
   if (wave < TR_NCLASS) {
     const int k = wave;
     const int P = c.ptok[k];
-    const int first = (n0[k] + P - 1) / P, last = (base[k] + P - 1) / P;
+    const int n0k = k == 0 ? n0[0] : k == 1 ? n0[1] : k == 2 ? n0[2] : n0[3];
+    const int n1k = k == 0 ? tot[0] : k == 1 ? tot[1] : k == 2 ? tot[2] : tot[3];
+    const int first = (n0k + P - 1) / P, last = (n1k + P - 1) / P;
     int32_t* pt = tr_ptab(c, layer, s, k);
     int reuse = last;
     for (int j0 = first; j0 < last; j0 += 64) {
@@ -155,11 +187,11 @@ struct QVec {
 // D / NV lanes).
 //
 // The codes are rint(fl(d / s)), d = fl(x - z).  Each quotient is first taken as q = fl(d * r)
-// with r = v_rcp_f32(s) (1 ulp): |q - fl(d / s)| <= 2^-22 q <= 2^-14 for q <= 255, so when every
-// q of the lane lies more than 2^-12 from the nearest half-integer, rint(q) = rint(fl(d / s))
-// exactly.  Lanes that miss this (or with s = 0, or s outside [2^-100, 2^100]) redo their values
-// with the correctly rounded divide; the codes are the same either way.  On the fast path the
-// codes already lie in [0, 2^b - 1]: 0 <= d <= R and r ~ (2^b - 1) / R to within 2^-22.
+// with r = v_rcp_f32(s) (1 ulp): |q - fl(d / s)| <= 2^-22 q, and q <= n = 2^b - 1 (up to
+// rounding), so when every q of the lane lies more than n * 2^-20 from the nearest half-integer,
+// rint(q) = rint(fl(d / s)) exactly.  Lanes that miss this (or with s = 0, or s outside
+// [2^-100, 2^100]) redo their values with the correctly rounded divide; the codes are the same
+// either way.  On the fast path the codes already lie in [0, n]: 0 <= d <= R and r ~ n / R.
 template <int D, int NV>
 __device__ __forceinline__ void eq4_quant(QVec<NV>& q, const uint32_t* w, int cls) {
 #pragma clang fp contract(off)
@@ -197,7 +229,7 @@ __device__ __forceinline__ void eq4_quant(QVec<NV>& q, const uint32_t* w, int cl
     dist = fmaxf(dist, fabsf(qq - cf));
     q.f[e] = cf;
   }
-  if (!(dist < 0.5f - 0x1p-12f && sc >= 0x1p-100f && sc <= 0x1p100f)) {
+  if (!(dist < 0.5f - nlev * 0x1p-20f && sc >= 0x1p-100f && sc <= 0x1p100f)) {
 #pragma unroll
     for (int e = 0; e < NV; ++e)
       q.f[e] = sc == 0.0f ? 0.0f : __builtin_amdgcn_fmed3f(rintf((x[e] - z) / sc), 0.0f, nlev);

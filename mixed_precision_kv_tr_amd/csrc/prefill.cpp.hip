@@ -69,15 +69,19 @@ __device__ __forceinline__ float xor32_sum(float v) {
 //   unit  = (r0 | full << 31, rend, kt0 | kt1 << 16, partial slot or -1)
 //   merge = (r0, rend, first slot, chunks)
 // Units are listed heaviest first: full tiles from the last (longest key range), then local.
-template <int NT>
+// Sum over the 64 lanes of a wave (the result in every lane).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Run by one wave (the other waves of the workgroup do not take part): tiles in chunks of 64, one
+// per lane, with wave-level sums and scans only -- no workgroup barriers.
 __device__ __forceinline__ void build_units(int sh, int p0, int window, int nfull, int nl, const int32_t* rl,
                                             int32_t* counts, int4* units, int4* merges) {
   constexpr int NC = 8;                            // candidate chunk sizes 16 << j key tiles
-  constexpr int NW = NT / 64;
-  __shared__ int32_t red[NW][NC];
-  __shared__ int32_t scan[NW][3];
-  __shared__ int32_t kch_s, base_s[3];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int nft = (nfull + BM - 1) / BM, nlt = (nl + BM - 1) / BM, ntl = nft + nlt;
   auto tile_range = [&](int k, int& r0, int& rend, int& full, int& klo, int& khi) {
     full = k < nft;
@@ -93,7 +97,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
   int want[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) want[j] = 0;
-  for (int k = tid; k < ntl; k += NT) {
+  for (int k = lane; k < ntl; k += 64) {
     int r0, rend, full, klo, khi;
     tile_range(k, r0, rend, full, klo, khi);
     const int nkt = khi - klo;
@@ -103,46 +107,26 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
       want[j] += (nkt > kc) ? (nkt + kc - 1) / kc : 0;
     }
   }
+  int kch = 1 << 30;                               // no split
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) want[j] += __shfl_xor(want[j], o, 64);
-    if (lane == 0) red[wave][j] = want[j];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int kch = 1 << 30;                             // no split
-    for (int j = NC - 1; j >= 0; --j) {
-      int tot = 0;
-      for (int w = 0; w < NW; ++w) tot += red[w][j];
-      if (tot <= kSlotsPerHead) kch = 16 << j;
-    }
-    kch_s = kch;
-    base_s[0] = base_s[1] = base_s[2] = 0;
-  }
-  __syncthreads();
-  const int kch = kch_s;
+  for (int j = NC - 1; j >= 0; --j)
+    if (wave_sum(want[j]) <= kSlotsPerHead) kch = 16 << j;
   // pass B: units, slots and merges in tile order (exclusive scans carried across chunks)
-  for (int k0 = 0; k0 < ntl; k0 += NT) {
-    const int k = k0 + tid;
+  int base[3] = {0, 0, 0};
+  for (int k0 = 0; k0 < ntl; k0 += 64) {
+    const int k = k0 + lane;
     int r0 = 0, rend = 0, full = 0, klo = 0, khi = 0, nch = 0;
     if (k < ntl) {
       tile_range(k, r0, rend, full, klo, khi);
       nch = (khi - klo > kch) ? (khi - klo + kch - 1) / kch : 1;
     }
     const int v[3] = {nch, nch > 1 ? nch : 0, nch > 1 ? 1 : 0};
-    int incl[3];
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      incl[x] = (int)tr_wave_incl_scan((uint32_t)v[x]);
-      if (lane == 63) scan[wave][x] = incl[x];
-    }
-    __syncthreads();
     int pos[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      pos[x] = base_s[x] + incl[x] - v[x];
-      for (int w = 0; w < wave; ++w) pos[x] += scan[w][x];
+      const int incl = (int)tr_wave_incl_scan((uint32_t)v[x]);
+      pos[x] = base[x] + incl - v[x];
+      base[x] += __shfl(incl, 63, 64);
     }
     if (k < ntl) {
       for (int cc = 0; cc < nch; ++cc) {
@@ -151,25 +135,20 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
       }
       if (nch > 1) merges[pos[2]] = make_int4(r0, rend, pos[1], nch);
     }
-    __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-      for (int x = 0; x < 3; ++x)
-        for (int w = 0; w < NW; ++w) base_s[x] += scan[w][x];
-    }
-    __syncthreads();
   }
-  if (tid == 0) {
+  if (lane == 0) {
     counts[sh * 4 + 0] = nfull;
     counts[sh * 4 + 1] = nl;
-    counts[sh * 4 + 2] = base_s[0];
-    counts[sh * 4 + 3] = base_s[2];
+    counts[sh * 4 + 2] = base[0];
+    counts[sh * 4 + 3] = base[2];
   }
 }
 
 // Stable partition of the query rows of one (seq, head) by mode, NT threads: thread t takes
 // the contiguous rows [t R, t R + R), counts its full and local rows, one block-wide scan gives
-// every thread its output offsets, and a second pass over its rows writes them.
+// every thread its output offsets, and a second pass over its rows writes them.  The modes are
+// loaded 4 rows at a time (addresses clamped into the column, so the loads go out together) and,
+// for R <= 16, kept as 2-bit codes for the second pass.
 template <int D, int NT>
 __device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p0, int T, int window,
                                              const uint8_t* __restrict__ mode, int32_t* __restrict__ rows,
@@ -183,11 +162,27 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p
   const uint8_t* mcol = mode + (int64_t)s * T * c.H + h;
   const int R = (T + NT - 1) / NT;
   const int i0 = min(T, tid * R), i1 = min(T, i0 + R);
+  // 2-bit code of a row's mode: 0 skip, 1 local, 2 full, 3 invalid (flagged, treated as skip)
+  auto load4 = [&](int r0, uint32_t (&m)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + r0 + u;
+      const uint32_t x = mcol[(int64_t)min(i, T - 1) * c.H];
+      m[u] = i < i1 ? (x > TR_MODE_FULL ? 3u : x) : 0u;
+    }
+  };
+  const bool cached = R <= 16;
+  uint32_t mp = 0;
   uint32_t nf = 0, nlc = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int m = mcol[(int64_t)i * c.H];
-    nf += m == TR_MODE_FULL;
-    nlc += m == TR_MODE_LOCAL;
+  for (int r0 = 0; r0 < R; r0 += 4) {
+    uint32_t m[4];
+    load4(r0, m);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      nf += m[u] == TR_MODE_FULL;
+      nlc += m[u] == TR_MODE_LOCAL;
+      if (cached && r0 + u < 16) mp |= m[u] << (2 * (r0 + u));
+    }
   }
   const uint32_t incf = tr_wave_incl_scan(nf), incl = tr_wave_incl_scan(nlc);
   if (lane == 63) {
@@ -206,26 +201,34 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p
     tl += wl[w];
   }
   const int nfull = (int)tf, nl = (int)tl;
-  for (int i = i0; i < i1; ++i) {
-    int m = mcol[(int64_t)i * c.H];
-    if (m > TR_MODE_FULL) {
-      atomicOr(c.err, TR_ERRF_BAD_MODE);
-      m = TR_MODE_SKIP;
-    }
-    if (m == TR_MODE_FULL) {
-      rl[bf++] = i;
-    } else if (m == TR_MODE_LOCAL) {
-      rl[nfull + bl++] = i;
-    } else {
-      uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * c.H + h) * D);
+  for (int r0 = 0; r0 < R; r0 += 4) {
+    uint32_t m[4];
+    if (cached) {
 #pragma unroll
-      for (int x = 0; x < D / 8; ++x) o[x] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) m[u] = (mp >> (2 * (r0 + u))) & 3u;
+    } else {
+      load4(r0, m);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + r0 + u;
+      if (i >= i1) break;
+      if (m[u] == TR_MODE_FULL) {
+        rl[bf++] = i;
+      } else if (m[u] == TR_MODE_LOCAL) {
+        rl[nfull + bl++] = i;
+      } else {
+        if (m[u] == 3u) atomicOr(c.err, TR_ERRF_BAD_MODE);
+        uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * c.H + h) * D);
+#pragma unroll
+        for (int x = 0; x < D / 8; ++x) o[x] = make_uint4(0, 0, 0, 0);
+      }
     }
   }
   __threadfence_block();
   __syncthreads();
-  build_units<NT>(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph,
-                  merges + (int64_t)sh * (kSlotsPerHead / 2));
+  if (wave == 0)
+    build_units(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph, merges + (int64_t)sh * (kSlotsPerHead / 2));
 }
 
 // Preparation of a prefill call, one launch: workgroups [0, B*H) compact the query rows of one
@@ -434,9 +437,11 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
     krow[1] = live ? make_uint4(kw[4], kw[5], kw[6], kw[7]) : make_uint4(0, 0, 0, 0);
     if (part == 0)
       dsz[(int64_t)sh * np + p] = live ? make_float2(qk.s * kscale, qk.z * kscale) : make_float2(0.0f, 0.0f);
-    // v_hat = fp16(s * f + z); b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's sign
+    // v_hat = fp16(s * f + z); b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's sign.
+    // The column is XOR-swizzled by 16 * (part & 3): the lanes of one store hold 16 positions of
+    // 4 parts whose rows are 16 rows (a multiple of 64 banks) apart, so without it they collide.
     const float zv = cls == 3 ? -0.0f : qv.z;
-    const int tpos = vt_pos(tk);
+    const int tpos = vt_pos(tk) ^ (16 * (part & 3));
 #pragma unroll
     for (int e = 0; e < NV; ++e) vt[part * NV + e][tpos] = live ? (_Float16)fmaf(qv.s, qv.f[e], zv) : (_Float16)0.0f;
   }
@@ -447,11 +452,12 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
   }
   if (!dense) return;
   __syncthreads();
-  // V^T rows: D rows x TP positions (128 bytes each), 16 bytes per thread.
+  // V^T rows: D rows x TP positions (128 bytes each), 16 bytes per thread; row d was written by
+  // part d / 16, so its segment seg sits at seg ^ 2 (part & 3).
   constexpr int SEGS = TP / 8;
   for (int x = tid; x < D * SEGS; x += NT) {
     const int d = x / SEGS, seg = x % SEGS;
-    const uint4 v = *reinterpret_cast<const uint4*>(&vt[d][seg * 8]);
+    const uint4 v = *reinterpret_cast<const uint4*>(&vt[d][8 * (seg ^ (2 * ((d / NV) & 3)))]);
     *reinterpret_cast<uint4*>(dv + ((int64_t)sh * D + d) * np + tile * TP + seg * 8) = v;
   }
 }

@@ -1,6 +1,7 @@
 """Host check of the argument behind the quantizer's fast path (the GPU kernels round each
 quotient d / s of Eq. (4) from q = fl(d * r), r an approximate reciprocal of s with at most 1 ulp
-error, and fall back to the correctly rounded divide when q lies within 2^-12 of a half-integer).
+error, and fall back to the correctly rounded divide when q lies within (2^b - 1) * 2^-20 of a
+half-integer).
 
 The claim: whenever q passes that test, rint(q) equals rint(fl(d / s)).  It is checked here in
 float32 with the reciprocal pushed a full ulp either way, on Eq. (4)'s own inputs (bf16 groups,
@@ -8,7 +9,9 @@ b in {2, 4, 8}) and on quotients steered next to half-integers, where the claim 
 
 import numpy as np
 
-MARGIN = np.float32(0.5 - 2.0 ** -12)
+
+def margin(b: int) -> np.float32:
+    return np.float32(0.5) - np.float32(2 ** b - 1) * np.float32(2.0 ** -20)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -17,7 +20,7 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
-def check(d: np.ndarray, s: np.ndarray):
+def check(d: np.ndarray, s: np.ndarray, b: int):
     d = d.astype(np.float32)
     s = s.astype(np.float32)
     exact = np.rint(d / s)
@@ -26,7 +29,7 @@ def check(d: np.ndarray, s: np.ndarray):
     for r in (r0, np.nextafter(r0, np.float32(np.inf)), np.nextafter(r0, np.float32(0))):
         q = d * r
         cf = np.rint(q)
-        ok = np.abs(q - cf) < MARGIN
+        ok = np.abs(q - cf) < margin(b)
         assert np.array_equal(cf[ok], exact[ok]), "fast path disagrees with the exact divide"
         fast_taken += int(ok.sum())
     return fast_taken
@@ -42,7 +45,7 @@ def test_eq4_groups():
             z = mn + np.float32(0)
             s = (mx - mn) / nlev + np.float32(0)
             d = x - z[:, None]
-            taken = check(d, np.broadcast_to(s[:, None], d.shape))
+            taken = check(d, np.broadcast_to(s[:, None], d.shape), b)
             assert taken > 0.99 * 3 * d.size
 
 
@@ -59,4 +62,4 @@ def test_near_half_integers():
             direction = np.float32(np.inf) if steps > 0 else np.float32(0)
             for _ in range(abs(steps)):
                 dd = np.nextafter(dd, direction)
-            check(dd, s)
+            check(dd, s, b)
