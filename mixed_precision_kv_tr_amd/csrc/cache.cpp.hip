@@ -81,66 +81,119 @@ __global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int la
 }
 
 // Small appends (n <= 64 tokens per sequence, e.g. one decode step): slot assignment, page
-// allocation and quantization of one sequence in one workgroup -- a single launch.
+// allocation and quantization of one sequence in one workgroup -- a single launch.  The inputs of
+// the first two passes are loaded before anything else; wave 0 then assigns the slots and pages
+// (keeping every new position's slot and the class pages it touches in LDS), and after one
+// barrier the groups are quantized and stored without another global lookup.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_write_small(CacheLayout c, int layer, int p0, int n,
                                                         const uint16_t* __restrict__ kin,
                                                         const uint16_t* __restrict__ vin,
                                                         const uint8_t* __restrict__ bits) {
   constexpr int LPG = D / 8;
+  constexpr int GPI = kBlock / LPG;                // groups per pass
+  constexpr int NPF = 2;                           // passes loaded up front
+  constexpr int kPg = 32;                          // pages per class one call can touch: n <= 64, >= 4 tokens a page
+  __shared__ int32_t tslot[64], tcls[64];
+  __shared__ int32_t pgs[TR_NCLASS][kPg];
+  __shared__ int32_t fps[TR_NCLASS];
   const int s = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, part = tid % LPG;
+  const int ngroups = n * c.H * 2;
+  auto src_of = [&](int gid) {
+    const int g = gid < ngroups ? gid : 0;
+    const int kv = g & 1, th = g >> 1;
+    const int h = th % c.H, i = th / c.H;
+    return (kv ? vin : kin) + (((int64_t)s * n + i) * c.H + h) * D + part * 8;
+  };
+  uint4 raw[NPF];
+#pragma unroll
+  for (int x = 0; x < NPF; ++x) raw[x] = *reinterpret_cast<const uint4*>(src_of(x * GPI + tid / LPG));
+
   if (tid < 64) {
-    uint32_t a = 0, b = 0;
+    int cls = 3;
     if (lane < n) {
-      int cls = tr_class_of_bits(bits[(int64_t)s * n + lane]);
+      cls = tr_class_of_bits(bits[(int64_t)s * n + lane]);
       if (cls < 0) {
         atomicOr(c.err, TR_ERRF_BAD_BITS);
         cls = 3;
       }
+    }
+    uint32_t a = 0, b = 0;
+    if (lane < n) {
       if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
     }
     const uint32_t ia = tr_wave_incl_scan(a), ib = tr_wave_incl_scan(b);
-    const int32_t* pre0 = tr_prefix_row(c, layer, s, p0);
-    const int n0[4] = {pre0[0], pre0[1], pre0[2], pre0[3]};
+    const int4 pre0 = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, p0));
+    const int n0[4] = {pre0.x, pre0.y, pre0.z, pre0.w};
+    const int inc[4] = {(int)(ia & 0xffffu), (int)(ia >> 16), (int)(ib & 0xffffu), (int)(ib >> 16)};
     if (lane < n) {
-      int4 v;
-      v.x = n0[0] + (int)(ia & 0xffffu);
-      v.y = n0[1] + (int)(ia >> 16);
-      v.z = n0[2] + (int)(ib & 0xffffu);
-      v.w = n0[3] + (int)(ib >> 16);
-      *reinterpret_cast<int4*>(const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + lane + 1))) = v;
+      *reinterpret_cast<int4*>(const_cast<int32_t*>(tr_prefix_row(c, layer, s, p0 + lane + 1))) =
+          make_int4(n0[0] + inc[0], n0[1] + inc[1], n0[2] + inc[2], n0[3] + inc[3]);
+      const int own = cls == 0 ? inc[0] : cls == 1 ? inc[1] : cls == 2 ? inc[2] : inc[3];
+      const int nb = cls == 0 ? n0[0] : cls == 1 ? n0[1] : cls == 2 ? n0[2] : n0[3];
+      tslot[lane] = nb + own - 1;                  // slots before it in its class, plus its own
+      tcls[lane] = cls;
     }
     const uint32_t ta = __shfl(ia, 63, 64), tb = __shfl(ib, 63, 64);
-    if (lane < TR_NCLASS) {
-      const int k = lane;
-      const int tot = k == 0 ? (int)(ta & 0xffffu) : k == 1 ? (int)(ta >> 16) : k == 2 ? (int)(tb & 0xffffu) : (int)(tb >> 16);
-      const int P = c.ptok[k];
-      const int first = (n0[k] + P - 1) / P, last = (n0[k] + tot + P - 1) / P;
-      int32_t* pt = tr_ptab(c, layer, s, k);
-      int reuse = first;
-      while (reuse < last && pt[reuse] >= 0) ++reuse;
-      const int need = last - reuse;
-      if (need > 0) {
-        const int id0 = atomicAdd(c.next_page, need);
-        const bool ok = (int64_t)id0 + need <= c.pool_pages;
-        if (!ok) atomicOr(c.err, TR_ERRF_NO_PAGES);
-        for (int j = 0; j < need; ++j) pt[reuse + j] = ok ? id0 + j : -1;
-      }
+    // Pages: lanes 16k .. 16k + 15 take class k, entries fp + (lane & 15) and fp + 16 + (lane & 15)
+    // of its page table, fp = the page of its first new slot.  Entries from the first page no slot
+    // used before are reused while set (pages kept from before a truncation); the rest are new.
+    const int k = lane >> 4, jl = lane & 15;
+    const int tot = k == 0 ? (int)(ta & 0xffffu) : k == 1 ? (int)(ta >> 16) : k == 2 ? (int)(tb & 0xffffu) : (int)(tb >> 16);
+    const int n0k = k == 0 ? n0[0] : k == 1 ? n0[1] : k == 2 ? n0[2] : n0[3];
+    const int P = c.ptok[0] >> k;                  // tokens per page halve with each doubling of b
+    const int fp = n0k / P, first = (n0k + P - 1) / P, last = (n0k + tot + P - 1) / P;
+    int32_t* pt = c.ptab + ((int64_t)layer * c.B + s) * c.pt_stride + tr_sel4(k, c.pt_off);
+    const int e0 = fp + jl, e1 = fp + 16 + jl;
+    int v0 = e0 < last ? pt[e0] : -1;
+    int v1 = e1 < last ? pt[e1] : -1;
+    const uint32_t sh16 = 16 * k;
+    const uint32_t m0 = (uint32_t)(__ballot(e0 >= first && e0 < last && v0 < 0) >> sh16) & 0xffffu;
+    const uint32_t m1 = (uint32_t)(__ballot(e1 >= first && e1 < last && v1 < 0) >> sh16) & 0xffffu;
+    const int reuse = m0 ? fp + __ffs(m0) - 1 : m1 ? fp + 16 + __ffs(m1) - 1 : max(first, last);
+    const int need = last - reuse;
+    int id0 = 0;
+    if (jl == 0 && need > 0) id0 = atomicAdd(c.next_page, need);
+    id0 = __shfl(id0, 16 * k, 64);
+    const bool ok = (int64_t)id0 + need <= c.pool_pages;
+    if (jl == 0 && need > 0 && !ok) atomicOr(c.err, TR_ERRF_NO_PAGES);
+    if (e0 >= reuse && e0 < last) {
+      v0 = ok ? id0 + (e0 - reuse) : -1;
+      pt[e0] = v0;
     }
+    if (e1 >= reuse && e1 < last) {
+      v1 = ok ? id0 + (e1 - reuse) : -1;
+      pt[e1] = v1;
+    }
+    pgs[k][jl] = v0;
+    pgs[k][jl + 16] = v1;
+    if (jl == 0) fps[k] = fp;
   }
   __syncthreads();
-  const int ngroups = n * c.H * 2;
-  const int part = tid % LPG;
-  for (int g0 = 0; g0 < ngroups; g0 += kBlock / LPG) {
-    const int gid = g0 + tid / LPG;
+  auto do_pass = [&](int x, uint4 w4) {
+    const int gid = x * GPI + tid / LPG;
     const bool live = gid < ngroups;
     const int g = live ? gid : 0;
     const int kv = g & 1, th = g >> 1;
     const int h = th % c.H, i = th / c.H;
-    const uint16_t* src = (kv ? vin : kin) + (((int64_t)s * n + i) * c.H + h) * D;
-    quantize_group<D>(c, layer, s, p0 + i, h, kv, part, live, src, live ? bits[(int64_t)s * n + i] : 16);
-  }
+    const int cls = tcls[i];
+    const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+    QVec<8> q;
+    eq4_quant<D, 8>(q, w, cls);
+    if (!live) return;
+    const int slot = tslot[i];
+    const int page = pgs[cls][(slot >> tr_sel4(cls, c.ptok_log2)) - fps[cls]];
+    if (page < 0) return;                          // pool exhausted (flagged)
+    const int j = slot & (tr_sel4(cls, c.ptok) - 1);
+    uint8_t* base = c.pool + (int64_t)page * c.page_bytes;
+    if (h == 0 && kv == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p0 + i;
+    put_piece<8>(c, base, j, h, kv, part, cls, q);
+  };
+#pragma unroll
+  for (int x = 0; x < NPF; ++x)
+    if (x * GPI < ngroups) do_pass(x, raw[x]);
+  for (int x = NPF; x * GPI < ngroups; ++x) do_pass(x, *reinterpret_cast<const uint4*>(src_of(x * GPI + tid / LPG)));
 }
 
 // Read back positions tok0 .. tok0+n-1 of every sequence (position order).

@@ -387,13 +387,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   }
 }
 
-// Log-sum-exp merge of the chunks of windows that span more than one chunk.
+// Log-sum-exp merge of the chunks of windows that span more than one chunk: one workgroup per
+// (seq, head), thread d = channel d.  Chunks go in batches of 32: every load of a batch -- the
+// channel's 32 partial values and, in lane k of each wave, chunk k's (max, sum) -- is issued at
+// once (indices clamped into the window), then the batch folds into a running (max, num, den)
+// with the chunk weights broadcast from their lanes.
 template <int D>
 __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH, int max_chunks,
                                                       const uint8_t* __restrict__ mode,
                                                       const float* __restrict__ part, uint16_t* __restrict__ out) {
+  constexpr int KB = 32;
   const int sh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, lane = d & 63;
   const int m = mode[sh];
   if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) return;
   const int lo = (m == TR_MODE_FULL) ? 0 : max(0, t - window);
@@ -401,14 +406,26 @@ __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH,
   const int nch = (L + CH - 1) / CH;
   if (nch == 1) return;                            // written by k_decode
   const float* base = part + (int64_t)sh * max_chunks * (D + 2);
-  float M = -INFINITY;
-  for (int k = 0; k < nch; ++k) M = fmaxf(M, base[(int64_t)k * (D + 2) + D]);
-  float num = 0.0f, den = 0.0f;
-  for (int k = 0; k < nch; ++k) {
-    const float* pk = base + (int64_t)k * (D + 2);
-    const float wgt = exp2f(pk[D] - M);
-    num = fmaf(wgt, pk[d], num);
-    den = fmaf(wgt, pk[D + 1], den);
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+  for (int k0 = 0; k0 < nch; k0 += KB) {
+    float v[KB];
+#pragma unroll
+    for (int x = 0; x < KB; ++x) v[x] = base[(int64_t)min(k0 + x, nch - 1) * (D + 2) + d];
+    const int kk = k0 + (lane & (KB - 1));
+    const float* pk = base + (int64_t)min(kk, nch - 1) * (D + 2);
+    const bool own = kk < nch && lane < KB;        // lanes KB..63 repeat lanes 0..KB-1
+    const float mk = own ? pk[D] : -INFINITY;
+    const float lk = pk[D + 1];
+    const float Mn = fmaxf(M, wave_max(mk));
+    const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+    const float wk = own ? exp2f(mk - Mn) : 0.0f;
+    den = den * a + wave_sum(wk * lk);
+    float nb = 0.0f;
+#pragma unroll
+    for (int x = 0; x < KB; ++x)
+      nb = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), x)), v[x], nb);
+    num = num * a + nb;
+    M = Mn;
   }
   out[(int64_t)sh * D + d] = tr_f32_to_bf16(num / den);
 }
