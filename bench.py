@@ -50,23 +50,25 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # reports traffic as null.
 TRAFFIC = {
     "k_decode": {
-        "fetch_kib": 169362.9, "write_kib": 3097.1, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 169336.5, "write_kib": 3097.1, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip":
-                "7ed929ac13da511781b11ce96e571a17df834d00dc4e2daf4e6d8ae1b398f0b2",
+                "f2dc4c5181d5e83974ffd050bf9453267766d7c944e0025f0d8da7d104df1873",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "54bd8db721150d71b7a243f1fe0ffd7a85065e875b9990cf48cf5b3e1e2d3718",
+                "7d7f94cabb6ff027ac0edf19e61d2fc40846745c6b5ece2be2158bc82b5503ff",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
-                "deccfa7c21582ee2fb81b10673d54efc556bbce562ffa21c31648783721cf4ba"}},
+                "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
     "k_prefill_attn": {
-        "fetch_kib": 18126.6, "write_kib": 10438.6, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 19616.7, "write_kib": 20851.5, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip":
-                "db3e31706351f29b4ac3edf2f8fa0e7e46f9e133b6403a386f4433ed7f8dfba4",
+                "aa3e62eab78ea5e2a1aaa647c5d70ca9b8179b82cbcfeb9d81f0c505896550ee",
+            "mixed_precision_kv_tr_amd/csrc/kv_write.h":
+                "9d6e257372d22db06451b5b6f79416dc406d1f73fc789d0e186d1a873befb101",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "54bd8db721150d71b7a243f1fe0ffd7a85065e875b9990cf48cf5b3e1e2d3718",
+                "7d7f94cabb6ff027ac0edf19e61d2fc40846745c6b5ece2be2158bc82b5503ff",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
-                "deccfa7c21582ee2fb81b10673d54efc556bbce562ffa21c31648783721cf4ba"}},
+                "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
 }
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, TFLOP/s

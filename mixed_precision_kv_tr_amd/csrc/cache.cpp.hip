@@ -2,13 +2,14 @@
 //
 // Write path of one tr_kv_quantize_write call (TriRoute review page, xllm-io.github.io,
 // Eq. (4) and the inference paragraph after Algorithm 1):
-//   k_assign_slots   one workgroup per sequence: block-wide scan of the new tokens' width
-//                    classes -> prefix counts (slot of each token in its class stream) and
-//                    deterministic page allocation from the shared pool (one atomic per
-//                    (sequence, class) that needs pages).
-//   k_quantize_write one (token, head, K|V) group of D values per D/8 lanes: 128-bit loads,
-//                    min/max across the group's lanes, fp32 s and z, correctly rounded
-//                    divides, round-half-to-even codes, packed stores into the class page.
+//   n <= 64 (decode steps): k_write_small, one workgroup per sequence -- slot assignment, page
+//                    allocation and quantization in one launch.
+//   n > 64:          k_assign_slots (one workgroup per sequence: prefix counts, the slot of
+//                    each token in its class stream, and pages from the shared pool), then the
+//                    64-position tile kernel of the prefill path without its dense staging
+//                    (prefill.cpp.hip): 16 channels per lane, reciprocal fast path with an
+//                    exact fallback, packed stores into the class pages.
+// The Eq. (4) arithmetic is shared by both through kv_write.h.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -43,41 +44,6 @@ __global__ void k_reset(CacheLayout c) {
 __global__ __launch_bounds__(kAssignBlock) void k_assign_slots(CacheLayout c, int layer, int p0, int n,
                                                                const uint8_t* __restrict__ bits) {
   tr_assign_slots_seq(c, layer, p0, n, bits, blockIdx.x);
-}
-
-// Eq. (4) on one group = one (token, head) K or V vector of D bf16 values, held by the D/8
-// lanes that call this together (8 values each); the lanes shuffle, so every lane of the group
-// must call it, `live` or not.
-template <int D>
-__device__ __forceinline__ void quantize_group(const CacheLayout& c, int layer, int s, int p, int h, int kv, int part,
-                                               bool live, const uint16_t* src, int bval) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(src + part * 8);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  const int cls = eq4_class(bval);
-  QVec<8> q;
-  eq4_quant<D, 8>(q, w, cls);
-  if (live) store_piece<8>(c, layer, s, p, h, kv, part, cls, q);
-}
-
-// Grid-wide quantize of n tokens per sequence (after k_assign_slots).
-template <int D>
-__global__ __launch_bounds__(kBlock) void k_quantize_write(CacheLayout c, int layer, int p0, int n,
-                                                           const uint16_t* __restrict__ kin,
-                                                           const uint16_t* __restrict__ vin,
-                                                           const uint8_t* __restrict__ bits) {
-  constexpr int LPG = D / 8;
-  const int64_t ngroups = (int64_t)c.B * n * c.H * 2;
-  const int64_t gid = (blockIdx.x * (int64_t)kBlock + threadIdx.x) / LPG;
-  const int part = threadIdx.x % LPG;
-  const bool live = gid < ngroups;
-  const int64_t g = live ? gid : 0;
-  const int kv = (int)(g & 1);
-  const int64_t th = g >> 1;
-  const int h = (int)(th % c.H);
-  const int64_t tok = th / c.H;
-  const int s = (int)(tok / n), i = (int)(tok % n);
-  const uint16_t* src = (kv ? vin : kin) + (tok * c.H + h) * D;
-  quantize_group<D>(c, layer, s, p0 + i, h, kv, part, live, src, live ? bits[(int64_t)s * n + i] : 16);
 }
 
 // Small appends (n <= 64 tokens per sequence, e.g. one decode step): slot assignment, page
@@ -271,14 +237,7 @@ tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, 
   }
   hipLaunchKernelGGL(k_assign_slots, dim3(L.B), dim3(kAssignBlock), 0, stream, L, layer, p0, n, bits);
   TR_LAUNCH_CHECK();
-  const int64_t lanes = (int64_t)L.B * n * L.H * 2 * (L.D / 8);
-  const int grid = (int)((lanes + kBlock - 1) / kBlock);
-  if (L.D == 64)
-    hipLaunchKernelGGL(k_quantize_write<64>, dim3(grid), dim3(kBlock), 0, stream, L, layer, p0, n, k, v, bits);
-  else
-    hipLaunchKernelGGL(k_quantize_write<128>, dim3(grid), dim3(kBlock), 0, stream, L, layer, p0, n, k, v, bits);
-  TR_LAUNCH_CHECK();
-  return TR_OK;
+  return tr_write_tiles_launch(c, layer, p0, k, v, bits, n, stream);
 }
 
 extern "C" {

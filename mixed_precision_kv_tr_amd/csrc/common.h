@@ -131,3 +131,7 @@ tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q
                             uint16_t* out, hipStream_t stream);
 tr_status tr_write_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                           const uint8_t* bits, int n, hipStream_t stream);
+// Quantize-write of positions [p0, p0 + n) whose slots are assigned, 64-position tiles per (seq,
+// head) (the prefill write kernel without its dense staging).
+tr_status tr_write_tiles_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                                const uint8_t* bits, int n, hipStream_t stream);

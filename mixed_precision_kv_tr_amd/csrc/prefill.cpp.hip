@@ -757,6 +757,8 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
 
 // Merge of the chunks of split tiles: per row, out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
 // A partial row is D + 4 floats: O[D], then the reference max and the sum (16-byte aligned rows).
+// Chunks go in pairs: both chunks' loads are issued together (the second clamped to the last
+// chunk and weighted 0 when past it), and pairs fold into a running (max, num, den).
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, const int32_t* __restrict__ rows,
                                                           const int32_t* __restrict__ counts,
@@ -765,6 +767,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
   constexpr int MPH = kSlotsPerHead / 2;
   constexpr int TPR = kBlock / BM;                 // threads per row
   constexpr int CPT = D / TPR;                     // channels per thread
+  constexpr int64_t SLOT = (int64_t)BM * (D + 4);
   const int BH = c.B * c.H;
   const int mi = blockIdx.x / BH, sh = blockIdx.x % BH;
   if (mi >= counts[sh * 4 + 3]) return;
@@ -773,27 +776,35 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
   const int ri = mg.x + r;
   if (ri >= mg.y) return;
   const int s = sh / c.H, h = sh % c.H;
-  const float* base = part + ((int64_t)sh * kSlotsPerHead + mg.z) * BM * (D + 4) + (int64_t)r * (D + 4);
-  constexpr int64_t SLOT = (int64_t)BM * (D + 4);
-  float M = -INFINITY;
-  for (int k = 0; k < mg.w; ++k) M = fmaxf(M, base[k * SLOT + D]);
+  const float* base = part + ((int64_t)sh * kSlotsPerHead + mg.z) * SLOT + (int64_t)r * (D + 4);
+  const int nch = mg.w;
+  float M = -INFINITY, den = 0.0f;
   float acc[CPT];
 #pragma unroll
   for (int x = 0; x < CPT; ++x) acc[x] = 0.0f;
-  float den = 0.0f;
-  for (int k = 0; k < mg.w; ++k) {
-    const float* pk = base + k * SLOT;
-    const float m = pk[D];
-    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-    den = fmaf(w, pk[D + 1], den);
+  for (int k0 = 0; k0 < nch; k0 += 2) {
+    const float* p0 = base + k0 * SLOT;
+    const float* p1 = base + min(k0 + 1, nch - 1) * SLOT;
+    float v0[CPT], v1[CPT];
 #pragma unroll
     for (int x = 0; x < CPT; x += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(pk + d0 + x);
-      acc[x] = fmaf(w, v.x, acc[x]);
-      acc[x + 1] = fmaf(w, v.y, acc[x + 1]);
-      acc[x + 2] = fmaf(w, v.z, acc[x + 2]);
-      acc[x + 3] = fmaf(w, v.w, acc[x + 3]);
+      const float4 a0 = *reinterpret_cast<const float4*>(p0 + d0 + x);
+      const float4 a1 = *reinterpret_cast<const float4*>(p1 + d0 + x);
+      v0[x] = a0.x; v0[x + 1] = a0.y; v0[x + 2] = a0.z; v0[x + 3] = a0.w;
+      v1[x] = a1.x; v1[x + 1] = a1.y; v1[x + 2] = a1.z; v1[x + 3] = a1.w;
     }
+    const float2 ml0 = *reinterpret_cast<const float2*>(p0 + D);
+    const float2 ml1 = *reinterpret_cast<const float2*>(p1 + D);
+    const bool two = k0 + 1 < nch;
+    const float m1 = two ? ml1.x : -INFINITY;
+    const float Mn = fmaxf(M, fmaxf(ml0.x, m1));
+    const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+    const float w0 = (ml0.x == -INFINITY) ? 0.0f : exp2f(ml0.x - Mn);
+    const float w1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - Mn);
+    den = den * a + fmaf(w0, ml0.y, w1 * ml1.y);
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) acc[x] = acc[x] * a + fmaf(w0, v0[x], w1 * v1[x]);
+    M = Mn;
   }
   const float inv = 1.0f / den;
   const int i = rows[(int64_t)sh * c.N + ri];
@@ -810,6 +821,22 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
 }  // namespace
 
 namespace {
+
+// Quantize-write of positions [p0, p0 + T) in 64-position tiles (slots already assigned); tiles
+// from dense_from on are also staged for the prefill attention.
+template <int D>
+tr_status launch_write_tiles(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                             const uint8_t* bits, int T, int dense_from, hipStream_t stream) {
+  const CacheLayout& L = c->lay;
+  const float kscale = (float)(1.4426950408889634 / sqrt((double)D));
+  const int tile0 = p0 / kWriteTile, ntile = (p0 + T + kWriteTile - 1) / kWriteTile - tile0;
+  const int64_t blocks = (int64_t)L.B * L.H * ntile;
+  if (blocks > (int64_t)1 << 30) return TR_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid((int)blocks)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
+                     ntile, dense_from, c->np, kscale, k, v, bits, c->dk, c->dv, c->dsz);
+  TR_LAUNCH_CHECK();
+  return TR_OK;
+}
 
 template <int D>
 tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint16_t* k,
@@ -839,10 +866,8 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   }
   if (fused) {
     TrProfScope prof(c, TR_PROF_WRITE, stream);
-    const int tile0 = p0 / kWriteTile, ntile = (pend + kWriteTile - 1) / kWriteTile - tile0;
-    hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid(BH * ntile)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
-                       ntile, write_from, c->np, kscale, k, v, bits, c->dk, c->dv, c->dsz);
-    TR_LAUNCH_CHECK();
+    const tr_status st = launch_write_tiles<D>(c, layer, p0, k, v, bits, T, write_from, stream);
+    if (st != TR_OK) return st;
   }
   if (dense_to > 0) {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
@@ -868,4 +893,10 @@ tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q
                             uint16_t* out, hipStream_t stream) {
   if (c->lay.D == 64) return prefill_launch_d<64>(c, layer, p0, q, k, v, bits, mode, T, window, out, stream);
   return prefill_launch_d<128>(c, layer, p0, q, k, v, bits, mode, T, window, out, stream);
+}
+
+tr_status tr_write_tiles_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
+                                const uint8_t* bits, int n, hipStream_t stream) {
+  if (c->lay.D == 64) return launch_write_tiles<64>(c, layer, p0, k, v, bits, n, 1 << 30, stream);
+  return launch_write_tiles<128>(c, layer, p0, k, v, bits, n, 1 << 30, stream);
 }
