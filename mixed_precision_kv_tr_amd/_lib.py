@@ -50,7 +50,7 @@ _status_str = _sig("tr_status_str", ctypes.c_char_p, ctypes.c_int)
 _truncate = _sig("tr_kv_cache_truncate", ctypes.c_int, _vp, _i32, _i32)
 _prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
 _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
-PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_compact", "prefill_attn")
+PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn")
 
 STATUS_NAMES = {0: "TR_OK", 1: "TR_ERR_INVALID_ARG", 2: "TR_ERR_CAPACITY", 3: "TR_ERR_OUT_OF_PAGES",
                 4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE"}
