@@ -144,7 +144,10 @@ __device__ __forceinline__ void score_phase(const CacheLayout& c, const int32_t*
 #ifndef TR_DECODE_U1
 #define TR_DECODE_U1 4
 #endif
-  constexpr int U = (C == 3) ? 1 : TR_DECODE_U1;   // sub-iterations per batch
+#ifndef TR_DECODE_UK3
+#define TR_DECODE_UK3 4                            // bf16 keys: 4 x 8 keys (8 KB) per batch
+#endif
+  constexpr int U = (C == 3) ? TR_DECODE_UK3 : TR_DECODE_U1;   // sub-iterations per batch
   constexpr int NQ = (C == 2) ? 1 : E / 2;
   const int lane = threadIdx.x;
   const int part = lane % LPK, kslot = lane / LPK;
@@ -228,7 +231,13 @@ __device__ __forceinline__ void value_phase(const CacheLayout& c, const int32_t*
 #ifndef TR_DECODE_U2
 #define TR_DECODE_U2 2
 #endif
-  constexpr int U = (C == 0) ? TR_DECODE_U2 : 1;
+#ifndef TR_DECODE_UV
+#define TR_DECODE_UV 1
+#endif
+#ifndef TR_DECODE_UV3
+#define TR_DECODE_UV3 1
+#endif
+  constexpr int U = (C == 0) ? TR_DECODE_U2 : (C == 3) ? TR_DECODE_UV3 : TR_DECODE_UV;
   constexpr int RB = D * b / 8;
   constexpr int STEP = KPW * U;
   const int lane = threadIdx.x;
@@ -264,8 +273,10 @@ __device__ __forceinline__ void value_phase(const CacheLayout& c, const int32_t*
   }
 }
 
+// Occupancy floor handed to the compiler.  With 4 it settles at 96 VGPRs for D = 128 (5 waves per
+// SIMD, no spills; a 1.3B-shaped decode has ~4100 items for 5120 wave slots) and at 120 for D = 64.
 #ifndef TR_DECODE_WAVES
-#define TR_DECODE_WAVES 5
+#define TR_DECODE_WAVES 4
 #endif
 template <int D>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_WAVES, 8))) void k_decode(CacheLayout c, int layer, int t, int window, int CH, int nch_grid,
