@@ -20,10 +20,9 @@ struct tr_kv_cache {
   int32_t* rows;
   int32_t* row_counts;
   // prefill scratch: the cache range a prefill call reads, dequantized once, position order
-  //   dk [B][H][NP][D] uint16: K code as a bf16 integer (exact), or the stored bf16 (b = 16)
+  //   dk [B][H][NP][D] uint16: k_hat = s * c + z as fp16, key-major
   //   dv [B][H][D][NP] uint16: v_hat = s * c + z as fp16, channel-major; within each group of
   //                            16 positions, bits 2 and 3 of the position are swapped
-  //   dsz [B][H][NP] float2:   (s_K, z_K) * log2(e) / sqrt(D); (log2(e)/sqrt(D), 0) for b = 16
   // prefill attention work: units (128-row tile, key-tile chunk) [B][H][pf_uph] int4, merges of
   // split tiles [B][H][TR_PREFILL_SLOTS / 2] int4, partial results of split tiles
   // [B][H][TR_PREFILL_SLOTS][128][D + 4] floats (O, max, sum, padding)
@@ -34,7 +33,6 @@ struct tr_kv_cache {
   int32_t np;                     // N rounded up to a multiple of 64 (the write tile)
   uint16_t* dk;
   uint16_t* dv;
-  float2* dsz;
   // optional kernel timing (tr_profile_enable): HIP events around each kernel launch
   bool prof_on;
   struct ProfRec { int fam; hipEvent_t a, b; };

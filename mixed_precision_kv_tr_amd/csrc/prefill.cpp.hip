@@ -8,9 +8,9 @@
 //   skip rows (and rows with an invalid mode) get zeros right here.  Then the attention work
 //   units of the (seq, head).
 // Dense staging: the cache range the call's queries read, dequantized once into
-//   position-ordered scratch: K as its code in bf16 (an exact integer <= 255, or the stored
-//   bf16 for b = 16) plus per-key (s_K, z_K) * log2(e)/sqrt(D); V as v_hat = s * c + z (fp32)
-//   rounded to fp16, stored channel-major.  Every 128-row tile of a (seq, head) then reads this
+//   position-ordered scratch: k_hat = s * c + z and v_hat = s * c + z (fp32, Eq. (4)'s
+//   reconstruction) rounded to fp16 (the stored bf16 for b = 16, exact in fp16), K key-major
+//   and V channel-major.  Every 128-row tile of a (seq, head) then reads this
 //   instead of re-unpacking the pages (a (seq, head) stays on one XCD, so the re-reads hit its
 //   L2).  k_prefill_write (one workgroup per (seq, head, 32 positions)) quantizes the call's
 //   own K/V into the pages and stages them from registers; k_prefill_dense stages the tiles
@@ -18,9 +18,9 @@
 // k_prefill_attn (one workgroup = 4 waves = one 128-row tile), per 32-key tile:
 //     staging   16-byte copies of K rows and V^T rows into double-buffered LDS, the next
 //               tile's copies in flight in registers while the current one is computed.
-//     QK^T      S^T[32 keys x 32 queries] per wave = v_mfma_f32_32x32x16_bf16 over D/16 steps;
-//               the score is alpha * (q . c) + beta * sum(q) -- Eq. (4)'s reconstruction
-//               folded out of the product, so K stays exact in the matrix cores.
+//     QK^T      S^T[32 keys x 32 queries] per wave = v_mfma_f32_32x32x16_f16 over D/16 steps,
+//               q pre-scaled by log2(e)/sqrt(D) in fp16 and the accumulator started at the
+//               row's -m_ref, so the MFMA result is already the exponent of the softmax.
 //     softmax   fp32 in registers, each lane holds 16 keys of one query; running reference
 //               max with a lazy rescale (only when a row's max grows by more than 2^8);
 //               masks only on tiles that cross a row's window edge; waves skip tiles outside
@@ -292,9 +292,13 @@ __device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cas
 // 16-key step, the key order of the S^T accumulator) are contiguous.
 __device__ __forceinline__ int vt_pos(int k) { return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
+__device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
+  return (uint32_t)f16_bits(lo) | ((uint32_t)f16_bits(hi) << 16);
+}
+
 template <int D, int C>
 __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout& c, int h, int j, int part,
-                                            uint16_t* krow, _Float16 (*vt)[40], int tk, float2* szk_out) {
+                                            uint16_t* krow, _Float16 (*vt)[40], int tk) {
   constexpr int DPL = D / 8;
   constexpr int b = 2 << C;
   constexpr int SLB = DPL * b / 8;                 // slice bytes
@@ -306,23 +310,20 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
   if constexpr (C == 3) {
 #pragma unroll
     for (int e = 0; e < DPL / 2; ++e) {
-      ko[e] = wk[e];
+      ko[e] = f16_pair(tr_bf16_lo(wk[e]), tr_bf16_hi(wk[e]));
       vt[part * DPL + 2 * e][vt_pos(tk)] = (_Float16)tr_bf16_lo(wv[e]);
       vt[part * DPL + 2 * e + 1][vt_pos(tk)] = (_Float16)tr_bf16_hi(wv[e]);
     }
-    *szk_out = make_float2(1.0f, 0.0f);
   } else {
     const int P = c.ptok[C];
     const float2 szk = reinterpret_cast<const float2*>(pb + c.sk_off[C])[(int64_t)h * P + j];
     const float2 szv = reinterpret_cast<const float2*>(pb + c.sv_off[C])[(int64_t)h * P + j];
 #pragma unroll
     for (int e = 0; e < DPL; e += 2) {
-      const float k0 = (float)code_at<b>(wk, e), k1 = (float)code_at<b>(wk, e + 1);
-      ko[e / 2] = (__float_as_uint(k0) >> 16) | (__float_as_uint(k1) & 0xffff0000u);
+      ko[e / 2] = f16_pair(fmaf(szk.x, (float)code_at<b>(wk, e), szk.y), fmaf(szk.x, (float)code_at<b>(wk, e + 1), szk.y));
       vt[part * DPL + e][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
       vt[part * DPL + e + 1][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
     }
-    *szk_out = szk;
   }
 #pragma unroll
   for (int x = 0; x < DPL / 8; ++x)
@@ -333,8 +334,7 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
 // are written as zeros (they are only ever read masked).
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int layer, int tile0, int ntile, int pend,
-                                                          int np, float kscale, uint16_t* __restrict__ dk,
-                                                          uint16_t* __restrict__ dv, float2* __restrict__ dsz) {
+                                                          int np, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   constexpr int DPL = D / 8;
   __shared__ _Float16 vt[D][40];                   // v_hat tile, channel-major (row = 80 B)
   const int lin = xcd_linear(c.B * c.H * ntile);
@@ -344,7 +344,6 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
   const int tid = threadIdx.x, tk = tid / 8, part = tid % 8;
   const int p = tile * 32 + tk;
   uint16_t* krow = dk + ((int64_t)sh * np + p) * D + part * DPL;
-  float2 szk = make_float2(0.0f, 0.0f);
   if (p < pend) {
     const int32_t* pr0 = tr_prefix_row(c, layer, s, p);
     const int32_t* pr1 = tr_prefix_row(c, layer, s, p + 1);
@@ -357,10 +356,10 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
     const int j = slot & (c.ptok[cls] - 1);
     const uint8_t* pb = c.pool + (int64_t)(page < 0 ? 0 : page) * c.page_bytes;
     switch (cls) {
-      case 0: dense_token<D, 0>(pb, c, h, j, part, krow, vt, tk, &szk); break;
-      case 1: dense_token<D, 1>(pb, c, h, j, part, krow, vt, tk, &szk); break;
-      case 2: dense_token<D, 2>(pb, c, h, j, part, krow, vt, tk, &szk); break;
-      default: dense_token<D, 3>(pb, c, h, j, part, krow, vt, tk, &szk); break;
+      case 0: dense_token<D, 0>(pb, c, h, j, part, krow, vt, tk); break;
+      case 1: dense_token<D, 1>(pb, c, h, j, part, krow, vt, tk); break;
+      case 2: dense_token<D, 2>(pb, c, h, j, part, krow, vt, tk); break;
+      default: dense_token<D, 3>(pb, c, h, j, part, krow, vt, tk); break;
     }
   } else {
 #pragma unroll
@@ -368,7 +367,6 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 #pragma unroll
     for (int e = 0; e < DPL; ++e) vt[part * DPL + e][vt_pos(tk)] = (_Float16)0.0f;
   }
-  if (part == 0) dsz[(int64_t)sh * np + p] = make_float2(szk.x * kscale, szk.y * kscale);
   __syncthreads();
   // V^T rows: D rows x 32 positions (64 bytes each), 16 bytes per thread.
   for (int x = tid; x < D * 4; x += kBlock) {
@@ -383,7 +381,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 // ntile); D/16 lanes per position, 16 channels of K and of V each.  A lane issues all its loads
 // (bits, prefix counts, K, V), then the page-table lookup of its slot, and quantizes while that
 // lookup is in flight.  Codes, scales and page stores are the plain write path's (the same Eq. (4)
-// helpers); tiles from dense_from on also get their dk / dsz rows and V^T columns from the values
+// helpers); tiles from dense_from on also get their k_hat rows and v_hat columns from the values
 // in registers, without re-reading the pages, and zeros at positions >= p0 + T.  Runs after the
 // slot assignment of the same positions.
 constexpr int kWriteTile = 64;
@@ -391,11 +389,11 @@ constexpr int kWriteNV = 16;                       // channels per lane
 
 template <int D>
 __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int layer, int p0, int T, int tile0,
-                                                         int ntile, int dense_from, int np, float kscale,
+                                                         int ntile, int dense_from, int np,
                                                          const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin,
                                                          const uint8_t* __restrict__ bits, uint16_t* __restrict__ dk,
-                                                         uint16_t* __restrict__ dv, float2* __restrict__ dsz) {
+                                                         uint16_t* __restrict__ dv) {
   constexpr int NV = kWriteNV;
   constexpr int LPG = D / NV;
   constexpr int NT = 4 * D;
@@ -430,17 +428,18 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
   }
   const bool dense = tile >= dense_from;           // else the tile also holds earlier positions
   if (dense) {
+    // k_hat, v_hat = fp16(s * f + z); b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's
+    // sign.
+    const float zk = cls == 3 ? -0.0f : qk.z, zv = cls == 3 ? -0.0f : qv.z;
     uint32_t kw[NV / 2];
-    bf16_words<NV>(qk, kw);
+#pragma unroll
+    for (int e = 0; e < NV / 2; ++e)
+      kw[e] = live ? f16_pair(fmaf(qk.s, qk.f[2 * e], zk), fmaf(qk.s, qk.f[2 * e + 1], zk)) : 0u;
     uint4* krow = reinterpret_cast<uint4*>(dk + ((int64_t)sh * np + p) * D + part * NV);
-    krow[0] = live ? make_uint4(kw[0], kw[1], kw[2], kw[3]) : make_uint4(0, 0, 0, 0);
-    krow[1] = live ? make_uint4(kw[4], kw[5], kw[6], kw[7]) : make_uint4(0, 0, 0, 0);
-    if (part == 0)
-      dsz[(int64_t)sh * np + p] = live ? make_float2(qk.s * kscale, qk.z * kscale) : make_float2(0.0f, 0.0f);
-    // v_hat = fp16(s * f + z); b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's sign.
-    // The column is XOR-swizzled by 16 * (part & 3): the lanes of one store hold 16 positions of
-    // 4 parts whose rows are 16 rows (a multiple of 64 banks) apart, so without it they collide.
-    const float zv = cls == 3 ? -0.0f : qv.z;
+    krow[0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    krow[1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
+    // The V^T column is XOR-swizzled by 16 * (part & 3): the lanes of one store hold 16 positions
+    // of 4 parts whose rows are 16 rows (a multiple of 64 banks) apart, so without it they collide.
     const int tpos = vt_pos(tk) ^ (16 * (part & 3));
 #pragma unroll
     for (int e = 0; e < NV; ++e) vt[part * NV + e][tpos] = live ? (_Float16)fmaf(qv.s, qv.f[e], zv) : (_Float16)0.0f;
@@ -464,10 +463,8 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
 
 template <int D>
 struct alignas(16) PrefillTile {
-  uint16_t ks[BN][D + 8];      // K codes as bf16 integers / stored bf16, key-major
+  uint16_t ks[BN][D + 8];      // k_hat fp16, key-major
   uint16_t vt[D][BN + 8];      // v_hat fp16, channel-major, keys in vt_pos order
-  alignas(16) float alpha[BN]; // s_K * log2(e) / sqrt(D)
-  alignas(16) float beta[BN];  // z_K * log2(e) / sqrt(D)
 };
 
 template <int D, int G>
@@ -488,8 +485,8 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D == 64 ? TR_PREFILL_WAVES : 2))) void k_prefill_attn(
     CacheLayout c, int p0, int T, int window, int np, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const int4* __restrict__ units, int uph,
-    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, const float2* __restrict__ dsz,
-    float* __restrict__ part, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, float kscale, float* __restrict__ part,
+    uint16_t* __restrict__ out) {
   constexpr int KS = D / 16;           // MFMA k-steps for QK^T
   constexpr int MT = D / 32;           // 32-channel tiles of O^T
   constexpr int KPT = D / 64;          // 16-byte K pieces per thread per tile
@@ -513,18 +510,20 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   const int t = row_ok ? p0 + i : -1;
   const int lo = row_ok ? (full ? 0 : max(0, t - window)) : 0x7fffffff;
 
-  // Q^T operand (B of the QK^T MFMA): column n = query, k = channels 16*ks + 8*g .. +7.
-  bf16x8 qb[KS];
-  float qsum = 0.0f;
+  // Q^T operand (B of the QK^T MFMA): column n = query, k = channels 16*ks + 8*g .. +7, as
+  // fp16(q * log2(e) / sqrt(D)) so the product is the score in the log2 domain.
+  f16x8 qb[KS];
   const uint16_t* qrow = q + (((int64_t)s * T + i) * c.H + h) * D;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    uint4 raw = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-    qb[ks] = __builtin_bit_cast(bf16x8, raw);
-    qsum += (tr_bf16_lo(raw.x) + tr_bf16_hi(raw.x)) + (tr_bf16_lo(raw.y) + tr_bf16_hi(raw.y)) +
-            (tr_bf16_lo(raw.z) + tr_bf16_hi(raw.z)) + (tr_bf16_lo(raw.w) + tr_bf16_hi(raw.w));
+    const uint4 raw = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      qb[ks][2 * x] = (_Float16)(tr_bf16_lo(w[x]) * kscale);
+      qb[ks][2 * x + 1] = (_Float16)(tr_bf16_hi(w[x]) * kscale);
+    }
   }
-  qsum = xor32_sum(qsum);
 
   // Wave and workgroup key-position ranges.
   int wlo = lo, whi = row_ok ? t + 1 : -1, tmin = row_ok ? t : 0x7fffffff, lomax = row_ok ? lo : -1;
@@ -558,9 +557,7 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   // (tid % 4); for D = 128 every thread moves two pieces of each.
   const uint16_t* kbase = dk + (int64_t)sh * np * D;
   const uint16_t* vbase = dv + (int64_t)sh * D * np;
-  const float2* sbase = dsz + (int64_t)sh * np;
   uint4 rk[KPT], rv[VPT];
-  float2 rs = make_float2(0.0f, 0.0f);
   auto load_tile = [&](int kb) {
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
@@ -572,7 +569,6 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
       const int e = tid + x * kBlock;
       rv[x] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(e >> 2) * np + kb + (e & 3) * 8);
     }
-    if (tid < BN) rs = sbase[kb + tid];
   };
   auto store_tile = [&](PrefillTile<D>& tl) {
 #pragma unroll
@@ -584,10 +580,6 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     for (int x = 0; x < VPT; ++x) {
       const int e = tid + x * kBlock;
       *reinterpret_cast<uint4*>(&tl.vt[e >> 2][(e & 3) * 8]) = rv[x];
-    }
-    if (tid < BN) {
-      tl.alpha[tid] = rs.x;
-      tl.beta[tid] = rs.y;
     }
   };
 
@@ -612,33 +604,30 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     const int kb = kb0 + it * BN;
     // ---- compute tile it (waves outside their windows skip it) ----
     if (it < ntiles && wave_live && kb < whi && kb + BN - 1 >= wlo) {
+      // x = score - mref: the accumulator starts at -mref (the lane's query), so the MFMA
+      // result is x itself.
+      const float nm = (mref == -INFINITY) ? 0.0f : -mref;
       f32x16 sacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[r] = nm;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&tl.ks[n][16 * ks + 8 * g]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&tl.ks[n][16 * ks + 8 * g]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[ks], sacc, 0, 0, 0);
       }
-      // x = score - mref = alpha * S + (beta * sum(q) - mref): two fused multiply-adds.  Only tiles
-      // that cross a row's window edge are masked (a wave-uniform choice between two versions):
-      // key kb + 4g + off (off = 8 * r4 + x) is visible iff lo <= key <= t, i.e. iff
+      // Only tiles that cross a row's window edge are masked (a wave-uniform choice between two
+      // versions): key kb + 4g + off (off = 8 * r4 + x) is visible iff lo <= key <= t, i.e. iff
       // (unsigned)(off - dlo) <= (unsigned)(t - lo) with dlo = lo - kb - 4g.
       float sv[16];
       float tmax = -INFINITY;
-      const float nm = (mref == -INFINITY) ? 0.0f : -mref;
       auto scores = [&](auto masked) {
         const int dlo = row_ok ? lo - kb - 4 * g : 0x40000000;   // rows past the tile's end: all masked
         const uint32_t span = row_ok ? (uint32_t)(t - lo) : 0u;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int k0 = 8 * r4 + 4 * g;
-          const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[k0]);
-          const float4 be = *reinterpret_cast<const float4*>(&tl.beta[k0]);
-          const float alv[4] = {al.x, al.y, al.z, al.w}, bev[4] = {be.x, be.y, be.z, be.w};
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            float v = fmaf(alv[x], sacc[4 * r4 + x], fmaf(bev[x], qsum, nm));
+            float v = sacc[4 * r4 + x];
             if constexpr (decltype(masked)::value) {
               if ((uint32_t)(8 * r4 + x - dlo) > span) v = -INFINITY;
             }
@@ -828,12 +817,11 @@ template <int D>
 tr_status launch_write_tiles(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                              const uint8_t* bits, int T, int dense_from, hipStream_t stream) {
   const CacheLayout& L = c->lay;
-  const float kscale = (float)(1.4426950408889634 / sqrt((double)D));
   const int tile0 = p0 / kWriteTile, ntile = (p0 + T + kWriteTile - 1) / kWriteTile - tile0;
   const int64_t blocks = (int64_t)L.B * L.H * ntile;
   if (blocks > (int64_t)1 << 30) return TR_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid((int)blocks)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
-                     ntile, dense_from, c->np, kscale, k, v, bits, c->dk, c->dv, c->dsz);
+                     ntile, dense_from, c->np, k, v, bits, c->dk, c->dv);
   TR_LAUNCH_CHECK();
   return TR_OK;
 }
@@ -872,13 +860,13 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   if (dense_to > 0) {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
     hipLaunchKernelGGL(k_prefill_dense<D>, dim3(xcd_grid(BH * dense_to)), dim3(kBlock), 0, stream, L, layer, 0, dense_to, pend,
-                       c->np, kscale, c->dk, c->dv, c->dsz);
+                       c->np, c->dk, c->dv);
     TR_LAUNCH_CHECK();
   }
   TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
   hipLaunchKernelGGL((k_prefill_attn<D, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
                      stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
-                     c->dsz, c->pf_part, out);
+                     kscale, c->pf_part, out);
   TR_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_prefill_merge<D>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
                      c->row_counts, c->pf_merges, c->pf_part, out);
