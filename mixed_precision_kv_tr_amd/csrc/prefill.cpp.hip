@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
       if (!(kb + BN - 1 <= tmin && kb >= lomax)) scores(std::true_type());
       else scores(std::false_type());
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(sv[r], sv[r + 1]));
+      for (int r = 0; r < 16; r += 2) tmax = tr_max(tmax, tr_max(sv[r], sv[r + 1]));   // v_maximum3, no quieting
       tmax = xor32_max(tmax);
       // Lazy rescale: x is relative to the running reference mref; it moves only when some
       // row's maximum exceeds it by more than kRescale (so p <= 2^kRescale in fp16), or on the
@@ -658,12 +658,17 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
         if (!first) mref += shift;
         else if (tmax > -INFINITY) mref = tmax;
       }
+      // p in fp16 (the PV operand); the row sum adds those same fp16 weights, two per v_dot2 with
+      // an fp32 accumulator, so numerator and denominator use identical weights.
       f16x8 pk[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sv[r]);
-        lsum += p;
-        pk[r >> 3][r & 7] = (_Float16)p;
+      for (int r = 0; r < 16; ++r) pk[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(sv[r]);
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const f16x2 pp = {pk[r >> 3][r & 7], pk[r >> 3][(r & 7) + 1]};
+        lsum = __builtin_amdgcn_fdot2(pp, one2, lsum, false);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
