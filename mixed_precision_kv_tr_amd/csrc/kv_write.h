@@ -188,10 +188,12 @@ struct QVec {
 //
 // The codes are rint(fl(d / s)), d = fl(x - z).  Each quotient is first taken as q = fl(d * r)
 // with r = v_rcp_f32(s) (1 ulp): |q - fl(d / s)| <= 2^-22 q, and q <= n = 2^b - 1 (up to
-// rounding), so when every q of the lane lies more than n * 2^-20 from the nearest half-integer,
-// rint(q) = rint(fl(d / s)) exactly.  Lanes that miss this (or with s = 0, or s outside
-// [2^-100, 2^100]) redo their values with the correctly rounded divide; the codes are the same
-// either way.  On the fast path the codes already lie in [0, n]: 0 <= d <= R and r ~ n / R.
+// rounding), so when q lies more than n * 2^-20 from the nearest half-integer, rint(q) =
+// rint(fl(d / s)) exactly.  Values that miss this (or with s = 0, or s outside [2^-100, 2^100])
+// are redone with the correctly rounded divide; the codes are the same either way.  Such values
+// are common (bf16 inputs often put d / s on a half-integer exactly), so the fallback is taken
+// per value rather than per lane.  On the fast path the codes already lie in [0, n]: 0 <= d <= R
+// and r ~ n / R.
 template <int D, int NV>
 __device__ __forceinline__ void eq4_quant(QVec<NV>& q, const uint32_t* w, int cls) {
 #pragma clang fp contract(off)
@@ -221,18 +223,17 @@ __device__ __forceinline__ void eq4_quant(QVec<NV>& q, const uint32_t* w, int cl
   q.s = sc;
   q.z = z;
   const float r = __builtin_amdgcn_rcpf(sc);
-  float dist = 0.0f;
+  const float lim = 0.5f - nlev * 0x1p-20f;
+  const bool sc_ok = sc >= 0x1p-100f && sc <= 0x1p100f;
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
-    const float qq = (x[e] - z) * r;
+    const float d = x[e] - z;
+    const float qq = d * r;
     const float cf = rintf(qq);
-    dist = fmaxf(dist, fabsf(qq - cf));
     q.f[e] = cf;
-  }
-  if (!(dist < 0.5f - nlev * 0x1p-20f && sc >= 0x1p-100f && sc <= 0x1p100f)) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e)
-      q.f[e] = sc == 0.0f ? 0.0f : __builtin_amdgcn_fmed3f(rintf((x[e] - z) / sc), 0.0f, nlev);
+    // Per value, so that a wave runs the divide only for the elements some lane needs it for.
+    if (!(fabsf(qq - cf) < lim && sc_ok))
+      q.f[e] = sc == 0.0f ? 0.0f : __builtin_amdgcn_fmed3f(rintf(d / sc), 0.0f, nlev);
   }
 }
 
