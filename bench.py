@@ -50,23 +50,23 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # reports traffic as null.
 TRAFFIC = {
     "k_decode": {
-        "fetch_kib": 169336.5, "write_kib": 3097.1, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 167631.2, "write_kib": 2114.2, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip":
-                "f2dc4c5181d5e83974ffd050bf9453267766d7c944e0025f0d8da7d104df1873",
+                "7374d4773a2208d0b61e9410eee6b2fb28bb53d44a08ef08b2125bcfc975ddca",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "7d7f94cabb6ff027ac0edf19e61d2fc40846745c6b5ece2be2158bc82b5503ff",
+                "d6ab9c658c2eb38ea59724ae7ebc6902d4db48a8e58059395e49b0cd3d87c94b",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
                 "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
     "k_prefill_attn": {
-        "fetch_kib": 19616.7, "write_kib": 20851.5, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 19238.9, "write_kib": 19046.0, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip":
-                "aa3e62eab78ea5e2a1aaa647c5d70ca9b8179b82cbcfeb9d81f0c505896550ee",
+                "ad9164a04896822155eaaa88db7f84d1a4efc995245eef7c763820a40b42d52d",
             "mixed_precision_kv_tr_amd/csrc/kv_write.h":
-                "9d6e257372d22db06451b5b6f79416dc406d1f73fc789d0e186d1a873befb101",
+                "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "7d7f94cabb6ff027ac0edf19e61d2fc40846745c6b5ece2be2158bc82b5503ff",
+                "d6ab9c658c2eb38ea59724ae7ebc6902d4db48a8e58059395e49b0cd3d87c94b",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
                 "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
 }
