@@ -272,6 +272,7 @@ static void free_all(tr_kv_cache* c) {
   (void)hipFree(c->row_counts);
   (void)hipFree(c->dk);
   (void)hipFree(c->dv);
+  (void)hipFree(c->dkf);
   (void)hipFree(c->pf_units);
   (void)hipFree(c->pf_merges);
   (void)hipFree(c->pf_part);
@@ -292,6 +293,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   c->partials = nullptr;
   c->rows = c->row_counts = nullptr;
   c->dk = c->dv = nullptr;
+  c->dkf = nullptr;
   c->pf_units = c->pf_merges = nullptr;
   c->pf_part = nullptr;
   c->prof_on = false;
@@ -347,6 +349,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   c->np = (L.N + 63) / 64 * 64;
   ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->dkf, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;
   c->pf_uph = tr_prefill_units_per_head(L.N);
   ok = ok && hipMalloc((void**)&c->pf_units, sizeof(int4) * (size_t)L.B * L.H * c->pf_uph) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->pf_merges, sizeof(int4) * (size_t)L.B * L.H * (TR_PREFILL_SLOTS / 2)) == hipSuccess;

@@ -20,7 +20,8 @@ struct tr_kv_cache {
   int32_t* rows;
   int32_t* row_counts;
   // prefill scratch: the cache range a prefill call reads, dequantized once, position order
-  //   dk [B][H][NP][D] uint16: k_hat = s * c + z as fp16, key-major
+  //   dk [B][H][NP][D] uint16: K code as a bf16 integer (exact), or the stored bf16 (b = 16)
+  //   dkf [B][H][NP] float2:   (alpha, r) = (s_K * log2(e) / sqrt(D), z_K / s_K) per key
   //   dv [B][H][D][NP] uint16: v_hat = s * c + z as fp16, channel-major; within each group of
   //                            16 positions, bits 2 and 3 of the position are swapped
   // prefill attention work: units (128-row tile, key-tile chunk) [B][H][pf_uph] int4, merges of
@@ -32,6 +33,7 @@ struct tr_kv_cache {
   int32_t pf_uph;
   int32_t np;                     // N rounded up to a multiple of 64 (the write tile)
   uint16_t* dk;
+  float2* dkf;
   uint16_t* dv;
   // optional kernel timing (tr_profile_enable): HIP events around each kernel launch
   bool prof_on;

@@ -7,10 +7,10 @@
 //   rows, then local rows -- so that a 128-row tile holds one mode and its key range is tight;
 //   skip rows (and rows with an invalid mode) get zeros right here.  Then the attention work
 //   units of the (seq, head).
-// Dense staging: the cache range the call's queries read, dequantized once into
-//   position-ordered scratch: k_hat = s * c + z and v_hat = s * c + z (fp32, Eq. (4)'s
-//   reconstruction) rounded to fp16 (the stored bf16 for b = 16, exact in fp16), K key-major
-//   and V channel-major.  Every 128-row tile of a (seq, head) then reads this
+// Dense staging: the cache range the call's queries read, staged once in position order: K as
+//   its code in bf16 (an exact integer <= 255, or the stored bf16 for b = 16) with per-key
+//   (alpha, r) = (s_K * log2(e)/sqrt(D), z_K / s_K); V as v_hat = s * c + z (fp32) rounded to
+//   fp16, channel-major.  Every 128-row tile of a (seq, head) then reads this
 //   instead of re-unpacking the pages (a (seq, head) stays on one XCD, so the re-reads hit its
 //   L2).  k_prefill_write (one workgroup per (seq, head, 32 positions)) quantizes the call's
 //   own K/V into the pages and stages them from registers; k_prefill_dense stages the tiles
@@ -18,9 +18,11 @@
 // k_prefill_attn (one workgroup = 4 waves = one 128-row tile), per 32-key tile:
 //     staging   16-byte copies of K rows and V^T rows into double-buffered LDS, the next
 //               tile's copies in flight in registers while the current one is computed.
-//     QK^T      S^T[32 keys x 32 queries] per wave = v_mfma_f32_32x32x16_f16 over D/16 steps,
-//               q pre-scaled by log2(e)/sqrt(D) in fp16 and the accumulator started at the
-//               row's -m_ref, so the MFMA result is already the exponent of the softmax.
+//     QK^T      S^T[32 keys x 32 queries] per wave = v_mfma_f32_32x32x16_bf16 over D/16 steps
+//               on the exact codes, plus one k-step that adds r * sum(q) (r and sum(q) as bf16
+//               hi + lo pairs); the exponent is then alpha * S - m_ref, one FMA per score.
+//               This is Eq. (4)'s reconstruction folded out of the product:
+//               q . (s c + z) = s (q . c + (z / s) sum(q)).
 //     softmax   fp32 in registers, each lane holds 16 keys of one query; running reference
 //               max with a lazy rescale (only when a row's max grows by more than 2^8);
 //               masks only on tiles that cross a row's window edge; waves skip tiles outside
@@ -296,9 +298,19 @@ __device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
   return (uint32_t)f16_bits(lo) | ((uint32_t)f16_bits(hi) << 16);
 }
 
+// Per-key factors of the QK^T product: alpha = s * kscale and r = z / s, so that
+// kscale * q . (s c + z) = alpha * (q . c + r * sum(q)).  b = 16 keys (stored bf16 x, "codes" x)
+// take (kscale, 0); a constant group (s = 0, codes 0) takes (kscale, z).
+__device__ __forceinline__ float2 key_factors(bool native, float s, float z, float kscale) {
+  if (native) return make_float2(kscale, 0.0f);
+  if (s == 0.0f) return make_float2(kscale, z);
+  return make_float2(s * kscale, z / s);
+}
+
 template <int D, int C>
 __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout& c, int h, int j, int part,
-                                            uint16_t* krow, _Float16 (*vt)[40], int tk) {
+                                            uint16_t* krow, _Float16 (*vt)[40], int tk, float kscale,
+                                            float2* kf_out) {
   constexpr int DPL = D / 8;
   constexpr int b = 2 << C;
   constexpr int SLB = DPL * b / 8;                 // slice bytes
@@ -310,20 +322,23 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
   if constexpr (C == 3) {
 #pragma unroll
     for (int e = 0; e < DPL / 2; ++e) {
-      ko[e] = f16_pair(tr_bf16_lo(wk[e]), tr_bf16_hi(wk[e]));
+      ko[e] = wk[e];
       vt[part * DPL + 2 * e][vt_pos(tk)] = (_Float16)tr_bf16_lo(wv[e]);
       vt[part * DPL + 2 * e + 1][vt_pos(tk)] = (_Float16)tr_bf16_hi(wv[e]);
     }
+    *kf_out = key_factors(true, 1.0f, 0.0f, kscale);
   } else {
     const int P = c.ptok[C];
     const float2 szk = reinterpret_cast<const float2*>(pb + c.sk_off[C])[(int64_t)h * P + j];
     const float2 szv = reinterpret_cast<const float2*>(pb + c.sv_off[C])[(int64_t)h * P + j];
 #pragma unroll
     for (int e = 0; e < DPL; e += 2) {
-      ko[e / 2] = f16_pair(fmaf(szk.x, (float)code_at<b>(wk, e), szk.y), fmaf(szk.x, (float)code_at<b>(wk, e + 1), szk.y));
+      const float k0 = (float)code_at<b>(wk, e), k1 = (float)code_at<b>(wk, e + 1);
+      ko[e / 2] = (__float_as_uint(k0) >> 16) | (__float_as_uint(k1) & 0xffff0000u);
       vt[part * DPL + e][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
       vt[part * DPL + e + 1][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
     }
+    *kf_out = key_factors(false, szk.x, szk.y, kscale);
   }
 #pragma unroll
   for (int x = 0; x < DPL / 8; ++x)
@@ -334,7 +349,8 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
 // are written as zeros (they are only ever read masked).
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int layer, int tile0, int ntile, int pend,
-                                                          int np, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+                                                          int np, float kscale, uint16_t* __restrict__ dk,
+                                                          uint16_t* __restrict__ dv, float2* __restrict__ dkf) {
   constexpr int DPL = D / 8;
   __shared__ _Float16 vt[D][40];                   // v_hat tile, channel-major (row = 80 B)
   const int lin = xcd_linear(c.B * c.H * ntile);
@@ -344,6 +360,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
   const int tid = threadIdx.x, tk = tid / 8, part = tid % 8;
   const int p = tile * 32 + tk;
   uint16_t* krow = dk + ((int64_t)sh * np + p) * D + part * DPL;
+  float2 kf = make_float2(0.0f, 0.0f);
   if (p < pend) {
     const int32_t* pr0 = tr_prefix_row(c, layer, s, p);
     const int32_t* pr1 = tr_prefix_row(c, layer, s, p + 1);
@@ -356,10 +373,10 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
     const int j = slot & (c.ptok[cls] - 1);
     const uint8_t* pb = c.pool + (int64_t)(page < 0 ? 0 : page) * c.page_bytes;
     switch (cls) {
-      case 0: dense_token<D, 0>(pb, c, h, j, part, krow, vt, tk); break;
-      case 1: dense_token<D, 1>(pb, c, h, j, part, krow, vt, tk); break;
-      case 2: dense_token<D, 2>(pb, c, h, j, part, krow, vt, tk); break;
-      default: dense_token<D, 3>(pb, c, h, j, part, krow, vt, tk); break;
+      case 0: dense_token<D, 0>(pb, c, h, j, part, krow, vt, tk, kscale, &kf); break;
+      case 1: dense_token<D, 1>(pb, c, h, j, part, krow, vt, tk, kscale, &kf); break;
+      case 2: dense_token<D, 2>(pb, c, h, j, part, krow, vt, tk, kscale, &kf); break;
+      default: dense_token<D, 3>(pb, c, h, j, part, krow, vt, tk, kscale, &kf); break;
     }
   } else {
 #pragma unroll
@@ -367,6 +384,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 #pragma unroll
     for (int e = 0; e < DPL; ++e) vt[part * DPL + e][vt_pos(tk)] = (_Float16)0.0f;
   }
+  if (part == 0) dkf[(int64_t)sh * np + p] = kf;
   __syncthreads();
   // V^T rows: D rows x 32 positions (64 bytes each), 16 bytes per thread.
   for (int x = tid; x < D * 4; x += kBlock) {
@@ -381,19 +399,19 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
 // ntile); D/16 lanes per position, 16 channels of K and of V each.  A lane issues all its loads
 // (bits, prefix counts, K, V), then the page-table lookup of its slot, and quantizes while that
 // lookup is in flight.  Codes, scales and page stores are the plain write path's (the same Eq. (4)
-// helpers); tiles from dense_from on also get their k_hat rows and v_hat columns from the values
-// in registers, without re-reading the pages, and zeros at positions >= p0 + T.  Runs after the
+// helpers); tiles from dense_from on also get their K rows, key factors and v_hat columns from
+// the values in registers, without re-reading the pages, and zeros at positions >= p0 + T.  Runs after the
 // slot assignment of the same positions.
 constexpr int kWriteTile = 64;
 constexpr int kWriteNV = 16;                       // channels per lane
 
 template <int D>
 __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int layer, int p0, int T, int tile0,
-                                                         int ntile, int dense_from, int np,
+                                                         int ntile, int dense_from, int np, float kscale,
                                                          const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin,
                                                          const uint8_t* __restrict__ bits, uint16_t* __restrict__ dk,
-                                                         uint16_t* __restrict__ dv) {
+                                                         uint16_t* __restrict__ dv, float2* __restrict__ dkf) {
   constexpr int NV = kWriteNV;
   constexpr int LPG = D / NV;
   constexpr int NT = 4 * D;
@@ -428,16 +446,16 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
   }
   const bool dense = tile >= dense_from;           // else the tile also holds earlier positions
   if (dense) {
-    // k_hat, v_hat = fp16(s * f + z); b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's
-    // sign.
-    const float zk = cls == 3 ? -0.0f : qk.z, zv = cls == 3 ? -0.0f : qv.z;
+    // K: the codes (or the b = 16 values) as bf16 plus the key's (alpha, r); v_hat =
+    // fp16(s * f + z), where b = 16 takes z = -0 so that fma(1, x, -0) = x keeps a zero's sign.
+    const float zv = cls == 3 ? -0.0f : qv.z;
     uint32_t kw[NV / 2];
-#pragma unroll
-    for (int e = 0; e < NV / 2; ++e)
-      kw[e] = live ? f16_pair(fmaf(qk.s, qk.f[2 * e], zk), fmaf(qk.s, qk.f[2 * e + 1], zk)) : 0u;
+    bf16_words<NV>(qk, kw);
     uint4* krow = reinterpret_cast<uint4*>(dk + ((int64_t)sh * np + p) * D + part * NV);
-    krow[0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-    krow[1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
+    krow[0] = live ? make_uint4(kw[0], kw[1], kw[2], kw[3]) : make_uint4(0, 0, 0, 0);
+    krow[1] = live ? make_uint4(kw[4], kw[5], kw[6], kw[7]) : make_uint4(0, 0, 0, 0);
+    if (part == 0)
+      dkf[(int64_t)sh * np + p] = live ? key_factors(cls == 3, qk.s, qk.z, kscale) : make_float2(0.0f, 0.0f);
     // The V^T column is XOR-swizzled by 16 * (part & 3): the lanes of one store hold 16 positions
     // of 4 parts whose rows are 16 rows (a multiple of 64 banks) apart, so without it they collide.
     const int tpos = vt_pos(tk) ^ (16 * (part & 3));
@@ -463,8 +481,10 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
 
 template <int D>
 struct alignas(16) PrefillTile {
-  uint16_t ks[BN][D + 8];      // k_hat fp16, key-major
+  uint16_t ks[BN][D + 8];      // K codes as bf16 integers / stored bf16, key-major; columns
+                               // D .. D + 7 hold the key's (r_hi, r_hi, r_lo, 0, ...) in bf16
   uint16_t vt[D][BN + 8];      // v_hat fp16, channel-major, keys in vt_pos order
+  alignas(16) float alpha[BN]; // s_K * log2(e) / sqrt(D) (or log2(e) / sqrt(D))
 };
 
 template <int D, int G>
@@ -485,8 +505,8 @@ template <int D, int G>
 __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D == 64 ? TR_PREFILL_WAVES : 2))) void k_prefill_attn(
     CacheLayout c, int p0, int T, int window, int np, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const int4* __restrict__ units, int uph,
-    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, float kscale, float* __restrict__ part,
-    uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, const float2* __restrict__ dkf,
+    float* __restrict__ part, uint16_t* __restrict__ out) {
   constexpr int KS = D / 16;           // MFMA k-steps for QK^T
   constexpr int MT = D / 32;           // 32-channel tiles of O^T
   constexpr int KPT = D / 64;          // 16-byte K pieces per thread per tile
@@ -510,19 +530,26 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   const int t = row_ok ? p0 + i : -1;
   const int lo = row_ok ? (full ? 0 : max(0, t - window)) : 0x7fffffff;
 
-  // Q^T operand (B of the QK^T MFMA): column n = query, k = channels 16*ks + 8*g .. +7, as
-  // fp16(q * log2(e) / sqrt(D)) so the product is the score in the log2 domain.
-  f16x8 qb[KS];
+  // Q^T operand (B of the QK^T MFMA): column n = query, k = channels 16*ks + 8*g .. +7.
+  bf16x8 qb[KS];
+  float qsum = 0.0f;
   const uint16_t* qrow = q + (((int64_t)s * T + i) * c.H + h) * D;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint4 raw = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      qb[ks][2 * x] = (_Float16)(tr_bf16_lo(w[x]) * kscale);
-      qb[ks][2 * x + 1] = (_Float16)(tr_bf16_hi(w[x]) * kscale);
-    }
+    qb[ks] = __builtin_bit_cast(bf16x8, raw);
+    qsum += (tr_bf16_lo(raw.x) + tr_bf16_hi(raw.x)) + (tr_bf16_lo(raw.y) + tr_bf16_hi(raw.y)) +
+            (tr_bf16_lo(raw.z) + tr_bf16_hi(raw.z)) + (tr_bf16_lo(raw.w) + tr_bf16_hi(raw.w));
+  }
+  qsum = xor32_sum(qsum);
+  // The zero-point k-step's B operand: (sq_hi, sq_lo, sq_hi, 0, ...) at k = 0 .. 7 (lanes g = 0),
+  // zeros at k = 8 .. 15, against the keys' (r_hi, r_hi, r_lo, 0, ...): r * sum(q) to ~2^-16.
+  bf16x8 qz;
+  {
+    const uint16_t hi = tr_f32_to_bf16(qsum);
+    const uint16_t lo = tr_f32_to_bf16(qsum - tr_bf16_lo(hi));
+    const uint4 w = g == 0 ? make_uint4((uint32_t)hi | ((uint32_t)lo << 16), hi, 0, 0) : make_uint4(0, 0, 0, 0);
+    qz = __builtin_bit_cast(bf16x8, w);
   }
 
   // Wave and workgroup key-position ranges.
@@ -557,7 +584,9 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   // (tid % 4); for D = 128 every thread moves two pieces of each.
   const uint16_t* kbase = dk + (int64_t)sh * np * D;
   const uint16_t* vbase = dv + (int64_t)sh * D * np;
+  const float2* fbase = dkf + (int64_t)sh * np;
   uint4 rk[KPT], rv[VPT];
+  float2 rf = make_float2(0.0f, 0.0f);
   auto load_tile = [&](int kb) {
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
@@ -569,6 +598,7 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
       const int e = tid + x * kBlock;
       rv[x] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(e >> 2) * np + kb + (e & 3) * 8);
     }
+    if (tid < BN) rf = fbase[kb + tid];
   };
   auto store_tile = [&](PrefillTile<D>& tl) {
 #pragma unroll
@@ -580,6 +610,12 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     for (int x = 0; x < VPT; ++x) {
       const int e = tid + x * kBlock;
       *reinterpret_cast<uint4*>(&tl.vt[e >> 2][(e & 3) * 8]) = rv[x];
+    }
+    if (tid < BN) {
+      tl.alpha[tid] = rf.x;
+      const uint16_t hi = tr_f32_to_bf16(rf.y);
+      const uint16_t lo = tr_f32_to_bf16(rf.y - tr_bf16_lo(hi));
+      *reinterpret_cast<uint4*>(&tl.ks[tid][D]) = make_uint4((uint32_t)hi | ((uint32_t)hi << 16), lo, 0, 0);
     }
   };
 
@@ -604,16 +640,15 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     const int kb = kb0 + it * BN;
     // ---- compute tile it (waves outside their windows skip it) ----
     if (it < ntiles && wave_live && kb < whi && kb + BN - 1 >= wlo) {
-      // x = score - mref: the accumulator starts at -mref (the lane's query), so the MFMA
-      // result is x itself.
+      // S = q . c + r * sum(q) (the zero-point k-step first, on a zero accumulator); then
+      // x = score - mref = alpha * S - mref, one FMA per score.
       const float nm = (mref == -INFINITY) ? 0.0f : -mref;
-      f32x16 sacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = nm;
+      f32x16 sacc = {};
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&tl.ks[n][D]), qz, sacc, 0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&tl.ks[n][16 * ks + 8 * g]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[ks], sacc, 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&tl.ks[n][16 * ks + 8 * g]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
       }
       // Only tiles that cross a row's window edge are masked (a wave-uniform choice between two
       // versions): key kb + 4g + off (off = 8 * r4 + x) is visible iff lo <= key <= t, i.e. iff
@@ -625,9 +660,11 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
         const uint32_t span = row_ok ? (uint32_t)(t - lo) : 0u;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[8 * r4 + 4 * g]);
+          const float alv[4] = {al.x, al.y, al.z, al.w};
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            float v = sacc[4 * r4 + x];
+            float v = fmaf(alv[x], sacc[4 * r4 + x], nm);
             if constexpr (decltype(masked)::value) {
               if ((uint32_t)(8 * r4 + x - dlo) > span) v = -INFINITY;
             }
@@ -822,11 +859,12 @@ template <int D>
 tr_status launch_write_tiles(tr_kv_cache* c, int layer, int p0, const uint16_t* k, const uint16_t* v,
                              const uint8_t* bits, int T, int dense_from, hipStream_t stream) {
   const CacheLayout& L = c->lay;
+  const float kscale = (float)(1.4426950408889634 / sqrt((double)D));
   const int tile0 = p0 / kWriteTile, ntile = (p0 + T + kWriteTile - 1) / kWriteTile - tile0;
   const int64_t blocks = (int64_t)L.B * L.H * ntile;
   if (blocks > (int64_t)1 << 30) return TR_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid((int)blocks)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
-                     ntile, dense_from, c->np, k, v, bits, c->dk, c->dv);
+                     ntile, dense_from, c->np, kscale, k, v, bits, c->dk, c->dv, c->dkf);
   TR_LAUNCH_CHECK();
   return TR_OK;
 }
@@ -865,13 +903,13 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   if (dense_to > 0) {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
     hipLaunchKernelGGL(k_prefill_dense<D>, dim3(xcd_grid(BH * dense_to)), dim3(kBlock), 0, stream, L, layer, 0, dense_to, pend,
-                       c->np, c->dk, c->dv);
+                       c->np, kscale, c->dk, c->dv, c->dkf);
     TR_LAUNCH_CHECK();
   }
   TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
   hipLaunchKernelGGL((k_prefill_attn<D, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
                      stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
-                     kscale, c->pf_part, out);
+                     c->dkf, c->pf_part, out);
   TR_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_prefill_merge<D>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
                      c->row_counts, c->pf_merges, c->pf_part, out);
