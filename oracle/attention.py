@@ -9,7 +9,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
     Attn_t^full  = Attn(q_t, K[<= t],     V[<= t])
 
 Attn(q, K, V) is softmax attention with scores q . k_j / sqrt(D).  The same page routes
-attention per head by default, so the mode is indexed by (query, head).  Positions are
+attention per head by default, so the mode is indexed by (query, head).  With grouped-query
+attention (the page's experimental setup, section 5, uses H_kv = H/4) query head h reads KV
+head h // (H / H_kv); H_kv = H is plain multi-head attention.  Positions are
 0-based; the local window is the inclusive range [max(0, t - w), t] (w + 1 keys once t >= w).
 Everything is float64; K and V are whatever the caller passes (for TriRoute: the cached,
 dequantized values, see ``reference.attend_cached``).
@@ -37,7 +39,7 @@ def routed_attention(q, k, v, mode, q_pos, window: int):
     """Routed attention, Eq. (2).
 
     q:     float [Tq, H, D]   queries
-    k, v:  float [Tk, H, D]   keys / values by absolute position 0 .. Tk-1
+    k, v:  float [Tk, Hkv, D] keys / values by absolute position 0 .. Tk-1; Hkv divides H
     mode:  int   [Tq, H]      0 = skip, 1 = local-w, 2 = full
     q_pos: int   [Tq]         absolute position t of each query (t < Tk)
     window: w >= 0
@@ -50,8 +52,12 @@ def routed_attention(q, k, v, mode, q_pos, window: int):
     mode = np.asarray(mode)
     q_pos = np.asarray(q_pos, dtype=np.int64)
     Tq, H, D = q.shape
-    if k.shape[1:] != (H, D) or v.shape != k.shape:
-        raise ValueError("k/v must be [Tk, H, D] matching q")
+    if k.ndim != 3 or k.shape[2] != D or v.shape != k.shape:
+        raise ValueError("k/v must be [Tk, Hkv, D] matching q's D")
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the KV head count must divide the query head count")
+    group = H // Hkv
     if window < 0:
         raise ValueError("window must be >= 0")
     if Tq and (q_pos.min() < 0 or q_pos.max() >= k.shape[0]):
@@ -67,8 +73,8 @@ def routed_attention(q, k, v, mode, q_pos, window: int):
             if m not in (MODE_LOCAL, MODE_FULL):
                 raise ValueError("mode must be 0, 1 or 2")
             lo, hi = key_range(t, m, window)
-            kk = k[lo:hi + 1, h, :]
-            vv = v[lo:hi + 1, h, :]
+            kk = k[lo:hi + 1, h // group, :]
+            vv = v[lo:hi + 1, h // group, :]
             scores = (kk @ q[i, h, :]) * inv_sqrt_d
             p = np.exp(scores - scores.max())
             out[i, h, :] = (p @ vv) / p.sum()

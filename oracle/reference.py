@@ -17,13 +17,13 @@ from .quantize import bf16_bits_to_f32, dequantize, quantize
 def attend_cached(q_bits, k_bits, v_bits, bits, mode, q_pos, window: int):
     """Quantize-write every token of one sequence, then run routed attention over the cache.
 
-    q_bits: uint16 bf16 [Tq, H, D]      queries
+    q_bits: uint16 bf16 [Tq, Hq, D]     queries (Hq a multiple of H: grouped-query attention)
     k_bits, v_bits: uint16 bf16 [T, H, D]  K/V of positions 0 .. T-1 (the cache contents)
     bits:   int [T]                      width b of each position, shared by K, V and heads
-    mode:   int [Tq, H]                  0 skip, 1 local, 2 full
+    mode:   int [Tq, Hq]                 0 skip, 1 local, 2 full
     q_pos:  int [Tq]                     position of each query (< T)
 
-    Returns a dict with the attention output (float64 [Tq, H, D]), the cache contents
+    Returns a dict with the attention output (float64 [Tq, Hq, D]), the cache contents
     (codes uint16 [T, 2, H, D]; scale, zero float32 [T, 2, H]; index 0 = K, 1 = V) and the
     dequantized K/V (float64 [T, H, D]).
     """

@@ -226,3 +226,38 @@ def test_cached_attends_to_the_quantized_values():
     assert np.max(np.abs(res2["out"] - res16["out"])) > 1e-3
     # the first query has a single key: its output is exactly the dequantized value row
     np.testing.assert_array_equal(res2["out"][0], res2["v_hat"][0])
+
+
+# --- grouped-query attention (query head h reads KV head h // (H / H_kv)) -------------------
+
+def test_gqa_all_full_equals_sdpa_with_grouped_kv():
+    rng = np.random.default_rng(21)
+    T, Hq, Hkv, D = 29, 8, 2, 16
+    q, k, v = rand(rng, T, Hq, D), rand(rng, T, Hkv, D), rand(rng, T, Hkv, D)
+    out = oracle.routed_attention(q, k, v, np.full((T, Hq), MODE_FULL), np.arange(T), 0)
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(out, ref.numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_mixed_modes_equal_mha_on_repeated_kv():
+    rng = np.random.default_rng(22)
+    T, Hq, Hkv, D, w = 37, 6, 3, 8, 4
+    q, k, v = rand(rng, T, Hq, D), rand(rng, T, Hkv, D), rand(rng, T, Hkv, D)
+    mode = rng.integers(0, 3, size=(T, Hq))
+    out = oracle.routed_attention(q, k, v, mode, np.arange(T), w)
+    rep = Hq // Hkv                                      # KV head j serves query heads j*rep .. j*rep+rep-1
+    ref = oracle.routed_attention(q, np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1), mode, np.arange(T), w)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=0)
+    # a KV head mapping h % Hkv (instead of h // rep) would differ
+    bad = oracle.routed_attention(q, np.tile(k, (1, rep, 1)), np.tile(v, (1, rep, 1)), mode, np.arange(T), w)
+    assert not np.allclose(out, bad)
+
+
+def test_gqa_rejects_a_kv_head_count_that_does_not_divide():
+    rng = np.random.default_rng(23)
+    q, k = rand(rng, 4, 6, 8), rand(rng, 4, 4, 8)
+    with pytest.raises(ValueError):
+        oracle.routed_attention(q, k, k, np.full((4, 6), MODE_FULL), np.arange(4), 0)

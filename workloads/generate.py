@@ -65,20 +65,21 @@ def _normal_bf16(shape, gen, device, scale=None) -> torch.Tensor:
 def random_case(batch: int, tokens: int, heads: int, head_dim: int, *, window: int,
                 bit_weights: dict, mode_weights: dict, seed: int = 0, device="cpu",
                 clustered_bits: bool = False, n_queries: int | None = None,
-                layer: int = 0, cid: int = 99) -> dict:
+                layer: int = 0, cid: int = 99, kv_heads: int | None = None) -> dict:
     """One layer of inputs for `batch` sequences of `tokens` positions.
 
     Returns bf16 q [B, Tq, H, D] (Tq = tokens, or n_queries trailing positions), bf16 k, v
-    [B, tokens, H, D], uint8 bits [B, tokens] (values 2/4/8/16) and uint8 mode [B, Tq, H]
-    (0 skip, 1 local, 2 full).
+    [B, tokens, Hkv, D] (Hkv = kv_heads, default H; grouped-query attention when smaller),
+    uint8 bits [B, tokens] (values 2/4/8/16) and uint8 mode [B, Tq, H] (0 skip, 1 local, 2 full).
     """
     dev = torch.device(device)
     Tq = tokens if n_queries is None else int(n_queries)
+    hkv = heads if kv_heads is None else int(kv_heads)
     g_scale = _gen(dev, seed, cid, layer, "kscale")
-    kscale = torch.exp(0.5 * torch.randn((heads, head_dim), generator=g_scale, device=dev,
+    kscale = torch.exp(0.5 * torch.randn((hkv, head_dim), generator=g_scale, device=dev,
                                          dtype=torch.float32))
-    k = _normal_bf16((batch, tokens, heads, head_dim), _gen(dev, seed, cid, layer, "k"), dev, kscale)
-    v = _normal_bf16((batch, tokens, heads, head_dim), _gen(dev, seed, cid, layer, "v"), dev)
+    k = _normal_bf16((batch, tokens, hkv, head_dim), _gen(dev, seed, cid, layer, "k"), dev, kscale)
+    v = _normal_bf16((batch, tokens, hkv, head_dim), _gen(dev, seed, cid, layer, "v"), dev)
     q = _normal_bf16((batch, Tq, heads, head_dim), _gen(dev, seed, cid, layer, "q"), dev)
     bits = _bits(batch, tokens, bit_weights, clustered_bits, _gen(dev, seed, cid, layer, "bits"),
                  _gen(dev, seed, cid, layer, "runs"), dev)
