@@ -59,13 +59,17 @@ enum { TR_MODE_SKIP = 0, TR_MODE_LOCAL = 1, TR_MODE_FULL = 2 };
 typedef struct {
   int32_t num_layers;       /* >= 1 */
   int32_t batch;            /* sequences per layer, >= 1 */
-  int32_t num_heads;        /* KV heads = query heads (MHA), >= 1 */
+  int32_t num_heads;        /* KV heads, >= 1 (the heads the cache stores) */
   int32_t head_dim;         /* 64 or 128 */
   int32_t max_tokens;       /* per-sequence capacity in positions, >= 1 */
   int32_t page_code_bytes;  /* K (and V) code bytes of one head in one page; 0 -> 4096.
                                A power of two in [1024, 65536].  A page of width b holds
                                page_code_bytes * 8 / (head_dim * b) tokens. */
   int64_t pool_pages;       /* pages in the pool; 0 -> enough for any mix of widths */
+  int32_t num_query_heads;  /* query heads of the attention calls: 0 -> num_heads (multi-head
+                               attention), else a multiple of num_heads (grouped-query attention:
+                               query head h reads KV head h / (num_query_heads / num_heads); the
+                               review page's experimental setup, section 5, uses H_kv = H/4) */
 } tr_kv_cache_desc;
 
 /* Opaque cache: per (layer, sequence, width class) a stream of pages of the pool, fp32
@@ -102,17 +106,18 @@ tr_status tr_kv_quantize_write(tr_kv_cache* cache, int32_t layer, const void* k,
 
 /* Eq. (2) decode: one query per sequence at position t = len - 1 (its K/V must already be
  * written with tr_kv_quantize_write), attending in its per-head mode to the cached K/V.
- *   q:    bf16 [batch, num_heads, head_dim]
- *   mode: uint8 [batch, num_heads] (TR_MODE_*)
+ *   q:    bf16 [batch, num_query_heads, head_dim]
+ *   mode: uint8 [batch, num_query_heads] (TR_MODE_*)
  *   window: w >= 0 for local heads
- *   out:  bf16 [batch, num_heads, head_dim]; skip heads get zeros */
+ *   out:  bf16 [batch, num_query_heads, head_dim]; skip heads get zeros */
 tr_status tr_routed_attn_decode(tr_kv_cache* cache, int32_t layer, const void* q, const uint8_t* mode,
                                 int32_t window, void* out, void* stream);
 
 /* Prefill: write T new tokens with Eq. (4), then run Eq. (2) for all T queries (causal, each
  * query at its own position len + i, reading the cache just written).
- *   q, k, v: bf16 [batch, T, num_heads, head_dim];  bits: uint8 [batch, T]
- *   mode:    uint8 [batch, T, num_heads];            out: bf16 [batch, T, num_heads, head_dim] */
+ *   q:    bf16 [batch, T, num_query_heads, head_dim]; k, v: bf16 [batch, T, num_heads, head_dim]
+ *   bits: uint8 [batch, T];  mode: uint8 [batch, T, num_query_heads]
+ *   out:  bf16 [batch, T, num_query_heads, head_dim] */
 tr_status tr_routed_attn_prefill(tr_kv_cache* cache, int32_t layer, const void* q, const void* k,
                                  const void* v, const uint8_t* bits, const uint8_t* mode, int32_t T,
                                  int32_t window, void* out, void* stream);

@@ -26,7 +26,8 @@ _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 
 class _Desc(ctypes.Structure):
     _fields_ = [("num_layers", _i32), ("batch", _i32), ("num_heads", _i32), ("head_dim", _i32),
-                ("max_tokens", _i32), ("page_code_bytes", _i32), ("pool_pages", _i64)]
+                ("max_tokens", _i32), ("page_code_bytes", _i32), ("pool_pages", _i64),
+                ("num_query_heads", _i32)]
 
 
 def _sig(name, res, *args):
@@ -112,12 +113,14 @@ class KVCache:
 
 
 def tr_kv_cache_alloc(num_layers: int, batch: int, num_heads: int, head_dim: int, max_tokens: int,
-                      page_code_bytes: int = 0, pool_pages: int = 0) -> KVCache:
-    d = _Desc(num_layers, batch, num_heads, head_dim, max_tokens, page_code_bytes, pool_pages)
+                      page_code_bytes: int = 0, pool_pages: int = 0, num_query_heads: int = 0) -> KVCache:
+    """num_heads: KV heads; num_query_heads: query heads (0 = num_heads; a multiple for GQA)."""
+    d = _Desc(num_layers, batch, num_heads, head_dim, max_tokens, page_code_bytes, pool_pages, num_query_heads)
     h = _vp()
     _check(_alloc(ctypes.byref(d), ctypes.byref(h)), "tr_kv_cache_alloc")
     return KVCache(h.value, dict(num_layers=num_layers, batch=batch, num_heads=num_heads, head_dim=head_dim,
-                                 max_tokens=max_tokens, page_code_bytes=page_code_bytes, pool_pages=pool_pages))
+                                 max_tokens=max_tokens, page_code_bytes=page_code_bytes, pool_pages=pool_pages,
+                                 num_query_heads=num_query_heads or num_heads))
 
 
 def tr_kv_cache_free(cache: KVCache):

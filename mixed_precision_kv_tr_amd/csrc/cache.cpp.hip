@@ -285,6 +285,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   if (d->num_layers < 1 || d->batch < 1 || d->num_heads < 1 || d->max_tokens < 1 || d->pool_pages < 0)
     return TR_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return TR_ERR_UNSUPPORTED;
+  const int hq = d->num_query_heads ? d->num_query_heads : d->num_heads;
+  if (hq < d->num_heads || hq % d->num_heads) return TR_ERR_INVALID_ARG;
   const int cb = d->page_code_bytes ? d->page_code_bytes : 4096;
   if (cb < 1024 || cb > 65536 || (cb & (cb - 1))) return TR_ERR_INVALID_ARG;
 
@@ -299,6 +301,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   c->prof_on = false;
   CacheLayout& L = c->lay;
   L.L = d->num_layers; L.B = d->batch; L.H = d->num_heads; L.D = d->head_dim; L.N = d->max_tokens;
+  c->hq = hq;
+  c->grp = hq / L.H;
   L.cb = cb;
   int64_t page_bytes = 0;
   L.pt_stride = 0;
@@ -343,18 +347,18 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   ok = ok && hipMalloc((void**)&L.next_page, sizeof(int32_t)) == hipSuccess;
   ok = ok && hipMalloc((void**)&L.err, sizeof(uint32_t)) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->partials,
-                       sizeof(float) * (size_t)L.B * L.H * c->max_chunks * (L.D + 2)) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * L.H * L.N) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * L.H * 4) == hipSuccess;
+                       sizeof(float) * (size_t)L.B * hq * c->max_chunks * (L.D + 2)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * hq * L.N) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * hq * 4) == hipSuccess;
   c->np = (L.N + 63) / 64 * 64;
   ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->dkf, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;
   c->pf_uph = tr_prefill_units_per_head(L.N);
-  ok = ok && hipMalloc((void**)&c->pf_units, sizeof(int4) * (size_t)L.B * L.H * c->pf_uph) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->pf_merges, sizeof(int4) * (size_t)L.B * L.H * (TR_PREFILL_SLOTS / 2)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->pf_units, sizeof(int4) * (size_t)L.B * hq * c->pf_uph) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->pf_merges, sizeof(int4) * (size_t)L.B * hq * (TR_PREFILL_SLOTS / 2)) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->pf_part,
-                       sizeof(float) * (size_t)L.B * L.H * TR_PREFILL_SLOTS * 128 * (L.D + 4)) == hipSuccess;
+                       sizeof(float) * (size_t)L.B * hq * TR_PREFILL_SLOTS * 128 * (L.D + 4)) == hipSuccess;
   if (!ok) {
     hipGetLastError();
     free_all(c);

@@ -10,23 +10,25 @@
 #include "triroute.h"
 
 struct tr_kv_cache {
-  CacheLayout lay;
+  CacheLayout lay;                // lay.H = KV heads (what the cache stores)
+  int32_t hq;                     // query heads of the attention calls (a multiple of lay.H)
+  int32_t grp;                    // hq / lay.H: query heads per KV head (1 = multi-head)
   int device;
   std::vector<int32_t> len;       // host mirror: tokens written per layer (same for every sequence)
-  // decode split-K partials: [B][H][max_chunks][D + 2] floats (o[D], m, l)
+  // decode split-K partials: [B][HQ][max_chunks][D + 2] floats (o[D], m, l)
   float* partials;
   int32_t max_chunks;
-  // prefill scratch: compacted query rows per (seq, head) [B][H][N] and counts [B][H][2]
+  // prefill scratch: compacted query rows per (seq, query head) [B][HQ][N] and counts [B][HQ][4]
   int32_t* rows;
   int32_t* row_counts;
-  // prefill scratch: the cache range a prefill call reads, dequantized once, position order
+  // prefill scratch: the cache range a prefill call reads, staged once per KV head, position order
   //   dk [B][H][NP][D] uint16: K code as a bf16 integer (exact), or the stored bf16 (b = 16)
   //   dkf [B][H][NP] float2:   (alpha, r) = (s_K * log2(e) / sqrt(D), z_K / s_K) per key
   //   dv [B][H][D][NP] uint16: v_hat = s * c + z as fp16, channel-major; within each group of
   //                            16 positions, bits 2 and 3 of the position are swapped
-  // prefill attention work: units (128-row tile, key-tile chunk) [B][H][pf_uph] int4, merges of
-  // split tiles [B][H][TR_PREFILL_SLOTS / 2] int4, partial results of split tiles
-  // [B][H][TR_PREFILL_SLOTS][128][D + 4] floats (O, max, sum, padding)
+  // prefill attention work, per (seq, query head): units (128-row tile, key-tile chunk)
+  // [B][HQ][pf_uph] int4, merges of split tiles [B][HQ][TR_PREFILL_SLOTS / 2] int4, partial
+  // results of split tiles [B][HQ][TR_PREFILL_SLOTS][128][D + 4] floats (O, max, sum, padding)
   int4* pf_units;
   int4* pf_merges;
   float* pf_part;
@@ -62,6 +64,17 @@ inline int tr_decode_max_chunk(const CacheLayout& L) {
 #define TR_PREFILL_SLOTS 16
 #endif
 inline int tr_prefill_units_per_head(int T) { return (T + 127) / 128 + 1 + TR_PREFILL_SLOTS; }
+
+// Workgroups are dealt to the 8 XCDs round-robin by id; this gives XCD x the contiguous run
+// [x * per, (x + 1) * per) of the n work items (grid = 8 * per, per = ceil(n / 8)), so that
+// neighbouring items -- which share cache lines -- go through the same L2.  -1 for the padding
+// workgroups.
+__device__ __forceinline__ int tr_xcd_linear(int n) {
+  const int per = (n + 7) >> 3;
+  const int lin = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  return lin < n ? lin : -1;
+}
+inline int tr_xcd_grid(int n) { return ((n + 7) >> 3) << 3; }
 
 // Kernel families reported by tr_profile_read.
 enum { TR_PROF_WRITE = 0, TR_PROF_DECODE_SPLIT = 1, TR_PROF_DECODE_COMBINE = 2, TR_PROF_PREFILL_COMPACT = 3,

@@ -1,13 +1,15 @@
 // Decode routed attention over the mixed-width paged cache (TriRoute review page,
 // xllm-io.github.io: Eq. (2) modes read by a query; Eq. (4) codes written per token).
 //
-// One query per (sequence, head) at position t.  Its key set is the position window
+// One query per (sequence, query head) at position t, reading the K/V of its KV head
+// (query head h reads KV head h / G with G query heads per KV head; G = 1 is plain multi-head
+// attention).  Its key set is the position window
 // [lo, t] (lo = 0 for full, max(0, t - w) for local; skip heads read nothing).  The window is
 // split into position chunks (split-K); every chunk maps, through the per-position class
 // prefix counts, to one contiguous slot range per width class, so out-of-window keys are
 // never read and each inner loop runs over a single width (wave-uniform unpacking).
 //
-// k_decode: one wavefront = one workgroup = one (seq, head, chunk) work item, with no
+// k_decode: one wavefront = one workgroup = one (seq, query head, chunk) work item, with no
 // cross-wave synchronization, so every wave streams independently.
 //   prologue the chunk's page ids of every class and q -> LDS.
 //   phase 1  K codes -> scores in LDS.  Each lane takes a 16/32-byte slice of a key row;
@@ -282,14 +284,14 @@ template <int D>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_WAVES, 8))) void k_decode(CacheLayout c, int layer, int t, int window, int CH, int nch_grid,
                                                   int max_chunks, float kscale, const uint16_t* __restrict__ q,
                                                   const uint8_t* __restrict__ mode, float* __restrict__ part,
-                                                  uint16_t* __restrict__ out) {
+                                                  uint16_t* __restrict__ out, int HQ, int G) {
   __shared__ float qs[D];
   __shared__ float sc[kItemMax];
   __shared__ int32_t pg[TR_NCLASS][kPgMax];
   const int lane = threadIdx.x;
   const int k = blockIdx.x % nch_grid;
-  const int sh = blockIdx.x / nch_grid;
-  const int h = sh % c.H, s = sh / c.H;
+  const int sh = blockIdx.x / nch_grid;             // (seq, query head)
+  const int s = sh / HQ, h = (sh % HQ) / G;         // sequence, KV head it reads
   const int m = mode[sh];
   uint16_t* o = out + (int64_t)sh * D;
   if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) {
@@ -448,7 +450,7 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
   const CacheLayout& L = c->lay;
   const int t = c->len[layer] - 1;
   const int n = t + 1;
-  const int BH = L.B * L.H;
+  const int BH = L.B * c->hq;                       // (seq, query head) pairs
   const int max_ch = tr_decode_max_chunk(L);
   // About 8192 work items if every head were full (a few times the waves the chip holds at
   // once), but no chunk below kMinChunk positions.
@@ -466,10 +468,10 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
     TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
     if (L.D == 64)
       hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
-                         c->max_chunks, kscale, q, mode, c->partials, out);
+                         c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp);
     else
       hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
-                         c->max_chunks, kscale, q, mode, c->partials, out);
+                         c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp);
     TR_LAUNCH_CHECK();
   }
   if (nch > 1) {

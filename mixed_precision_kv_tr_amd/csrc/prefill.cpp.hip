@@ -2,11 +2,14 @@
 // xllm-io.github.io: Eq. (2) for every query of the prompt, reading the K/V that Eq. (4) has
 // just written -- the inference paragraph after Algorithm 1).
 //
-// k_prefill_prep (one workgroup per (seq, head), plus one per sequence for the slot
+// Heads: the cache holds H KV heads; the queries have HQ = G * H heads, and query head h reads
+//   KV head h / G (grouped-query attention; G = 1 is multi-head).  Staging is per KV head; the
+//   compaction, attention and merge are per query head.
+// k_prefill_prep (one workgroup per (seq, query head), plus one per sequence for the slot
 //   assignment of the call's positions): stable partition of the T query rows by mode -- full
 //   rows, then local rows -- so that a 128-row tile holds one mode and its key range is tight;
 //   skip rows (and rows with an invalid mode) get zeros right here.  Then the attention work
-//   units of the (seq, head).
+//   units of the (seq, query head).
 // Dense staging: the cache range the call's queries read, staged once in position order: K as
 //   its code in bf16 (an exact integer <= 255, or the stored bf16 for b = 16) with per-key
 //   (alpha, r) = (s_K * log2(e)/sqrt(D), z_K / s_K); V as v_hat = s * c + z (fp32) rounded to
@@ -152,16 +155,16 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
 // loaded 4 rows at a time (addresses clamped into the column, so the loads go out together) and,
 // for R <= 16, kept as 2-bit codes for the second pass.
 template <int D, int NT>
-__device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p0, int T, int window,
+__device__ __forceinline__ void compact_rows(const CacheLayout& c, int HQ, int sh, int p0, int T, int window,
                                              const uint8_t* __restrict__ mode, int32_t* __restrict__ rows,
                                              int32_t* __restrict__ counts, int4* __restrict__ units,
                                              int4* __restrict__ merges, int uph, uint16_t* __restrict__ out) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t wf[NW], wl[NW];
-  const int s = sh / c.H, h = sh % c.H;
+  const int s = sh / HQ, h = sh % HQ;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int32_t* rl = rows + (int64_t)sh * c.N;
-  const uint8_t* mcol = mode + (int64_t)s * T * c.H + h;
+  const uint8_t* mcol = mode + (int64_t)s * T * HQ + h;
   const int R = (T + NT - 1) / NT;
   const int i0 = min(T, tid * R), i1 = min(T, i0 + R);
   // 2-bit code of a row's mode: 0 skip, 1 local, 2 full, 3 invalid (flagged, treated as skip)
@@ -169,7 +172,7 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + r0 + u;
-      const uint32_t x = mcol[(int64_t)min(i, T - 1) * c.H];
+      const uint32_t x = mcol[(int64_t)min(i, T - 1) * HQ];
       m[u] = i < i1 ? (x > TR_MODE_FULL ? 3u : x) : 0u;
     }
   };
@@ -221,7 +224,7 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p
         rl[nfull + bl++] = i;
       } else {
         if (m[u] == 3u) atomicOr(c.err, TR_ERRF_BAD_MODE);
-        uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * c.H + h) * D);
+        uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * HQ + h) * D);
 #pragma unroll
         for (int x = 0; x < D / 8; ++x) o[x] = make_uint4(0, 0, 0, 0);
       }
@@ -233,8 +236,9 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int sh, int p
     build_units(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph, merges + (int64_t)sh * (kSlotsPerHead / 2));
 }
 
-// Preparation of a prefill call, one launch: workgroups [0, B*H) compact the query rows of one
-// (seq, head) each and list its attention work units; with assign set, workgroups [B*H, B*H + B)
+// Preparation of a prefill call, one launch: workgroups [0, B*HQ) compact the query rows of one
+// (seq, query head) each and list its attention work units; with assign set, workgroups
+// [B*HQ, B*HQ + B)
 // assign the slots and pages of the call's positions, one sequence each (independent work that
 // the quantize-write needs, so it overlaps the compaction instead of taking a launch of its own).
 template <int D>
@@ -242,25 +246,15 @@ __global__ __launch_bounds__(TR_ASSIGN_THREADS) void k_prefill_prep(CacheLayout 
                                                                     int window, const uint8_t* __restrict__ mode,
                                                                     const uint8_t* __restrict__ bits, int32_t* rows,
                                                                     int32_t* counts, int4* units, int4* merges,
-                                                                    int uph, uint16_t* __restrict__ out) {
-  const int BH = c.B * c.H;
+                                                                    int uph, uint16_t* __restrict__ out, int HQ) {
+  const int BH = c.B * HQ;
   if ((int)blockIdx.x >= BH) {
     tr_assign_slots_seq(c, layer, p0, T, bits, blockIdx.x - BH);
     return;
   }
-  compact_rows<D, TR_ASSIGN_THREADS>(c, blockIdx.x, p0, T, window, mode, rows, counts, units, merges, uph, out);
+  compact_rows<D, TR_ASSIGN_THREADS>(c, HQ, blockIdx.x, p0, T, window, mode, rows, counts, units, merges, uph, out);
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin by id; this gives XCD x the contiguous run
-// [x * per, (x + 1) * per) of the n work items (grid = 8 * per, per = ceil(n / 8)), so that
-// neighbouring tiles -- which share cache lines of the dense scratch and of the class pages --
-// are written through the same L2.  -1 for the padding workgroups.
-__device__ __forceinline__ int xcd_linear(int n) {
-  const int per = (n + 7) >> 3;
-  const int lin = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  return lin < n ? lin : -1;
-}
-inline int xcd_grid(int n) { return ((n + 7) >> 3) << 3; }
 
 template <int NB>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int e) {
@@ -353,7 +347,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_dense(CacheLayout c, int lay
                                                           uint16_t* __restrict__ dv, float2* __restrict__ dkf) {
   constexpr int DPL = D / 8;
   __shared__ _Float16 vt[D][40];                   // v_hat tile, channel-major (row = 80 B)
-  const int lin = xcd_linear(c.B * c.H * ntile);
+  const int lin = tr_xcd_linear(c.B * c.H * ntile);
   if (lin < 0) return;
   const int tile = tile0 + lin % ntile, sh = lin / ntile;
   const int s = sh / c.H, h = sh % c.H;
@@ -418,7 +412,7 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
   constexpr int TP = kWriteTile;
   static_assert(NT / LPG == TP, "one position per lane group");
   __shared__ _Float16 vt[D][TP + 8];               // v_hat tile, channel-major (row = 144 B)
-  const int lin = xcd_linear(c.B * c.H * ntile);
+  const int lin = tr_xcd_linear(c.B * c.H * ntile);
   if (lin < 0) return;
   const int tile = tile0 + lin % ntile, sh = lin / ntile;
   const int s = sh / c.H, h = sh % c.H;
@@ -506,16 +500,17 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     CacheLayout c, int p0, int T, int window, int np, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const int4* __restrict__ units, int uph,
     const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, const float2* __restrict__ dkf,
-    float* __restrict__ part, uint16_t* __restrict__ out) {
+    float* __restrict__ part, uint16_t* __restrict__ out, int HQ, int QG) {
   constexpr int KS = D / 16;           // MFMA k-steps for QK^T
   constexpr int MT = D / 32;           // 32-channel tiles of O^T
   constexpr int KPT = D / 64;          // 16-byte K pieces per thread per tile
   constexpr int VPT = D / 64;          // 16-byte V^T pieces per thread per tile
   __shared__ PrefillSmem<D, G> sm;
 
-  const int BH = c.B * c.H;
-  const int u = blockIdx.x / BH, sh = blockIdx.x % BH;
-  const int s = sh / c.H, h = sh % c.H;
+  const int BH = c.B * HQ;
+  const int u = blockIdx.x / BH, sh = blockIdx.x % BH;   // sh: (seq, query head)
+  const int s = sh / HQ, h = sh % HQ;
+  const int64_t skv = (int64_t)s * c.H + h / QG;         // its KV head's dense rows
   if (u >= counts[sh * 4 + 2]) return;
   const int4 unit = units[(int64_t)sh * uph + u];
   const bool full = unit.x < 0;
@@ -533,7 +528,7 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   // Q^T operand (B of the QK^T MFMA): column n = query, k = channels 16*ks + 8*g .. +7.
   bf16x8 qb[KS];
   float qsum = 0.0f;
-  const uint16_t* qrow = q + (((int64_t)s * T + i) * c.H + h) * D;
+  const uint16_t* qrow = q + (((int64_t)s * T + i) * HQ + h) * D;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint4 raw = row_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
@@ -582,9 +577,9 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
 
   // Staging: thread -> K row (tid / 8), 16-byte piece (tid % 8); V^T row (tid / 4), piece
   // (tid % 4); for D = 128 every thread moves two pieces of each.
-  const uint16_t* kbase = dk + (int64_t)sh * np * D;
-  const uint16_t* vbase = dv + (int64_t)sh * D * np;
-  const float2* fbase = dkf + (int64_t)sh * np;
+  const uint16_t* kbase = dk + skv * np * D;
+  const uint16_t* vbase = dv + skv * D * np;
+  const float2* fbase = dkf + skv * np;
   uint4 rk[KPT], rv[VPT];
   float2 rf = make_float2(0.0f, 0.0f);
   auto load_tile = [&](int kb) {
@@ -772,7 +767,7 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     return;
   }
   const float inv = 1.0f / ltot;
-  uint16_t* orow = out + (((int64_t)s * T + i) * c.H + h) * D;
+  uint16_t* orow = out + (((int64_t)s * T + i) * HQ + h) * D;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -794,19 +789,19 @@ template <int D>
 __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, const int32_t* __restrict__ rows,
                                                           const int32_t* __restrict__ counts,
                                                           const int4* __restrict__ merges, const float* __restrict__ part,
-                                                          uint16_t* __restrict__ out) {
+                                                          uint16_t* __restrict__ out, int HQ) {
   constexpr int MPH = kSlotsPerHead / 2;
   constexpr int TPR = kBlock / BM;                 // threads per row
   constexpr int CPT = D / TPR;                     // channels per thread
   constexpr int64_t SLOT = (int64_t)BM * (D + 4);
-  const int BH = c.B * c.H;
+  const int BH = c.B * HQ;
   const int mi = blockIdx.x / BH, sh = blockIdx.x % BH;
   if (mi >= counts[sh * 4 + 3]) return;
   const int4 mg = merges[(int64_t)sh * MPH + mi];
   const int r = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * CPT;
   const int ri = mg.x + r;
   if (ri >= mg.y) return;
-  const int s = sh / c.H, h = sh % c.H;
+  const int s = sh / HQ, h = sh % HQ;
   const float* base = part + ((int64_t)sh * kSlotsPerHead + mg.z) * SLOT + (int64_t)r * (D + 4);
   const int nch = mg.w;
   float M = -INFINITY, den = 0.0f;
@@ -839,7 +834,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
   }
   const float inv = 1.0f / den;
   const int i = rows[(int64_t)sh * c.N + ri];
-  uint16_t* orow = out + (((int64_t)s * T + i) * c.H + h) * D + d0;
+  uint16_t* orow = out + (((int64_t)s * T + i) * HQ + h) * D + d0;
 #pragma unroll
   for (int x = 0; x < CPT; x += 4) {
     uint2 w;
@@ -863,7 +858,7 @@ tr_status launch_write_tiles(tr_kv_cache* c, int layer, int p0, const uint16_t* 
   const int tile0 = p0 / kWriteTile, ntile = (p0 + T + kWriteTile - 1) / kWriteTile - tile0;
   const int64_t blocks = (int64_t)L.B * L.H * ntile;
   if (blocks > (int64_t)1 << 30) return TR_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(k_prefill_write<D>, dim3(xcd_grid((int)blocks)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
+  hipLaunchKernelGGL(k_prefill_write<D>, dim3(tr_xcd_grid((int)blocks)), dim3(4 * D), 0, stream, L, layer, p0, T, tile0,
                      ntile, dense_from, c->np, kscale, k, v, bits, c->dk, c->dv, c->dkf);
   TR_LAUNCH_CHECK();
   return TR_OK;
@@ -874,7 +869,8 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
                            const uint16_t* v, const uint8_t* bits, const uint8_t* mode, int T, int window,
                            uint16_t* out, hipStream_t stream) {
   const CacheLayout& L = c->lay;
-  const int BH = L.B * L.H;
+  const int BH = L.B * L.H;              // (seq, KV head): dense staging
+  const int BQ = L.B * c->hq;            // (seq, query head): compaction, attention, merge
   const float kscale = (float)(1.4426950408889634 / sqrt((double)D));
   const int uph = tr_prefill_units_per_head(T);
   if (uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
@@ -891,8 +887,8 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   }
   {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
-    hipLaunchKernelGGL(k_prefill_prep<D>, dim3(BH + (fused ? L.B : 0)), dim3(TR_ASSIGN_THREADS), 0, stream, L, layer,
-                       p0, T, window, mode, bits, c->rows, c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out);
+    hipLaunchKernelGGL(k_prefill_prep<D>, dim3(BQ + (fused ? L.B : 0)), dim3(TR_ASSIGN_THREADS), 0, stream, L, layer,
+                       p0, T, window, mode, bits, c->rows, c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out, c->hq);
     TR_LAUNCH_CHECK();
   }
   if (fused) {
@@ -902,17 +898,17 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   }
   if (dense_to > 0) {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
-    hipLaunchKernelGGL(k_prefill_dense<D>, dim3(xcd_grid(BH * dense_to)), dim3(kBlock), 0, stream, L, layer, 0, dense_to, pend,
+    hipLaunchKernelGGL(k_prefill_dense<D>, dim3(tr_xcd_grid(BH * dense_to)), dim3(kBlock), 0, stream, L, layer, 0, dense_to, pend,
                        c->np, kscale, c->dk, c->dv, c->dkf);
     TR_LAUNCH_CHECK();
   }
   TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
-  hipLaunchKernelGGL((k_prefill_attn<D, TR_PREFILL_GROUPS>), dim3(BH * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
+  hipLaunchKernelGGL((k_prefill_attn<D, TR_PREFILL_GROUPS>), dim3(BQ * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
                      stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
-                     c->dkf, c->pf_part, out);
+                     c->dkf, c->pf_part, out, c->hq, c->grp);
   TR_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_prefill_merge<D>, dim3(BH * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
-                     c->row_counts, c->pf_merges, c->pf_part, out);
+  hipLaunchKernelGGL(k_prefill_merge<D>, dim3(BQ * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
+                     c->row_counts, c->pf_merges, c->pf_part, out, c->hq);
   TR_LAUNCH_CHECK();
   return TR_OK;
 }

@@ -24,7 +24,8 @@ def run_decode(tr, case, window, page_code_bytes=0, layers=1, layer=0, split_at=
     """Write positions 0..C-1, then the new token C (a second write), then decode at t = C."""
     k, v, bits, q, mode = case["k"], case["v"], case["bits"], case["q"], case["mode"]
     B, T, H, D = k.shape
-    cache = tr.tr_kv_cache_alloc(layers, B, H, D, T, page_code_bytes=page_code_bytes)
+    HQ = q.shape[1]
+    cache = tr.tr_kv_cache_alloc(layers, B, H, D, T, page_code_bytes=page_code_bytes, num_query_heads=HQ)
     C = T - 1
     cut = C if split_at is None else split_at
     if cut > 0:
@@ -32,7 +33,7 @@ def run_decode(tr, case, window, page_code_bytes=0, layers=1, layer=0, split_at=
                                 bits[:, :cut].contiguous())
     tr.tr_kv_quantize_write(cache, layer, k[:, cut:].contiguous(), v[:, cut:].contiguous(),
                             bits[:, cut:].contiguous())
-    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
     tr.tr_routed_attn_decode(cache, layer, q, mode, window, out)
     status = tr.tr_kv_cache_status(cache)
     cache.close()
@@ -146,3 +147,41 @@ def test_decode_bad_mode_is_flagged(tr):
     out, status = run_decode(tr, case, 3)
     assert status == 6
     assert torch.count_nonzero(out[0, 1].float()) == 0
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_grouped_query_heads(tr, G, D):
+    """Grouped-query attention: 8 query heads over 8 / G KV heads, query head h reading KV
+    head h // G (the oracle's mapping, pinned against SDPA's grouped-query mode)."""
+    say(f"decode GQA G={G} D={D}")
+    case = random_case(3, 700, 8, D, window=40, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.2, "local": 0.4, "full": 0.4}, seed=G * 13 + D,
+                       device="cuda", n_queries=1, kv_heads=8 // G)
+    case["q"], case["mode"] = case["q"][:, 0].contiguous(), case["mode"][:, 0].contiguous()
+    out, status = run_decode(tr, case, 40)
+    assert status == 0
+    check(case, out, 40, range(3), f"G={G} D={D}")
+
+
+def test_decode_grouped_query_heads_share_kv(tr):
+    """Query heads of one group given the same query and mode return the same row."""
+    case = random_case(2, 300, 8, 128, window=20, bit_weights={2: 0.4, 4: 0.3, 8: 0.2, 16: 0.1},
+                       mode_weights={"local": 0.5, "full": 0.5}, seed=77, device="cuda", n_queries=1, kv_heads=2)
+    q = case["q"][:, 0].contiguous()
+    mode = case["mode"][:, 0].contiguous()
+    q[:, 1:4] = q[:, 0:1]
+    mode[:, 1:4] = mode[:, 0:1]
+    case["q"], case["mode"] = q, mode
+    out, status = run_decode(tr, case, 20)
+    assert status == 0
+    for h in (1, 2, 3):
+        assert torch.equal(out[:, h], out[:, 0])
+    check(case, out, 20, range(2), "GQA shared rows")
+
+
+def test_alloc_rejects_bad_query_head_count(tr):
+    with pytest.raises(tr.TriRouteError):
+        tr.tr_kv_cache_alloc(1, 1, 3, 64, 16, num_query_heads=4)
+    with pytest.raises(tr.TriRouteError):
+        tr.tr_kv_cache_alloc(1, 1, 4, 64, 16, num_query_heads=2)

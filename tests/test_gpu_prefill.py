@@ -23,11 +23,12 @@ def run_prefill(tr, case, window, cuts=None, page_code_bytes=0, layers=1, layer=
     """Prefill positions 0..T-1 in one call, or in pieces split at `cuts` (chunked prefill)."""
     q, k, v, bits, mode = (case[x] for x in ("q", "k", "v", "bits", "mode"))
     B, T, H, D = k.shape
-    cache = tr.tr_kv_cache_alloc(layers, B, H, D, T, page_code_bytes=page_code_bytes)
-    out = torch.full((B, T, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    HQ = q.shape[2]
+    cache = tr.tr_kv_cache_alloc(layers, B, H, D, T, page_code_bytes=page_code_bytes, num_query_heads=HQ)
+    out = torch.full((B, T, HQ, D), float("nan"), dtype=torch.bfloat16, device="cuda")
     edges = [0] + (cuts or []) + [T]
     for a, b in zip(edges[:-1], edges[1:]):
-        piece = torch.empty((B, b - a, H, D), dtype=torch.bfloat16, device="cuda")
+        piece = torch.empty((B, b - a, HQ, D), dtype=torch.bfloat16, device="cuda")
         tr.tr_routed_attn_prefill(cache, layer, q[:, a:b].contiguous(), k[:, a:b].contiguous(),
                                   v[:, a:b].contiguous(), bits[:, a:b].contiguous(), mode[:, a:b].contiguous(),
                                   b - a, window, piece)
@@ -160,3 +161,24 @@ def test_prefill_bad_mode_is_flagged(tr):
     cache.close()
     assert status == 6
     assert torch.count_nonzero(out[0, 7, 1].float()) == 0
+
+
+@pytest.mark.parametrize("G", [2, 4])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_grouped_query_heads(tr, G, D):
+    """Grouped-query attention: 8 query heads over 8 / G KV heads (query head h reads KV head
+    h // G), in one call and in two chunks; cache contents bit-exact per KV head."""
+    say(f"prefill GQA G={G} D={D}")
+    case = random_case(2, 333, 8, D, window=25, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.2, "local": 0.4, "full": 0.4}, seed=G * 17 + D,
+                       device="cuda", kv_heads=8 // G)
+    cache, out, status = run_prefill(tr, case, 25)
+    assert status == 0
+    B, T, H, _ = case["k"].shape
+    check_codes(export_layer(tr, cache, 0, 0, T, B, H, D), case["k"], case["v"], case["bits"], where="GQA")
+    cache.close()
+    check(case, out, 25, range(2), f"G={G} D={D}")
+    cache, out2, status = run_prefill(tr, case, 25, cuts=[130])
+    cache.close()
+    assert status == 0
+    check(case, out2, 25, range(2), f"G={G} D={D} chunked")
