@@ -84,23 +84,28 @@ def row_bytes(b: np.ndarray, D: int) -> np.ndarray:
     return np.where(b == 16, 4 * D, 2 * D * b // 8 + 16)
 
 
-def decode_layer_bytes(bits: np.ndarray, mode: np.ndarray, C: int, w: int, D: int):
+def decode_layer_bytes(bits: np.ndarray, mode: np.ndarray, C: int, w: int, D: int, kv_heads: int = 0):
     """Algorithmic bytes of one decode layer: (split-kernel bytes, whole-layer bytes).
 
-    bits [B, C+1] (position C is the new token), mode [B, H]."""
+    bits [B, C+1] (position C is the new token), mode [B, H] over H query heads; kv_heads KV
+    heads (0 = H), query head h reading KV head h // (H / kv_heads).  A KV head's rows are
+    counted once over the union of the windows of the query heads that read it."""
     B, H = mode.shape
+    Hkv = kv_heads or H
+    G = H // Hkv
     rb = row_bytes(bits.astype(np.int64), D)               # [B, C+1]
     csum = np.concatenate([np.zeros((B, 1), np.int64), np.cumsum(rb, axis=1)], axis=1)
     attn = 0
     for s in range(B):
-        for h in range(H):
-            m = int(mode[s, h])
-            if m == 0:
+        for hk in range(Hkv):
+            ms = [int(m) for m in mode[s, hk * G:(hk + 1) * G]]
+            active = [m for m in ms if m in (1, 2)]
+            if not active:
                 continue
-            lo = 0 if m == 2 else max(0, C - w)
-            attn += int(csum[s, C + 1] - csum[s, lo]) + 2 * D    # keys + q
+            lo = 0 if 2 in active else max(0, C - w)
+            attn += int(csum[s, C + 1] - csum[s, lo]) + 2 * D * len(active)    # keys + q
     out = B * H * 2 * D
-    write = int((4 * D + rb[:, C]).sum()) * H
+    write = int((4 * D + rb[:, C]).sum()) * Hkv
     return attn, attn + out + write
 
 
@@ -212,9 +217,9 @@ def u16(t):
 
 # --------------------------------------------------------------------------------------------
 
-def bench_decode(tr, args):
-    cfg = CONFIGS[3]
+def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
     B, H, D, C, w, Lyr = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens, cfg.window, cfg.layers
+    Hkv = cfg.num_kv_heads
     dev = torch.device("cuda")
     log(f"[decode] generating {Lyr} layers of {cfg.name}")
     per_layer, samples = [], []
@@ -230,16 +235,16 @@ def bench_decode(tr, args):
         if cache is None:
             # pool sized from layer 0's realized width mix, with 25% headroom for the others
             pool_pages = int(pool_pages_needed([bits_np], ptok) * Lyr * 1.25) + 64
-            cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, C + 1, page_code_bytes=args.page_code_bytes,
-                                         pool_pages=pool_pages)
+            cache = tr.tr_kv_cache_alloc(Lyr, B, Hkv, D, C + 1, page_code_bytes=args.page_code_bytes,
+                                         pool_pages=pool_pages, num_query_heads=H)
         tr.tr_kv_quantize_write(cache, layer, case["k"][:, :C].contiguous(), case["v"][:, :C].contiguous(),
                                 case["bits"][:, :C].contiguous())
-        a, t = decode_layer_bytes(bits_np, mode_np, C, w, D)
+        a, t = decode_layer_bytes(bits_np, mode_np, C, w, D, Hkv)
         acc_attn.append(a)
         acc_total.append(t)
         per_layer.append({x: case[x][:, C:C + 1].contiguous() for x in ("k", "v", "bits")} |
                          {"q": case["q"].contiguous(), "mode": case["mode"].contiguous()})
-        if layer == 0 and not args.no_cpu_baseline:
+        if layer == 0 and baseline and not args.no_cpu_baseline:
             for s in sample_seqs:
                 samples.append((u16(case["q"][s]), u16(case["k"][s]), u16(case["v"][s]), bits_np[s],
                                 mode_np[s], C, w))
@@ -279,8 +284,9 @@ def bench_decode(tr, args):
     avg_split_ms = ms_split / max(1, n_split)
     bytes_per_launch = float(np.mean(acc_attn))
     achieved = bytes_per_launch / (avg_split_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "kernel": "k_decode", "traffic_unit": "bytes per launch", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_decode"),
+    kname = "k_decode" if Hkv == H else "k_decode_grp"
+    roof = {"bound": "hbm", "kernel": kname, "traffic_unit": "bytes per launch", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kname),
             "avg_launch_us": round(avg_split_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch),
             "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
 
@@ -291,7 +297,7 @@ def bench_decode(tr, args):
         wall, _ = run_pool(_oracle_decode_worker, samples, workers)
         s_bytes = 0
         for (q, k, v, bits, mode, C_, w_) in samples:
-            a, t = decode_layer_bytes(bits[None], mode[None], C_, w_, D)
+            a, t = decode_layer_bytes(bits[None], mode[None], C_, w_, D, Hkv)
             s_bytes += t
         cpu = {"value": round(s_bytes / wall / 1e9, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
                "sample": f"layer 0, sequences {sample_seqs[0]}..{sample_seqs[-1]} of {cfg.name}: quantize the "
@@ -301,14 +307,14 @@ def bench_decode(tr, args):
     return {"ms": ms, "gbs": gbs, "bytes": step_bytes, "roofline": roof, "cpu": cpu, "cfg": cfg}
 
 
-def bench_prefill(tr, args):
-    cfg = CONFIGS[2]
+def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True):
     B, H, D, T, w, Lyr = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens, cfg.window, cfg.layers
     dev = torch.device("cuda")
     log(f"[prefill] generating {Lyr} layers of {cfg.name}")
     cases = [layer_inputs(cfg, layer, seed=args.seed, device=dev) for layer in range(Lyr)]
     flops = [prefill_layer_flops(c["mode"].cpu().numpy(), w, D) for c in cases]
-    cache = tr.tr_kv_cache_alloc(Lyr, B, H, D, T, page_code_bytes=args.page_code_bytes)
+    cache = tr.tr_kv_cache_alloc(Lyr, B, cfg.num_kv_heads, D, T, page_code_bytes=args.page_code_bytes,
+                                 num_query_heads=H)
     outs = [torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(Lyr)]
 
     def step():
@@ -343,7 +349,7 @@ def bench_prefill(tr, args):
             "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": int(fl_per_launch),
             "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
     cpu = None
-    if not args.no_cpu_baseline:
+    if baseline and not args.no_cpu_baseline:
         c0 = cases[0]
         job = (u16(c0["q"][0]), u16(c0["k"][0]), u16(c0["v"][0]), c0["bits"][0].cpu().numpy(),
                c0["mode"][0].cpu().numpy(), w)
@@ -364,7 +370,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill"], default=None)
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query workloads")
     ap.add_argument("--page-code-bytes", type=int, default=0,
                     help="cache page size: K (and V) code bytes per head per page; 0 = the library default")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -384,6 +391,9 @@ def main():
 
     dec = bench_decode(tr, args) if args.only in (None, "decode") else None
     pre = bench_prefill(tr, args) if args.only in (None, "prefill") else None
+    gqa = args.only is None and not args.no_gqa
+    gdec = bench_decode(tr, args, CONFIGS[5], baseline=False) if gqa or args.only == "gqa_decode" else None
+    gpre = bench_prefill(tr, args, CONFIGS[6], baseline=False) if gqa or args.only == "gqa_prefill" else None
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
@@ -407,6 +417,24 @@ def main():
             line.update({"value": pobj["value"], "unit": "tokens/s", "ms_per_step": pobj["ms_per_step"],
                          "dtype": "bf16", "config": {"workload": cfg.name}, "roofline": pobj["roofline"],
                          "cpu_baseline": pobj["cpu_baseline"]})
+    # grouped-query workloads: same objects, no CPU baseline
+    extra = {}
+    if gdec:
+        extra["decode"] = {"workload": gdec["cfg"].name, "value": round(gdec["gbs"], 1), "unit": "GB/s",
+                           "ms_per_step": round(gdec["ms"], 4), "hbm_frac": round(gdec["gbs"] / HBM_PEAK_GBS, 4),
+                           "bytes_per_step": int(gdec["bytes"]), "roofline": gdec["roofline"]}
+    if gpre:
+        extra["prefill"] = {"workload": gpre["cfg"].name, "value": round(gpre["tok_s"], 1), "unit": "tokens/s",
+                            "ms_per_step": round(gpre["ms"], 4), "tflops": round(gpre["tflops"], 2),
+                            "roofline": gpre["roofline"]}
+    if extra:
+        if "value" in line:
+            line["gqa"] = extra
+        else:
+            o = extra.get("decode") or extra.get("prefill")
+            line.update({"value": o["value"], "unit": o["unit"], "ms_per_step": o["ms_per_step"],
+                         "dtype": "fp32" if "decode" in extra else "bf16", "config": {"workload": o["workload"]},
+                         "roofline": o["roofline"], "cpu_baseline": None})
     print(json.dumps(line), flush=True)
 
 

@@ -49,12 +49,23 @@ struct tr_kv_cache {
 // TR_DECODE_MIN_CHUNK positions unless those limits force it.
 #define TR_DECODE_ITEM_MAX 512
 #define TR_DECODE_PG_MAX 34
+#ifndef TR_DECODE_MIN_CHUNK
 #define TR_DECODE_MIN_CHUNK 256
+#endif
 
 // Largest decode chunk (positions) this layout allows.
 inline int tr_decode_max_chunk(const CacheLayout& L) {
   const int by_pages = (TR_DECODE_PG_MAX - 2) * L.ptok[3];
   return by_pages < TR_DECODE_ITEM_MAX ? by_pages : TR_DECODE_ITEM_MAX;
+}
+
+// Grouped-query decode items hold the scores of several query heads, so their chunks are
+// shorter (at most TR_DECODE_GRP_ITEM_MAX positions; not below TR_DECODE_MIN_CHUNK, so the
+// partial-result slots sized for the plain items suffice).
+#define TR_DECODE_GRP_ITEM_MAX 256
+inline int tr_decode_grp_max_chunk(const CacheLayout& L) {
+  const int by_pages = (TR_DECODE_PG_MAX - 2) * L.ptok[3];
+  return by_pages < TR_DECODE_GRP_ITEM_MAX ? by_pages : TR_DECODE_GRP_ITEM_MAX;
 }
 
 // Prefill: partial-result slots per (seq, head) for key-split row tiles, and the work units of a

@@ -164,6 +164,30 @@ def test_decode_grouped_query_heads(tr, G, D):
     check(case, out, 40, range(3), f"G={G} D={D}")
 
 
+def test_decode_grouped_mode_mixes(tr):
+    """Groups of 4 query heads with every kind of mode mix: a local head inside a group that
+    also has a full head only sees its window; an all-skip group writes zeros."""
+    B, C, H, Hkv, D, w = 1, 1500, 16, 4, 128, 100
+    case = random_case(B, C + 1, H, D, window=w, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"local": 1.0}, seed=41, device="cuda", n_queries=1, kv_heads=Hkv)
+    case["q"] = case["q"][:, 0].contiguous()
+    case["mode"] = torch.tensor([[2, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0, 0, 2, 2, 0, 2]], dtype=torch.uint8,
+                                device="cuda")
+    out, status = run_decode(tr, case, w)
+    assert status == 0
+    assert torch.count_nonzero(out[0, 8:12].float()) == 0
+    check(case, out, w, [0], "GQA mode mixes")
+
+
+def test_decode_config5_gqa_full_size_sampled(tr):
+    cfg = CONFIGS[5]
+    say(f"decode {cfg.name} full size, sampled sequences")
+    case = layer_inputs(cfg, 0, device="cuda")
+    out, status = run_decode(tr, case, cfg.window)
+    assert status == 0
+    check(case, out, cfg.window, [0, 17, 31], cfg.name)
+
+
 def test_decode_grouped_query_heads_share_kv(tr):
     """Query heads of one group given the same query and mode return the same row."""
     case = random_case(2, 300, 8, 128, window=20, bit_weights={2: 0.4, 4: 0.3, 8: 0.2, 16: 0.1},

@@ -182,3 +182,13 @@ def test_prefill_grouped_query_heads(tr, G, D):
     cache.close()
     assert status == 0
     check(case, out2, 25, range(2), f"G={G} D={D} chunked")
+
+
+def test_prefill_config6_gqa_layer_full_size(tr):
+    cfg = CONFIGS[6]
+    say(f"prefill {cfg.name}, one layer, all sequences")
+    case = layer_inputs(cfg, 3, device="cuda")
+    cache, out, status = run_prefill(tr, case, cfg.window)
+    cache.close()
+    assert status == 0
+    check(case, out, cfg.window, range(cfg.batch), cfg.name)

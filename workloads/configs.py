@@ -27,6 +27,11 @@ class WorkloadConfig:
     bit_weights: dict = field(default_factory=dict)    # {2: p, 4: p, 8: p, 16: p}
     mode_weights: dict = field(default_factory=dict)   # {"skip": p, "local": p, "full": p}
     clustered_bits: bool = False                       # b in runs of geometric(mean 16) length
+    kv_heads: int = 0                                  # KV heads (0 = heads; fewer: grouped-query)
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.kv_heads or self.heads
 
     @property
     def positions(self) -> int:
@@ -51,6 +56,14 @@ CONFIGS = {
                       {2: 0.6, 4: 0.3, 8: 0.08, 16: 0.02},
                       {"skip": 0.0, "local": 0.3, "full": 0.7},
                       clustered_bits=True),
+    # Grouped-query variants with the model table's KV-head counts (160M: 3 KV heads for 12
+    # query heads; 1.3B: 4 for 16), otherwise the shapes and mixes of workloads 2 and 3.
+    5: WorkloadConfig(5, "1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128", "decode", 24, 32, 16, 128, 8192, 512,
+                      {2: 0.3, 4: 0.4, 8: 0.2, 16: 0.1},
+                      {"skip": 0.2, "local": 0.4, "full": 0.4}, kv_heads=4),
+    6: WorkloadConfig(6, "160m-gqa-prefill-L12-B4-T2048-H12-KV3-D64", "prefill", 12, 4, 12, 64, 2048, 256,
+                      {2: 0.25, 4: 0.35, 8: 0.25, 16: 0.15},
+                      {"skip": 0.15, "local": 0.45, "full": 0.4}, kv_heads=3),
 }
 
 

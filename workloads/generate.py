@@ -91,18 +91,21 @@ def random_case(batch: int, tokens: int, heads: int, head_dim: int, *, window: i
 def layer_inputs(cfg: WorkloadConfig, layer: int, seed: int = 1234, device="cpu") -> dict:
     """Inputs of one layer of a workload.
 
-    prefill: q, k, v [B, T, H, D]; bits [B, T]; mode [B, T, H]; queries at positions 0..T-1.
-    decode:  k, v [B, C+1, H, D] (positions 0..C; the new token is position C); bits [B, C+1];
+    prefill: q [B, T, H, D]; k, v [B, T, Hkv, D]; bits [B, T]; mode [B, T, H]; queries at
+             positions 0..T-1.
+    decode:  k, v [B, C+1, Hkv, D] (positions 0..C; the new token is position C); bits [B, C+1];
              q [B, H, D] and mode [B, H] for the one query at position C.
+    (H = cfg.heads query heads, Hkv = cfg.num_kv_heads.)
     """
     if cfg.kind == "prefill":
         return random_case(cfg.batch, cfg.tokens, cfg.heads, cfg.head_dim, window=cfg.window,
                            bit_weights=cfg.bit_weights, mode_weights=cfg.mode_weights, seed=seed,
-                           device=device, clustered_bits=cfg.clustered_bits, layer=layer, cid=cfg.cid)
+                           device=device, clustered_bits=cfg.clustered_bits, layer=layer, cid=cfg.cid,
+                           kv_heads=cfg.num_kv_heads)
     case = random_case(cfg.batch, cfg.tokens + 1, cfg.heads, cfg.head_dim, window=cfg.window,
                        bit_weights=cfg.bit_weights, mode_weights=cfg.mode_weights, seed=seed,
                        device=device, clustered_bits=cfg.clustered_bits, n_queries=1,
-                       layer=layer, cid=cfg.cid)
+                       layer=layer, cid=cfg.cid, kv_heads=cfg.num_kv_heads)
     case["q"] = case["q"][:, 0]
     case["mode"] = case["mode"][:, 0]
     return case
