@@ -50,7 +50,9 @@ struct tr_kv_cache {
 #define TR_DECODE_ITEM_MAX 512
 #define TR_DECODE_PG_MAX 34
 #ifndef TR_DECODE_MIN_CHUNK
+#ifndef TR_DECODE_MIN_CHUNK
 #define TR_DECODE_MIN_CHUNK 256
+#endif
 #endif
 
 // Largest decode chunk (positions) this layout allows.
@@ -59,14 +61,6 @@ inline int tr_decode_max_chunk(const CacheLayout& L) {
   return by_pages < TR_DECODE_ITEM_MAX ? by_pages : TR_DECODE_ITEM_MAX;
 }
 
-// Grouped-query decode items hold the scores of several query heads, so their chunks are
-// shorter (at most TR_DECODE_GRP_ITEM_MAX positions; not below TR_DECODE_MIN_CHUNK, so the
-// partial-result slots sized for the plain items suffice).
-#define TR_DECODE_GRP_ITEM_MAX 256
-inline int tr_decode_grp_max_chunk(const CacheLayout& L) {
-  const int by_pages = (TR_DECODE_PG_MAX - 2) * L.ptok[3];
-  return by_pages < TR_DECODE_GRP_ITEM_MAX ? by_pages : TR_DECODE_GRP_ITEM_MAX;
-}
 
 // Prefill: partial-result slots per (seq, head) for key-split row tiles, and the work units of a
 // prefill of T tokens per (seq, head): one per 128-row tile (full and local rows fill separate

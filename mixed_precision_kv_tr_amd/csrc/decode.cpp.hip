@@ -28,7 +28,6 @@
 //            (o[D], m, l).  Skip heads: chunk 0 writes zeros.
 // k_decode_combine: log-sum-exp merge of multi-chunk windows -> bf16.
 #include <math.h>
-#include <stdlib.h>
 
 #include "common.h"
 
@@ -517,368 +516,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// Grouped-query decode: one wave per (seq, KV head, group of GW query heads, chunk).  The KV
-// rows of a chunk are fetched and unpacked once and dotted with all GW queries, so each KV byte
-// leaves HBM once per group.  The chunk range is the union of the group's windows ([0, t] if any
-// head is full, else [t - w, t]); a local head's scores below t - w are -inf.  Partial results
-// use the per-query-head slots of the plain items.
-template <int D, int GW>
-struct alignas(16) GrpSmem {
-  uint32_t q0[GW][D / 2];                  // class 0 operand pairs (16d + k, 16d + k + 8)
-  uint32_t q1[GW][D / 2];                  // class 1 operand pairs (8d + k, 8d + k + 4)
-  uint32_t q3[GW][D / 2];                  // class 3 operand pairs (2k, 2k + 1): the bf16 row
-  float qf[GW][D];                         // class 2 operands
-  float sc[GW][TR_DECODE_GRP_ITEM_MAX];    // scores, then weights
-  int32_t pg[TR_NCLASS][kPgMax];
-};
-
-// Phase 1, class C, slots [a, e): GW scores per key.  thr[i] = first slot query head i sees
-// (a for full heads, the slot of position t - w for local heads, e or more for inactive heads).
-template <int D, int C, int GW>
-__device__ __forceinline__ void score_phase_g(const CacheLayout& c, GrpSmem<D, GW>& sm, int first, int h, int a,
-                                              int e, int off, const float (&sig)[GW], const float (&sig0)[GW],
-                                              const int (&thr)[GW], float kscale) {
-  constexpr int b = 2 << C;
-  constexpr int SB = (C == 3) ? 32 : 16;
-  constexpr int E = SB * 8 / b;
-  constexpr int LPK = D * b / 8 / SB;
-  constexpr int KPW = kWave / LPK;
-  constexpr int NW = SB / 4;
-#ifndef TR_DECODE_GU1
-#define TR_DECODE_GU1 2
-#endif
-#ifndef TR_DECODE_GUK3
-#define TR_DECODE_GUK3 2
-#endif
-  constexpr int U = (C == 3) ? TR_DECODE_GUK3 : TR_DECODE_GU1;   // sub-iterations per batch
-  constexpr int NP = (C == 2) ? E : E / 2;     // q operands per head per lane
-  const int lane = threadIdx.x;
-  const int part = lane % LPK, kslot = lane / LPK;
-  const int* pg = sm.pg[C];
-  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1;
-  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + part * SB;
-  const int64_t side_off = c.sk_off[C] + (int64_t)h * c.ptok[C] * 8;
-  constexpr int RB = D * b / 8;
-  constexpr int STEP = KPW * U;
-  const uint32_t ob = opaque_v(0x43004300u);
-  const uint32_t m0 = opaque_s(C == 0 ? 0x00030003u : 0x000f000fu), m1 = opaque_s(0x000c000cu),
-                 m2 = opaque_s(0x00300030u);
-  Batch<U, NW, (C < 3)> cur, nxt;
-  load_batch<U, NW, (C < 3), LPK>(cur, c, pg, first, lp, pm, a, e, kslot, code_off, side_off, RB);
-  for (int base = a; base < e; base += STEP) {
-    if (base + STEP < e) load_batch<U, NW, (C < 3), LPK>(nxt, c, pg, first, lp, pm, base + STEP, e, kslot, code_off,
-                                                        side_off, RB);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // the key slice as dot operands, once for all heads (class 0: pairs 128 + c * 4^(k % 3))
-      uint32_t kw[(C == 2) ? 1 : NP];
-      float kf[(C == 2) ? E : 1];
-      if constexpr (C == 0) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t w = cur.w[u][d], w6 = w >> 6, w12 = w >> 12;
-          kw[8 * d + 0] = (w & m0) | ob;
-          kw[8 * d + 1] = (w & m1) | ob;
-          kw[8 * d + 2] = (w & m2) | ob;
-          kw[8 * d + 3] = (w6 & m0) | ob;
-          kw[8 * d + 4] = (w6 & m1) | ob;
-          kw[8 * d + 5] = (w6 & m2) | ob;
-          kw[8 * d + 6] = (w12 & m0) | ob;
-          kw[8 * d + 7] = (w12 & m1) | ob;
-        }
-      } else if constexpr (C == 1) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) kw[4 * d + k] = ((cur.w[u][d] >> (4 * k)) & m0) | ob;
-      } else if constexpr (C == 2) {
-        unpack_codes<8, NW>(cur.w[u], kf);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) kw[k] = cur.w[u][k];
-      }
-      float dot[GW];
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        float acc = 0.0f;
-        if constexpr (C == 2) {
-          const float4* qv = reinterpret_cast<const float4*>(&sm.qf[i][part * E]);
-#pragma unroll
-          for (int x = 0; x < E / 4; ++x) {
-            const float4 qq = qv[x];
-            acc = fmaf(qq.x, kf[4 * x], acc);
-            acc = fmaf(qq.y, kf[4 * x + 1], acc);
-            acc = fmaf(qq.z, kf[4 * x + 2], acc);
-            acc = fmaf(qq.w, kf[4 * x + 3], acc);
-          }
-        } else {
-          const uint32_t* qrow = (C == 0) ? sm.q0[i] : (C == 1) ? sm.q1[i] : sm.q3[i];
-          const uint4* qv = reinterpret_cast<const uint4*>(qrow + part * NP);
-#pragma unroll
-          for (int x = 0; x < NP / 4; ++x) {
-            const uint4 qq = qv[x];
-            acc = dot2(kw[4 * x], qq.x, acc);
-            acc = dot2(kw[4 * x + 1], qq.y, acc);
-            acc = dot2(kw[4 * x + 2], qq.z, acc);
-            acc = dot2(kw[4 * x + 3], qq.w, acc);
-          }
-        }
-        dot[i] = sum_adjacent<LPK>(acc);
-      }
-      const int j = base + u * KPW + kslot;
-      if (j < e && part == 0) {
-#pragma unroll
-        for (int i = 0; i < GW; ++i) {
-          float x;
-          if constexpr (C == 0) x = fmaf(cur.sz[u].x, dot[i], fmaf(-128.0f * cur.sz[u].x, sig0[i], cur.sz[u].y * sig[i]));
-          else if constexpr (C == 1) x = fmaf(cur.sz[u].x, dot[i], fmaf(-128.0f, cur.sz[u].x, cur.sz[u].y) * sig[i]);
-          else if constexpr (C == 2) x = fmaf(cur.sz[u].x, dot[i], cur.sz[u].y * sig[i]);
-          else x = dot[i];
-          sm.sc[i][off + (j - a)] = (j >= thr[i]) ? x * kscale : -INFINITY;
-        }
-      }
-    }
-    cur = nxt;
-  }
-}
-
-// Phase 2, class C: acc[i][16] (channels 16 * part ..) += p_i * v_hat.
-template <int D, int C, int GW>
-__device__ __forceinline__ void value_phase_g(const CacheLayout& c, GrpSmem<D, GW>& sm, int first, int h, int a,
-                                              int e, int off, float (&acc)[GW][16], float (&zacc)[GW]) {
-  constexpr int b = 2 << C;
-  constexpr int VLPK = D / 16;                     // lanes per key
-  constexpr int KPW = kWave / VLPK;
-  constexpr int NW = b / 2;                        // 16 codes of b bits
-#ifndef TR_DECODE_GV0
-#define TR_DECODE_GV0 4
-#endif
-#ifndef TR_DECODE_GV1
-#define TR_DECODE_GV1 2
-#endif
-  constexpr int U = (C == 0) ? TR_DECODE_GV0 : (C == 1) ? TR_DECODE_GV1 : 1;
-  constexpr int RB = D * b / 8;
-  constexpr int STEP = KPW * U;
-  const int lane = threadIdx.x;
-  const int part = lane % VLPK, kslot = lane / VLPK;
-  const int* pg = sm.pg[C];
-  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1;
-  const int64_t code_off = c.v_off[C] + (int64_t)h * c.cb + part * (2 * b);
-  const int64_t side_off = c.sv_off[C] + (int64_t)h * c.ptok[C] * 8;
-  Batch<U, NW, (C < 3)> cur, nxt;
-  load_batch<U, NW, (C < 3), VLPK>(cur, c, pg, first, lp, pm, a, e, kslot, code_off, side_off, RB);
-  for (int base = a; base < e; base += STEP) {
-    if (base + STEP < e) load_batch<U, NW, (C < 3), VLPK>(nxt, c, pg, first, lp, pm, base + STEP, e, kslot,
-                                                         code_off, side_off, RB);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int jr = base + u * KPW + kslot;
-      const int jc = off + (min(jr, e - 1) - a);
-      float p[GW];
-#pragma unroll
-      for (int i = 0; i < GW; ++i) p[i] = (jr < e) ? sm.sc[i][jc] : 0.0f;
-      if constexpr (C < 3) {
-        float cf[16];
-        if constexpr (C < 2) unpack_codes_scaled<b, NW>(cur.w[u], cf);
-        else unpack_codes<b, NW>(cur.w[u], cf);
-#pragma unroll
-        for (int i = 0; i < GW; ++i) {
-          const float ps = p[i] * cur.sz[u].x;
-          if (part == 0) zacc[i] = fmaf(p[i], cur.sz[u].y, zacc[i]);
-#pragma unroll
-          for (int k = 0; k < 16; ++k) acc[i][k] = fmaf(C < 2 ? ps * unpack_scale<b>(k) : ps, cf[k], acc[i][k]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float lo = tr_bf16_lo(cur.w[u][k]), hi = tr_bf16_hi(cur.w[u][k]);
-#pragma unroll
-          for (int i = 0; i < GW; ++i) {
-            acc[i][2 * k] = fmaf(p[i], lo, acc[i][2 * k]);
-            acc[i][2 * k + 1] = fmaf(p[i], hi, acc[i][2 * k + 1]);
-          }
-        }
-      }
-    }
-    cur = nxt;
-  }
-}
-
-#ifndef TR_DECODE_GRP_WAVES
-#define TR_DECODE_GRP_WAVES 4
-#endif
-template <int D, int GW>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_GRP_WAVES, 8))) void k_decode_grp(
-    CacheLayout c, int layer, int t, int window, int CH, int nch_grid, int max_chunks, float kscale,
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ mode, float* __restrict__ part,
-    uint16_t* __restrict__ out, int HQ, int G) {
-  __shared__ GrpSmem<D, GW> sm;
-  const int lane = threadIdx.x;
-  const int k = blockIdx.x % nch_grid;
-  const int it = blockIdx.x / nch_grid;             // (seq, KV head, group)
-  const int ngrp = G / GW;
-  const int s = it / (c.H * ngrp), h = (it / ngrp) % c.H, sub = it % ngrp;
-  const int64_t sh0 = (int64_t)s * HQ + h * G + sub * GW;   // first (seq, query head) of the group
-  int mm[GW];
-  bool anyf = false, anyl = false;
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    mm[i] = mode[sh0 + i];
-    anyf |= mm[i] == TR_MODE_FULL;
-    anyl |= mm[i] == TR_MODE_LOCAL;
-  }
-  if (k == 0) {
-#pragma unroll
-    for (int i = 0; i < GW; ++i) {
-      if (mm[i] != TR_MODE_LOCAL && mm[i] != TR_MODE_FULL) {
-        uint16_t* o = out + (sh0 + i) * D;
-        for (int d = lane; d < D; d += kWave) o[d] = 0;
-        if (lane == 0 && mm[i] != TR_MODE_SKIP) atomicOr(c.err, TR_ERRF_BAD_MODE);
-      }
-    }
-  }
-  if (!anyf && !anyl) return;
-  const int lol = max(0, t - window);              // first position of the local heads
-  const int lo = anyf ? 0 : lol;
-  const int L = t + 1 - lo;
-  const int nch = (L + CH - 1) / CH;
-  if (k >= nch) return;
-  const int per = (L + nch - 1) / nch;
-  const int p0 = lo + k * per, p1 = min(p0 + per, t + 1);
-
-  const int32_t* pa = tr_prefix_row(c, layer, s, p0);
-  const int32_t* pe = tr_prefix_row(c, layer, s, p1);
-  const int32_t* pl = tr_prefix_row(c, layer, s, min(max(lol, p0), p1));
-  int a[4], e[4], off[4], first[4], al[4];
-  int nk = 0;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    a[x] = pa[x];
-    e[x] = pe[x];
-    al[x] = pl[x];
-    off[x] = nk;
-    nk += e[x] - a[x];
-    first[x] = a[x] >> c.ptok_log2[x];
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    if (e[x] > a[x]) {
-      const int np = ((e[x] - 1) >> c.ptok_log2[x]) - first[x] + 1;
-      const int32_t* pt = tr_ptab(c, layer, s, x) + first[x];
-      for (int i = lane; i < np; i += kWave) sm.pg[x][i] = pt[i];
-    }
-  }
-  // q of the group: fp32, and bf16 pairs in each class's operand order
-  float sig[GW], sig0[GW];
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    const uint16_t* qr = q + (sh0 + i) * D;
-    float qpart = 0.0f, qpart0 = 0.0f;
-#pragma unroll
-    for (int d = lane; d < D; d += kWave) {
-      const float v = tr_bf16_lo((uint32_t)qr[d]);
-      sm.qf[i][d] = v;
-      qpart += v;
-      qpart0 += v * q_scale_k2(d & 7);
-    }
-    sig[i] = wave_sum(qpart);
-    sig0[i] = wave_sum(qpart0);
-#pragma unroll
-    for (int n = lane; n < D / 2; n += kWave) {
-      const int g16 = n >> 3, k16 = n & 7;           // class 0: word n = (16 g + k, 16 g + k + 8)
-      const int g8 = n >> 2, k8 = n & 3;             // class 1: word n = (8 g + k, 8 g + k + 4)
-      const float sk = q_scale_k2(k16);
-      sm.q0[i][n] = bf16_bits(tr_bf16_lo(qr[16 * g16 + k16]) * sk) |
-                    (bf16_bits(tr_bf16_lo(qr[16 * g16 + k16 + 8]) * sk) << 16);
-      sm.q1[i][n] = (uint32_t)qr[8 * g8 + k8] | ((uint32_t)qr[8 * g8 + k8 + 4] << 16);
-      sm.q3[i][n] = (uint32_t)qr[2 * n] | ((uint32_t)qr[2 * n + 1] << 16);
-    }
-  }
-  __syncthreads();
-
-#define TR_GRP_THR(X)                                                                         \
-  int thr##X[GW];                                                                             \
-  _Pragma("unroll") for (int i = 0; i < GW; ++i) thr##X[i] =                                  \
-      mm[i] == TR_MODE_FULL ? a[X] : mm[i] == TR_MODE_LOCAL ? al[X] : 0x7fffffff;
-  TR_GRP_THR(0)
-  TR_GRP_THR(1)
-  TR_GRP_THR(2)
-  TR_GRP_THR(3)
-#undef TR_GRP_THR
-  if (e[0] > a[0]) score_phase_g<D, 0, GW>(c, sm, first[0], h, a[0], e[0], off[0], sig, sig0, thr0, kscale);
-  if (e[1] > a[1]) score_phase_g<D, 1, GW>(c, sm, first[1], h, a[1], e[1], off[1], sig, sig0, thr1, kscale);
-  if (e[2] > a[2]) score_phase_g<D, 2, GW>(c, sm, first[2], h, a[2], e[2], off[2], sig, sig0, thr2, kscale);
-  if (e[3] > a[3]) score_phase_g<D, 3, GW>(c, sm, first[3], h, a[3], e[3], off[3], sig, sig0, thr3, kscale);
-  __syncthreads();
-
-  // softmax per head; a head with no key in this chunk gets weights 0, max -inf and sum 0
-  float mx[GW], lsum[GW];
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    float m = -INFINITY;
-    for (int x = lane; x < nk; x += kWave) m = fmaxf(m, sm.sc[i][x]);
-    m = wave_max(m);
-    float l = 0.0f;
-    for (int x = lane; x < nk; x += kWave) {
-      const float p = (m == -INFINITY) ? 0.0f : exp2f(sm.sc[i][x] - m);
-      sm.sc[i][x] = p;
-      l += p;
-    }
-    mx[i] = m;
-    lsum[i] = wave_sum(l);
-  }
-  __syncthreads();
-
-  float acc[GW][16], zacc[GW];
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    zacc[i] = 0.0f;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) acc[i][x] = 0.0f;
-  }
-  if (e[0] > a[0]) value_phase_g<D, 0, GW>(c, sm, first[0], h, a[0], e[0], off[0], acc, zacc);
-  if (e[1] > a[1]) value_phase_g<D, 1, GW>(c, sm, first[1], h, a[1], e[1], off[1], acc, zacc);
-  if (e[2] > a[2]) value_phase_g<D, 2, GW>(c, sm, first[2], h, a[2], e[2], off[2], acc, zacc);
-  if (e[3] > a[3]) value_phase_g<D, 3, GW>(c, sm, first[3], h, a[3], e[3], off[3], acc, zacc);
-
-  // Sum over the key slots; lane p < VLPK then holds channels [16 p, 16 p + 16).
-  constexpr int VLPK = D / 16;
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
-#pragma unroll
-    for (int x = 0; x < 16; ++x) acc[i][x] = sum_strided<VLPK>(acc[i][x]);
-    zacc[i] = wave_sum(zacc[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    if (mm[i] != TR_MODE_LOCAL && mm[i] != TR_MODE_FULL) continue;
-    if (nch == 1) {
-      if (lane < VLPK) {
-        const float inv = 1.0f / lsum[i];
-        uint32_t pk[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-          pk[x] = (uint32_t)tr_f32_to_bf16((acc[i][2 * x] + zacc[i]) * inv) |
-                  ((uint32_t)tr_f32_to_bf16((acc[i][2 * x + 1] + zacc[i]) * inv) << 16);
-        uint4* dst = reinterpret_cast<uint4*>(out + (sh0 + i) * D + 16 * lane);
-        dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-      }
-    } else {
-      float* dst = part + ((sh0 + i) * max_chunks + k) * (D + 2);
-      if (lane < VLPK) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) dst[16 * lane + x] = acc[i][x] + zacc[i];
-      }
-      if (lane == 0) {
-        dst[D] = mx[i];
-        dst[D + 1] = lsum[i];
-      }
-    }
-  }
-}
-
 // Log-sum-exp merge of the chunks of windows that span more than one chunk: one workgroup per
 // (seq, head), thread d = channel d.  Chunks go in batches of 32: every load of a batch -- the
 // channel's 32 partial values and, in lane k of each wave, chunk k's (max, sum) -- is issued at
@@ -887,18 +524,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
 template <int D>
 __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH, int max_chunks,
                                                       const uint8_t* __restrict__ mode,
-                                                      const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                      int HQ, int GW) {
+                                                      const float* __restrict__ part, uint16_t* __restrict__ out) {
   constexpr int KB = 32;
   const int sh = blockIdx.x;
   const int d = threadIdx.x, lane = d & 63;
   const int m = mode[sh];
   if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) return;
-  // chunks cover the window union of the head's item group (GW query heads; 1 for plain items)
-  const int g0 = sh - (sh % HQ) % GW;
-  bool anyf = false;
-  for (int i = 0; i < GW; ++i) anyf |= mode[g0 + i] == TR_MODE_FULL;
-  const int lo = anyf ? 0 : max(0, t - window);
+  const int lo = (m == TR_MODE_FULL) ? 0 : max(0, t - window);
   const int L = t + 1 - lo;
   const int nch = (L + CH - 1) / CH;
   if (nch == 1) return;                            // written by k_decode
@@ -915,7 +547,7 @@ __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH,
     const float lk = pk[D + 1];
     const float Mn = fmaxf(M, wave_max(mk));
     const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
-    const float wk = (own && mk != -INFINITY) ? exp2f(mk - Mn) : 0.0f;   // -inf: no key of this head
+    const float wk = own ? exp2f(mk - Mn) : 0.0f;
     den = den * a + wave_sum(wk * lk);
     float nb = 0.0f;
 #pragma unroll
@@ -935,18 +567,10 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
   const int t = c->len[layer] - 1;
   const int n = t + 1;
   const int BH = L.B * c->hq;                       // (seq, query head) pairs
-  // Query heads per item: a group of GW heads sharing one KV head (grouped-query attention),
-  // or one head per item.
-#ifndef TR_DECODE_GW_MAX
-#define TR_DECODE_GW_MAX 1
-#endif
-  const int GW = (c->grp % 4 == 0 && TR_DECODE_GW_MAX >= 4) ? 4 : (c->grp % 2 == 0 && TR_DECODE_GW_MAX >= 2) ? 2 : 1;
-  const int groups = GW > 1 ? L.B * L.H * (c->grp / GW) : BH;
-  const int max_ch = GW > 1 ? tr_decode_grp_max_chunk(L) : tr_decode_max_chunk(L);
+  const int max_ch = tr_decode_max_chunk(L);
   // About 8192 work items if every head were full (a few times the waves the chip holds at
   // once), but no chunk below kMinChunk positions.
-  int nch = (8192 + groups - 1) / groups;
-  if (const char* env = getenv("TR_DECODE_NCH")) nch = atoi(env);
+  int nch = (8192 + BH - 1) / BH;
   if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
   if (nch < (n + max_ch - 1) / max_ch) nch = (n + max_ch - 1) / max_ch;
   if (nch > c->max_chunks) nch = c->max_chunks;
@@ -954,30 +578,25 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
   const int CH = (n + nch - 1) / nch;
   if (CH > max_ch) return TR_ERR_UNSUPPORTED;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
-  const int grid = groups * nch;
+  const int grid = BH * nch;
   {
     TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
-#define TR_DEC_ARGS L, layer, t, window, CH, nch, c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp
-    if (L.D == 64) {
-      if (GW == 4) hipLaunchKernelGGL((k_decode_grp<64, 4>), dim3(grid), dim3(kWave), 0, stream, TR_DEC_ARGS);
-      else if (GW == 2) hipLaunchKernelGGL((k_decode_grp<64, 2>), dim3(grid), dim3(kWave), 0, stream, TR_DEC_ARGS);
-      else hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, TR_DEC_ARGS);
-    } else {
-      if (GW == 4) hipLaunchKernelGGL((k_decode_grp<128, 4>), dim3(grid), dim3(kWave), 0, stream, TR_DEC_ARGS);
-      else if (GW == 2) hipLaunchKernelGGL((k_decode_grp<128, 2>), dim3(grid), dim3(kWave), 0, stream, TR_DEC_ARGS);
-      else hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, TR_DEC_ARGS);
-    }
-#undef TR_DEC_ARGS
+    if (L.D == 64)
+      hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
+                         c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp);
+    else
+      hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
+                         c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp);
     TR_LAUNCH_CHECK();
   }
   if (nch > 1) {
     TrProfScope prof(c, TR_PROF_DECODE_COMBINE, stream);
     if (L.D == 64)
       hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, c->max_chunks, mode,
-                         c->partials, out, c->hq, GW);
+                         c->partials, out);
     else
       hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, t, window, CH, c->max_chunks, mode,
-                         c->partials, out, c->hq, GW);
+                         c->partials, out);
     TR_LAUNCH_CHECK();
   }
   return TR_OK;
