@@ -11,10 +11,15 @@ Second object (``prefill``): routed prefill on the 160M-shaped workload -- 12 la
 sequences x T = 2048 x 12 heads x head_dim 64, w = 256; one step = the 12 layer calls
 (quantize-write of the prompt, then causal routed attention), tokens/s = 4 * 2048 / step time.
 
+Third object (``gqa``): the same two measurements on grouped-query variants of the two
+workloads (decode: 16 query heads over 4 KV heads; prefill: 12 over 3), without a CPU baseline.
+
 Accounting (algorithmic, from the realized seeded draws):
-  decode bytes  = per attended (key, head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
-                  4*D for b = 16; plus per non-skip (seq, head) 2*D (q); per (seq, head) 2*D
-                  (out); plus the new token's write: 4*D read + its stored bytes.
+  decode bytes  = per attended (key, KV head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
+                  4*D for b = 16, counted once over the union of the windows of the query heads
+                  that read the KV head; plus per non-skip (seq, query head) 2*D (q); per (seq,
+                  query head) 2*D (out); plus the new token's write: 4*D read + its stored bytes
+                  per KV head.
   prefill flops = 4*D per attended (query, key, head) pair.
 
 Timing: warmup steps, then K steps between HIP events on the launch stream (torch's current
@@ -50,23 +55,23 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # reports traffic as null.
 TRAFFIC = {
     "k_decode": {
-        "fetch_kib": 167631.2, "write_kib": 2114.2, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 167571.0, "write_kib": 2114.2, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip":
-                "7374d4773a2208d0b61e9410eee6b2fb28bb53d44a08ef08b2125bcfc975ddca",
+                "d61fb6b9a8536951583f825b6160ac7bfcf98292881966a81d8f15cb44a56359",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "d6ab9c658c2eb38ea59724ae7ebc6902d4db48a8e58059395e49b0cd3d87c94b",
+                "276fdf41f0e7fbd044afbbc21b91fc101043b25abc3474558bdf68e322b00a3e",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
                 "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
     "k_prefill_attn": {
-        "fetch_kib": 19238.9, "write_kib": 19046.0, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 19191.4, "write_kib": 20850.9, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip":
-                "ad9164a04896822155eaaa88db7f84d1a4efc995245eef7c763820a40b42d52d",
+                "5191c5bfc83dd713f47715b644320defab98346d098ba80fdd28221365631d14",
             "mixed_precision_kv_tr_amd/csrc/kv_write.h":
                 "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "d6ab9c658c2eb38ea59724ae7ebc6902d4db48a8e58059395e49b0cd3d87c94b",
+                "276fdf41f0e7fbd044afbbc21b91fc101043b25abc3474558bdf68e322b00a3e",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
                 "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
 }
@@ -284,7 +289,7 @@ def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
     avg_split_ms = ms_split / max(1, n_split)
     bytes_per_launch = float(np.mean(acc_attn))
     achieved = bytes_per_launch / (avg_split_ms * 1e-3) / 1e9
-    kname = "k_decode" if Hkv == H else "k_decode_grp"
+    kname = "k_decode"
     roof = {"bound": "hbm", "kernel": kname, "traffic_unit": "bytes per launch", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kname),
             "avg_launch_us": round(avg_split_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch),

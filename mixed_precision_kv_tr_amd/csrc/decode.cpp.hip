@@ -255,7 +255,7 @@ __device__ __forceinline__ void score_phase(const CacheLayout& c, const int32_t*
   constexpr int KPW = kWave / LPK;                 // keys per wave sub-iteration
   constexpr int NW = SB / 4;
 #ifndef TR_DECODE_U1
-#define TR_DECODE_U1 4
+#define TR_DECODE_U1 2
 #endif
 #ifndef TR_DECODE_UK3
 #define TR_DECODE_UK3 4                            // bf16 keys: 4 x 8 keys (8 KB) per batch
@@ -300,6 +300,7 @@ __device__ __forceinline__ void score_phase(const CacheLayout& c, const int32_t*
                                                         side_off, RB);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (base + u * KPW >= e) break;              // past the class's last key: nothing to compute
       float dot = 0.0f;
       if constexpr (C == 0) {
 #pragma unroll
@@ -365,6 +366,7 @@ __device__ __forceinline__ void value_phase(const CacheLayout& c, const int32_t*
                                                          code_off, side_off, RB);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (base + u * KPW >= e) break;              // past the class's last key
       const int jr = base + u * KPW + kslot;
       const float p = (jr < e) ? pw[off + (min(jr, e - 1) - a)] : 0.0f;
       if constexpr (C < 2) {
