@@ -14,6 +14,12 @@ sequences x T = 2048 x 12 heads x head_dim 64, w = 256; one step = the 12 layer 
 Third object (``gqa``): the same two measurements on grouped-query variants of the two
 workloads (decode: 16 query heads over 4 KV heads; prefill: 12 over 3), without a CPU baseline.
 
+Fourth object (``baselines``): the pages' comparison points run through the same kernels on the
+same shapes -- dense (every token bf16, every head full), KV quantization only at one width for
+every token (b = 4, b = 2; every head full), routing only (bf16 cache, routed modes) and TriRoute
+-- for decode (4 layers of the 1.3B-shaped decode) and prefill (the 160M-shaped prefill), each
+with its time per layer and its speedup over dense.
+
 Accounting (algorithmic, from the realized seeded draws):
   decode bytes  = per attended (key, KV head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
                   4*D for b = 16, counted once over the union of the windows of the query heads
@@ -367,6 +373,43 @@ def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True):
     return {"ms": ms, "tok_s": tok_s, "tflops": tflops, "roofline": roof, "cpu": cpu, "cfg": cfg}
 
 
+# The pages' baselines as configurations of the same kernels: dense (every token stored as
+# bf16, every head attending fully), KV-quantization only (one width for every token, every
+# head full: KIVI-style), routing only (bf16 cache, routed modes) and TriRoute (both).  Same
+# shapes, windows and seeded q/k/v as the workload; only the width and mode draws change.
+BASELINE_VARIANTS = (
+    ("dense_bf16", {16: 1.0}, {"full": 1.0}),
+    ("kv_quant_uniform_b4", {4: 1.0}, {"full": 1.0}),
+    ("kv_quant_uniform_b2", {2: 1.0}, {"full": 1.0}),
+    ("routing_only_bf16", {16: 1.0}, None),
+    ("triroute", None, None),
+)
+
+
+def bench_baselines(tr, args):
+    """Decode (4 layers of the 1.3B-shaped decode) and prefill (the 160M-shaped prefill) per variant."""
+    from dataclasses import replace
+    res = {}
+    for kind, base, layers in (("decode", CONFIGS[3], args.baseline_layers), ("prefill", CONFIGS[2], None)):
+        out = {}
+        for name, bw, mw in BASELINE_VARIANTS:
+            cfg = replace(base, layers=layers or base.layers, bit_weights=bw or base.bit_weights,
+                          mode_weights=mw or base.mode_weights)
+            if kind == "decode":
+                r = bench_decode(tr, args, cfg, baseline=False)
+                out[name] = {"ms_per_layer": round(r["ms"] / cfg.layers, 5), "bytes_per_layer": int(r["bytes"] / cfg.layers),
+                             "gbs": round(r["gbs"], 1), "kernel_us": r["roofline"]["avg_launch_us"]}
+            else:
+                r = bench_prefill(tr, args, cfg, baseline=False)
+                out[name] = {"ms_per_layer": round(r["ms"] / cfg.layers, 5), "tok_s": round(r["tok_s"], 1),
+                             "tflops": round(r["tflops"], 2), "kernel_us": r["roofline"]["avg_launch_us"]}
+        d = out["dense_bf16"]["ms_per_layer"]
+        for v in out.values():
+            v["speedup_vs_dense"] = round(d / v["ms_per_layer"], 3)
+        res[kind] = {"shape": (f"{base.name} shape, {layers or base.layers} layers"), "variants": out}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,8 +418,10 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill", "baselines"], default=None)
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query workloads")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the dense / uniform-width / routing-only runs")
+    ap.add_argument("--baseline-layers", type=int, default=4, help="decode layers per baseline variant")
     ap.add_argument("--page-code-bytes", type=int, default=0,
                     help="cache page size: K (and V) code bytes per head per page; 0 = the library default")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -399,6 +444,8 @@ def main():
     gqa = args.only is None and not args.no_gqa
     gdec = bench_decode(tr, args, CONFIGS[5], baseline=False) if gqa or args.only == "gqa_decode" else None
     gpre = bench_prefill(tr, args, CONFIGS[6], baseline=False) if gqa or args.only == "gqa_prefill" else None
+    base = (bench_baselines(tr, args) if (args.only is None and not args.no_baselines) or args.only == "baselines"
+            else None)
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
@@ -432,6 +479,12 @@ def main():
         extra["prefill"] = {"workload": gpre["cfg"].name, "value": round(gpre["tok_s"], 1), "unit": "tokens/s",
                             "ms_per_step": round(gpre["ms"], 4), "tflops": round(gpre["tflops"], 2),
                             "roofline": gpre["roofline"]}
+    if base:
+        if "value" in line:
+            line["baselines"] = base
+        else:
+            line.update({"value": base["decode"]["variants"]["triroute"]["speedup_vs_dense"], "unit": "x vs dense",
+                         "config": {"workload": base["decode"]["shape"]}, "baselines": base})
     if extra:
         if "value" in line:
             line["gqa"] = extra

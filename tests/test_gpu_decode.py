@@ -209,3 +209,19 @@ def test_alloc_rejects_bad_query_head_count(tr):
         tr.tr_kv_cache_alloc(1, 1, 3, 64, 16, num_query_heads=4)
     with pytest.raises(tr.TriRouteError):
         tr.tr_kv_cache_alloc(1, 1, 4, 64, 16, num_query_heads=2)
+
+
+@pytest.mark.parametrize("variant", ["dense_bf16", "uniform_b4", "uniform_b2", "routing_only_bf16"])
+def test_decode_baseline_variants(tr, variant):
+    """The comparison configurations the benchmark runs (dense bf16 cache with every head full,
+    one width for every token, bf16 with routed modes) against the oracle."""
+    bw, mw = {"dense_bf16": ({16: 1.0}, {"full": 1.0}), "uniform_b4": ({4: 1.0}, {"full": 1.0}),
+              "uniform_b2": ({2: 1.0}, {"full": 1.0}),
+              "routing_only_bf16": ({16: 1.0}, {"skip": 0.2, "local": 0.4, "full": 0.4})}[variant]
+    say(f"decode baseline variant {variant}")
+    case = random_case(4, 1201, 8, 128, window=100, bit_weights=bw, mode_weights=mw, seed=len(variant),
+                       device="cuda", n_queries=1)
+    case["q"], case["mode"] = case["q"][:, 0].contiguous(), case["mode"][:, 0].contiguous()
+    out, status = run_decode(tr, case, 100)
+    assert status == 0
+    check(case, out, 100, range(4), variant)

@@ -192,3 +192,18 @@ def test_prefill_config6_gqa_layer_full_size(tr):
     cache.close()
     assert status == 0
     check(case, out, cfg.window, range(cfg.batch), cfg.name)
+
+
+@pytest.mark.parametrize("variant", ["dense_bf16", "uniform_b4", "uniform_b2", "routing_only_bf16"])
+def test_prefill_baseline_variants(tr, variant):
+    """The comparison configurations the benchmark runs, against the oracle."""
+    bw, mw = {"dense_bf16": ({16: 1.0}, {"full": 1.0}), "uniform_b4": ({4: 1.0}, {"full": 1.0}),
+              "uniform_b2": ({2: 1.0}, {"full": 1.0}),
+              "routing_only_bf16": ({16: 1.0}, {"skip": 0.15, "local": 0.45, "full": 0.4})}[variant]
+    say(f"prefill baseline variant {variant}")
+    case = random_case(2, 450, 4, 64, window=60, bit_weights=bw, mode_weights=mw, seed=len(variant) + 1,
+                       device="cuda")
+    cache, out, status = run_prefill(tr, case, 60)
+    cache.close()
+    assert status == 0
+    check(case, out, 60, range(2), variant)
