@@ -18,6 +18,8 @@ xllm-io.github.io, section "core formulas"):
 * ``attend_cached`` -- the inference step that combines them (the paragraph after
   Algorithm 1 on the same page: each token's K/V is stored at its chosen width, and later
   queries attend to what was stored).
+* ``controller_route`` -- Eq. (5) with Eq. (11)'s whitening and the hard argmax of inference:
+  the routing decisions (a mode per head, a width per token) from a token's residual state.
 
 Readings where the pages leave a step open (all in fp32 for the quantizer, fp64 for attention):
 the quantization group is one head's D-vector of one token, separately for K and V; "round"
@@ -35,6 +37,7 @@ for either equation, so no function is pinned to a value the pages print.
 from .quantize import BITS_ALLOWED, bf16_bits_to_f32, dequantize, quantize
 from .attention import MODE_FULL, MODE_LOCAL, MODE_SKIP, routed_attention
 from .reference import attend_cached
+from .controller import BIT_CHOICES, controller_logits, controller_route
 
 __all__ = [
     "BITS_ALLOWED",
@@ -45,5 +48,8 @@ __all__ = [
     "quantize",
     "dequantize",
     "routed_attention",
+    "BIT_CHOICES",
+    "controller_logits",
+    "controller_route",
     "attend_cached",
 ]

@@ -13,7 +13,8 @@ import torch
 from .configs import WorkloadConfig
 
 MODE_CODES = {"skip": 0, "local": 1, "full": 2}
-_STREAMS = {"q": 0, "k": 1, "v": 2, "kscale": 3, "bits": 4, "mode": 5, "runs": 6}
+_STREAMS = {"q": 0, "k": 1, "v": 2, "kscale": 3, "bits": 4, "mode": 5, "runs": 6,
+            "ctl_x": 7, "ctl_side": 8, "ctl_w": 9}
 
 
 def _gen(device, seed: int, cid: int, layer: int, stream: str) -> torch.Generator:
@@ -109,3 +110,38 @@ def layer_inputs(cfg: WorkloadConfig, layer: int, seed: int = 1234, device="cpu"
     case["q"] = case["q"][:, 0]
     case["mode"] = case["mode"][:, 0]
     return case
+
+
+def controller_case(tokens: int, d: int, heads: int, *, d_side: int = 8, d_r: int = 128, seed: int = 0,
+                    device="cpu", layer: int = 0, cid: int = 99) -> dict:
+    """Inputs of the routing controller for one layer: residual states x (bf16 [tokens, d], N(0, 1)
+    with a few channels scaled up 8x, as residual streams carry outlier channels), side features
+    (float32 [tokens, d_side], N(0, 1)) and random weights at the usual 1/sqrt(fan_in) scale:
+
+        w1 bf16 [d_r][d], w1_side [d_r][d_side], b1, w2 [d_r][d_r] (in x out), b2,
+        mu_a, sigma_a, mu_b, sigma_b [d_r], w_a [d_r][3 heads] (in x out), w_b [d_r][4].
+
+    The head weights get a 3x gain so that the decisions are not near-uniform ties.  No trained
+    weights exist for the pages' controller; these only give the kernel realistic shapes."""
+    dev = torch.device(device)
+    gx = _gen(dev, seed, cid, layer, "ctl_x")
+    x = torch.randn((tokens, d), generator=gx, device=dev, dtype=torch.float32)
+    x[:, : max(1, d // 64)] *= 8.0
+    side = torch.randn((tokens, d_side), generator=_gen(dev, seed, cid, layer, "ctl_side"), device=dev,
+                       dtype=torch.float32)
+    gw = _gen(dev, seed, cid, layer, "ctl_w")
+    rn = lambda *shape: torch.randn(shape, generator=gw, device=dev, dtype=torch.float32)
+    w = {
+        "w1": (rn(d_r, d) / d ** 0.5).to(torch.bfloat16),
+        "w1_side": rn(d_r, d_side) / max(1, d_side) ** 0.5,
+        "b1": 0.1 * rn(d_r),
+        "w2": rn(d_r, d_r) / d_r ** 0.5,
+        "b2": 0.1 * rn(d_r),
+        "mu_a": 0.1 * rn(d_r),
+        "sigma_a": 0.5 + torch.rand((d_r,), generator=gw, device=dev, dtype=torch.float32),
+        "mu_b": 0.1 * rn(d_r),
+        "sigma_b": 0.5 + torch.rand((d_r,), generator=gw, device=dev, dtype=torch.float32),
+        "w_a": 3.0 * rn(d_r, 3 * heads) / d_r ** 0.5,
+        "w_b": 3.0 * rn(d_r, 4) / d_r ** 0.5,
+    }
+    return {"x": x.to(torch.bfloat16), "side": side, "w": w}
