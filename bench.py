@@ -20,6 +20,10 @@ every token (b = 4, b = 2; every head full), routing only (bf16 cache, routed mo
 -- for decode (4 layers of the 1.3B-shaped decode) and prefill (the 160M-shaped prefill), each
 with its time per layer and its speedup over dense.
 
+Fifth object (``controller``): the routing controller (Eq. 5, Eq. 11, hard argmax) that writes
+the mode and width arrays, timed on one layer's tokens for the 160M and 1.3B prefill shapes and a
+1.3B decode step, with random weights.
+
 Accounting (algorithmic, from the realized seeded draws):
   decode bytes  = per attended (key, KV head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
                   4*D for b = 16, counted once over the union of the windows of the query heads
@@ -410,6 +414,36 @@ def bench_baselines(tr, args):
     return res
 
 
+def bench_controller(tr, args):
+    """Routing controller (Eq. 5 + Eq. 11 + hard argmax) on one layer's tokens: a 160M-shaped
+    prefill layer (4 x 2048 tokens, d = 768, 12 heads), a 1.3B-shaped one (d = 2048, 16 heads) and
+    a 1.3B decode step (32 tokens).  Random weights (no trained controller exists); 8 side features.
+    Bytes: x (2 d per token) + decisions (heads + 1 per token) + the weights once; FLOP: the trunk
+    and heads, 2 * (d + 8) * 128 + 2 * 128 * 128 + 2 * 128 * (3 heads + 4) per token."""
+    from workloads import controller_case
+    out = {}
+    for name, M, d, H in (("prefill_160m", 8192, 768, 12), ("prefill_1.3b", 8192, 2048, 16), ("decode_1.3b", 32, 2048, 16)):
+        c = controller_case(M, d, H, d_side=8, seed=args.seed, device="cuda")
+        mode = torch.empty((M, H), dtype=torch.uint8, device="cuda")
+        bits = torch.empty((M,), dtype=torch.uint8, device="cuda")
+        cw = tr.ControllerWeights(c["w"])
+        stream = torch.cuda.current_stream().cuda_stream
+        call = lambda: tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits, stream)
+        for _ in range(5):
+            call()
+        reps = 200
+        ms = time_steps(call, reps)
+        wbytes = sum(v.numel() * v.element_size() for v in c["w"].values())
+        nbytes = M * (2 * d + 4 * 8 + H + 1) + wbytes
+        flops = M * (2 * (d + 8) * 128 + 2 * 128 * 128 + 2 * 128 * (3 * H + 4))
+        out[name] = {"tokens": M, "d": d, "heads": H, "us_per_call": round(ms * 1e3, 2),
+                     "tokens_per_s": round(M / (ms * 1e-3), 1), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        del c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -418,9 +452,11 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill", "baselines"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill", "baselines", "controller"],
+                    default=None)
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query workloads")
     ap.add_argument("--no-baselines", action="store_true", help="skip the dense / uniform-width / routing-only runs")
+    ap.add_argument("--no-controller", action="store_true", help="skip the routing-controller timing")
     ap.add_argument("--baseline-layers", type=int, default=4, help="decode layers per baseline variant")
     ap.add_argument("--page-code-bytes", type=int, default=0,
                     help="cache page size: K (and V) code bytes per head per page; 0 = the library default")
@@ -446,6 +482,8 @@ def main():
     gpre = bench_prefill(tr, args, CONFIGS[6], baseline=False) if gqa or args.only == "gqa_prefill" else None
     base = (bench_baselines(tr, args) if (args.only is None and not args.no_baselines) or args.only == "baselines"
             else None)
+    ctl = (bench_controller(tr, args) if (args.only is None and not args.no_controller) or args.only == "controller"
+           else None)
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
@@ -479,6 +517,13 @@ def main():
         extra["prefill"] = {"workload": gpre["cfg"].name, "value": round(gpre["tok_s"], 1), "unit": "tokens/s",
                             "ms_per_step": round(gpre["ms"], 4), "tflops": round(gpre["tflops"], 2),
                             "roofline": gpre["roofline"]}
+    if ctl:
+        if "value" in line:
+            line["controller"] = ctl
+        else:
+            line.update({"value": ctl["prefill_1.3b"]["tokens_per_s"], "unit": "tokens/s",
+                         "config": {"workload": "routing controller, 8192 tokens, d = 2048, 16 heads"},
+                         "controller": ctl})
     if base:
         if "value" in line:
             line["baselines"] = base

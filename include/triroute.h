@@ -12,8 +12,10 @@
  *   - the inference paragraph after Algorithm 1: hard decisions, skipped work never
  *     materialized, each token's KV stored at its chosen width, one left-to-right pass,
  *     compatible with batching and KV paging.
- * The routing decisions (mode per query head, b per token) are inputs to every call, as in the
- * page's problem statement; the controller that produces them is not part of this library.
+ * The routing decisions (mode per query head, b per token) are inputs to every attention call,
+ * as in the page's problem statement.  tr_controller_route (below) produces them on the device
+ * from the residual stream with the page's controller at inference (Eq. (5), Eq. (11), hard
+ * argmax), given its weights.
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers (HIP device memory), owned by the caller, unless
@@ -148,6 +150,58 @@ int64_t tr_kv_cache_pages_used(tr_kv_cache* cache, void* stream);
  * launches and total_ms are HOST arrays of 5 elements. */
 tr_status tr_profile_enable(tr_kv_cache* cache, int32_t enable);
 tr_status tr_profile_read(tr_kv_cache* cache, int64_t* launches, double* total_ms);
+
+/* Weights of the routing controller for one layer (TriRoute review page, "core formulas" item 5,
+ * Eq. (5): a shared trunk maps [Norm(x_t); psi_t] to h_t in R^d_r, RMSNorm, then one linear head
+ * per axis; item 10, Eq. (11): per-axis whitening with frozen statistics).  Host struct holding
+ * DEVICE pointers; read during the call only.  The trunk is Linear(d + d_side -> 128) with bias,
+ * SiLU, Linear(128 -> 128) with bias; Norm and RMSNorm have unit gain and eps 1e-6; the
+ * whitening is (hhat - mu) / (sigma + 1e-5); the heads have no bias.
+ *   w1       bf16  layer 1, residual part, PACKED by tr_controller_pack_w1 from [128][d] (out x
+ *            in, row-major) -- d * 128 values in the matrix-core operand order
+ *   w1_side  float [128][d_side]        layer 1, side-feature part (out x in); NULL if d_side = 0
+ *   b1, b2   float [128]
+ *   w2       float [128][128]           layer 2, stored in x out (element [i][o])
+ *   mu_a, sigma_a, mu_b, sigma_b  float [128]   Eq. (11) statistics, attention / bit axis
+ *   w_a      float [128][3 * heads]     attention head, in x out; head h's logits are columns
+ *                                       3h (skip), 3h + 1 (local), 3h + 2 (full)
+ *   w_b      float [128][4]             bit head, in x out; columns b = 2, 4, 8, 16 */
+typedef struct {
+  int32_t d;                /* model width: a multiple of 64, 64 .. 16384 */
+  int32_t d_side;           /* side features per token, 0 .. 32 */
+  int32_t d_r;              /* trunk width: must be 128 (the page's d_r) */
+  int32_t heads;            /* attention heads routed per token, 1 .. 64 */
+  const void* w1;
+  const float* w1_side;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+  const float* mu_a;
+  const float* sigma_a;
+  const float* mu_b;
+  const float* sigma_b;
+  const float* w_a;
+  const float* w_b;
+} tr_controller_weights;
+
+/* Pack the controller's first-layer weights (bf16 [128][d], out x in, row-major, device) into
+ * the operand order tr_controller_route reads: w1_packed (bf16, d * 128 values, device, caller
+ * owned, not overlapping w1) at [s][n][16] holds, for k-step s = 4 g + j and trunk unit n, the
+ * channels 64 g + 8 j .. + 7 and 64 g + 32 + 8 j .. + 7 of row n.  d: a multiple of 64. */
+tr_status tr_controller_pack_w1(const void* w1, void* w1_packed, int32_t d, void* stream);
+
+/* Routing decisions at inference (the inference paragraph after Algorithm 1: the routers take
+ * the hard argmax) for n_tokens tokens of one layer, written straight into the layouts the
+ * attention calls read:
+ *   x:    bf16 [n_tokens, d] residual states (e.g. [batch, T] flattened)
+ *   side: float [n_tokens, d_side] side features psi_t (NULL if d_side = 0)
+ *   mode: uint8 [n_tokens, heads]  argmax of each head's 3 logits (TR_MODE_*)
+ *   bits: uint8 [n_tokens]         (2, 4, 8, 16)[argmax of the 4 width logits]
+ * Ties go to the lowest index.  The trunk's first layer runs on the matrix cores with the bf16
+ * x and w1 as exact operands and fp32 accumulation; everything after it is fp32.  n_tokens = 0
+ * is a no-op. */
+tr_status tr_controller_route(const tr_controller_weights* w, const void* x, const float* side,
+                              int64_t n_tokens, uint8_t* mode, uint8_t* bits, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* tr_status_str(tr_status status);

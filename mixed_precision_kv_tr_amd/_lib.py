@@ -30,6 +30,11 @@ class _Desc(ctypes.Structure):
                 ("num_query_heads", _i32)]
 
 
+class _CtlWeights(ctypes.Structure):
+    _fields_ = [("d", _i32), ("d_side", _i32), ("d_r", _i32), ("heads", _i32)] + [
+        (n, _vp) for n in ("w1", "w1_side", "b1", "w2", "b2", "mu_a", "sigma_a", "mu_b", "sigma_b", "w_a", "w_b")]
+
+
 def _sig(name, res, *args):
     fn = getattr(lib, name)
     fn.restype = res
@@ -49,6 +54,8 @@ _status = _sig("tr_kv_cache_status", ctypes.c_int, _vp, _vp)
 _pages = _sig("tr_kv_cache_pages_used", _i64, _vp, _vp)
 _status_str = _sig("tr_status_str", ctypes.c_char_p, ctypes.c_int)
 _truncate = _sig("tr_kv_cache_truncate", ctypes.c_int, _vp, _i32, _i32)
+_ctl_pack = _sig("tr_controller_pack_w1", ctypes.c_int, _vp, _vp, _i32, _vp)
+_ctl_route = _sig("tr_controller_route", ctypes.c_int, ctypes.POINTER(_CtlWeights), _vp, _vp, _i64, _vp, _vp, _vp)
 _prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
 _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
 PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn")
@@ -167,6 +174,39 @@ def tr_kv_cache_pages_used(cache: KVCache, stream=None) -> int:
 
 def tr_kv_cache_truncate(cache: KVCache, layer: int, new_len: int):
     _check(_truncate(cache.handle, layer, new_len), "tr_kv_cache_truncate")
+
+
+class ControllerWeights:
+    """The C struct tr_controller_weights built once from a dict of device tensors (and holding
+    them alive, with w1 packed by tr_controller_pack_w1), so that a call passes one pointer."""
+
+    NAMES = ("w1", "w1_side", "b1", "w2", "b2", "mu_a", "sigma_a", "mu_b", "sigma_b", "w_a", "w_b")
+
+    def __init__(self, weights: dict, stream=None):
+        import torch
+        d_r, d = weights["w1"].shape
+        side = weights.get("w1_side")
+        self.d_side = int(side.shape[1]) if side is not None else 0
+        self.heads = weights["w_a"].shape[1] // 3
+        self.tensors = dict(weights)
+        # the first layer in the matrix-core operand order (packed once, on the device)
+        self.tensors["w1"] = torch.empty_like(weights["w1"])
+        _check(_ctl_pack(_ptr(weights["w1"]), _ptr(self.tensors["w1"]), int(d), _stream(stream)),
+               "tr_controller_pack_w1")
+        self.struct = _CtlWeights(d, self.d_side, d_r, self.heads,
+                                  *[_ptr(self.tensors[n]) if (n != "w1_side" or self.d_side) else None
+                                    for n in self.NAMES])
+
+
+def tr_controller_route(weights, x, side, n_tokens: int, mode, bits, stream=None):
+    """weights: a ControllerWeights, or a dict of device tensors w1 (bf16 [128][d], unpacked), w1_side
+    ([128][d_side]), b1, w2 ([128][128], in x out), b2, mu_a, sigma_a, mu_b, sigma_b, w_a
+    ([128][3 heads], in x out), w_b ([128][4]); x bf16 [n, d]; side float32 [n, d_side] or None;
+    mode uint8 [n, heads] and bits uint8 [n] receive the decisions."""
+    if not isinstance(weights, ControllerWeights):
+        weights = ControllerWeights(weights)
+    _check(_ctl_route(ctypes.byref(weights.struct), _ptr(x), _ptr(side) if weights.d_side else None,
+                      int(n_tokens), _ptr(mode), _ptr(bits), _stream(stream)), "tr_controller_route")
 
 
 def tr_profile_enable(cache: KVCache, enable: bool = True):

@@ -63,3 +63,35 @@ def test_host_side_validation_without_gpu():
     assert _export(None, 0, 0, 1, None, None, None, None, None) == 1
     with pytest.raises(tr.TriRouteError):
         tr.tr_kv_cache_alloc(1, 1, 1, 96, 16)
+
+
+def test_controller_host_validation_without_gpu():
+    import mixed_precision_kv_tr_amd as tr
+    from mixed_precision_kv_tr_amd._lib import _CtlWeights, _ctl_route
+
+    fake = 0x1000                                    # never dereferenced: every call below fails
+    w = _CtlWeights(256, 0, 128, 4, *([fake] * 11))  # or returns before any launch
+    route = lambda w, n: _ctl_route(ctypes.byref(w), fake, None, n, fake, fake, None)
+    assert route(w, 0) == 0                          # no tokens: nothing to do
+    assert route(w, -1) == 1
+    for field, bad in (("d_r", 64), ("d", 100), ("d", 32), ("d", 96), ("d_side", 33), ("heads", 0), ("heads", 65)):
+        w2 = _CtlWeights.from_buffer_copy(w)
+        setattr(w2, field, bad)
+        assert route(w2, 5) == 1, field
+    w3 = _CtlWeights.from_buffer_copy(w)
+    w3.w_b = None
+    assert route(w3, 5) == 1
+    w4 = _CtlWeights.from_buffer_copy(w)
+    w4.d_side = 4                                    # side features without a side pointer
+    assert _ctl_route(ctypes.byref(w4), fake, None, 5, fake, fake, None) == 1
+    assert _ctl_route(None, fake, None, 5, fake, fake, None) == 1
+
+
+def test_controller_pack_host_validation_without_gpu():
+    from mixed_precision_kv_tr_amd._lib import _ctl_pack
+    a, b = 0x1000, 0x2000                            # never dereferenced: every call fails first
+    assert _ctl_pack(None, b, 128, None) == 1
+    assert _ctl_pack(a, None, 128, None) == 1
+    assert _ctl_pack(a, a, 128, None) == 1
+    for d in (0, 32, 100, 16448):
+        assert _ctl_pack(a, b, d, None) == 1
