@@ -20,6 +20,8 @@ xllm-io.github.io, section "core formulas"):
   queries attend to what was stored).
 * ``controller_route`` -- Eq. (5) with Eq. (11)'s whitening and the hard argmax of inference:
   the routing decisions (a mode per head, a width per token) from a token's residual state.
+* ``moe_ffn`` -- Eq. (3): E SwiGLU experts plus the null expert, top-k of a softmax gate with
+  the weights renormalized over the selected set.
 
 Readings where the pages leave a step open (all in fp32 for the quantizer, fp64 for attention):
 the quantization group is one head's D-vector of one token, separately for K and V; "round"
@@ -38,6 +40,8 @@ from .quantize import BITS_ALLOWED, bf16_bits_to_f32, dequantize, quantize
 from .attention import MODE_FULL, MODE_LOCAL, MODE_SKIP, routed_attention
 from .reference import attend_cached
 from .controller import BIT_CHOICES, controller_logits, controller_route
+from . import moe
+from .moe import gate as moe_gate, moe_ffn
 
 __all__ = [
     "BITS_ALLOWED",
@@ -51,5 +55,7 @@ __all__ = [
     "BIT_CHOICES",
     "controller_logits",
     "controller_route",
+    "moe_gate",
+    "moe_ffn",
     "attend_cached",
 ]

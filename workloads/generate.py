@@ -14,7 +14,7 @@ from .configs import WorkloadConfig
 
 MODE_CODES = {"skip": 0, "local": 1, "full": 2}
 _STREAMS = {"q": 0, "k": 1, "v": 2, "kscale": 3, "bits": 4, "mode": 5, "runs": 6,
-            "ctl_x": 7, "ctl_side": 8, "ctl_w": 9}
+            "ctl_x": 7, "ctl_side": 8, "ctl_w": 9, "moe_x": 10, "moe_z": 11, "moe_w": 12}
 
 
 def _gen(device, seed: int, cid: int, layer: int, stream: str) -> torch.Generator:
@@ -145,3 +145,23 @@ def controller_case(tokens: int, d: int, heads: int, *, d_side: int = 8, d_r: in
         "w_b": 3.0 * rn(d_r, 4) / d_r ** 0.5,
     }
     return {"x": x.to(torch.bfloat16), "side": side, "w": w}
+
+
+def moe_case(tokens: int, d: int, d_e: int, experts: int, *, seed: int = 0, device="cpu", layer: int = 0,
+             cid: int = 99, null_bias: float = 0.0) -> dict:
+    """Inputs of the expert FFN for one layer: x (bf16 [tokens, d], N(0, 1) with a few 8x channels),
+    gate logits z (float32 [tokens, experts + 1], N(0, 1); index 0 is the null expert, shifted by
+    null_bias), and random bf16 weights w_gate, w_up [E][d_e][d] at 1/sqrt(d) and w_down [E][d][d_e]
+    at 1/sqrt(d_e).  No trained weights exist; these only give the kernels realistic shapes."""
+    dev = torch.device(device)
+    x = torch.randn((tokens, d), generator=_gen(dev, seed, cid, layer, "moe_x"), device=dev, dtype=torch.float32)
+    x[:, : max(1, d // 64)] *= 8.0
+    z = torch.randn((tokens, experts + 1), generator=_gen(dev, seed, cid, layer, "moe_z"), device=dev,
+                    dtype=torch.float32)
+    z[:, 0] += null_bias
+    gw = _gen(dev, seed, cid, layer, "moe_w")
+    rn = lambda *shape: torch.randn(shape, generator=gw, device=dev, dtype=torch.float32)
+    return {"x": x.to(torch.bfloat16), "z": z,
+            "w_gate": (rn(experts, d_e, d) / d ** 0.5).to(torch.bfloat16),
+            "w_up": (rn(experts, d_e, d) / d ** 0.5).to(torch.bfloat16),
+            "w_down": (rn(experts, d, d_e) / d_e ** 0.5).to(torch.bfloat16)}
