@@ -24,6 +24,9 @@ Fifth object (``controller``): the routing controller (Eq. 5, Eq. 11, hard argma
 the mode and width arrays, timed on one layer's tokens for the 160M and 1.3B prefill shapes and a
 1.3B decode step, with random weights.
 
+Sixth object (``moe``): the expert FFN of Eq. 3 (8 SwiGLU experts plus the null expert, top-2),
+timed on one layer's tokens for the 160M and 1.3B shapes and a 1.3B decode step, random weights.
+
 Accounting (algorithmic, from the realized seeded draws):
   decode bytes  = per attended (key, KV head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
                   4*D for b = 16, counted once over the union of the windows of the query heads
@@ -444,6 +447,36 @@ def bench_controller(tr, args):
     return out
 
 
+def bench_moe(tr, args):
+    """Expert FFN (Eq. 3): E = 8 SwiGLU experts plus the null expert, top-2, on one layer's tokens:
+    the 160M prefill layer (8192 tokens, d = 768, expert width 1024 = half the model's 2048 FFN),
+    the 1.3B one (d = 2048, expert width 2688 ~ half of 5461, rounded to 128) and a 1.3B decode step
+    (32 tokens).  Random weights; gate logits N(0, 1).  FLOP: 6 d d_e per (token, non-null expert)."""
+    from workloads import moe_case
+    out = {}
+    for name, M, d, de in (("prefill_160m", 8192, 768, 1024), ("prefill_1.3b", 8192, 2048, 2688),
+                           ("decode_1.3b", 32, 2048, 2688)):
+        c = moe_case(M, d, de, 8, seed=args.seed, device="cuda")
+        moe = tr.tr_moe_alloc(d, de, 8, 2, M)
+        tr.tr_moe_set_weights(moe, c["w_gate"], c["w_up"], c["w_down"])
+        y = torch.empty((M, d), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        call = lambda: tr.tr_moe_ffn(moe, c["x"], c["z"], M, y, stream)
+        for _ in range(3):
+            call()
+        ms = time_steps(call, 50)
+        chosen = torch.topk(c["z"], 2, dim=1).indices
+        active = int((chosen != 0).sum())
+        flops = 6.0 * d * de * active
+        out[name] = {"tokens": M, "d": d, "d_expert": de, "experts": 8, "top_k": 2, "us_per_call": round(ms * 1e3, 2),
+                     "tokens_per_s": round(M / (ms * 1e-3), 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "active_choices": active}
+        moe.close()
+        del c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,11 +485,12 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill", "baselines", "controller"],
+    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill", "baselines", "controller", "moe"],
                     default=None)
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query workloads")
     ap.add_argument("--no-baselines", action="store_true", help="skip the dense / uniform-width / routing-only runs")
     ap.add_argument("--no-controller", action="store_true", help="skip the routing-controller timing")
+    ap.add_argument("--no-moe", action="store_true", help="skip the expert-FFN timing")
     ap.add_argument("--baseline-layers", type=int, default=4, help="decode layers per baseline variant")
     ap.add_argument("--page-code-bytes", type=int, default=0,
                     help="cache page size: K (and V) code bytes per head per page; 0 = the library default")
@@ -484,6 +518,7 @@ def main():
             else None)
     ctl = (bench_controller(tr, args) if (args.only is None and not args.no_controller) or args.only == "controller"
            else None)
+    moe = bench_moe(tr, args) if (args.only is None and not args.no_moe) or args.only == "moe" else None
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
@@ -517,6 +552,12 @@ def main():
         extra["prefill"] = {"workload": gpre["cfg"].name, "value": round(gpre["tok_s"], 1), "unit": "tokens/s",
                             "ms_per_step": round(gpre["ms"], 4), "tflops": round(gpre["tflops"], 2),
                             "roofline": gpre["roofline"]}
+    if moe:
+        if "value" in line:
+            line["moe"] = moe
+        else:
+            line.update({"value": moe["prefill_1.3b"]["tflops"], "unit": "TFLOP/s",
+                         "config": {"workload": "expert FFN, 8192 tokens, d = 2048, 8 experts, top-2"}, "moe": moe})
     if ctl:
         if "value" in line:
             line["controller"] = ctl

@@ -203,6 +203,44 @@ tr_status tr_controller_pack_w1(const void* w1, void* w1_packed, int32_t d, void
 tr_status tr_controller_route(const tr_controller_weights* w, const void* x, const float* side,
                               int64_t n_tokens, uint8_t* mode, uint8_t* bits, void* stream);
 
+/* Expert FFN with a null expert (review page, "core formulas" item 3, Eq. (3)):
+ *   FFN_t = sum_{j in S_t} p_tj / sum_{j' in S_t} p_tj' * f_j(RMSNorm(x_t)),  p_t = softmax(z_t),
+ * over E experts plus the null expert f_0 = 0 (gate index 0), S_t the top_k largest p_t (ties to
+ * the lower index), each expert a SwiGLU FFN f(u) = W2 (silu(W1 u) * (W3 u)) with no biases.
+ * The hidden activation enters the down product as bf16; products run on the matrix cores with
+ * bf16 operands and fp32 accumulation.  The gate logits come from the caller (e.g. an expert head
+ * of the controller, Eq. (5)).  A handle owns the packed weights and the scratch of calls up to
+ * max_tokens tokens. */
+typedef struct {
+  int32_t d;                /* model width: a multiple of 128, 128 .. 16384 */
+  int32_t d_expert;         /* expert hidden width: a multiple of 128 */
+  int32_t experts;          /* E: 1 .. 64 (the gate has E + 1 logits) */
+  int32_t top_k;            /* 1 or 2 (1 with the null expert chosen = the MoD-style FFN skip) */
+  int32_t max_tokens;       /* tokens per call, >= 1 */
+} tr_moe_desc;
+
+typedef struct tr_moe tr_moe;
+
+/* Allocate a handle (device memory via hipMalloc on the current device); nothing on error. */
+tr_status tr_moe_alloc(const tr_moe_desc* desc, tr_moe** out);
+
+/* Free the handle's device memory (synchronizes the device).  NULL is a no-op. */
+tr_status tr_moe_free(tr_moe* moe);
+
+/* Copy the experts' weights into the handle, packed into the matrix-core operand order:
+ *   w_gate, w_up: bf16 [E][d_expert][d]  (W1, W3: out x in, row-major)
+ *   w_down:       bf16 [E][d][d_expert]  (W2: out x in)
+ * Device pointers; asynchronous on `stream`, the inputs may be freed once the stream has
+ * reached the call. */
+tr_status tr_moe_set_weights(tr_moe* moe, const void* w_gate, const void* w_up, const void* w_down, void* stream);
+
+/* Eq. (3) for n_tokens tokens (0 <= n_tokens <= max_tokens; 0 is a no-op):
+ *   x:           bf16 [n_tokens, d] FFN inputs before Norm
+ *   gate_logits: float [n_tokens, E + 1], index 0 = the null expert
+ *   y:           float [n_tokens, d] receives FFN_t (a token whose choices are all the null
+ *                expert gets zeros).  Deterministic: no atomics. */
+tr_status tr_moe_ffn(tr_moe* moe, const void* x, const float* gate_logits, int32_t n_tokens, float* y, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* tr_status_str(tr_status status);
 

@@ -13,7 +13,7 @@ _EXPORTS = (
     "tr_kv_quantize_write", "tr_routed_attn_decode", "tr_routed_attn_prefill", "tr_kv_cache_export",
     "tr_kv_cache_status", "tr_kv_cache_pages_used", "tr_status_str", "tr_kv_cache_truncate",
     "tr_profile_enable", "tr_profile_read", "PROFILE_FAMILIES", "tr_controller_route",
-    "ControllerWeights",
+    "ControllerWeights", "MoE", "tr_moe_alloc", "tr_moe_set_weights", "tr_moe_ffn",
 )
 
 __all__ = list(_EXPORTS)

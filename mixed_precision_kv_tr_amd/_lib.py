@@ -35,6 +35,10 @@ class _CtlWeights(ctypes.Structure):
         (n, _vp) for n in ("w1", "w1_side", "b1", "w2", "b2", "mu_a", "sigma_a", "mu_b", "sigma_b", "w_a", "w_b")]
 
 
+class _MoeDesc(ctypes.Structure):
+    _fields_ = [("d", _i32), ("d_expert", _i32), ("experts", _i32), ("top_k", _i32), ("max_tokens", _i32)]
+
+
 def _sig(name, res, *args):
     fn = getattr(lib, name)
     fn.restype = res
@@ -56,6 +60,10 @@ _status_str = _sig("tr_status_str", ctypes.c_char_p, ctypes.c_int)
 _truncate = _sig("tr_kv_cache_truncate", ctypes.c_int, _vp, _i32, _i32)
 _ctl_pack = _sig("tr_controller_pack_w1", ctypes.c_int, _vp, _vp, _i32, _vp)
 _ctl_route = _sig("tr_controller_route", ctypes.c_int, ctypes.POINTER(_CtlWeights), _vp, _vp, _i64, _vp, _vp, _vp)
+_moe_alloc = _sig("tr_moe_alloc", ctypes.c_int, ctypes.POINTER(_MoeDesc), ctypes.POINTER(_vp))
+_moe_free = _sig("tr_moe_free", ctypes.c_int, _vp)
+_moe_set = _sig("tr_moe_set_weights", ctypes.c_int, _vp, _vp, _vp, _vp, _vp)
+_moe_ffn = _sig("tr_moe_ffn", ctypes.c_int, _vp, _vp, _vp, _i32, _vp, _vp)
 _prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
 _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
 PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn")
@@ -207,6 +215,40 @@ def tr_controller_route(weights, x, side, n_tokens: int, mode, bits, stream=None
         weights = ControllerWeights(weights)
     _check(_ctl_route(ctypes.byref(weights.struct), _ptr(x), _ptr(side) if weights.d_side else None,
                       int(n_tokens), _ptr(mode), _ptr(bits), _stream(stream)), "tr_controller_route")
+
+
+class MoE:
+    """Owning handle of a tr_moe (freed on close / garbage collection)."""
+
+    def __init__(self, handle: int, desc: dict):
+        self.handle = handle
+        self.desc = desc
+
+    def close(self):
+        if self.handle:
+            _moe_free(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tr_moe_alloc(d: int, d_expert: int, experts: int, top_k: int, max_tokens: int) -> MoE:
+    desc = _MoeDesc(d, d_expert, experts, top_k, max_tokens)
+    h = _vp()
+    _check(_moe_alloc(ctypes.byref(desc), ctypes.byref(h)), "tr_moe_alloc")
+    return MoE(h.value, dict(d=d, d_expert=d_expert, experts=experts, top_k=top_k, max_tokens=max_tokens))
+
+
+def tr_moe_set_weights(moe: MoE, w_gate, w_up, w_down, stream=None):
+    _check(_moe_set(moe.handle, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _stream(stream)), "tr_moe_set_weights")
+
+
+def tr_moe_ffn(moe: MoE, x, gate_logits, n_tokens: int, y, stream=None):
+    _check(_moe_ffn(moe.handle, _ptr(x), _ptr(gate_logits), int(n_tokens), _ptr(y), _stream(stream)), "tr_moe_ffn")
 
 
 def tr_profile_enable(cache: KVCache, enable: bool = True):

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtriroute.so")
-SOURCES = ["cache.cpp.hip", "decode.cpp.hip", "prefill.cpp.hip", "controller.cpp.hip"]
+SOURCES = ["cache.cpp.hip", "decode.cpp.hip", "prefill.cpp.hip", "controller.cpp.hip", "moe.cpp.hip"]
 
 
 def hipcc() -> str:

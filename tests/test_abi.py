@@ -95,3 +95,15 @@ def test_controller_pack_host_validation_without_gpu():
     assert _ctl_pack(a, a, 128, None) == 1
     for d in (0, 32, 100, 16448):
         assert _ctl_pack(a, b, d, None) == 1
+
+
+def test_moe_host_validation_without_gpu():
+    from mixed_precision_kv_tr_amd._lib import _MoeDesc, _moe_alloc, _moe_ffn, _moe_set, _moe_free
+    h = ctypes.c_void_p()
+    for bad in ((100, 128, 4, 2, 16), (128, 100, 4, 2, 16), (128, 128, 0, 2, 16), (128, 128, 65, 2, 16),
+                (128, 128, 4, 3, 16), (128, 128, 4, 0, 16), (128, 128, 4, 2, 0), (64, 128, 4, 2, 16)):
+        assert _moe_alloc(ctypes.byref(_MoeDesc(*bad)), ctypes.byref(h)) == 1, bad
+    assert _moe_alloc(None, ctypes.byref(h)) == 1
+    assert _moe_ffn(None, 0x1000, 0x1000, 4, 0x1000, None) == 1
+    assert _moe_set(None, 0x1000, 0x1000, 0x1000, None) == 1
+    assert _moe_free(None) == 0
