@@ -8,11 +8,11 @@
 //                 index) and the renormalized weights exp(z_j - z_max) / sum over S_t.
 //   k_moe_lists   one workgroup per (slot, expert, null included): the tokens whose slot-th
 //                 choice is that expert, in token order (a block scan) -- the ragged batches.
-//   k_moe_up      one workgroup per (slot, expert, 32 listed tokens, 128 hidden units): the gate
+//   k_moe_up      one workgroup per (slot, expert, 32 or 64 listed tokens, 128 hidden units): the gate
 //                 and up products on the matrix cores (x rows gathered from the list, bf16 x and
 //                 packed bf16 W1 / W3 as exact operands, fp32 accumulation), then the RMSNorm
 //                 scale, silu(g) * u and bf16 rounding into the hidden buffer.
-//   k_moe_down    per slot, in slot order: one workgroup per (expert, 32 listed tokens, 128 output
+//   k_moe_down    per slot, in slot order: one workgroup per (expert, 32 or 64 listed tokens, 128 output
 //                 channels): the down product of the gathered hidden rows, times the token's
 //                 weight, stored (slot 0; the null expert stores zeros) or added (slot 1) into the
 //                 fp32 output -- no atomics, so the result does not depend on scheduling.
@@ -22,6 +22,8 @@
 // k-step and a lane reads 64 contiguous bytes of its activation row per group of 4 k-steps.
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -44,7 +46,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTile = 32;         // tokens per tile
+// Token tiles of 32 * MB listed tokens: each wave computes its 32 units for MB 32-token blocks,
+// so a weight load feeds MB matrix-core products.  MB = 2 for calls of more than 512 tokens
+// (weights re-read half as often), MB = 1 below (a decode step's few tokens per expert).
+constexpr int kSmallCall = 512;
 constexpr int kUnits = 128;       // output units per workgroup (4 waves x 32)
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopK = 2;
@@ -154,8 +159,9 @@ __global__ __launch_bounds__(1024) void k_moe_lists(const int32_t* __restrict__ 
   if (tid == 0) counts[blockIdx.x] = base;
 }
 
-// The tile a workgroup takes: tiles of 32 listed tokens over the (slot, expert) lists in order,
+// The tile a workgroup takes: tiles of kTile listed tokens over the (slot, expert) lists in order,
 // restricted to slots [s0, s1) and experts [e0, E]; returns false past the last tile.
+template <int kTile>
 __device__ __forceinline__ bool find_tile(const int32_t* counts, int E, int s0, int s1, int e0, int id, int& slot,
                                           int& e, int& tile, int& cnt) {
   for (int s = s0; s < s1; ++s) {
@@ -175,15 +181,18 @@ __device__ __forceinline__ bool find_tile(const int32_t* counts, int E, int s0, 
   return false;
 }
 
-// Gate and up products for 32 tokens of one (slot, expert) list and 128 hidden units.
+// Gate and up products for 32 kMB tokens of one (slot, expert) list and 128 hidden units: each
+// wave computes 32 units for kMB 32-token blocks.
+template <int kMB>
 __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, const int32_t* __restrict__ lists,
                                                 const int32_t* __restrict__ counts, const float* __restrict__ inv_rms,
                                                 const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
                                                 uint16_t* __restrict__ hbuf, int d, int de, int E, int k, int cap) {
+  constexpr int kTile = 32 * kMB;
   __shared__ int32_t tok[kTile];
   __shared__ float inv[kTile];
   int slot, e, tile, cnt;
-  if (!find_tile(counts, E, 0, k, 1, blockIdx.x, slot, e, tile, cnt)) return;
+  if (!find_tile<kTile>(counts, E, 0, k, 1, blockIdx.x, slot, e, tile, cnt)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ntok = min(kTile, cnt - tile * kTile);
   const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kTile;
@@ -195,61 +204,74 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
   __syncthreads();
   const int r = lane & 31, kh = lane >> 5;
   const int n = blockIdx.y * kUnits + 32 * wave + r;  // hidden unit of this lane's B column
-  const uint16_t* xr = x + (int64_t)tok[r] * d + 32 * kh;
+  const uint16_t* xr[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) xr[mb] = x + (int64_t)tok[32 * mb + r] * d + 32 * kh;
   const int64_t mat = (int64_t)de * d, wstep = (int64_t)de * 16;
   const uint16_t* gr = wg + (e - 1) * mat + (int64_t)n * 16 + 8 * kh;
   const uint16_t* ur = wu + (e - 1) * mat + (int64_t)n * 16 + 8 * kh;
-  f32x16 ag = {}, au = {};
-  const int ns = d / 16;
-  // two k-steps (32 channels of the lane's half group) per stage, the next stage in flight
-  uint4 xa[2], ga[2], ua[2];
-  auto load = [&](int st, uint4 (&xv)[2], uint4 (&gv)[2], uint4 (&uv)[2]) {
+  f32x16 ag[kMB] = {}, au[kMB] = {};
+  const int ns = d / 16;                          // a multiple of 8
+  // kPS k-steps per stage, the next stage in flight; each weight load feeds kMB token blocks
+  constexpr int kPS = 4 / kMB;
+  uint4 xa[kPS][kMB], ga[kPS], ua[kPS];
+  auto load = [&](int st, uint4 (&xv)[kPS][kMB], uint4 (&gv)[kPS], uint4 (&uv)[kPS]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kPS; ++q) {
       const int s = st + q, g = s >> 2, j = s & 3;
-      xv[q] = gload16(xr + 64 * g + 8 * j);
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) xv[q][mb] = gload16(xr[mb] + 64 * g + 8 * j);
       gv[q] = gload16(gr + s * wstep);
       uv[q] = gload16(ur + s * wstep);
     }
   };
   load(0, xa, ga, ua);
-  for (int st = 0; st < ns; st += 2) {
-    uint4 xn[2], gn[2], un[2];
-    load(min(st + 2, ns - 2), xn, gn, un);         // clamped: the loads never branch
+  for (int st = 0; st < ns; st += kPS) {
+    uint4 xn[kPS][kMB], gn[kPS], un[kPS];
+    load(min(st + kPS, ns - kPS), xn, gn, un);    // clamped: the loads never branch
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      ag = mfma(xa[q], ga[q], ag);
-      au = mfma(xa[q], ua[q], au);
+    for (int q = 0; q < kPS; ++q) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        ag[mb] = mfma(xa[q][mb], ga[q], ag[mb]);
+        au[mb] = mfma(xa[q][mb], ua[q], au[mb]);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      xa[q] = xn[q];
+    for (int q = 0; q < kPS; ++q) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) xa[q][mb] = xn[q][mb];
       ga[q] = gn[q];
       ua[q] = un[q];
     }
   }
-  // D[row][unit]: this lane holds unit n for rows 8 (reg / 4) + 4 kh + reg % 4
+  // D[row][unit]: this lane holds unit n for rows 32 mb + 8 (reg / 4) + 4 kh + reg % 4
 #pragma unroll
-  for (int reg = 0; reg < 16; ++reg) {
-    const int row = 8 * (reg >> 2) + 4 * kh + (reg & 3);
-    if (row < ntok) {
-      const float gv = ag[reg] * inv[row], uv = au[reg] * inv[row];
-      const float h = gv / (1.0f + expf(-gv)) * uv;
-      hbuf[((int64_t)tok[row] * k + slot) * de + n] = tr_f32_to_bf16(h);
+  for (int mb = 0; mb < kMB; ++mb) {
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) {
+      const int row = 32 * mb + 8 * (reg >> 2) + 4 * kh + (reg & 3);
+      if (row < ntok) {
+        const float gv = ag[mb][reg] * inv[row], uv = au[mb][reg] * inv[row];
+        const float h = gv / (1.0f + expf(-gv)) * uv;
+        hbuf[((int64_t)tok[row] * k + slot) * de + n] = tr_f32_to_bf16(h);
+      }
     }
   }
 }
 
-// Down product for one slot: 32 tokens of one (slot, expert) list and 128 output channels.
+// Down product for one slot: 32 kMB tokens of one (slot, expert) list and 128 output channels.
+template <int kMB>
 __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ lists,
                                                   const int32_t* __restrict__ counts, const float* __restrict__ wt,
                                                   const uint16_t* __restrict__ wd, float* __restrict__ y, int d, int de,
                                                   int E, int k, int cap, int slot) {
+  constexpr int kTile = 32 * kMB;
   __shared__ int32_t tok[kTile];
   __shared__ float wgt[kTile];
   int s_, e, tile, cnt;
   // slot 0 also takes the null expert's tiles (zeros); later slots skip it
-  if (!find_tile(counts, E, slot, slot + 1, slot == 0 ? 0 : 1, blockIdx.x, s_, e, tile, cnt)) return;
+  if (!find_tile<kTile>(counts, E, slot, slot + 1, slot == 0 ? 0 : 1, blockIdx.x, s_, e, tile, cnt)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ntok = min(kTile, cnt - tile * kTile);
   const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kTile;
@@ -261,42 +283,52 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
   __syncthreads();
   const int r = lane & 31, kh = lane >> 5;
   const int n = blockIdx.y * kUnits + 32 * wave + r;  // output channel of this lane's B column
-  f32x16 acc = {};
+  f32x16 acc[kMB] = {};
   if (e > 0) {
-    const uint16_t* hr = hbuf + ((int64_t)tok[r] * k + slot) * de + 32 * kh;
+    const uint16_t* hr[kMB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) hr[mb] = hbuf + ((int64_t)tok[32 * mb + r] * k + slot) * de + 32 * kh;
     const int64_t wstep = (int64_t)d * 16;
     const uint16_t* dr = wd + (int64_t)(e - 1) * d * de + (int64_t)n * 16 + 8 * kh;
-    const int ns = de / 16;
-    uint4 ha[2], wa[2];
-    auto load = [&](int st, uint4 (&hv)[2], uint4 (&wv)[2]) {
+    const int ns = de / 16;                       // a multiple of 8
+    constexpr int kPS = 4 / kMB;
+    uint4 ha[kPS][kMB], wa[kPS];
+    auto load = [&](int st, uint4 (&hv)[kPS][kMB], uint4 (&wv)[kPS]) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kPS; ++q) {
         const int s = st + q, g = s >> 2, j = s & 3;
-        hv[q] = gload16(hr + 64 * g + 8 * j);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) hv[q][mb] = gload16(hr[mb] + 64 * g + 8 * j);
         wv[q] = gload16(dr + s * wstep);
       }
     };
     load(0, ha, wa);
-    for (int st = 0; st < ns; st += 2) {
-      uint4 hn[2], wn[2];
-      load(min(st + 2, ns - 2), hn, wn);
+    for (int st = 0; st < ns; st += kPS) {
+      uint4 hn[kPS][kMB], wn[kPS];
+      load(min(st + kPS, ns - kPS), hn, wn);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) acc = mfma(ha[q], wa[q], acc);
+      for (int q = 0; q < kPS; ++q)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        ha[q] = hn[q];
+        for (int mb = 0; mb < kMB; ++mb) acc[mb] = mfma(ha[q][mb], wa[q], acc[mb]);
+#pragma unroll
+      for (int q = 0; q < kPS; ++q) {
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) ha[q][mb] = hn[q][mb];
         wa[q] = wn[q];
       }
     }
   }
 #pragma unroll
-  for (int reg = 0; reg < 16; ++reg) {
-    const int row = 8 * (reg >> 2) + 4 * kh + (reg & 3);
-    if (row < ntok) {
-      float* dst = y + (int64_t)tok[row] * d + n;
-      const float v = e > 0 ? acc[reg] * wgt[row] : 0.0f;
-      if (slot == 0) *dst = v;
-      else *dst += v;
+  for (int mb = 0; mb < kMB; ++mb) {
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) {
+      const int row = 32 * mb + 8 * (reg >> 2) + 4 * kh + (reg & 3);
+      if (row < ntok) {
+        float* dst = y + (int64_t)tok[row] * d + n;
+        const float v = e > 0 ? acc[mb][reg] * wgt[row] : 0.0f;
+        if (slot == 0) *dst = v;
+        else *dst += v;
+      }
     }
   }
 }
@@ -376,13 +408,18 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
   hipLaunchKernelGGL(k_moe_lists, dim3(K * (E + 1)), dim3(1024), 0, st, m->sel, M, K, E, m->max_tokens, m->lists,
                      m->counts);
   // upper bounds on the tile counts (the workgroups past the real count exit at once)
-  const int tiles_up = K * ((M + kTile - 1) / kTile) + K * E;
-  hipLaunchKernelGGL(k_moe_up, dim3(tiles_up, m->de / kUnits), dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                     m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d, m->de, E, K, m->max_tokens);
-  const int tiles_dn = (M + kTile - 1) / kTile + E + 1;
-  for (int s = 0; s < K; ++s)
-    hipLaunchKernelGGL(k_moe_down, dim3(tiles_dn, m->d / kUnits), dim3(256), 0, st, m->hbuf, m->lists, m->counts,
-                       m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s);
+  auto run = [&](auto mb) {
+    constexpr int MB = decltype(mb)::value, T = 32 * MB;
+    const int tiles_up = K * ((M + T - 1) / T) + K * E;
+    hipLaunchKernelGGL(k_moe_up<MB>, dim3(tiles_up, m->de / kUnits), dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                       m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d, m->de, E, K, m->max_tokens);
+    const int tiles_dn = (M + T - 1) / T + E + 1;
+    for (int s = 0; s < K; ++s)
+      hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn, m->d / kUnits), dim3(256), 0, st, m->hbuf, m->lists,
+                         m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s);
+  };
+  if (M > kSmallCall) run(std::integral_constant<int, 2>());
+  else run(std::integral_constant<int, 1>());
   TR_LAUNCH_CHECK();
   return TR_OK;
 }
