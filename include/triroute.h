@@ -63,7 +63,8 @@ typedef struct {
   int32_t batch;            /* sequences per layer, >= 1 */
   int32_t num_heads;        /* KV heads, >= 1 (the heads the cache stores) */
   int32_t head_dim;         /* 64 or 128 */
-  int32_t max_tokens;       /* per-sequence capacity in positions, >= 1 */
+  int32_t max_tokens;       /* per-sequence capacity in positions, >= 1; at most
+                               2^30 / head_dim (TR_ERR_UNSUPPORTED beyond) */
   int32_t page_code_bytes;  /* K (and V) code bytes of one head in one page; 0 -> 4096.
                                A power of two in [1024, 65536].  A page of width b holds
                                page_code_bytes * 8 / (head_dim * b) tokens. */

@@ -285,6 +285,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   if (d->num_layers < 1 || d->batch < 1 || d->num_heads < 1 || d->max_tokens < 1 || d->pool_pages < 0)
     return TR_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return TR_ERR_UNSUPPORTED;
+  // one (seq, head)'s dense prefill staging must stay addressable by a 32-bit buffer offset
+  if ((int64_t)d->max_tokens * d->head_dim > (1LL << 30) - 64LL * d->head_dim) return TR_ERR_UNSUPPORTED;
   const int hq = d->num_query_heads ? d->num_query_heads : d->num_heads;
   if (hq < d->num_heads || hq % d->num_heads) return TR_ERR_INVALID_ARG;
   const int cb = d->page_code_bytes ? d->page_code_bytes : 4096;

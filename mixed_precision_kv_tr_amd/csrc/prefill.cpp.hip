@@ -67,9 +67,9 @@ __device__ __forceinline__ float xor32_sum(float v) {
 }
 
 // Work units of the attention kernel for one (seq, head), after the row compaction: one per
-// 128-row tile, except that a tile whose key range spans more than kch key tiles is cut into
-// chunks of kch key tiles that run as separate units, write partial (max, sum, O) rows, and are
-// merged by k_prefill_merge.  kch is the smallest of 16, 32, 64, ... key tiles for which the
+// 128-row tile, except that a tile whose key range spans n > kch key tiles is cut into
+// ceil(n / kch) near-equal chunks that run as separate units, write partial (max, sum, O) rows,
+// and are merged by k_prefill_merge.  kch is the smallest of 16, 32, 64, ... key tiles for which the
 // head's partial results fit its kSlotsPerHead slots (no split if none does).
 //   unit  = (r0 | full << 31, rend, kt0 | kt1 << 16, partial slot or -1)
 //   merge = (r0, rend, first slot, chunks)
@@ -135,7 +135,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
     }
     if (k < ntl) {
       for (int cc = 0; cc < nch; ++cc) {
-        const int kt0 = klo + cc * kch, kt1 = min(khi, kt0 + kch);
+        const int kt0 = klo + ((khi - klo) * cc) / nch, kt1 = klo + ((khi - klo) * (cc + 1)) / nch;
         units[pos[0] + cc] = make_int4(r0 | (full << 31), rend, kt0 | (kt1 << 16), nch > 1 ? pos[1] + cc : -1);
       }
       if (nch > 1) merges[pos[2]] = make_int4(r0, rend, pos[1], nch);
@@ -481,22 +481,25 @@ struct alignas(16) PrefillTile {
   alignas(16) float alpha[BN]; // s_K * log2(e) / sqrt(D) (or log2(e) / sqrt(D))
 };
 
-template <int D, int G>
+template <int D>
 struct PrefillSmem {
-  PrefillTile<D> tile[G][2];   // per key group: double buffer
-  int32_t wrange[4][4];        // per row wave: lo, hi, tmin, lomax
+  PrefillTile<D> tile[2];      // double buffer
 };
 
-#ifndef TR_PREFILL_GROUPS
-#define TR_PREFILL_GROUPS 1
-#endif
-// G groups of 4 waves share the same 128 query rows and split the key tiles round-robin;
-// their (max, sum, O) states merge through LDS at the end.
+// Buffer-resource loads: the base and size live in scalar registers, the tile's key offset is a
+// scalar offset, so advancing a tile costs no vector instructions; reads past the size return 0.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
 #ifndef TR_PREFILL_WAVES
 #define TR_PREFILL_WAVES 4
 #endif
-template <int D, int G>
-__global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D == 64 ? TR_PREFILL_WAVES : 2))) void k_prefill_attn(
+template <int D>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D == 64 ? TR_PREFILL_WAVES : 2))) void k_prefill_attn(
     CacheLayout c, int p0, int T, int window, int np, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, const int4* __restrict__ units, int uph,
     const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, const float2* __restrict__ dkf,
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   constexpr int MT = D / 32;           // 32-channel tiles of O^T
   constexpr int KPT = D / 64;          // 16-byte K pieces per thread per tile
   constexpr int VPT = D / 64;          // 16-byte V^T pieces per thread per tile
-  __shared__ PrefillSmem<D, G> sm;
+  __shared__ PrefillSmem<D> sm;
 
   const int BH = c.B * HQ;
   const int u = blockIdx.x / BH, sh = blockIdx.x % BH;   // sh: (seq, query head)
@@ -516,9 +519,53 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   const bool full = unit.x < 0;
   const int r0 = unit.x & 0x7fffffff, rend = unit.y;
   const int kt0 = unit.z & 0xffff, kt1 = unit.z >> 16, slot = unit.w;
-  const int grp = threadIdx.x / kBlock;              // key group
-  const int tid = threadIdx.x % kBlock, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
+  const int kb0 = kt0 * BN;                        // this unit's key tiles [kt0, kt1)
+  const int ntiles = kt1 - kt0;
+
+  // Staging: thread -> K row (tid / 8), 16-byte piece (tid % 8); V^T row (tid / 4), piece
+  // (tid % 4); for D = 128 every thread moves two pieces of each.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(dk + skv * np * D, (uint32_t)np * D * 2u);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(dv + skv * D * np, (uint32_t)np * D * 2u);
+  const __amdgpu_buffer_rsrc_t frs = make_rsrc(dkf + skv * np, (uint32_t)np * 8u);
+  uint32_t voff[VPT];
+#pragma unroll
+  for (int x = 0; x < VPT; ++x) {
+    const int e = tid + x * kBlock;
+    voff[x] = (uint32_t)(((e >> 2) * np + (e & 3) * 8) * 2);
+  }
+  u32x4 rk[KPT], rv[VPT];
+  u32x2 rf = {0u, 0u};
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) rk[x] = __builtin_amdgcn_raw_buffer_load_b128(krs, (tid + x * kBlock) * 16, kb * D * 2, 0);
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) rv[x] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[x], kb * 2, 0);
+    if (tid < BN) rf = __builtin_amdgcn_raw_buffer_load_b64(frs, tid * 8, kb * 8, 0);
+  };
+  auto store_tile = [&](PrefillTile<D>& tl) {
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * kBlock;
+      *reinterpret_cast<u32x4*>(&tl.ks[(e * 8) / D][(e * 8) % D]) = rk[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * kBlock;
+      *reinterpret_cast<u32x4*>(&tl.vt[e >> 2][(e & 3) * 8]) = rv[x];
+    }
+    if (tid < BN) {
+      tl.alpha[tid] = __uint_as_float(rf.x);
+      const float r = __uint_as_float(rf.y);
+      const uint16_t hi = tr_f32_to_bf16(r);
+      const uint16_t lo = tr_f32_to_bf16(r - tr_bf16_lo(hi));
+      *reinterpret_cast<uint4*>(&tl.ks[tid][D]) = make_uint4((uint32_t)hi | ((uint32_t)hi << 16), lo, 0, 0);
+    }
+  };
+  // The first tile's loads go out before the query rows', so the two round trips overlap.
+  if (ntiles > 0) load_tile(kb0);
+
   const int ri = r0 + wave * 32 + n;
   const bool row_ok = ri < rend;
   const int i = row_ok ? rows[(int64_t)sh * c.N + ri] : 0;
@@ -542,12 +589,13 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
   bf16x8 qz;
   {
     const uint16_t hi = tr_f32_to_bf16(qsum);
-    const uint16_t lo = tr_f32_to_bf16(qsum - tr_bf16_lo(hi));
-    const uint4 w = g == 0 ? make_uint4((uint32_t)hi | ((uint32_t)lo << 16), hi, 0, 0) : make_uint4(0, 0, 0, 0);
+    const uint16_t lo2 = tr_f32_to_bf16(qsum - tr_bf16_lo(hi));
+    const uint4 w = g == 0 ? make_uint4((uint32_t)hi | ((uint32_t)lo2 << 16), hi, 0, 0) : make_uint4(0, 0, 0, 0);
     qz = __builtin_bit_cast(bf16x8, w);
   }
 
-  // Wave and workgroup key-position ranges.
+  // The wave's key-position range: [wlo, whi) holds every visible key of its rows; tiles at or
+  // below tmin are causal for all of them, tiles at or above lomax inside every window.
   int wlo = lo, whi = row_ok ? t + 1 : -1, tmin = row_ok ? t : 0x7fffffff, lomax = row_ok ? lo : -1;
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) {
@@ -556,199 +604,134 @@ __global__ __launch_bounds__(kBlock * G) __attribute__((amdgpu_waves_per_eu(D ==
     tmin = min(tmin, __shfl_xor(tmin, o, 64));
     lomax = max(lomax, __shfl_xor(lomax, o, 64));
   }
-  if (lane == 0 && grp == 0) {
-    sm.wrange[wave][0] = wlo;
-    sm.wrange[wave][1] = whi;
-    sm.wrange[wave][2] = tmin;
-    sm.wrange[wave][3] = lomax;
-  }
-  __syncthreads();
-  int blo = 0x7fffffff, bhi = -1;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    blo = min(blo, sm.wrange[w][0]);
-    bhi = max(bhi, sm.wrange[w][1]);
-  }
+  wlo = __builtin_amdgcn_readfirstlane(wlo);
+  whi = __builtin_amdgcn_readfirstlane(whi);
+  tmin = __builtin_amdgcn_readfirstlane(tmin);
+  lomax = __builtin_amdgcn_readfirstlane(lomax);
   const bool wave_live = whi > 0;
-  (void)blo;
-  (void)bhi;
-  const int kb0 = kt0 * BN;                        // this unit's key tiles [kt0, kt1)
-  const int ntiles = kt1 - kt0;
-
-  // Staging: thread -> K row (tid / 8), 16-byte piece (tid % 8); V^T row (tid / 4), piece
-  // (tid % 4); for D = 128 every thread moves two pieces of each.
-  const uint16_t* kbase = dk + skv * np * D;
-  const uint16_t* vbase = dv + skv * D * np;
-  const float2* fbase = dkf + skv * np;
-  uint4 rk[KPT], rv[VPT];
-  float2 rf = make_float2(0.0f, 0.0f);
-  auto load_tile = [&](int kb) {
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * kBlock;                  // 16-byte piece index in the K tile
-      rk[x] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(kb + (e * 8) / D) * D + (e * 8) % D);
-    }
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * kBlock;
-      rv[x] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(e >> 2) * np + kb + (e & 3) * 8);
-    }
-    if (tid < BN) rf = fbase[kb + tid];
-  };
-  auto store_tile = [&](PrefillTile<D>& tl) {
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * kBlock;
-      *reinterpret_cast<uint4*>(&tl.ks[(e * 8) / D][(e * 8) % D]) = rk[x];
-    }
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * kBlock;
-      *reinterpret_cast<uint4*>(&tl.vt[e >> 2][(e & 3) * 8]) = rv[x];
-    }
-    if (tid < BN) {
-      tl.alpha[tid] = rf.x;
-      const uint16_t hi = tr_f32_to_bf16(rf.y);
-      const uint16_t lo = tr_f32_to_bf16(rf.y - tr_bf16_lo(hi));
-      *reinterpret_cast<uint4*>(&tl.ks[tid][D]) = make_uint4((uint32_t)hi | ((uint32_t)hi << 16), lo, 0, 0);
-    }
-  };
 
   f32x16 o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mt][r] = 0.0f;
-  float mref = -INFINITY, lsum = 0.0f;
+  // Running reference m_ref of the row (log2 domain), with nm = -m_ref (0 before the row's first
+  // visible key) and the threshold that triggers a rescale: any visible key before the first
+  // one, then a tile maximum more than kRescale above m_ref.
+  float mref = -INFINITY, lsum = 0.0f, nm = 0.0f, thr = -INFINITY;
 
-  // Group grp handles key tiles grp, grp + G, grp + 2G, ...; every group runs the same number
-  // of rounds so the block barrier stays uniform.
-  const int rounds = (ntiles + G - 1) / G;
-  if (grp < ntiles) load_tile(kb0 + grp * BN);
-  if (grp < ntiles) store_tile(sm.tile[grp][0]);
-  if (grp + G < ntiles) load_tile(kb0 + (grp + G) * BN);
-  __syncthreads();
-
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int it = rd * G + grp;
-    const PrefillTile<D>& tl = sm.tile[grp][rd & 1];
-    const int kb = kb0 + it * BN;
-    // ---- compute tile it (waves outside their windows skip it) ----
-    if (it < ntiles && wave_live && kb < whi && kb + BN - 1 >= wlo) {
-      // S = q . c + r * sum(q) (the zero-point k-step first, on a zero accumulator); then
-      // x = score - mref = alpha * S - mref, one FMA per score.
-      const float nm = (mref == -INFINITY) ? 0.0f : -mref;
-      f32x16 sacc = {};
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&tl.ks[n][D]), qz, sacc, 0, 0, 0);
+  auto compute = [&](const PrefillTile<D>& tl, int kb) {
+    // S = q . c + r * sum(q) (the zero-point k-step first, on a zero accumulator); then
+    // x = score - mref = alpha * S - mref, one FMA per score.
+    f32x16 sacc = {};
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&tl.ks[n][D]), qz, sacc, 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&tl.ks[n][16 * ks + 8 * g]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
-      }
-      // Only tiles that cross a row's window edge are masked (a wave-uniform choice between two
-      // versions): key kb + 4g + off (off = 8 * r4 + x) is visible iff lo <= key <= t, i.e. iff
-      // (unsigned)(off - dlo) <= (unsigned)(t - lo) with dlo = lo - kb - 4g.
-      float sv[16];
-      float tmax = -INFINITY;
-      auto scores = [&](auto masked) {
-        const int dlo = row_ok ? lo - kb - 4 * g : 0x40000000;   // rows past the tile's end: all masked
-        const uint32_t span = row_ok ? (uint32_t)(t - lo) : 0u;
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&tl.ks[n][16 * ks + 8 * g]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc, 0, 0, 0);
+    }
+    // Lane (n, g) holds keys kb + 4g + off, off = 8 * r4 + x.  Only tiles that cross a row's window
+    // edge are masked, each with the cheapest test that suffices (a wave-uniform choice): key
+    // visible iff off <= t - kb - 4g (causal edge) and off >= lo - kb - 4g (window's left edge).
+    float sv[16];
+    auto scores = [&](auto mask) {
+      constexpr int M = decltype(mask)::value;     // 0 none, 1 causal edge, 2 left edge, 3 both
+      const int dt = row_ok ? t - kb - 4 * g : -1;                // rows past the tile's end: all masked
+      const int dl = row_ok ? lo - kb - 4 * g : 0x40000000;
+      const uint32_t span = row_ok ? (uint32_t)(t - lo) : 0u;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[8 * r4 + 4 * g]);
-          const float alv[4] = {al.x, al.y, al.z, al.w};
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 al = *reinterpret_cast<const float4*>(&tl.alpha[8 * r4 + 4 * g]);
+        const float alv[4] = {al.x, al.y, al.z, al.w};
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            float v = fmaf(alv[x], sacc[4 * r4 + x], nm);
-            if constexpr (decltype(masked)::value) {
-              if ((uint32_t)(8 * r4 + x - dlo) > span) v = -INFINITY;
-            }
-            sv[4 * r4 + x] = v;
+        for (int x = 0; x < 4; ++x) {
+          const int off = 8 * r4 + x;
+          float v = fmaf(alv[x], sacc[4 * r4 + x], nm);
+          if constexpr (M == 1) {
+            if (off > dt) v = -INFINITY;
+          } else if constexpr (M == 2) {
+            if (off < dl) v = -INFINITY;
+          } else if constexpr (M == 3) {
+            if ((uint32_t)(off - dl) > span) v = -INFINITY;
           }
+          sv[4 * r4 + x] = v;
         }
-      };
-      if (!(kb + BN - 1 <= tmin && kb >= lomax)) scores(std::true_type());
-      else scores(std::false_type());
+      }
+    };
+    const bool cross_t = kb + BN - 1 > tmin, cross_lo = kb < lomax;
+    if (!cross_t && !cross_lo) scores(std::integral_constant<int, 0>());
+    else scores(std::integral_constant<int, 3>());
+    float tmax = tr_max(sv[0], sv[1]);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) tmax = tr_max(tmax, tr_max(sv[r], sv[r + 1]));   // v_maximum3, no quieting
-      tmax = xor32_max(tmax);
-      // Lazy rescale: x is relative to the running reference mref; it moves only when some
-      // row's maximum exceeds it by more than kRescale (so p <= 2^kRescale in fp16), or on the
-      // first visible key of a row.
-      const bool first = (mref == -INFINITY);
-      const bool need = first ? (tmax > -INFINITY) : (tmax > kRescale);
-      if (__any(need)) {
-        const float shift = first ? ((tmax > -INFINITY) ? tmax : 0.0f) : fmaxf(tmax, 0.0f);
-        const float corr = first ? 0.0f : exp2f(-shift);
+    for (int r = 2; r < 16; r += 2) tmax = tr_max(tmax, tr_max(sv[r], sv[r + 1]));   // v_maximum3, no quieting
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = tr_max(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // Lazy rescale: x is relative to the running reference mref; it moves only when some
+    // row's maximum exceeds it by more than kRescale (so p <= 2^kRescale in fp16), or on the
+    // first visible key of a row.
+    if (__any(tmax > thr)) {
+      // Rows past their threshold move the reference to the tile maximum (a row's first visible
+      // keys set it); the others keep theirs.  O and the sum need scaling only in rows that
+      // already hold weight, and that part is skipped when no row of the wave does.
+      const bool move = tmax > thr, first = (mref == -INFINITY);
+      const float shift = move ? tmax : 0.0f;
+      if (__any(move && !first)) {
+        const float corr = first ? 1.0f : exp2f(-shift);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[mt][r] *= corr;
         lsum *= corr;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] -= shift;
-        if (!first) mref += shift;
-        else if (tmax > -INFINITY) mref = tmax;
-      }
-      // p in fp16 (the PV operand); the row sum adds those same fp16 weights, two per v_dot2 with
-      // an fp32 accumulator, so numerator and denominator use identical weights.
-      f16x8 pk[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pk[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(sv[r]);
-      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const f16x2 pp = {pk[r >> 3][r & 7], pk[r >> 3][(r & 7) + 1]};
-        lsum = __builtin_amdgcn_fdot2(pp, one2, lsum, false);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int r = 0; r < 16; ++r) sv[r] -= shift;
+      if (move) mref = first ? tmax : mref + tmax;
+      const bool none = (mref == -INFINITY);
+      nm = none ? 0.0f : -mref;
+      thr = none ? -INFINITY : kRescale;
+    }
+    // p in fp16 (the PV operand); the row sum adds those same fp16 weights, two per v_dot2 with
+    // an fp32 accumulator, so numerator and denominator use identical weights.
+    f16x8 pk[2];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const f16x8 av = *reinterpret_cast<const f16x8*>(&tl.vt[32 * mt + n][16 * kh + 8 * g]);
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kh], o[mt], 0, 0, 0);
-        }
+    for (int r = 0; r < 16; ++r) pk[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(sv[r]);
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const f16x2 pp = {pk[r >> 3][r & 7], pk[r >> 3][(r & 7) + 1]};
+      lsum = __builtin_amdgcn_fdot2(pp, one2, lsum, false);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const f16x8 av = *reinterpret_cast<const f16x8*>(&tl.vt[32 * mt + n][16 * kh + 8 * g]);
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kh], o[mt], 0, 0, 0);
       }
     }
-    // ---- stage this group's next tile into its other buffer, issue loads for the one after ----
-    if (it + G < ntiles) store_tile(sm.tile[grp][(rd + 1) & 1]);
-    if (it + 2 * G < ntiles) load_tile(kb0 + (it + 2 * G) * BN);
+  };
+
+  if (ntiles > 0) store_tile(sm.tile[0]);
+  if (ntiles > 1) load_tile(kb0 + BN);
+  __syncthreads();
+  // Key tile it sits in buffer it & 1; the loop is unrolled by two so that every LDS address is
+  // a loop-invariant base plus a constant.  While tile it is computed, tile it + 1 (loaded one
+  // step earlier) goes into the other buffer and the loads of tile it + 2 are issued.
+  auto step = [&](int it, auto buf) {
+    constexpr int b = decltype(buf)::value;
+    const int kb = kb0 + it * BN;
+    if (wave_live && kb < whi && kb + BN - 1 >= wlo) compute(sm.tile[b], kb);
+    if (it + 1 < ntiles) store_tile(sm.tile[b ^ 1]);
+    if (it + 2 < ntiles) load_tile(kb + 2 * BN);
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, std::integral_constant<int, 0>());
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>());
   }
-  // ---- merge the groups' (mref, lsum, O) -- same (row, channel) mapping in every group ----
-  if constexpr (G > 1) {
-    float* st = reinterpret_cast<float*>(&sm.tile[0][0]);   // tile buffers are free now
-    constexpr int NS = MT * 16 + 2;
-    static_assert(sizeof(PrefillTile<D>) * 2 * G >= sizeof(float) * NS * kBlock * (G > 1 ? 1 : 0), "merge space");
-    for (int src = G - 1; src >= 1; --src) {
-      if (grp == src) {
-        float* my = st + tid * NS;
-        my[0] = mref;
-        my[1] = lsum;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) my[2 + mt * 16 + r] = o[mt][r];
-      }
-      __syncthreads();
-      if (grp == 0) {
-        const float* ot = st + tid * NS;
-        const float m2 = ot[0];
-        const float mnew = fmaxf(mref, m2);
-        const float a1 = (mref == -INFINITY) ? 0.0f : exp2f(mref - mnew);
-        const float a2 = (m2 == -INFINITY) ? 0.0f : exp2f(m2 - mnew);
-        lsum = lsum * a1 + ot[1] * a2;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[mt][r] = o[mt][r] * a1 + ot[2 + mt * 16 + r] * a2;
-        mref = mnew;
-      }
-      __syncthreads();
-    }
-  }
-  if (grp != 0) return;
   const float ltot = xor32_sum(lsum);
   if (!row_ok) return;
   if (slot >= 0) {
@@ -903,7 +886,7 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
     TR_LAUNCH_CHECK();
   }
   TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
-  hipLaunchKernelGGL((k_prefill_attn<D, TR_PREFILL_GROUPS>), dim3(BQ * uph), dim3(kBlock * TR_PREFILL_GROUPS), 0,
+  hipLaunchKernelGGL(k_prefill_attn<D>, dim3(BQ * uph), dim3(kBlock), 0,
                      stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
                      c->dkf, c->pf_part, out, c->hq, c->grp);
   TR_LAUNCH_CHECK();

@@ -53,6 +53,8 @@ def test_host_side_validation_without_gpu():
     assert _alloc(ctypes.byref(bad_dim), ctypes.byref(h)) == 5 and h.value is None
     bad_page = _Desc(1, 1, 1, 64, 16, 3000, 0)
     assert _alloc(ctypes.byref(bad_page), ctypes.byref(h)) == 1
+    too_long = _Desc(1, 1, 1, 128, (1 << 23), 0, 0)          # staging offsets need < 2^31 bytes
+    assert _alloc(ctypes.byref(too_long), ctypes.byref(h)) == 5 and h.value is None
     zero_layers = _Desc(0, 1, 1, 64, 16, 0, 0)
     assert _alloc(ctypes.byref(zero_layers), ctypes.byref(h)) == 1
     assert _free(None) == 0
