@@ -128,14 +128,16 @@ __device__ __forceinline__ uint16_t tr_f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave (called with all 64 lanes active).
 __device__ __forceinline__ uint32_t tr_wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
+  // DPP: shifts by 1, 2, 4, 8 inside each row of 16 lanes (lanes before the shift read 0), then
+  // each row adds the total of the rows before it through the row_bcast:15 / row_bcast:31 moves.
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // rows 1, 3 += rows 0, 2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // rows 2, 3 += rows 0-1
   return v;
 }
 

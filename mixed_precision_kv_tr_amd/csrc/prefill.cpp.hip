@@ -7,9 +7,9 @@
 //   compaction, attention and merge are per query head.
 // k_prefill_prep (one workgroup per (seq, query head), plus one per sequence for the slot
 //   assignment of the call's positions): stable partition of the T query rows by mode -- full
-//   rows, then local rows -- so that a 128-row tile holds one mode and its key range is tight;
-//   skip rows (and rows with an invalid mode) get zeros right here.  Then the attention work
-//   units of the (seq, query head).
+//   rows, then local rows, then skip rows (and rows with an invalid mode) -- so that a 128-row
+//   tile holds one mode and its key range is tight.  Then the attention work units of the
+//   (seq, query head).
 // Dense staging: the cache range the call's queries read, staged once in position order: K as
 //   its code in bf16 (an exact integer <= 255, or the stored bf16 for b = 16) with per-key
 //   (alpha, r) = (s_K * log2(e)/sqrt(D), z_K / s_K); V as v_hat = s * c + z (fp32) rounded to
@@ -19,8 +19,9 @@
 //   own K/V into the pages and stages them from registers; k_prefill_dense stages the tiles
 //   holding earlier calls' positions from the pages.
 // k_prefill_attn (one workgroup = 4 waves = one 128-row tile), per 32-key tile:
-//     staging   16-byte copies of K rows and V^T rows into double-buffered LDS, the next
-//               tile's copies in flight in registers while the current one is computed.
+//     staging   16-byte buffer loads of K rows and V^T rows (the tile offset in a scalar
+//               register) into double-buffered LDS, the next tile's loads in flight in
+//               registers while the current one is computed.
 //     QK^T      S^T[32 keys x 32 queries] per wave = v_mfma_f32_32x32x16_bf16 over D/16 steps
 //               on the exact codes, plus one k-step that adds r * sum(q) (r and sum(q) as bf16
 //               hi + lo pairs); the exponent is then alpha * S - m_ref, one FMA per score.
@@ -34,6 +35,7 @@
 //               own scores; the dense V^T rows store keys in the S^T accumulator's order
 //               (vt_pos), so each V^T operand is one 16-byte LDS read.
 //   epilogue  O / l -> bf16, scattered back to the rows' original positions.
+// k_prefill_merge combines the chunks of split tiles and writes the zeros of the skip rows.
 #include <math.h>
 #include <stdint.h>
 
@@ -75,16 +77,19 @@ __device__ __forceinline__ float xor32_sum(float v) {
 //   merge = (r0, rend, first slot, chunks)
 // Units are listed heaviest first: full tiles from the last (longest key range), then local.
 // Sum over the 64 lanes of a wave (the result in every lane).
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane((int)tr_wave_incl_scan((uint32_t)v), 63); }
+
+// Row tiles whose first and last positions the compaction leaves in LDS; calls with more row
+// tiles read them back from the compacted row list instead.
+#ifndef TR_PREFILL_TILE_CAP
+#define TR_PREFILL_TILE_CAP 512
+#endif
+constexpr int kTileCap = TR_PREFILL_TILE_CAP;
 
 // Run by one wave (the other waves of the workgroup do not take part): tiles in chunks of 64, one
 // per lane, with wave-level sums and scans only -- no workgroup barriers.
 __device__ __forceinline__ void build_units(int sh, int p0, int window, int nfull, int nl, const int32_t* rl,
-                                            int32_t* counts, int4* units, int4* merges) {
+                                            const int32_t* tpos, int32_t* counts, int4* units, int4* merges) {
   constexpr int NC = 8;                            // candidate chunk sizes 16 << j key tiles
   const int lane = threadIdx.x & 63;
   const int nft = (nfull + BM - 1) / BM, nlt = (nl + BM - 1) / BM, ntl = nft + nlt;
@@ -93,7 +98,11 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
     const int ft = nft - 1 - k;                    // full tiles from the last
     r0 = full ? ft * BM : nfull + (k - nft) * BM;
     rend = full ? min(r0 + BM, nfull) : min(r0 + BM, nfull + nl);
-    const int tmin = p0 + rl[r0], tmax = p0 + rl[rend - 1];   // rows are in position order
+    // rows are in position order; row tile idx (full tiles in row order, then local) has its
+    // first and last positions at tpos[2 idx], tpos[2 idx + 1]
+    const int idx = full ? ft : k;
+    const bool lds = ntl <= kTileCap;
+    const int tmin = p0 + (lds ? tpos[2 * idx] : rl[r0]), tmax = p0 + (lds ? tpos[2 * idx + 1] : rl[rend - 1]);
     const int blo = full ? 0 : max(0, tmin - window);
     klo = blo >> 5;
     khi = (tmax + 1 + 31) >> 5;
@@ -158,9 +167,10 @@ template <int D, int NT>
 __device__ __forceinline__ void compact_rows(const CacheLayout& c, int HQ, int sh, int p0, int T, int window,
                                              const uint8_t* __restrict__ mode, int32_t* __restrict__ rows,
                                              int32_t* __restrict__ counts, int4* __restrict__ units,
-                                             int4* __restrict__ merges, int uph, uint16_t* __restrict__ out) {
+                                             int4* __restrict__ merges, int uph) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t wf[NW], wl[NW];
+  __shared__ int32_t tpos[2 * kTileCap];           // first / last position of each row tile
   const int s = sh / HQ, h = sh % HQ;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int32_t* rl = rows + (int64_t)sh * c.N;
@@ -206,6 +216,16 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int HQ, int s
     tl += wl[w];
   }
   const int nfull = (int)tf, nl = (int)tl;
+  const int nft = (nfull + BM - 1) / BM, ntl = nft + (nl + BM - 1) / BM;
+  // row d of a mode's list ends or starts a row tile: its position goes to the tile's LDS slots
+  auto mark = [&](int d, int nmode, int tile0, int i) {
+    const int idx = tile0 + d / BM;
+    if (idx < kTileCap) {
+      if (d % BM == 0) tpos[2 * idx] = i;
+      if (d % BM == BM - 1 || d == nmode - 1) tpos[2 * idx + 1] = i;
+    }
+  };
+  uint32_t bs = (uint32_t)i0 - bf - bl;            // skip rows before this thread's
   for (int r0 = 0; r0 < R; r0 += 4) {
     uint32_t m[4];
     if (cached) {
@@ -219,21 +239,22 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int HQ, int s
       const int i = i0 + r0 + u;
       if (i >= i1) break;
       if (m[u] == TR_MODE_FULL) {
+        mark((int)bf, nfull, 0, i);
         rl[bf++] = i;
       } else if (m[u] == TR_MODE_LOCAL) {
+        mark((int)bl, nl, nft, i);
         rl[nfull + bl++] = i;
       } else {
         if (m[u] == 3u) atomicOr(c.err, TR_ERRF_BAD_MODE);
-        uint4* o = reinterpret_cast<uint4*>(out + (((int64_t)s * T + i) * HQ + h) * D);
-#pragma unroll
-        for (int x = 0; x < D / 8; ++x) o[x] = make_uint4(0, 0, 0, 0);
+        rl[nfull + nl + bs++] = i;                   // skip rows: zeroed by k_prefill_merge
       }
     }
   }
-  __threadfence_block();
+  if (ntl > kTileCap) __threadfence_block();      // the unit list then reads the row list back
   __syncthreads();
   if (wave == 0)
-    build_units(sh, p0, window, nfull, nl, rl, counts, units + (int64_t)sh * uph, merges + (int64_t)sh * (kSlotsPerHead / 2));
+    build_units(sh, p0, window, nfull, nl, rl, tpos, counts, units + (int64_t)sh * uph,
+                merges + (int64_t)sh * (kSlotsPerHead / 2));
 }
 
 // Preparation of a prefill call, one launch: workgroups [0, B*HQ) compact the query rows of one
@@ -246,13 +267,13 @@ __global__ __launch_bounds__(TR_ASSIGN_THREADS) void k_prefill_prep(CacheLayout 
                                                                     int window, const uint8_t* __restrict__ mode,
                                                                     const uint8_t* __restrict__ bits, int32_t* rows,
                                                                     int32_t* counts, int4* units, int4* merges,
-                                                                    int uph, uint16_t* __restrict__ out, int HQ) {
+                                                                    int uph, int HQ) {
   const int BH = c.B * HQ;
   if ((int)blockIdx.x >= BH) {
     tr_assign_slots_seq(c, layer, p0, T, bits, blockIdx.x - BH);
     return;
   }
-  compact_rows<D, TR_ASSIGN_THREADS>(c, HQ, blockIdx.x, p0, T, window, mode, rows, counts, units, merges, uph, out);
+  compact_rows<D, TR_ASSIGN_THREADS>(c, HQ, blockIdx.x, p0, T, window, mode, rows, counts, units, merges, uph);
 }
 
 
@@ -779,12 +800,22 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
   constexpr int64_t SLOT = (int64_t)BM * (D + 4);
   const int BH = c.B * HQ;
   const int mi = blockIdx.x / BH, sh = blockIdx.x % BH;
+  const int s = sh / HQ, h = sh % HQ;
+  {
+    // The head's skip rows (listed after its full and local rows) get their zeros here: whole
+    // 2D-byte output rows per group of D / 8 threads, the list split over the head's workgroups.
+    constexpr int TPZ = D / 8, RPI = kBlock / TPZ;
+    const int nfull = counts[sh * 4 + 0], nl = counts[sh * 4 + 1], nskip = T - nfull - nl;
+    const int per = (nskip + MPH - 1) / MPH, k1 = min(nskip, (mi + 1) * per);
+    const int32_t* sl = rows + (int64_t)sh * c.N + nfull + nl;
+    for (int k = mi * per + (int)threadIdx.x / TPZ; k < k1; k += RPI)
+      reinterpret_cast<uint4*>(out + (((int64_t)s * T + sl[k]) * HQ + h) * D)[threadIdx.x % TPZ] = make_uint4(0, 0, 0, 0);
+  }
   if (mi >= counts[sh * 4 + 3]) return;
   const int4 mg = merges[(int64_t)sh * MPH + mi];
   const int r = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * CPT;
   const int ri = mg.x + r;
   if (ri >= mg.y) return;
-  const int s = sh / HQ, h = sh % HQ;
   const float* base = part + ((int64_t)sh * kSlotsPerHead + mg.z) * SLOT + (int64_t)r * (D + 4);
   const int nch = mg.w;
   float M = -INFINITY, den = 0.0f;
@@ -871,7 +902,7 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   {
     TrProfScope prof(c, TR_PROF_PREFILL_COMPACT, stream);
     hipLaunchKernelGGL(k_prefill_prep<D>, dim3(BQ + (fused ? L.B : 0)), dim3(TR_ASSIGN_THREADS), 0, stream, L, layer,
-                       p0, T, window, mode, bits, c->rows, c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, out, c->hq);
+                       p0, T, window, mode, bits, c->rows, c->row_counts, c->pf_units, c->pf_merges, c->pf_uph, c->hq);
     TR_LAUNCH_CHECK();
   }
   if (fused) {
