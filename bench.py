@@ -68,23 +68,23 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # reports traffic as null.
 TRAFFIC = {
     "k_decode": {
-        "fetch_kib": 167572.4, "write_kib": 2114.2, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 167570.6, "write_kib": 2114.2, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip":
                 "d61fb6b9a8536951583f825b6160ac7bfcf98292881966a81d8f15cb44a56359",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "ead09419937d13832f7e633562703695f9b970a67b2794f977bf7e66bc5ab634",
+                "54b76045567d72dcfd23ee7a5c6a52177cf05f1138eee2e357d1e32cabb42231",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
                 "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
     "k_prefill_attn": {
-        "fetch_kib": 19379.3, "write_kib": 19044.9, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 19358.5, "write_kib": 19047.9, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip":
-                "505d3639b36e7792700f111a214190b20e959000b7f677194872870ba163ac5c",
+                "e00c74bcde92fc1b6b35a2dd829e940a11f1c17f98bdbdf6729a977c0106b69c",
             "mixed_precision_kv_tr_amd/csrc/kv_write.h":
                 "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
             "mixed_precision_kv_tr_amd/csrc/common.h":
-                "ead09419937d13832f7e633562703695f9b970a67b2794f977bf7e66bc5ab634",
+                "54b76045567d72dcfd23ee7a5c6a52177cf05f1138eee2e357d1e32cabb42231",
             "mixed_precision_kv_tr_amd/csrc/layout.h":
                 "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
 }

@@ -146,9 +146,9 @@ int64_t tr_kv_cache_pages_used(tr_kv_cache* cache, void* stream);
  * the number of launches and their summed duration in milliseconds since the last read, and
  * clears the record.  Families (array index): 0 quantize-write (slot assignment + quantize),
  * 1 decode split-K, 2 decode combine, 3 prefill preparation (row compaction, work units, the
- * slot assignment of a prefill call, and dense staging of earlier positions), 4 prefill attention
- * (with the merge of key-split tiles).
- * launches and total_ms are HOST arrays of 5 elements. */
+ * slot assignment of a prefill call, and dense staging of earlier positions), 4 prefill attention,
+ * 5 prefill merge of key-split tiles (and the zeros of skip rows).
+ * launches and total_ms are HOST arrays of 6 elements. */
 tr_status tr_profile_enable(tr_kv_cache* cache, int32_t enable);
 tr_status tr_profile_read(tr_kv_cache* cache, int64_t* launches, double* total_ms);
 

@@ -66,7 +66,7 @@ _moe_set = _sig("tr_moe_set_weights", ctypes.c_int, _vp, _vp, _vp, _vp, _vp)
 _moe_ffn = _sig("tr_moe_ffn", ctypes.c_int, _vp, _vp, _vp, _i32, _vp, _vp)
 _prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
 _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
-PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn")
+PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn", "prefill_merge")
 
 STATUS_NAMES = {0: "TR_OK", 1: "TR_ERR_INVALID_ARG", 2: "TR_ERR_CAPACITY", 3: "TR_ERR_OUT_OF_PAGES",
                 4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE"}
@@ -257,7 +257,7 @@ def tr_profile_enable(cache: KVCache, enable: bool = True):
 
 def tr_profile_read(cache: KVCache) -> dict:
     """{family: (launches, total_ms)} since the last read (synchronizes)."""
-    n = (_i64 * 5)()
-    ms = (ctypes.c_double * 5)()
+    n = (_i64 * len(PROFILE_FAMILIES))()
+    ms = (ctypes.c_double * len(PROFILE_FAMILIES))()
     _check(_prof_read(cache.handle, n, ms), "tr_profile_read")
     return {name: (int(n[i]), float(ms[i])) for i, name in enumerate(PROFILE_FAMILIES)}

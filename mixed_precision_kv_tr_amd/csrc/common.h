@@ -83,7 +83,7 @@ inline int tr_xcd_grid(int n) { return ((n + 7) >> 3) << 3; }
 
 // Kernel families reported by tr_profile_read.
 enum { TR_PROF_WRITE = 0, TR_PROF_DECODE_SPLIT = 1, TR_PROF_DECODE_COMBINE = 2, TR_PROF_PREFILL_COMPACT = 3,
-       TR_PROF_PREFILL_ATTN = 4, TR_PROF_NFAM = 5 };
+       TR_PROF_PREFILL_ATTN = 4, TR_PROF_PREFILL_MERGE = 5, TR_PROF_NFAM = 6 };
 
 // Brackets the kernel launches of its scope with events when timing is on.
 struct TrProfScope {
@@ -98,7 +98,9 @@ struct TrProfScope {
       return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // No system-scope fence: the events only timestamp the stream, and a fence would add the
+    // write-back of the kernel's dirty L2 lines to the measured interval.
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
   }
   TrProfScope(tr_kv_cache* c_, int fam_, hipStream_t st_) : c(c_), fam(fam_), st(st_) {

@@ -916,11 +916,14 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
                        c->np, kscale, c->dk, c->dv, c->dkf);
     TR_LAUNCH_CHECK();
   }
-  TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
-  hipLaunchKernelGGL(k_prefill_attn<D>, dim3(BQ * uph), dim3(kBlock), 0,
-                     stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
-                     c->dkf, c->pf_part, out, c->hq, c->grp);
-  TR_LAUNCH_CHECK();
+  {
+    TrProfScope prof(c, TR_PROF_PREFILL_ATTN, stream);
+    hipLaunchKernelGGL(k_prefill_attn<D>, dim3(BQ * uph), dim3(kBlock), 0,
+                       stream, L, p0, T, window, c->np, q, c->rows, c->row_counts, c->pf_units, c->pf_uph, c->dk, c->dv,
+                       c->dkf, c->pf_part, out, c->hq, c->grp);
+    TR_LAUNCH_CHECK();
+  }
+  TrProfScope prof(c, TR_PROF_PREFILL_MERGE, stream);
   hipLaunchKernelGGL(k_prefill_merge<D>, dim3(BQ * (kSlotsPerHead / 2)), dim3(kBlock), 0, stream, L, T, c->rows,
                      c->row_counts, c->pf_merges, c->pf_part, out, c->hq);
   TR_LAUNCH_CHECK();
