@@ -207,3 +207,25 @@ def test_prefill_baseline_variants(tr, variant):
     cache.close()
     assert status == 0
     check(case, out, 60, range(2), variant)
+
+
+def test_prefill_long_prompt_sampled(tr):
+    """An 80000-token prompt: more row tiles than the compaction keeps in LDS (512), so the unit
+    list reads the tile bounds back from the row list, and full rows attend up to 80000 keys.
+    Checked on sampled query rows (the oracle attends only those) and every skip row."""
+    T, W = 80000, 512
+    say(f"prefill long prompt T={T}")
+    case = random_case(1, T, 1, 64, window=W, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.1, "local": 0.45, "full": 0.45}, seed=80, device="cuda")
+    cache, out, status = run_prefill(tr, case, W)
+    cache.close()
+    assert status == 0
+    mode = case["mode"].cpu().numpy()[0, :, 0]
+    rng = np.random.default_rng(5)
+    pos = np.unique(np.concatenate([[0, 1, 127, 128, T - 2, T - 1], rng.integers(0, T, 40)]))
+    ref = oracle.attend_cached(u16(case["q"])[0, pos], u16(case["k"])[0], u16(case["v"])[0],
+                               case["bits"].cpu().numpy()[0], mode[pos][:, None], pos, W)["out"]
+    got = bf16_to_f64(out)[0]
+    compare_out(got[pos], ref, f"T={T} sampled rows")
+    skip = np.nonzero(mode == 0)[0]
+    assert np.all(got[skip] == 0.0)
