@@ -19,7 +19,9 @@
 // Weight matrices are packed once (tr_moe_set_weights) into the operand order of the matrix-core
 // k-loop: for k-step s = 4 g + j and output unit n, 16 bf16 holding input channels 64 g + 8 j ..
 // + 7 and 64 g + 32 + 8 j .. + 7, so that the 32 units of a wave read one contiguous 1 KB per
-// k-step and a lane reads 64 contiguous bytes of its activation row per group of 4 k-steps.
+// k-step.  The gathered activation rows of a tile are shared by its four waves: each stage of
+// k-steps is loaded once per workgroup into double-buffered LDS (16-byte-padded rows), while each
+// wave's weight columns come straight from memory into registers, the next stage in flight.
 #include <math.h>
 #include <stdint.h>
 
@@ -204,46 +206,59 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
   __syncthreads();
   const int r = lane & 31, kh = lane >> 5;
   const int n = blockIdx.y * kUnits + 32 * wave + r;  // hidden unit of this lane's B column
-  const uint16_t* xr[kMB];
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) xr[mb] = x + (int64_t)tok[32 * mb + r] * d + 32 * kh;
+  // The tile's token rows are shared by the four waves: each stage of kPS k-steps (kPS * 16
+  // channels of every row) is loaded once per workgroup, one 16-byte piece per thread, into a
+  // double-buffered LDS tile whose 16-byte-padded rows spread over the banks.  Each wave's own
+  // weight columns stay in registers, the next stage's in flight.
+  constexpr int kPS = 4 / kMB;                      // k-steps per stage
+  constexpr int PR = 2 * kPS;                       // 16-byte pieces per row and stage
+  static_assert(kTile * PR == 256, "one piece per thread per stage");
+  __shared__ uint4 xs[2][kTile][PR + 1];
+  const int prow = tid / PR, pp = tid % PR;        // this thread's piece of each stage
+  const uint16_t* xrow = x + (int64_t)tok[prow] * d + 32 * (pp & 1);
+  auto xaddr = [&](int st) {                        // piece pp of stage st: k-step st + pp / 2, half pp & 1
+    const int s = st + (pp >> 1);
+    return xrow + 64 * (s >> 2) + 8 * (s & 3);
+  };
   const int64_t mat = (int64_t)de * d, wstep = (int64_t)de * 16;
   const uint16_t* gr = wg + (e - 1) * mat + (int64_t)n * 16 + 8 * kh;
   const uint16_t* ur = wu + (e - 1) * mat + (int64_t)n * 16 + 8 * kh;
   f32x16 ag[kMB] = {}, au[kMB] = {};
   const int ns = d / 16;                          // a multiple of 8
-  // kPS k-steps per stage, the next stage in flight; each weight load feeds kMB token blocks
-  constexpr int kPS = 4 / kMB;
-  uint4 xa[kPS][kMB], ga[kPS], ua[kPS];
-  auto load = [&](int st, uint4 (&xv)[kPS][kMB], uint4 (&gv)[kPS], uint4 (&uv)[kPS]) {
+  uint4 ga[kPS], ua[kPS];
+  auto wload = [&](int st, uint4 (&gv)[kPS], uint4 (&uv)[kPS]) {
 #pragma unroll
     for (int q = 0; q < kPS; ++q) {
-      const int s = st + q, g = s >> 2, j = s & 3;
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) xv[q][mb] = gload16(xr[mb] + 64 * g + 8 * j);
-      gv[q] = gload16(gr + s * wstep);
-      uv[q] = gload16(ur + s * wstep);
+      gv[q] = gload16(gr + (st + q) * wstep);
+      uv[q] = gload16(ur + (st + q) * wstep);
     }
   };
-  load(0, xa, ga, ua);
+  xs[0][prow][pp] = gload16(xaddr(0));
+  wload(0, ga, ua);
+  __syncthreads();
+  int buf = 0;
   for (int st = 0; st < ns; st += kPS) {
-    uint4 xn[kPS][kMB], gn[kPS], un[kPS];
-    load(min(st + kPS, ns - kPS), xn, gn, un);    // clamped: the loads never branch
+    const int nx = min(st + kPS, ns - kPS);       // clamped: the loads never branch
+    const uint4 xn = gload16(xaddr(nx));
+    uint4 gn[kPS], un[kPS];
+    wload(nx, gn, un);
 #pragma unroll
     for (int q = 0; q < kPS; ++q) {
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
-        ag[mb] = mfma(xa[q][mb], ga[q], ag[mb]);
-        au[mb] = mfma(xa[q][mb], ua[q], au[mb]);
+        const uint4 a = xs[buf][32 * mb + r][2 * q + kh];
+        ag[mb] = mfma(a, ga[q], ag[mb]);
+        au[mb] = mfma(a, ua[q], au[mb]);
       }
     }
+    xs[buf ^ 1][prow][pp] = xn;
 #pragma unroll
     for (int q = 0; q < kPS; ++q) {
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) xa[q][mb] = xn[q][mb];
       ga[q] = gn[q];
       ua[q] = un[q];
     }
+    buf ^= 1;
+    __syncthreads();
   }
   // D[row][unit]: this lane holds unit n for rows 32 mb + 8 (reg / 4) + 4 kh + reg % 4
 #pragma unroll
@@ -285,37 +300,43 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
   const int n = blockIdx.y * kUnits + 32 * wave + r;  // output channel of this lane's B column
   f32x16 acc[kMB] = {};
   if (e > 0) {
-    const uint16_t* hr[kMB];
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) hr[mb] = hbuf + ((int64_t)tok[32 * mb + r] * k + slot) * de + 32 * kh;
+    // hidden rows shared by the four waves through LDS, as in k_moe_up
+    constexpr int kPS = 4 / kMB;
+    constexpr int PR = 2 * kPS;
+    static_assert(kTile * PR == 256, "one piece per thread per stage");
+    __shared__ uint4 hs[2][kTile][PR + 1];
+    const int prow = tid / PR, pp = tid % PR;
+    const uint16_t* hrow = hbuf + ((int64_t)tok[prow] * k + slot) * de + 32 * (pp & 1);
+    auto haddr = [&](int st) {
+      const int s = st + (pp >> 1);
+      return hrow + 64 * (s >> 2) + 8 * (s & 3);
+    };
     const int64_t wstep = (int64_t)d * 16;
     const uint16_t* dr = wd + (int64_t)(e - 1) * d * de + (int64_t)n * 16 + 8 * kh;
     const int ns = de / 16;                       // a multiple of 8
-    constexpr int kPS = 4 / kMB;
-    uint4 ha[kPS][kMB], wa[kPS];
-    auto load = [&](int st, uint4 (&hv)[kPS][kMB], uint4 (&wv)[kPS]) {
+    uint4 wa[kPS];
+    auto wload = [&](int st, uint4 (&wv)[kPS]) {
 #pragma unroll
-      for (int q = 0; q < kPS; ++q) {
-        const int s = st + q, g = s >> 2, j = s & 3;
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) hv[q][mb] = gload16(hr[mb] + 64 * g + 8 * j);
-        wv[q] = gload16(dr + s * wstep);
-      }
+      for (int q = 0; q < kPS; ++q) wv[q] = gload16(dr + (st + q) * wstep);
     };
-    load(0, ha, wa);
+    hs[0][prow][pp] = gload16(haddr(0));
+    wload(0, wa);
+    __syncthreads();
+    int buf = 0;
     for (int st = 0; st < ns; st += kPS) {
-      uint4 hn[kPS][kMB], wn[kPS];
-      load(min(st + kPS, ns - kPS), hn, wn);
+      const int nx = min(st + kPS, ns - kPS);
+      const uint4 hn = gload16(haddr(nx));
+      uint4 wn[kPS];
+      wload(nx, wn);
 #pragma unroll
       for (int q = 0; q < kPS; ++q)
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[mb] = mfma(ha[q][mb], wa[q], acc[mb]);
+        for (int mb = 0; mb < kMB; ++mb) acc[mb] = mfma(hs[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
+      hs[buf ^ 1][prow][pp] = hn;
 #pragma unroll
-      for (int q = 0; q < kPS; ++q) {
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) ha[q][mb] = hn[q][mb];
-        wa[q] = wn[q];
-      }
+      for (int q = 0; q < kPS; ++q) wa[q] = wn[q];
+      buf ^= 1;
+      __syncthreads();
     }
   }
 #pragma unroll
