@@ -225,3 +225,28 @@ def test_decode_baseline_variants(tr, variant):
     out, status = run_decode(tr, case, 100)
     assert status == 0
     check(case, out, 100, range(4), variant)
+
+
+def test_profile_families_count_the_launches(tr):
+    """tr_profile_read: one entry per kernel family, launches counted while enabled, nothing
+    recorded while disabled."""
+    case = random_case(2, 300, 4, 64, window=40, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.2, "local": 0.4, "full": 0.4}, seed=11, device="cuda")
+    cache = tr.tr_kv_cache_alloc(1, 2, 4, 64, 301)
+    out = torch.empty((2, 300, 4, 64), dtype=torch.bfloat16, device="cuda")
+    tr.tr_profile_enable(cache, True)
+    tr.tr_routed_attn_prefill(cache, 0, case["q"], case["k"], case["v"], case["bits"], case["mode"], 300, 40, out)
+    tr.tr_kv_quantize_write(cache, 0, case["k"][:, :1].contiguous(), case["v"][:, :1].contiguous(),
+                            case["bits"][:, :1].contiguous(), 1)
+    dout = torch.empty((2, 4, 64), dtype=torch.bfloat16, device="cuda")
+    tr.tr_routed_attn_decode(cache, 0, case["q"][:, 0].contiguous(), case["mode"][:, 0].contiguous(), 40, dout)
+    prof = tr.tr_profile_read(cache)
+    assert set(prof) == {"write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn", "prefill_merge"}
+    for fam in ("write", "decode_split", "prefill_prep", "prefill_attn", "prefill_merge"):
+        n, ms = prof[fam]
+        assert n >= 1 and ms > 0.0, (fam, n, ms)
+    assert all(v == (0, 0.0) for v in tr.tr_profile_read(cache).values())   # the read clears
+    tr.tr_profile_enable(cache, False)
+    tr.tr_routed_attn_decode(cache, 0, case["q"][:, 0].contiguous(), case["mode"][:, 0].contiguous(), 40, dout)
+    assert all(v == (0, 0.0) for v in tr.tr_profile_read(cache).values())
+    cache.close()
