@@ -1,14 +1,23 @@
 """GPU parity of the expert FFN (Eq. (3)) against the oracle: |gpu - oracle| <= 2e-3 + 1e-2 |oracle|
-element-wise on fp32 outputs.  The GPU rounds the hidden activation to bf16 from an fp32 value and
-the oracle from a float64 one, so a value on a rounding boundary can differ by one bf16 step
-there -- a change of ~1e-4 in the output, well inside the tolerance."""
+element-wise on fp32 outputs.  The oracle computes Eq. (3) in float64 throughout; the GPU feeds the
+matrix cores bf16 operands (the normalized input and the hidden activation rounded to bf16) and
+accumulates in fp32, which the tolerance covers.
+
+Expert selection is a top-k of softmax probabilities, fp32 on the GPU and fp64 in the oracle.
+Where the k-th and (k+1)-th largest gate logits of a token differ by more than
+TAU = 1e-4 * (1 + max |z|) the selected set is unique and the oracle's must be used; inside that
+margin any set that takes every logit above the tie and k of the tied ones is a correct top-k, and
+the GPU's output must match the oracle evaluated on one of them.  (The GPU's probabilities carry
+fp32 rounding of ~1e-6 relative, two orders of magnitude below TAU.)"""
+
+import itertools
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from tests.gpu_helpers import compare_out, say, u16
+from tests.gpu_helpers import ATOL, RTOL, compare_out, say, u16
 from workloads import moe_case
 
 pytestmark = pytest.mark.gpu
@@ -38,14 +47,43 @@ def reference(c, k, rows):
                           u16(c["w_down"]), k)
 
 
+def tied_sets(z, k):
+    """Every correct top-k set of one token's logits z [E + 1] under the TAU margin."""
+    tau = 1e-4 * (1 + np.abs(z).max())
+    zk = np.sort(z)[::-1][k - 1]
+    sure = [j for j in range(z.size) if z[j] > zk + tau]
+    cand = [j for j in range(z.size) if abs(z[j] - zk) <= tau]
+    return [sure + list(extra) for extra in itertools.combinations(cand, k - len(sure))]
+
+
+def compare_with_ties(c, k, rows, y, where):
+    """compare_out on tokens whose top-k set is unique; each tied token must match the oracle on one
+    of its correct sets."""
+    z = c["z"].cpu().numpy()[rows].astype(np.float64)
+    sets = [tied_sets(z[i], k) for i in range(len(rows))]
+    unique = np.array([len(s) == 1 for s in sets])
+    ref, _, _ = reference(c, k, rows)
+    compare_out(y[unique], ref[unique], where)
+    args = (u16(c["w_gate"]), u16(c["w_up"]), u16(c["w_down"]), k)
+    for i in np.nonzero(~unique)[0]:
+        r = rows[i]
+        ok = False
+        for S in sets[i]:
+            alt, _, _ = oracle.moe_ffn(u16(c["x"])[[r]], c["z"].cpu().numpy()[[r]], *args, sel=np.array([S]))
+            err = np.abs(y[i] - alt[0])
+            ok = ok or bool(np.all(err <= ATOL + RTOL * np.abs(alt[0])))
+        assert ok, f"{where}: token {r} (tied gate logits) matches none of its correct top-{k} sets"
+    say(f"  {where}: {int((~unique).sum())} tokens with tied top-{k} sets")
+
+
 @pytest.mark.parametrize("M,d,de,E,k", [(100, 128, 128, 4, 2), (1000, 768, 1024, 8, 2), (33, 256, 384, 3, 1),
                                         (1, 128, 128, 1, 2), (77, 384, 256, 16, 1)])
 def test_moe_matches_oracle(tr, M, d, de, E, k):
     say(f"moe M={M} d={d} d_e={de} E={E} k={k}")
     c = moe_case(M, d, de, E, seed=M + E, device="cuda")
     y = run(tr, c, k)
-    ref, sel, _ = reference(c, k, np.arange(M))
-    compare_out(y, ref, f"M={M} d={d} E={E} k={k}")
+    compare_with_ties(c, k, np.arange(M), y, f"M={M} d={d} E={E} k={k}")
+    _, sel, _ = reference(c, k, np.arange(min(M, 64)))
     say(f"  null-expert share of the choices: {np.mean(sel == 0):.3f}")
 
 
@@ -55,10 +93,12 @@ def test_moe_null_expert_heavy(tr):
     for k in (1, 2):
         c = moe_case(300, 256, 256, 4, seed=9, device="cuda", null_bias=2.0)
         y = run(tr, c, k)
-        ref, sel, _ = reference(c, k, np.arange(300))
+        _, sel, _ = reference(c, k, np.arange(300))
         if k == 1:
-            assert np.all(y[sel[:, 0] == 0] == 0.0)
-        compare_out(y, ref, f"null-heavy k={k}")
+            z = c["z"].cpu().numpy()
+            alone = [i for i in range(300) if sel[i, 0] == 0 and len(tied_sets(z[i].astype(np.float64), 1)) == 1]
+            assert np.all(y[alone] == 0.0)
+        compare_with_ties(c, k, np.arange(300), y, f"null-heavy k={k}")
 
 
 def test_moe_partial_call_and_full_size_sample(tr):
@@ -67,7 +107,6 @@ def test_moe_partial_call_and_full_size_sample(tr):
     c = moe_case(2048, 2048, 2688, 8, seed=3, device="cuda", cid=5)
     y = run(tr, c, 2)
     rows = np.random.default_rng(0).choice(2048, 48, replace=False)
-    ref, _, _ = reference(c, 2, rows)
-    compare_out(y[rows], ref, "1.3B-shaped, sampled tokens")
+    compare_with_ties(c, 2, rows, y[rows], "1.3B-shaped, sampled tokens")
     y2 = run(tr, c, 2, n=1000)
     assert np.array_equal(y2[:1000], y[:1000]) and np.all(np.isnan(y2[1000:]))

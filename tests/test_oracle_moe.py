@@ -15,8 +15,7 @@ def _np(c):
 
 
 def _torch_ffn(c, k):
-    """Eq. (3) with torch's rms_norm / softmax / topk / silu / linear in float64; the hidden
-    activation rounded to bf16 by torch."""
+    """Eq. (3) with torch's rms_norm / softmax / topk / silu / linear, all in float64."""
     x = c["x"].double()
     u = F.rms_norm(x, (x.shape[1],), eps=1e-6)
     p = F.softmax(c["z"].double(), dim=1)
@@ -29,7 +28,7 @@ def _torch_ffn(c, k):
             if e == 0:
                 continue
             h = F.silu(F.linear(u[t], c["w_gate"][e - 1].double())) * F.linear(u[t], c["w_up"][e - 1].double())
-            y[t] += w[t, j] * F.linear(h.to(torch.bfloat16).double(), c["w_down"][e - 1].double())
+            y[t] += w[t, j] * F.linear(h, c["w_down"][e - 1].double())
     return y.numpy(), idx.numpy()
 
 
@@ -74,17 +73,21 @@ def test_expert_order_does_not_matter():
     np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-14)
 
 
-def test_bf16_rounding_of_the_hidden_activation():
-    r = oracle.moe._bf16_round
-    v = np.array([1.0, 1 + 2 ** -9, 1 + 3 * 2 ** -9, -(1 + 2 ** -8 + 2 ** -9), 3.0e-30, 0.0])
-    want = np.array([1.0, 1.0, 1 + 2 ** -7, -(1 + 2 ** -7), None, 0.0], dtype=object)
-    got = r(v)
-    for g, w, x in zip(got, want, v):
-        if w is None:                                 # a tiny value keeps 8 significant bits
-            assert abs(g - x) <= abs(x) * 2 ** -8
-        else:
-            assert g == w
-    # agrees with torch's float32 -> bfloat16 conversion on float32 values
-    f = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
-    tb = torch.from_numpy(f).to(torch.bfloat16).double().numpy()
-    assert np.array_equal(r(f.astype(np.float64)), tb)
+def test_given_selection_reweights_over_that_set():
+    """sel = the gate's own choice reproduces the default result; a single forced expert (k = 1)
+    gets weight 1, so the output is that expert's f_j(Norm(x)) alone, and a forced pair is the
+    p-weighted mean of the two single-expert outputs."""
+    c = moe_case(20, 128, 64, 4, seed=8)
+    x, z, wg, wu, wd = _np(c)
+    y, sel, wt = oracle.moe_ffn(x, z, wg, wu, wd, 2)
+    y_same, _, wt_same = oracle.moe_ffn(x, z, wg, wu, wd, 2, sel=sel)
+    assert np.array_equal(y_same, y) and np.array_equal(wt_same, wt)
+    ys = {e: oracle.moe_ffn(x, z, wg, wu, wd, 1, sel=np.full((20, 1), e))[0] for e in (2, 4)}
+    yt, _ = _torch_ffn(dict(c, z=torch.full_like(c["z"], -30.0).index_fill_(1, torch.tensor([2]), 0.0)), 1)
+    np.testing.assert_allclose(ys[2], yt, rtol=1e-9, atol=1e-12)
+    pair, _, wpair = oracle.moe_ffn(x, z, wg, wu, wd, 2, sel=np.tile([2, 4], (20, 1)))
+    z64 = z.astype(np.float64)
+    p = np.exp(z64 - z64.max(axis=1, keepdims=True))
+    w2 = p[:, 2] / (p[:, 2] + p[:, 4])
+    np.testing.assert_allclose(wpair[:, 0], w2, rtol=1e-12)
+    np.testing.assert_allclose(pair, w2[:, None] * ys[2] + (1 - w2)[:, None] * ys[4], rtol=1e-10, atol=1e-13)
