@@ -63,31 +63,11 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # HBM traffic of the dominant kernels from rocprofv3 PMC passes (FETCH_SIZE, then WRITE_SIZE,
 # KiB per dispatch, averaged over the timed launches), each divided by what the same counter
 # read per byte of a plain 1 GiB device-to-device copy in the same run (``--calib-copy-mib``).
-# ``sources`` lists the files the kernel is built from and their sha256 when the counters were
-# taken: once any of them changes the figures no longer describe the kernel and the bench
-# reports traffic as null.
-TRAFFIC = {
-    "k_decode": {
-        "fetch_kib": 167570.6, "write_kib": 2114.2, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
-        "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip":
-                "d61fb6b9a8536951583f825b6160ac7bfcf98292881966a81d8f15cb44a56359",
-            "mixed_precision_kv_tr_amd/csrc/common.h":
-                "54b76045567d72dcfd23ee7a5c6a52177cf05f1138eee2e357d1e32cabb42231",
-            "mixed_precision_kv_tr_amd/csrc/layout.h":
-                "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
-    "k_prefill_attn": {
-        "fetch_kib": 19358.5, "write_kib": 19047.9, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
-        "sources": {
-            "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip":
-                "e00c74bcde92fc1b6b35a2dd829e940a11f1c17f98bdbdf6729a977c0106b69c",
-            "mixed_precision_kv_tr_amd/csrc/kv_write.h":
-                "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
-            "mixed_precision_kv_tr_amd/csrc/common.h":
-                "54b76045567d72dcfd23ee7a5c6a52177cf05f1138eee2e357d1e32cabb42231",
-            "mixed_precision_kv_tr_amd/csrc/layout.h":
-                "c4e71728270ad9a2c4d779d3cec4170315d531efc9c28d32875352faef9a245d"}},
-}
+# Keyed by (kernel, workload): a figure describes one kernel on one workload only.  ``sources``
+# lists the files the kernel is built from and their sha256 when the counters were taken: once
+# any of them changes the figures no longer describe the kernel and the bench reports traffic
+# as null.
+TRAFFIC = {}
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, TFLOP/s
 METRIC = "mixed-bit KV decode GB/s (% HBM peak); routed prefill tokens/s (% MFMA peak)"
@@ -151,12 +131,40 @@ def _sha256(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """Calibrated HBM bytes per launch of ``kernel`` if its sources are unchanged, else None."""
-    t = TRAFFIC.get(kernel)
+def measured_traffic(kernel: str, workload: str):
+    """Calibrated HBM bytes per launch of ``kernel`` on ``workload`` if its sources are unchanged,
+    else None."""
+    t = TRAFFIC.get((kernel, workload))
     if not t or any(_sha256(f) != h for f, h in t["sources"].items()):
         return None
     return int(t["fetch_kib"] * 1024 / t["fetch_per_byte"] + t["write_kib"] * 1024 / t["write_per_byte"])
+
+
+SOURCE_GLOBS = ("mixed_precision_kv_tr_amd/csrc", "include", "workloads")
+
+
+def source_digest() -> str:
+    """sha256 (first 16 hex digits) over the kernel sources, the header, the workload generator
+    and this file: identifies the code a line was measured with (the GPU machine has no git)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join(d, f) for d in SOURCE_GLOBS for f in sorted(os.listdir(os.path.join(ROOT, d)))
+             if os.path.isfile(os.path.join(ROOT, d, f)) and not f.endswith(".pyc")]
+    for rel in sorted(files) + ["bench.py"]:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def git_sha():
+    """HEAD's commit if this tree is a git checkout, else None."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() or None if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
 
 
 def copy_calibration(mib: int, reps: int = 5):
@@ -186,19 +194,58 @@ def time_steps(step, K: int) -> float:
     return start.elapsed_time(end) / K
 
 
+LLC_FLUSH_BYTES = 512 << 20      # > the 256 MB last-level cache (Infinity Cache)
+
+
+def time_iters(step, iters: int, flush_buf=None) -> list:
+    """Per-iteration HIP-event times (ms) on the current stream.  With flush_buf, the buffer is
+    rewritten between iterations, outside the events, so that every iteration starts with a
+    cold last-level cache."""
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    evs = []
+    for i in range(iters):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0x7f)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 # --------------------------------------------------------------------------------------------
-# CPU oracle baseline (runs in worker processes on this host)
+# CPU oracle baseline (runs in spawned worker processes on this host, one BLAS thread each)
 
 def _oracle_decode_worker(args):
-    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    """One sequence of a decode step: its cached positions 0..C-1 are quantized and dequantized
+    first (untimed: the cache exists before the step); then, timed, `reps` times: Eq. 4 on the
+    new token C, and Eq. 2 for its one query per head over positions 0..C."""
     import oracle
-    q, k, v, bits, mode, C, w = args
+    q, k, v, bits, mode, C, w, reps = args
+    Hkv = k.shape[1]
+    k_hat = np.empty(k.shape, dtype=np.float64)
+    v_hat = np.empty(v.shape, dtype=np.float64)
+    b_old = np.broadcast_to(bits[:C, None].astype(np.int64), (C, Hkv))
+    for src, dst in ((k, k_hat), (v, v_hat)):
+        c_, s_, z_ = oracle.quantize(src[:C], b_old)
+        dst[:C] = oracle.dequantize(c_, s_, z_, b_old)
+    b_new = np.full((1, Hkv), int(bits[C]), dtype=np.int64)
+    qf = oracle.bf16_bits_to_f32(q).astype(np.float64)[None]
     t0 = time.perf_counter()
-    oracle.attend_cached(q[None], k, v, bits, mode[None], np.array([C]), w)
+    for _ in range(reps):
+        for src, dst in ((k, k_hat), (v, v_hat)):
+            c_, s_, z_ = oracle.quantize(src[C:C + 1], b_new)
+            dst[C:C + 1] = oracle.dequantize(c_, s_, z_, b_new)
+        oracle.routed_attention(qf, k_hat, v_hat, mode[None], np.array([C]), w)
     return time.perf_counter() - t0
 
 
 def _oracle_prefill_worker(args):
+    """One (layer, sequence) of a prefill step, timed whole: Eq. 4 on every token, then Eq. 2 for
+    every query."""
     import oracle
     q, k, v, bits, mode, w = args
     t0 = time.perf_counter()
@@ -210,23 +257,35 @@ def run_pool(fn, jobs, workers):
     ctx = mp.get_context("spawn")
     with ctx.Pool(workers, initializer=_pool_init) as pool:
         t0 = time.perf_counter()
-        cpu_times = pool.map(fn, jobs)
+        cpu_times = pool.map(fn, jobs, chunksize=1)
         wall = time.perf_counter() - t0
     return wall, cpu_times
 
 
 def _pool_init():
-    os.environ["OMP_NUM_THREADS"] = "1"
-    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
     sys.path.insert(0, ROOT)
 
 
 def cpu_workers() -> int:
+    """Cores this process may run on, capped at the 16 a one-GPU machine gives a job."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
     return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def u16(t):
@@ -235,13 +294,15 @@ def u16(t):
 
 # --------------------------------------------------------------------------------------------
 
-def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
+def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True, flush=False):
+    """Decode steps of a workload: per layer, the new token's quantize-write and routed decode.
+    flush: time iterations one by one with the last-level cache evicted before each (workloads
+    whose whole step fits in it); the step time is then the median."""
     B, H, D, C, w, Lyr = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens, cfg.window, cfg.layers
     Hkv = cfg.num_kv_heads
     dev = torch.device("cuda")
     log(f"[decode] generating {Lyr} layers of {cfg.name}")
     per_layer, samples = [], []
-    sample_seqs = list(range(args.cpu_sample_seqs))
     pcb = args.page_code_bytes or 4096
     ptok = {b: pcb * 8 // (D * b) for b in (2, 4, 8, 16)}
     cache = None
@@ -254,7 +315,7 @@ def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
             # pool sized from layer 0's realized width mix, with 25% headroom for the others
             pool_pages = int(pool_pages_needed([bits_np], ptok) * Lyr * 1.25) + 64
             cache = tr.tr_kv_cache_alloc(Lyr, B, Hkv, D, C + 1, page_code_bytes=args.page_code_bytes,
-                                         pool_pages=pool_pages, num_query_heads=H)
+                                         pool_pages=pool_pages, num_query_heads=H, prefill_tokens=-1)
         tr.tr_kv_quantize_write(cache, layer, case["k"][:, :C].contiguous(), case["v"][:, :C].contiguous(),
                                 case["bits"][:, :C].contiguous())
         a, t = decode_layer_bytes(bits_np, mode_np, C, w, D, Hkv)
@@ -263,9 +324,9 @@ def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
         per_layer.append({x: case[x][:, C:C + 1].contiguous() for x in ("k", "v", "bits")} |
                          {"q": case["q"].contiguous(), "mode": case["mode"].contiguous()})
         if layer == 0 and baseline and not args.no_cpu_baseline:
-            for s in sample_seqs:
+            for s in range(B):
                 samples.append((u16(case["q"][s]), u16(case["k"][s]), u16(case["v"][s]), bits_np[s],
-                                mode_np[s], C, w))
+                                mode_np[s], C, w, args.cpu_reps))
         del case
     torch.cuda.synchronize()
     st = tr.tr_kv_cache_status(cache)
@@ -281,10 +342,14 @@ def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
         for layer in range(Lyr):
             tr.tr_kv_cache_truncate(cache, layer, C)
 
+    flush_buf = torch.empty(LLC_FLUSH_BYTES, dtype=torch.uint8, device=dev) if flush else None
     for _ in range(args.warmup):
         step()
-    log(f"[decode] timing {args.steps} steps")
-    ms = time_steps(step, args.steps)
+    log(f"[decode] timing {args.steps} steps" + (" (last-level cache flushed before each)" if flush else ""))
+    if flush:
+        ms = float(np.median(time_iters(step, args.steps, flush_buf)))
+    else:
+        ms = time_steps(step, args.steps)
     st = tr.tr_kv_cache_status(cache)
     if st != 0:
         raise RuntimeError(f"decode steps failed with status {st}")
@@ -294,8 +359,11 @@ def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
     # per-kernel durations: same steps with event timing inside the library
     tr.tr_profile_read(cache)
     tr.tr_profile_enable(cache, True)
-    for _ in range(args.steps):
-        step()
+    if flush:
+        time_iters(step, args.steps, flush_buf)
+    else:
+        for _ in range(args.steps):
+            step()
     prof = tr.tr_profile_read(cache)
     tr.tr_profile_enable(cache, False)
     n_split, ms_split = prof["decode_split"]
@@ -304,28 +372,33 @@ def bench_decode(tr, args, cfg=CONFIGS[3], baseline=True):
     achieved = bytes_per_launch / (avg_split_ms * 1e-3) / 1e9
     kname = "k_decode"
     roof = {"bound": "hbm", "kernel": kname, "traffic_unit": "bytes per launch", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kname),
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kname, cfg.name),
             "avg_launch_us": round(avg_split_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch),
             "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
 
     cpu = None
     if samples:
         workers = min(cpu_workers(), len(samples))
-        log(f"[decode] oracle on {len(samples)} sampled sequences, {workers} worker processes")
-        wall, _ = run_pool(_oracle_decode_worker, samples, workers)
+        log(f"[decode] oracle on {len(samples)} sequences, {workers} worker processes")
+        wall, times = run_pool(_oracle_decode_worker, samples, workers)
         s_bytes = 0
-        for (q, k, v, bits, mode, C_, w_) in samples:
-            a, t = decode_layer_bytes(bits[None], mode[None], C_, w_, D, Hkv)
-            s_bytes += t
-        cpu = {"value": round(s_bytes / wall / 1e9, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
-               "sample": f"layer 0, sequences {sample_seqs[0]}..{sample_seqs[-1]} of {cfg.name}: quantize the "
-                         f"{C + 1}-token cache of each sequence and attend its one query per head; "
-                         f"{wall:.2f} s wall"}
+        for (q, k, v, bits, mode, C_, w_, reps) in samples:
+            s_bytes += decode_layer_bytes(bits[None], mode[None], C_, w_, D, Hkv)[1] * reps
+        busy = float(sum(times))
+        cpu = {"value": round(s_bytes / (busy / workers) / 1e9, 6), "unit": "GB/s", "cores": workers,
+               "kind": "oracle", "cpu_model": cpu_model(),
+               "sample": f"layer 0, all {B} sequences of {cfg.name}: per sequence, the step repeated "
+                         f"{args.cpu_reps} times (Eq. 4 on the new token, Eq. 2 for its {H} query heads over "
+                         f"{C + 1} positions) on a cache quantized beforehand (untimed); {busy:.2f} s of "
+                         f"timed work on {workers} worker processes (one BLAS thread each), value = the "
+                         f"sample's algorithmic bytes / (timed work / workers)"}
     cache.close()
     return {"ms": ms, "gbs": gbs, "bytes": step_bytes, "roofline": roof, "cpu": cpu, "cfg": cfg}
 
 
-def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True):
+def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True, flush=False):
+    """Prefill steps of a workload: every layer's quantize-write of the prompt and routed
+    attention of its queries.  flush: as for bench_decode."""
     B, H, D, T, w, Lyr = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens, cfg.window, cfg.layers
     dev = torch.device("cuda")
     log(f"[prefill] generating {Lyr} layers of {cfg.name}")
@@ -341,10 +414,14 @@ def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True):
             tr.tr_kv_cache_truncate(cache, layer, 0)
             tr.tr_routed_attn_prefill(cache, layer, c["q"], c["k"], c["v"], c["bits"], c["mode"], T, w, outs[layer])
 
+    flush_buf = torch.empty(LLC_FLUSH_BYTES, dtype=torch.uint8, device=dev) if flush else None
     for _ in range(args.warmup):
         step()
-    log(f"[prefill] timing {args.steps} steps")
-    ms = time_steps(step, args.steps)
+    log(f"[prefill] timing {args.steps} steps" + (" (last-level cache flushed before each)" if flush else ""))
+    if flush:
+        ms = float(np.median(time_iters(step, args.steps, flush_buf)))
+    else:
+        ms = time_steps(step, args.steps)
     st = tr.tr_kv_cache_status(cache)
     if st != 0:
         raise RuntimeError(f"prefill steps failed with status {st}")
@@ -353,8 +430,11 @@ def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True):
 
     tr.tr_profile_read(cache)
     tr.tr_profile_enable(cache, True)
-    for _ in range(args.steps):
-        step()
+    if flush:
+        time_iters(step, args.steps, flush_buf)
+    else:
+        for _ in range(args.steps):
+            step()
     prof = tr.tr_profile_read(cache)
     tr.tr_profile_enable(cache, False)
     n_attn, ms_attn = prof["prefill_attn"]
@@ -363,21 +443,45 @@ def bench_prefill(tr, args, cfg=CONFIGS[2], baseline=True):
     achieved = fl_per_launch / (avg_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": "k_prefill_attn", "achieved": round(achieved, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("k_prefill_attn"), "traffic_unit": "bytes per launch",
+            "traffic": measured_traffic("k_prefill_attn", cfg.name), "traffic_unit": "bytes per launch",
             "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": int(fl_per_launch),
             "kernels_us_per_step": {k: round(v[1] * 1e3 / args.steps, 1) for k, v in prof.items() if v[0]}}
     cpu = None
     if baseline and not args.no_cpu_baseline:
-        c0 = cases[0]
-        job = (u16(c0["q"][0]), u16(c0["k"][0]), u16(c0["v"][0]), c0["bits"][0].cpu().numpy(),
-               c0["mode"][0].cpu().numpy(), w)
-        log("[prefill] oracle on layer 0, sequence 0")
-        wall, _ = run_pool(_oracle_prefill_worker, [job], 1)
-        cpu = {"value": round(T / (wall * Lyr), 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"layer 0, sequence 0 of {cfg.name} ({T} tokens, {H} heads): quantize-write and "
-                         f"attend every query; {wall:.2f} s wall, scaled to {Lyr} layers"}
+        jobs = []
+        for layer, c in enumerate(cases):
+            for s in range(B):
+                jobs.append((u16(c["q"][s]), u16(c["k"][s]), u16(c["v"][s]), c["bits"][s].cpu().numpy(),
+                             c["mode"][s].cpu().numpy(), w))
+        workers = min(cpu_workers(), len(jobs))
+        log(f"[prefill] oracle on {len(jobs)} (layer, sequence) jobs, {workers} worker processes")
+        wall, times = run_pool(_oracle_prefill_worker, jobs, workers)
+        busy = float(sum(times))
+        cpu = {"value": round(B * T / (busy / workers), 3), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+               "cpu_model": cpu_model(),
+               "sample": f"the whole step of {cfg.name}: {Lyr} layers x {B} sequences, each job one (layer, "
+                         f"sequence): Eq. 4 on its {T} tokens, then Eq. 2 for every query and head; {busy:.2f} s "
+                         f"of work on {workers} worker processes (one BLAS thread each), value = "
+                         f"{B * T} tokens / (work / workers)"}
     cache.close()
     return {"ms": ms, "tok_s": tok_s, "tflops": tflops, "roofline": roof, "cpu": cpu, "cfg": cfg}
+
+
+def bench_small(tr, args):
+    """The workloads whose step fits in the last-level cache, each timed with the cache evicted
+    before every iteration (median of the iterations): the tiny prefill (T = 256, 1 layer), the
+    160M-shaped decode step (B = 8, C = 2048) and the long-context decode (B = 1, C = 65536)."""
+    out = {}
+    r = bench_prefill(tr, args, CONFIGS[0], baseline=False, flush=True)
+    out["tiny_prefill"] = {"workload": r["cfg"].name, "value": round(r["tok_s"], 1), "unit": "tokens/s",
+                           "us_per_step": round(r["ms"] * 1e3, 2), "tflops": round(r["tflops"], 3),
+                           "mfma_frac": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5), "roofline": r["roofline"]}
+    for key, cid in (("decode_160m", 1), ("longctx_decode", 4)):
+        r = bench_decode(tr, args, CONFIGS[cid], baseline=False, flush=True)
+        out[key] = {"workload": r["cfg"].name, "value": round(r["gbs"], 1), "unit": "GB/s",
+                    "us_per_step": round(r["ms"] * 1e3, 2), "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                    "bytes_per_step": int(r["bytes"]), "roofline": r["roofline"]}
+    return out
 
 
 # The pages' baselines as configurations of the same kernels: dense (every token stored as
@@ -484,9 +588,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["decode", "prefill", "gqa_decode", "gqa_prefill", "baselines", "controller", "moe"],
-                    default=None)
+    ap.add_argument("--cpu-reps", type=int, default=10,
+                    help="decode oracle: timed repetitions of each sampled sequence's step")
+    ap.add_argument("--only", choices=["decode", "prefill", "small", "gqa_decode", "gqa_prefill", "baselines",
+                                       "controller", "moe"], default=None)
+    ap.add_argument("--no-small", action="store_true", help="skip the workloads that fit in the last-level cache")
     ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query workloads")
     ap.add_argument("--no-baselines", action="store_true", help="skip the dense / uniform-width / routing-only runs")
     ap.add_argument("--no-controller", action="store_true", help="skip the routing-controller timing")
@@ -511,6 +617,7 @@ def main():
 
     dec = bench_decode(tr, args) if args.only in (None, "decode") else None
     pre = bench_prefill(tr, args) if args.only in (None, "prefill") else None
+    small = bench_small(tr, args) if (args.only is None and not args.no_small) or args.only == "small" else None
     gqa = args.only is None and not args.no_gqa
     gdec = bench_decode(tr, args, CONFIGS[5], baseline=False) if gqa or args.only == "gqa_decode" else None
     gpre = bench_prefill(tr, args, CONFIGS[6], baseline=False) if gqa or args.only == "gqa_prefill" else None
@@ -521,7 +628,8 @@ def main():
     moe = bench_moe(tr, args) if (args.only is None and not args.no_moe) or args.only == "moe" else None
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic",
+            "seed": args.seed, "source_sha256": source_digest(), "git_sha": git_sha()}
     if dec:
         cfg = dec["cfg"]
         line.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 4),
@@ -542,6 +650,14 @@ def main():
             line.update({"value": pobj["value"], "unit": "tokens/s", "ms_per_step": pobj["ms_per_step"],
                          "dtype": "bf16", "config": {"workload": cfg.name}, "roofline": pobj["roofline"],
                          "cpu_baseline": pobj["cpu_baseline"]})
+    if small:
+        if "value" in line:
+            line["small"] = small
+        else:
+            o = small["decode_160m"]
+            line.update({"value": o["value"], "unit": o["unit"], "ms_per_step": round(o["us_per_step"] / 1e3, 5),
+                         "dtype": "fp32", "config": {"workload": o["workload"]}, "roofline": o["roofline"],
+                         "cpu_baseline": None, "small": small})
     # grouped-query workloads: same objects, no CPU baseline
     extra = {}
     if gdec:

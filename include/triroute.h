@@ -29,6 +29,7 @@
  *     tr_kv_cache_status(); outputs touched by a bad element are unspecified.
  *   - No call throws; no call allocates except tr_kv_cache_alloc.
  *   - Inputs must be finite; for every quantized group max - min must be finite in fp32.
+ *     tr_routed_attn_prefill also bounds the V values it reads (see there).
  *   - Quantization is bit-exact: s = fl32(fl32(max - min) / (2^b - 1)) with a correctly
  *     rounded divide, z = min (+0 for a zero minimum), code = rint(fl32(fl32(x - z) / s)),
  *     codes 0 for a constant group.  Attention accumulates in fp32 and writes bf16 (RNE).
@@ -51,7 +52,8 @@ typedef enum {
   TR_ERR_OUT_OF_PAGES = 3,  /* sticky: the page pool ran out during a write */
   TR_ERR_HIP = 4,           /* a HIP runtime call failed (allocation, launch, copy) */
   TR_ERR_UNSUPPORTED = 5,   /* a valid but unsupported shape (head_dim not 64/128, ...) */
-  TR_ERR_BAD_VALUE = 6      /* sticky: a bits or mode element outside its domain was seen */
+  TR_ERR_BAD_VALUE = 6,     /* sticky: a bits or mode element outside its domain was seen */
+  TR_ERR_RANGE = 7          /* sticky: prefill met a stored V value with |v_hat| >= 65504 */
 } tr_status;
 
 /* Attention modes of Eq. (2): one uint8 per (sequence, query token, head). */
@@ -73,6 +75,14 @@ typedef struct {
                                attention), else a multiple of num_heads (grouped-query attention:
                                query head h reads KV head h / (num_query_heads / num_heads); the
                                review page's experimental setup, section 5, uses H_kv = H/4) */
+  int32_t prefill_tokens;   /* scratch of tr_routed_attn_prefill: a prefill call may reach
+                               positions up to prefill_tokens (len + T <= prefill_tokens).
+                               0 -> max_tokens; -1 -> none (a decode-only cache: no prefill
+                               scratch is allocated and tr_routed_attn_prefill returns
+                               TR_ERR_UNSUPPORTED); else 1 .. max_tokens.  The scratch grows
+                               with it: per (sequence, KV head) 4 * head_dim + 8 bytes per
+                               position, plus per (sequence, query head) 4 bytes per position
+                               and 16 partial tiles of 128 x (head_dim + 4) floats. */
 } tr_kv_cache_desc;
 
 /* Opaque cache: per (layer, sequence, width class) a stream of pages of the pool, fp32
@@ -81,7 +91,8 @@ typedef struct {
 typedef struct tr_kv_cache tr_kv_cache;
 
 /* Allocate and zero a cache (device memory via hipMalloc, on the current device).
- * *out receives the handle; nothing is allocated on error. */
+ * *out receives the handle; nothing is allocated on error.  Every field of the descriptor is
+ * read, so zero-initialize it (0 picks each field's default). */
 tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* desc, tr_kv_cache** out);
 
 /* Free every device buffer of the cache.  Synchronizes the device first.  NULL is a no-op. */
@@ -120,7 +131,15 @@ tr_status tr_routed_attn_decode(tr_kv_cache* cache, int32_t layer, const void* q
  * query at its own position len + i, reading the cache just written).
  *   q:    bf16 [batch, T, num_query_heads, head_dim]; k, v: bf16 [batch, T, num_heads, head_dim]
  *   bits: uint8 [batch, T];  mode: uint8 [batch, T, num_query_heads]
- *   out:  bf16 [batch, T, num_query_heads, head_dim] */
+ *   out:  bf16 [batch, T, num_query_heads, head_dim]
+ * Range: the prefill attention's PV product takes the stored values v_hat = s * c + z (the raw
+ * value for b = 16) in fp16, so every V value the call reads -- its own tokens' and, for a call
+ * that continues a sequence, the earlier positions' -- must satisfy |v_hat| < 65504.  V inputs
+ * with every |v| <= 65280 (the largest bf16 below 65504) always do (v_hat stays within its
+ * group's [min, max] up to 2^-22 relative).  A larger value sets the sticky TR_ERR_RANGE flag
+ * (tr_kv_cache_status) and leaves the call's outputs unspecified; the cache contents are written
+ * exactly as tr_kv_quantize_write would write them, and decode, which dequantizes in fp32, has no
+ * such limit. */
 tr_status tr_routed_attn_prefill(tr_kv_cache* cache, int32_t layer, const void* q, const void* k,
                                  const void* v, const uint8_t* bits, const uint8_t* mode, int32_t T,
                                  int32_t window, void* out, void* stream);
@@ -135,11 +154,21 @@ tr_status tr_kv_cache_export(const tr_kv_cache* cache, int32_t layer, int32_t to
                              uint16_t* codes, float* scale, float* zero, uint8_t* bits, void* stream);
 
 /* Synchronize `stream` and report the sticky device flags: TR_ERR_OUT_OF_PAGES, then
- * TR_ERR_BAD_VALUE, else TR_OK. */
+ * TR_ERR_BAD_VALUE, then TR_ERR_RANGE, else TR_OK. */
 tr_status tr_kv_cache_status(tr_kv_cache* cache, void* stream);
 
 /* Pages taken from the pool so far (synchronizes `stream`).  -1 on error. */
 int64_t tr_kv_cache_pages_used(tr_kv_cache* cache, void* stream);
+
+/* Diagnostics: the decode split-K.  Decode splits every attended window into position chunks
+ * (each chunk one work item, the chunks merged by a log-sum-exp combine); by default the library
+ * picks the count from the batch, heads and context.  n >= 1 forces n chunks over a full window
+ * [0, t] (chunk length ceil((t + 1) / n); a local window gets as many chunks of that length as it
+ * needs; n is capped at t + 1), n = 0 restores the automatic choice.  A later decode call returns
+ * TR_ERR_UNSUPPORTED, and launches nothing, if the forced chunks would exceed a work item's limit
+ * of 512 positions.  n must lie in [0, 64] (TR_ERR_INVALID_ARG otherwise).  Host-side only; the
+ * output is the same up to fp32 reduction order for every n. */
+tr_status tr_kv_cache_set_decode_chunks(tr_kv_cache* cache, int32_t n);
 
 /* Diagnostics: while enabled, the library's kernel launches on this cache are bracketed by HIP
  * events on the call's stream.  tr_profile_read synchronizes on them, returns per kernel family

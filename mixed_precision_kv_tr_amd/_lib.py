@@ -27,7 +27,7 @@ _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 class _Desc(ctypes.Structure):
     _fields_ = [("num_layers", _i32), ("batch", _i32), ("num_heads", _i32), ("head_dim", _i32),
                 ("max_tokens", _i32), ("page_code_bytes", _i32), ("pool_pages", _i64),
-                ("num_query_heads", _i32)]
+                ("num_query_heads", _i32), ("prefill_tokens", _i32)]
 
 
 class _CtlWeights(ctypes.Structure):
@@ -64,12 +64,13 @@ _moe_alloc = _sig("tr_moe_alloc", ctypes.c_int, ctypes.POINTER(_MoeDesc), ctypes
 _moe_free = _sig("tr_moe_free", ctypes.c_int, _vp)
 _moe_set = _sig("tr_moe_set_weights", ctypes.c_int, _vp, _vp, _vp, _vp, _vp)
 _moe_ffn = _sig("tr_moe_ffn", ctypes.c_int, _vp, _vp, _vp, _i32, _vp, _vp)
+_set_chunks = _sig("tr_kv_cache_set_decode_chunks", ctypes.c_int, _vp, _i32)
 _prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
 _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
 PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn", "prefill_merge")
 
 STATUS_NAMES = {0: "TR_OK", 1: "TR_ERR_INVALID_ARG", 2: "TR_ERR_CAPACITY", 3: "TR_ERR_OUT_OF_PAGES",
-                4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE"}
+                4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE", 7: "TR_ERR_RANGE"}
 
 
 class TriRouteError(RuntimeError):
@@ -128,14 +129,17 @@ class KVCache:
 
 
 def tr_kv_cache_alloc(num_layers: int, batch: int, num_heads: int, head_dim: int, max_tokens: int,
-                      page_code_bytes: int = 0, pool_pages: int = 0, num_query_heads: int = 0) -> KVCache:
-    """num_heads: KV heads; num_query_heads: query heads (0 = num_heads; a multiple for GQA)."""
-    d = _Desc(num_layers, batch, num_heads, head_dim, max_tokens, page_code_bytes, pool_pages, num_query_heads)
+                      page_code_bytes: int = 0, pool_pages: int = 0, num_query_heads: int = 0,
+                      prefill_tokens: int = 0) -> KVCache:
+    """num_heads: KV heads; num_query_heads: query heads (0 = num_heads; a multiple for GQA);
+    prefill_tokens: positions a prefill may reach (0 = max_tokens, -1 = no prefill scratch)."""
+    d = _Desc(num_layers, batch, num_heads, head_dim, max_tokens, page_code_bytes, pool_pages, num_query_heads,
+              prefill_tokens)
     h = _vp()
     _check(_alloc(ctypes.byref(d), ctypes.byref(h)), "tr_kv_cache_alloc")
     return KVCache(h.value, dict(num_layers=num_layers, batch=batch, num_heads=num_heads, head_dim=head_dim,
                                  max_tokens=max_tokens, page_code_bytes=page_code_bytes, pool_pages=pool_pages,
-                                 num_query_heads=num_query_heads or num_heads))
+                                 num_query_heads=num_query_heads or num_heads, prefill_tokens=prefill_tokens))
 
 
 def tr_kv_cache_free(cache: KVCache):
@@ -178,6 +182,11 @@ def tr_kv_cache_status(cache: KVCache, stream=None) -> int:
 
 def tr_kv_cache_pages_used(cache: KVCache, stream=None) -> int:
     return int(_pages(cache.handle, _stream(stream)))
+
+
+def tr_kv_cache_set_decode_chunks(cache: KVCache, n: int):
+    """Force n position chunks per full decode window (0 = the library's automatic choice)."""
+    _check(_set_chunks(cache.handle, n), "tr_kv_cache_set_decode_chunks")
 
 
 def tr_kv_cache_truncate(cache: KVCache, layer: int, new_len: int):

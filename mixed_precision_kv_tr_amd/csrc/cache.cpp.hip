@@ -251,6 +251,7 @@ const char* tr_status_str(tr_status s) {
     case TR_ERR_HIP: return "HIP runtime error";
     case TR_ERR_UNSUPPORTED: return "unsupported shape";
     case TR_ERR_BAD_VALUE: return "a bits or mode element outside its domain";
+    case TR_ERR_RANGE: return "a value outside the fp16 range of the prefill attention's V operand";
   }
   return "unknown status";
 }
@@ -289,6 +290,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   if ((int64_t)d->max_tokens * d->head_dim > (1LL << 30) - 64LL * d->head_dim) return TR_ERR_UNSUPPORTED;
   const int hq = d->num_query_heads ? d->num_query_heads : d->num_heads;
   if (hq < d->num_heads || hq % d->num_heads) return TR_ERR_INVALID_ARG;
+  if (d->prefill_tokens < -1 || d->prefill_tokens > d->max_tokens) return TR_ERR_INVALID_ARG;
   const int cb = d->page_code_bytes ? d->page_code_bytes : 4096;
   if (cb < 1024 || cb > 65536 || (cb & (cb - 1))) return TR_ERR_INVALID_ARG;
 
@@ -303,6 +305,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   c->prof_on = false;
   CacheLayout& L = c->lay;
   L.L = d->num_layers; L.B = d->batch; L.H = d->num_heads; L.D = d->head_dim; L.N = d->max_tokens;
+  L.pfN = d->prefill_tokens == 0 ? L.N : d->prefill_tokens < 0 ? 0 : d->prefill_tokens;
   c->hq = hq;
   c->grp = hq / L.H;
   L.cb = cb;
@@ -340,7 +343,9 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   {
     const int min_chunk = tr_decode_max_chunk(L) < TR_DECODE_MIN_CHUNK ? tr_decode_max_chunk(L) : TR_DECODE_MIN_CHUNK;
     c->max_chunks = (L.N + min_chunk - 1) / min_chunk + 1;
+    if (c->max_chunks < TR_DECODE_FORCE_MAX) c->max_chunks = TR_DECODE_FORCE_MAX;
   }
+  c->force_chunks = 0;
   (void)hipGetDevice(&c->device);
   bool ok = true;
   ok = ok && hipMalloc((void**)&L.pool, (size_t)(L.pool_pages * L.page_bytes)) == hipSuccess;
@@ -350,17 +355,19 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   ok = ok && hipMalloc((void**)&L.err, sizeof(uint32_t)) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->partials,
                        sizeof(float) * (size_t)L.B * hq * c->max_chunks * (L.D + 2)) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * hq * L.N) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * hq * 4) == hipSuccess;
-  c->np = (L.N + 63) / 64 * 64;
-  ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->dkf, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;
-  c->pf_uph = tr_prefill_units_per_head(L.N);
-  ok = ok && hipMalloc((void**)&c->pf_units, sizeof(int4) * (size_t)L.B * hq * c->pf_uph) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->pf_merges, sizeof(int4) * (size_t)L.B * hq * (TR_PREFILL_SLOTS / 2)) == hipSuccess;
-  ok = ok && hipMalloc((void**)&c->pf_part,
-                       sizeof(float) * (size_t)L.B * hq * TR_PREFILL_SLOTS * 128 * (L.D + 4)) == hipSuccess;
+  c->np = (L.pfN + 63) / 64 * 64;
+  c->pf_uph = L.pfN ? tr_prefill_units_per_head(L.pfN) : 0;
+  if (L.pfN > 0) {                                 // prefill scratch, sized by its capacity
+    ok = ok && hipMalloc((void**)&c->rows, sizeof(int32_t) * (size_t)L.B * hq * L.pfN) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->row_counts, sizeof(int32_t) * (size_t)L.B * hq * 4) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->dk, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->dv, sizeof(uint16_t) * (size_t)L.B * L.H * c->np * L.D) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->dkf, sizeof(float2) * (size_t)L.B * L.H * c->np) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->pf_units, sizeof(int4) * (size_t)L.B * hq * c->pf_uph) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->pf_merges, sizeof(int4) * (size_t)L.B * hq * (TR_PREFILL_SLOTS / 2)) == hipSuccess;
+    ok = ok && hipMalloc((void**)&c->pf_part,
+                         sizeof(float) * (size_t)L.B * hq * TR_PREFILL_SLOTS * 128 * (L.D + 4)) == hipSuccess;
+  }
   if (!ok) {
     hipGetLastError();
     free_all(c);
@@ -467,6 +474,13 @@ tr_status tr_kv_cache_status(tr_kv_cache* c, void* stream) {
   if (hipMemcpy(&flags, c->lay.err, sizeof(flags), hipMemcpyDeviceToHost) != hipSuccess) return TR_ERR_HIP;
   if (flags & TR_ERRF_NO_PAGES) return TR_ERR_OUT_OF_PAGES;
   if (flags & (TR_ERRF_BAD_BITS | TR_ERRF_BAD_MODE)) return TR_ERR_BAD_VALUE;
+  if (flags & TR_ERRF_RANGE) return TR_ERR_RANGE;
+  return TR_OK;
+}
+
+tr_status tr_kv_cache_set_decode_chunks(tr_kv_cache* c, int32_t n) {
+  if (!c || n < 0 || n > c->max_chunks) return TR_ERR_INVALID_ARG;
+  c->force_chunks = n;
   return TR_OK;
 }
 

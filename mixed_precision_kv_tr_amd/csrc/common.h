@@ -18,6 +18,7 @@ struct tr_kv_cache {
   // decode split-K partials: [B][HQ][max_chunks][D + 2] floats (o[D], m, l)
   float* partials;
   int32_t max_chunks;
+  int32_t force_chunks;           // tr_kv_cache_set_decode_chunks: 0 = automatic
   // prefill scratch: compacted query rows per (seq, query head) [B][HQ][N] and counts [B][HQ][4]
   int32_t* rows;
   int32_t* row_counts;
@@ -54,6 +55,10 @@ struct tr_kv_cache {
 #define TR_DECODE_MIN_CHUNK 256
 #endif
 #endif
+
+// Partial-result slots per (seq, query head) of the decode split-K are at least this many, so a
+// forced chunk count (tr_kv_cache_set_decode_chunks) up to it is always available.
+#define TR_DECODE_FORCE_MAX 64
 
 // Largest decode chunk (positions) this layout allows.
 inline int tr_decode_max_chunk(const CacheLayout& L) {

@@ -577,8 +577,9 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
   if (nch < (n + max_ch - 1) / max_ch) nch = (n + max_ch - 1) / max_ch;
   if (nch > c->max_chunks) nch = c->max_chunks;
   if (nch < 1) nch = 1;
+  if (c->force_chunks > 0) nch = c->force_chunks < n ? c->force_chunks : n;
   const int CH = (n + nch - 1) / nch;
-  if (CH > max_ch) return TR_ERR_UNSUPPORTED;
+  if (CH > max_ch || nch > c->max_chunks) return TR_ERR_UNSUPPORTED;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
   const int grid = BH * nch;
   {

@@ -29,9 +29,12 @@
 #define TR_ERRF_BAD_BITS 1u
 #define TR_ERRF_BAD_MODE 2u
 #define TR_ERRF_NO_PAGES 4u
+#define TR_ERRF_RANGE 8u                // prefill: a stored V value outside fp16's range
 
 struct CacheLayout {
   int32_t L, B, H, D, N;          // layers, batch, heads, head_dim, max_tokens
+  int32_t pfN;                    // positions a prefill call may reach (0: no prefill scratch);
+                                  // also the stride of the prefill row lists
   int32_t cb;                     // code bytes per head per page (K or V)
   int32_t page_bytes;
   int32_t ptok[TR_NCLASS];        // tokens per page (a power of two)

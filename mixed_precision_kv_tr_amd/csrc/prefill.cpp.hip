@@ -73,7 +73,8 @@ __device__ __forceinline__ float xor32_sum(float v) {
 // ceil(n / kch) near-equal chunks that run as separate units, write partial (max, sum, O) rows,
 // and are merged by k_prefill_merge.  kch is the smallest of 16, 32, 64, ... key tiles for which the
 // head's partial results fit its kSlotsPerHead slots (no split if none does).
-//   unit  = (r0 | full << 31, rend, kt0 | kt1 << 16, partial slot or -1)
+//   unit  = (r0 | full << 31, rend | (partial slot + 1, or 0) << 25, kt0, kt1)   (rend < 2^25:
+//           positions are below 2^24 for every cache tr_kv_cache_alloc accepts)
 //   merge = (r0, rend, first slot, chunks)
 // Units are listed heaviest first: full tiles from the last (longest key range), then local.
 // Sum over the 64 lanes of a wave (the result in every lane).
@@ -145,7 +146,7 @@ __device__ __forceinline__ void build_units(int sh, int p0, int window, int nful
     if (k < ntl) {
       for (int cc = 0; cc < nch; ++cc) {
         const int kt0 = klo + ((khi - klo) * cc) / nch, kt1 = klo + ((khi - klo) * (cc + 1)) / nch;
-        units[pos[0] + cc] = make_int4(r0 | (full << 31), rend, kt0 | (kt1 << 16), nch > 1 ? pos[1] + cc : -1);
+        units[pos[0] + cc] = make_int4(r0 | (full << 31), rend | ((nch > 1 ? pos[1] + cc + 1 : 0) << 25), kt0, kt1);
       }
       if (nch > 1) merges[pos[2]] = make_int4(r0, rend, pos[1], nch);
     }
@@ -173,7 +174,7 @@ __device__ __forceinline__ void compact_rows(const CacheLayout& c, int HQ, int s
   __shared__ int32_t tpos[2 * kTileCap];           // first / last position of each row tile
   const int s = sh / HQ, h = sh % HQ;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int32_t* rl = rows + (int64_t)sh * c.N;
+  int32_t* rl = rows + (int64_t)sh * c.pfN;
   const uint8_t* mcol = mode + (int64_t)s * T * HQ + h;
   const int R = (T + NT - 1) / NT;
   const int i0 = min(T, tid * R), i1 = min(T, i0 + R);
@@ -302,6 +303,12 @@ __device__ __forceinline__ void load_slice_c(const uint8_t* p, uint32_t* w) {
 
 __device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
+// The attention's PV product takes v_hat in fp16: a stored value with |v_hat| >= 65504 (fp16's
+// largest finite value) sets the sticky range flag instead of turning into an infinity silently.
+// Every V input with |v| <= 65280 (the largest bf16 below 65504) stays inside: v_hat lies within
+// its group's [min, max] up to 2^-22 relative.
+constexpr float kF16Max = 65504.0f;
+
 // Dequantize DPL channels of one (token, head) K/V pair of width class C into the dense
 // scratch (K row slice) and the LDS V^T tile.
 // Position of key k (0..31) of a tile inside a V^T row: bits 2 and 3 swapped within each group
@@ -342,17 +349,26 @@ __device__ __forceinline__ void dense_token(const uint8_t* pb, const CacheLayout
       vt[part * DPL + 2 * e + 1][vt_pos(tk)] = (_Float16)tr_bf16_hi(wv[e]);
     }
     *kf_out = key_factors(true, 1.0f, 0.0f, kscale);
+    float vmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL / 2; ++e) vmax = tr_max(vmax, tr_max(fabsf(tr_bf16_lo(wv[e])), fabsf(tr_bf16_hi(wv[e]))));
+    if (vmax >= kF16Max) atomicOr(c.err, TR_ERRF_RANGE);
   } else {
     const int P = c.ptok[C];
     const float2 szk = reinterpret_cast<const float2*>(pb + c.sk_off[C])[(int64_t)h * P + j];
     const float2 szv = reinterpret_cast<const float2*>(pb + c.sv_off[C])[(int64_t)h * P + j];
+    float vmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < DPL; e += 2) {
       const float k0 = (float)code_at<b>(wk, e), k1 = (float)code_at<b>(wk, e + 1);
       ko[e / 2] = (__float_as_uint(k0) >> 16) | (__float_as_uint(k1) & 0xffff0000u);
-      vt[part * DPL + e][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
-      vt[part * DPL + e + 1][vt_pos(tk)] = (_Float16)fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
+      const float v0 = fmaf(szv.x, (float)code_at<b>(wv, e), szv.y);
+      const float v1 = fmaf(szv.x, (float)code_at<b>(wv, e + 1), szv.y);
+      vmax = tr_max(vmax, tr_max(fabsf(v0), fabsf(v1)));
+      vt[part * DPL + e][vt_pos(tk)] = (_Float16)v0;
+      vt[part * DPL + e + 1][vt_pos(tk)] = (_Float16)v1;
     }
+    if (vmax >= kF16Max) atomicOr(c.err, TR_ERRF_RANGE);
     *kf_out = key_factors(false, szk.x, szk.y, kscale);
   }
 #pragma unroll
@@ -474,8 +490,14 @@ __global__ __launch_bounds__(4 * D) void k_prefill_write(CacheLayout c, int laye
     // The V^T column is XOR-swizzled by 16 * (part & 3): the lanes of one store hold 16 positions
     // of 4 parts whose rows are 16 rows (a multiple of 64 banks) apart, so without it they collide.
     const int tpos = vt_pos(tk) ^ (16 * (part & 3));
+    float vmax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < NV; ++e) vt[part * NV + e][tpos] = live ? (_Float16)fmaf(qv.s, qv.f[e], zv) : (_Float16)0.0f;
+    for (int e = 0; e < NV; ++e) {
+      const float vh = fmaf(qv.s, qv.f[e], zv);
+      vmax = tr_max(vmax, fabsf(vh));
+      vt[part * NV + e][tpos] = live ? (_Float16)vh : (_Float16)0.0f;
+    }
+    if (live && vmax >= kF16Max) atomicOr(c.err, TR_ERRF_RANGE);
   }
   if (live && base) {
     if (h == 0 && part == 0) reinterpret_cast<int32_t*>(base)[j] = p;
@@ -538,8 +560,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D == 64 
   if (u >= counts[sh * 4 + 2]) return;
   const int4 unit = units[(int64_t)sh * uph + u];
   const bool full = unit.x < 0;
-  const int r0 = unit.x & 0x7fffffff, rend = unit.y;
-  const int kt0 = unit.z & 0xffff, kt1 = unit.z >> 16, slot = unit.w;
+  const int r0 = unit.x & 0x7fffffff, rend = unit.y & 0x1ffffff;
+  const int kt0 = unit.z, kt1 = unit.w, slot = (unit.y >> 25) - 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int kb0 = kt0 * BN;                        // this unit's key tiles [kt0, kt1)
@@ -589,7 +611,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D == 64 
 
   const int ri = r0 + wave * 32 + n;
   const bool row_ok = ri < rend;
-  const int i = row_ok ? rows[(int64_t)sh * c.N + ri] : 0;
+  const int i = row_ok ? rows[(int64_t)sh * c.pfN + ri] : 0;
   const int t = row_ok ? p0 + i : -1;
   const int lo = row_ok ? (full ? 0 : max(0, t - window)) : 0x7fffffff;
 
@@ -807,7 +829,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
     constexpr int TPZ = D / 8, RPI = kBlock / TPZ;
     const int nfull = counts[sh * 4 + 0], nl = counts[sh * 4 + 1], nskip = T - nfull - nl;
     const int per = (nskip + MPH - 1) / MPH, k1 = min(nskip, (mi + 1) * per);
-    const int32_t* sl = rows + (int64_t)sh * c.N + nfull + nl;
+    const int32_t* sl = rows + (int64_t)sh * c.pfN + nfull + nl;
     for (int k = mi * per + (int)threadIdx.x / TPZ; k < k1; k += RPI)
       reinterpret_cast<uint4*>(out + (((int64_t)s * T + sl[k]) * HQ + h) * D)[threadIdx.x % TPZ] = make_uint4(0, 0, 0, 0);
   }
@@ -847,7 +869,7 @@ __global__ __launch_bounds__(kBlock) void k_prefill_merge(CacheLayout c, int T, 
     M = Mn;
   }
   const float inv = 1.0f / den;
-  const int i = rows[(int64_t)sh * c.N + ri];
+  const int i = rows[(int64_t)sh * c.pfN + ri];
   uint16_t* orow = out + (((int64_t)s * T + i) * HQ + h) * D + d0;
 #pragma unroll
   for (int x = 0; x < CPT; x += 4) {
@@ -887,7 +909,7 @@ tr_status prefill_launch_d(tr_kv_cache* c, int layer, int p0, const uint16_t* q,
   const int BQ = L.B * c->hq;            // (seq, query head): compaction, attention, merge
   const float kscale = (float)(1.4426950408889634 / sqrt((double)D));
   const int uph = tr_prefill_units_per_head(T);
-  if (uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
+  if (p0 + T > L.pfN || uph > c->pf_uph) return TR_ERR_UNSUPPORTED;
   const int pend = p0 + T;
   // Short calls take the one-launch append and stage every dense tile from the pages; longer
   // ones assign their slots beside the row compaction, then quantize and stage their own

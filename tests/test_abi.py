@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     import mixed_precision_kv_tr_amd as tr
-    for code in range(7):
+    for code in range(8):
         s = tr.tr_status_str(code)
         assert s and s != "unknown status"
     assert tr.tr_status_str(99) == "unknown status"
@@ -58,6 +58,11 @@ def test_host_side_validation_without_gpu():
     zero_layers = _Desc(0, 1, 1, 64, 16, 0, 0)
     assert _alloc(ctypes.byref(zero_layers), ctypes.byref(h)) == 1
     assert _free(None) == 0
+    from mixed_precision_kv_tr_amd._lib import _set_chunks
+    assert _set_chunks(None, 3) == 1
+    for bad_pf in (-2, 17):                                  # prefill capacity: -1, 0 or 1 .. max_tokens
+        d = _Desc(1, 1, 1, 64, 16, 0, 0, 0, bad_pf)
+        assert _alloc(ctypes.byref(d), ctypes.byref(h)) == 1 and h.value is None
     assert _length(None, 0) == -1
     assert _write(None, 0, None, None, None, 1, None) == 1
     assert _decode(None, 0, None, None, 0, None, None) == 1

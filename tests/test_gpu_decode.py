@@ -1,8 +1,6 @@
 """GPU parity of decode routed attention (Eq. 2 over the Eq. 4 cache) against the oracle:
 |gpu - oracle| <= 2e-3 + 1e-2 |oracle| element-wise, on the same dequantized K/V."""
 
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -20,8 +18,9 @@ def tr():
     return tr
 
 
-def run_decode(tr, case, window, page_code_bytes=0, layers=1, layer=0, split_at=None):
-    """Write positions 0..C-1, then the new token C (a second write), then decode at t = C."""
+def run_decode(tr, case, window, page_code_bytes=0, layers=1, layer=0, split_at=None, chunks=0):
+    """Write positions 0..C-1, then the new token C (a second write), then decode at t = C
+    (split into `chunks` position chunks if > 0)."""
     k, v, bits, q, mode = case["k"], case["v"], case["bits"], case["q"], case["mode"]
     B, T, H, D = k.shape
     HQ = q.shape[1]
@@ -34,9 +33,12 @@ def run_decode(tr, case, window, page_code_bytes=0, layers=1, layer=0, split_at=
     tr.tr_kv_quantize_write(cache, layer, k[:, cut:].contiguous(), v[:, cut:].contiguous(),
                             bits[:, cut:].contiguous())
     out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
-    tr.tr_routed_attn_decode(cache, layer, q, mode, window, out)
-    status = tr.tr_kv_cache_status(cache)
-    cache.close()
+    tr.tr_kv_cache_set_decode_chunks(cache, chunks)
+    try:
+        tr.tr_routed_attn_decode(cache, layer, q, mode, window, out)
+        status = tr.tr_kv_cache_status(cache)
+    finally:
+        cache.close()
     return out, status
 
 
@@ -119,6 +121,10 @@ def test_decode_config4_full_size(tr):
 
 
 def test_decode_chunking_and_paging_invariance(tr):
+    """Page sizes leave the output bit-identical; every forced split-K chunk count matches the
+    oracle: 5 and 8 chunks (one combine batch), 40 and 64 chunks (merges of more than 32 chunks,
+    i.e. two combine batches), a single chunk over a whole window of up to 512 positions, and a
+    single chunk over a longer window is refused."""
     say("decode: split-K chunk counts and page sizes agree")
     case = random_case(2, 2500, 4, 128, window=700, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
                        mode_weights={"local": 0.5, "full": 0.5}, seed=77, device="cuda", n_queries=1)
@@ -128,16 +134,20 @@ def test_decode_chunking_and_paging_invariance(tr):
         other, _ = run_decode(tr, case, 700, page_code_bytes=pcb)
         assert torch.equal(base, other), f"page_code_bytes={pcb} changed the output"
     refs = oracle_decode(case, 700, range(2))
-    for nch in ("1", "3", "40"):
-        os.environ["TR_DECODE_NCH"] = nch
-        try:
-            out, _ = run_decode(tr, case, 700)
-        finally:
-            del os.environ["TR_DECODE_NCH"]
+    for nch in (5, 8, 40, 64):
+        out, status = run_decode(tr, case, 700, chunks=nch)
+        assert status == 0
         got = bf16_to_f64(out)
         for s in range(2):
             compare_out(got[s], refs[s], f"nch={nch} seq {s}")
-
+    with pytest.raises(tr.TriRouteError):
+        run_decode(tr, case, 700, chunks=1)               # 2500 positions in one item: refused
+    short = random_case(2, 512, 4, 128, window=100, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                        mode_weights={"local": 0.5, "full": 0.5}, seed=78, device="cuda", n_queries=1)
+    short["q"], short["mode"] = short["q"][:, 0].contiguous(), short["mode"][:, 0].contiguous()
+    out, status = run_decode(tr, short, 100, chunks=1)
+    assert status == 0
+    check(short, out, 100, range(2), "nch=1, 512-position window")
 
 def test_decode_bad_mode_is_flagged(tr):
     case = random_case(1, 20, 2, 64, window=3, bit_weights={4: 1.0}, mode_weights={"full": 1.0},

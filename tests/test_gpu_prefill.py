@@ -229,3 +229,86 @@ def test_prefill_long_prompt_sampled(tr):
     compare_out(got[pos], ref, f"T={T} sampled rows")
     skip = np.nonzero(mode == 0)[0]
     assert np.all(got[skip] == 0.0)
+
+
+def test_prefill_d128_split_tiles(tr):
+    """head_dim 128 with key-split row tiles: 1536 mostly-full rows.  A full row tile near the end
+    spans ~48 key tiles of 32 keys; the unit list cuts such tiles into chunks (32 key tiles each
+    here: chunks of 16 would need more than the 16 partial slots of a head), so split units write
+    partial results and the head_dim-128 merge combines them."""
+    T, w = 1536, 300
+    say(f"prefill D=128 T={T}, split tiles")
+    case = random_case(2, T, 2, 128, window=w, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"skip": 0.05, "local": 0.15, "full": 0.8}, seed=1536, device="cuda")
+    cache, out, status = run_prefill(tr, case, w)
+    cache.close()
+    assert status == 0
+    full = (case["mode"].cpu().numpy() == 2).sum(axis=1)           # [B, H] full rows per head
+    assert full.min() > 1024                                       # so the last full tile spans > 32 key tiles
+    check(case, out, w, range(2), f"D=128 T={T}")
+
+
+def test_prefill_value_range_is_flagged_and_decode_is_not_limited(tr):
+    """A V value beyond fp16's range (the prefill attention's V operand) sets TR_ERR_RANGE in
+    prefill, while the cache stores it bit-exactly and decode over the same positions matches the
+    oracle; values up to 65280 (the largest bf16 below 65504) pass prefill unflagged and match."""
+    B, T, H, D, w = 1, 200, 2, 128, 50
+    case = random_case(B, T, H, D, window=w, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                       mode_weights={"local": 0.5, "full": 0.5}, seed=65504, device="cuda")
+    v = case["v"].float()
+    g = torch.Generator(device="cuda").manual_seed(3)
+    big = 7.0e4 + 10.0 * torch.randn((D,), generator=g, device="cuda")
+    v[0, 30, 0] = big                                             # a native (b = 16) row beyond fp16
+    v[0, 90, 1] = big.flip(0)                                     # an 8-bit group beyond fp16
+    case["bits"][0, 30], case["bits"][0, 90] = 16, 8
+    case["v"] = v.to(torch.bfloat16)
+    cache, out, status = run_prefill(tr, case, w)
+    assert status == 7                                            # TR_ERR_RANGE
+    check_codes(export_layer(tr, cache, 0, 0, T, B, H, D), case["k"], case["v"], case["bits"], where="range")
+    cache.close()
+    # decode at t = T - 1 over the same positions (written by tr_kv_quantize_write): no limit
+    dcase = {x: case[x] for x in ("k", "v", "bits")}
+    dcase["q"], dcase["mode"] = case["q"][:, T - 1].contiguous(), case["mode"][:, T - 1].contiguous()
+    dcase["mode"].fill_(2)
+    cache = tr.tr_kv_cache_alloc(1, B, H, D, T, prefill_tokens=-1)
+    tr.tr_kv_quantize_write(cache, 0, case["k"][:, :T - 1].contiguous(), case["v"][:, :T - 1].contiguous(),
+                            case["bits"][:, :T - 1].contiguous())
+    tr.tr_kv_quantize_write(cache, 0, case["k"][:, T - 1:].contiguous(), case["v"][:, T - 1:].contiguous(),
+                            case["bits"][:, T - 1:].contiguous())
+    dec = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    tr.tr_routed_attn_decode(cache, 0, dcase["q"], dcase["mode"], w, dec)
+    assert tr.tr_kv_cache_status(cache) == 0
+    cache.close()
+    ref = oracle.attend_cached(u16(dcase["q"])[0][None], u16(case["k"])[0], u16(case["v"])[0],
+                               case["bits"].cpu().numpy()[0], dcase["mode"].cpu().numpy()[0][None],
+                               np.array([T - 1]), w)["out"][0]
+    compare_out(bf16_to_f64(dec)[0], ref, "decode over values beyond fp16")
+    # the largest bf16 below fp16's limit: no flag, and prefill matches the oracle
+    v[0, 30, 0] = 65280.0
+    v[0, 90, 1] = -65280.0
+    case["v"] = v.to(torch.bfloat16)
+    cache, out, status = run_prefill(tr, case, w)
+    cache.close()
+    assert status == 0
+    check(case, out, w, [0], "prefill with |v| = 65280")
+
+
+def test_prefill_capacity_of_the_scratch(tr):
+    """prefill_tokens bounds the positions a prefill may reach; -1 makes a decode-only cache that
+    refuses prefill (host-side, nothing launched) but still writes and decodes."""
+    case = random_case(1, 64, 2, 64, window=8, bit_weights={4: 1.0}, mode_weights={"full": 1.0}, seed=6,
+                       device="cuda")
+    out = torch.empty((1, 64, 2, 64), dtype=torch.bfloat16, device="cuda")
+    args = (case["q"], case["k"], case["v"], case["bits"], case["mode"], 64, 8, out)
+    cache = tr.tr_kv_cache_alloc(1, 1, 2, 64, 200, prefill_tokens=-1)
+    with pytest.raises(tr.TriRouteError, match="UNSUPPORTED"):
+        tr.tr_routed_attn_prefill(cache, 0, *args)
+    assert tr.tr_kv_cache_length(cache, 0) == 0
+    cache.close()
+    cache = tr.tr_kv_cache_alloc(1, 1, 2, 64, 200, prefill_tokens=100)
+    tr.tr_routed_attn_prefill(cache, 0, *args)                     # positions 0 .. 63
+    with pytest.raises(tr.TriRouteError, match="UNSUPPORTED"):
+        tr.tr_routed_attn_prefill(cache, 0, *args)                 # would reach 128 > 100
+    assert tr.tr_kv_cache_length(cache, 0) == 64 and tr.tr_kv_cache_status(cache) == 0
+    cache.close()
+    check(case, out, 8, [0], "prefill within a 100-position scratch")
