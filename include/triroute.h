@@ -237,8 +237,9 @@ tr_status tr_controller_route(const tr_controller_weights* w, const void* x, con
  *   FFN_t = sum_{j in S_t} p_tj / sum_{j' in S_t} p_tj' * f_j(RMSNorm(x_t)),  p_t = softmax(z_t),
  * over E experts plus the null expert f_0 = 0 (gate index 0), S_t the top_k largest p_t (ties to
  * the lower index), each expert a SwiGLU FFN f(u) = W2 (silu(W1 u) * (W3 u)) with no biases.
- * The hidden activation enters the down product as bf16; products run on the matrix cores with
- * bf16 operands and fp32 accumulation.  The gate logits come from the caller (e.g. an expert head
+ * Products run on the matrix cores with bf16 operands and fp32 accumulation: x and the weights
+ * exactly (the RMSNorm scale applied to the fp32 sums), the hidden activation as a bf16 pair
+ * hi + lo (about 16 significant bits).   The gate logits come from the caller (e.g. an expert head
  * of the controller, Eq. (5)).  A handle owns the packed weights and the scratch of calls up to
  * max_tokens tokens. */
 typedef struct {

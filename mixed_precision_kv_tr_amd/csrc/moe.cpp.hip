@@ -11,9 +11,11 @@
 //   k_moe_up      one workgroup per (slot, expert, 32 or 64 listed tokens, 128 hidden units): the gate
 //                 and up products on the matrix cores (x rows gathered from the list, bf16 x and
 //                 packed bf16 W1 / W3 as exact operands, fp32 accumulation), then the RMSNorm
-//                 scale, silu(g) * u and bf16 rounding into the hidden buffer.
+//                 scale, silu(g) * u, stored into the hidden buffer as a bf16 pair: hi = bf16(h)
+//                 and lo = bf16(h - hi), together h to about 2^-16 relative.
 //   k_moe_down    per slot, in slot order: one workgroup per (expert, 32 or 64 listed tokens, 128 output
-//                 channels): the down product of the gathered hidden rows, times the token's
+//                 channels): the down product of the gathered hidden rows (hi and lo halves
+//                 against the same weights, both on the matrix cores), times the token's
 //                 weight, stored (slot 0; the null expert stores zeros) or added (slot 1) into the
 //                 fp32 output -- no atomics, so the result does not depend on scheduling.
 // Weight matrices are packed once (tr_moe_set_weights) into the operand order of the matrix-core
@@ -39,7 +41,7 @@ struct tr_moe {
   float* inv_rms;    // [max_tokens]
   int32_t* lists;    // [k][E + 1][max_tokens] tokens per (slot, expert), in token order
   int32_t* counts;   // [k][E + 1]
-  uint16_t* hbuf;    // [max_tokens * k][de] bf16 hidden rows (row t * k + slot)
+  uint16_t* hbuf;    // [max_tokens * k][2][de] bf16 hidden rows (row t * k + slot): hi, then lo
   bool weights_set;
 };
 
@@ -269,7 +271,10 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
       if (row < ntok) {
         const float gv = ag[mb][reg] * inv[row], uv = au[mb][reg] * inv[row];
         const float h = gv / (1.0f + expf(-gv)) * uv;
-        hbuf[((int64_t)tok[row] * k + slot) * de + n] = tr_f32_to_bf16(h);
+        const uint16_t hi = tr_f32_to_bf16(h);
+        uint16_t* hr = hbuf + ((int64_t)tok[row] * k + slot) * 2 * de + n;
+        hr[0] = hi;
+        hr[de] = tr_f32_to_bf16(h - tr_bf16_lo(hi));
       }
     }
   }
@@ -305,8 +310,9 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
     constexpr int PR = 2 * kPS;
     static_assert(kTile * PR == 256, "one piece per thread per stage");
     __shared__ uint4 hs[2][kTile][PR + 1];
+    __shared__ uint4 hl[2][kTile][PR + 1];        // the lo halves
     const int prow = tid / PR, pp = tid % PR;
-    const uint16_t* hrow = hbuf + ((int64_t)tok[prow] * k + slot) * de + 32 * (pp & 1);
+    const uint16_t* hrow = hbuf + ((int64_t)tok[prow] * k + slot) * 2 * de + 32 * (pp & 1);
     auto haddr = [&](int st) {
       const int s = st + (pp >> 1);
       return hrow + 64 * (s >> 2) + 8 * (s & 3);
@@ -320,19 +326,25 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
       for (int q = 0; q < kPS; ++q) wv[q] = gload16(dr + (st + q) * wstep);
     };
     hs[0][prow][pp] = gload16(haddr(0));
+    hl[0][prow][pp] = gload16(haddr(0) + de);
     wload(0, wa);
     __syncthreads();
     int buf = 0;
     for (int st = 0; st < ns; st += kPS) {
       const int nx = min(st + kPS, ns - kPS);
       const uint4 hn = gload16(haddr(nx));
+      const uint4 hln = gload16(haddr(nx) + de);
       uint4 wn[kPS];
       wload(nx, wn);
 #pragma unroll
       for (int q = 0; q < kPS; ++q)
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[mb] = mfma(hs[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
+        for (int mb = 0; mb < kMB; ++mb) {
+          acc[mb] = mfma(hs[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
+          acc[mb] = mfma(hl[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
+        }
       hs[buf ^ 1][prow][pp] = hn;
+      hl[buf ^ 1][prow][pp] = hln;
 #pragma unroll
       for (int q = 0; q < kPS; ++q) wa[q] = wn[q];
       buf ^= 1;
@@ -383,7 +395,7 @@ tr_status tr_moe_alloc(const tr_moe_desc* desc, tr_moe** out) {
   ok = ok && hipMalloc((void**)&m->inv_rms, sizeof(float) * M) == hipSuccess;
   ok = ok && hipMalloc((void**)&m->lists, sizeof(int32_t) * K * E1 * M) == hipSuccess;
   ok = ok && hipMalloc((void**)&m->counts, sizeof(int32_t) * K * E1) == hipSuccess;
-  ok = ok && hipMalloc((void**)&m->hbuf, 2 * M * K * q.d_expert) == hipSuccess;
+  ok = ok && hipMalloc((void**)&m->hbuf, 2 * 2 * M * K * q.d_expert) == hipSuccess;
   if (!ok) {
     tr_moe_free(m);
     return TR_ERR_HIP;
