@@ -53,7 +53,9 @@ typedef enum {
   TR_ERR_HIP = 4,           /* a HIP runtime call failed (allocation, launch, copy) */
   TR_ERR_UNSUPPORTED = 5,   /* a valid but unsupported shape (head_dim not 64/128, ...) */
   TR_ERR_BAD_VALUE = 6,     /* sticky: a bits or mode element outside its domain was seen */
-  TR_ERR_RANGE = 7          /* sticky: prefill met a stored V value with |v_hat| >= 65504 */
+  TR_ERR_RANGE = 7,         /* sticky: prefill met a stored V value with |v_hat| >= 65504 */
+  TR_ERR_SCRATCH = 8        /* tr_routed_attn_decode_noalloc: the call needs more scratch than
+                               its fixed array holds (nothing launched) */
 } tr_status;
 
 /* Attention modes of Eq. (2): one uint8 per (sequence, query token, head). */
@@ -126,6 +128,21 @@ tr_status tr_kv_quantize_write(tr_kv_cache* cache, int32_t layer, const void* k,
  *   out:  bf16 [batch, num_query_heads, head_dim]; skip heads get zeros */
 tr_status tr_routed_attn_decode(tr_kv_cache* cache, int32_t layer, const void* q, const uint8_t* mode,
                                 int32_t window, void* out, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): tr_routed_attn_decode with every argument and result
+ * the same, whose split-K partial results go to a fixed 8 MiB array in the library's device
+ * memory (one per GPU, held until the process ends) instead of the cache's scratch.  It calls
+ * no hipMalloc, hipFree or other allocating routine and records no profiling events.  The
+ * partials of one call take B * num_query_heads * chunks * (head_dim + 2) * 4 bytes; the call
+ * picks the chunk count as the plain entry point does, lowered to what fits, and returns
+ * TR_ERR_SCRATCH (launching nothing) when even the fewest chunks a full window allows (windows
+ * split into chunks of at most 512 positions) do not fit.  Calls on one GPU share the array:
+ * two calls whose executions overlap on one GPU (different streams without ordering) race and
+ * give unspecified results; calls ordered on one stream are safe.  Nothing in the array needs
+ * to start at zero (every chunk writes its own record before the merge reads it). */
+tr_status tr_routed_attn_decode_noalloc(tr_kv_cache* cache, int32_t layer, const void* q, const uint8_t* mode,
+                                        int32_t window, void* out, void* stream);
 
 /* Prefill: write T new tokens with Eq. (4), then run Eq. (2) for all T queries (causal, each
  * query at its own position len + i, reading the cache just written).

@@ -12,7 +12,7 @@ _EXPORTS = (
     "tr_kv_cache_alloc", "tr_kv_cache_free", "tr_kv_cache_reset", "tr_kv_cache_length",
     "tr_kv_quantize_write", "tr_routed_attn_decode", "tr_routed_attn_prefill", "tr_kv_cache_export",
     "tr_kv_cache_status", "tr_kv_cache_pages_used", "tr_status_str", "tr_kv_cache_truncate",
-    "tr_kv_cache_set_decode_chunks",
+    "tr_kv_cache_set_decode_chunks", "tr_routed_attn_decode_noalloc",
     "tr_profile_enable", "tr_profile_read", "PROFILE_FAMILIES", "tr_controller_route",
     "ControllerWeights", "MoE", "tr_moe_alloc", "tr_moe_set_weights", "tr_moe_ffn",
 )

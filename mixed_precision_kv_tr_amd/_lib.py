@@ -52,6 +52,7 @@ _reset = _sig("tr_kv_cache_reset", ctypes.c_int, _vp, _vp)
 _length = _sig("tr_kv_cache_length", _i32, _vp, _i32)
 _write = _sig("tr_kv_quantize_write", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _i32, _vp)
 _decode = _sig("tr_routed_attn_decode", ctypes.c_int, _vp, _i32, _vp, _vp, _i32, _vp, _vp)
+_decode_noalloc = _sig("tr_routed_attn_decode_noalloc", ctypes.c_int, _vp, _i32, _vp, _vp, _i32, _vp, _vp)
 _prefill = _sig("tr_routed_attn_prefill", ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp)
 _export = _sig("tr_kv_cache_export", ctypes.c_int, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
 _status = _sig("tr_kv_cache_status", ctypes.c_int, _vp, _vp)
@@ -70,7 +71,8 @@ _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ct
 PROFILE_FAMILIES = ("write", "decode_split", "decode_combine", "prefill_prep", "prefill_attn", "prefill_merge")
 
 STATUS_NAMES = {0: "TR_OK", 1: "TR_ERR_INVALID_ARG", 2: "TR_ERR_CAPACITY", 3: "TR_ERR_OUT_OF_PAGES",
-                4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE", 7: "TR_ERR_RANGE"}
+                4: "TR_ERR_HIP", 5: "TR_ERR_UNSUPPORTED", 6: "TR_ERR_BAD_VALUE", 7: "TR_ERR_RANGE",
+                8: "TR_ERR_SCRATCH"}
 
 
 class TriRouteError(RuntimeError):
@@ -162,6 +164,12 @@ def tr_kv_quantize_write(cache: KVCache, layer: int, k, v, bits, n_new: int | No
 def tr_routed_attn_decode(cache: KVCache, layer: int, q, mode, window: int, out, stream=None):
     _check(_decode(cache.handle, layer, _ptr(q), _ptr(mode), int(window), _ptr(out), _stream(stream)),
            "tr_routed_attn_decode")
+
+
+def tr_routed_attn_decode_noalloc(cache: KVCache, layer: int, q, mode, window: int, out, stream=None):
+    """tr_routed_attn_decode with the split-K partials in the library's fixed device array."""
+    _check(_decode_noalloc(cache.handle, layer, _ptr(q), _ptr(mode), int(window), _ptr(out), _stream(stream)),
+           "tr_routed_attn_decode_noalloc")
 
 
 def tr_routed_attn_prefill(cache: KVCache, layer: int, q, k, v, bits, mode, T: int, window: int, out,

@@ -252,6 +252,7 @@ const char* tr_status_str(tr_status s) {
     case TR_ERR_UNSUPPORTED: return "unsupported shape";
     case TR_ERR_BAD_VALUE: return "a bits or mode element outside its domain";
     case TR_ERR_RANGE: return "a value outside the fp16 range of the prefill attention's V operand";
+    case TR_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point's fixed array";
   }
   return "unknown status";
 }
@@ -431,6 +432,13 @@ tr_status tr_routed_attn_decode(tr_kv_cache* c, int32_t layer, const void* q, co
   if (!c || layer < 0 || layer >= c->lay.L || !q || !mode || !out || window < 0) return TR_ERR_INVALID_ARG;
   if (c->len[layer] < 1) return TR_ERR_INVALID_ARG;
   return tr_decode_launch(c, layer, (const uint16_t*)q, mode, window, (uint16_t*)out, (hipStream_t)stream);
+}
+
+tr_status tr_routed_attn_decode_noalloc(tr_kv_cache* c, int32_t layer, const void* q, const uint8_t* mode,
+                                        int32_t window, void* out, void* stream) {
+  if (!c || layer < 0 || layer >= c->lay.L || !q || !mode || !out || window < 0) return TR_ERR_INVALID_ARG;
+  if (c->len[layer] < 1) return TR_ERR_INVALID_ARG;
+  return tr_decode_noalloc_launch(c, layer, (const uint16_t*)q, mode, window, (uint16_t*)out, (hipStream_t)stream);
 }
 
 tr_status tr_routed_attn_prefill(tr_kv_cache* c, int32_t layer, const void* q, const void* k, const void* v,

@@ -151,6 +151,9 @@ __device__ __forceinline__ uint32_t tr_wave_incl_scan(uint32_t v) {
 // Decode entry points implemented in decode.hip / prefill.hip.
 tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
                            uint16_t* out, hipStream_t stream);
+// The same with the split-K partials in the library's file-scope device scratch (no allocation).
+tr_status tr_decode_noalloc_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
+                                   uint16_t* out, hipStream_t stream);
 // The whole prefill call: Eq. (4) write of positions [p0, p0 + T), then routed attention of their
 // queries over [0, p0 + T).
 tr_status tr_prefill_launch(tr_kv_cache* c, int layer, int p0, const uint16_t* q, const uint16_t* k,

@@ -29,6 +29,8 @@
 // k_decode_combine: log-sum-exp merge of multi-chunk windows -> bf16.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -563,44 +565,114 @@ __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH,
 
 }  // namespace
 
-tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
-                           uint16_t* out, hipStream_t stream) {
+namespace {
+
+// Chunks per window for a decode over n positions of BH (seq, query head) pairs with room for
+// `limit` partial records per pair: about 8192 work items if every head were full (a few times
+// the waves the chip holds at once), but no chunk below kMinChunk positions and none above the
+// work item's limit; 0 if `limit` cannot hold the chunks a full window needs.
+int decode_chunks(const tr_kv_cache* c, int n, int BH, int limit) {
+  const int max_ch = tr_decode_max_chunk(c->lay);
+  const int need = (n + max_ch - 1) / max_ch;      // fewest chunks a full window allows
+  int nch = (8192 + BH - 1) / BH;
+  if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
+  if (nch < need) nch = need;
+  if (nch > limit) nch = limit;
+  if (nch < 1) nch = 1;
+  if (c->force_chunks > 0) nch = c->force_chunks < n ? c->force_chunks : n;
+  const int CH = (n + nch - 1) / nch;
+  return (CH > max_ch || nch > limit) ? 0 : nch;
+}
+
+// The decode kernels with the split-K partial results in `part` (records of D + 2 floats,
+// `stride` records per (seq, query head)).
+tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window, uint16_t* out,
+                     int nch, float* part, int stride, bool prof_ok, hipStream_t stream) {
   const CacheLayout& L = c->lay;
   const int t = c->len[layer] - 1;
   const int n = t + 1;
   const int BH = L.B * c->hq;                       // (seq, query head) pairs
-  const int max_ch = tr_decode_max_chunk(L);
-  // About 8192 work items if every head were full (a few times the waves the chip holds at
-  // once), but no chunk below kMinChunk positions.
-  int nch = (8192 + BH - 1) / BH;
-  if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
-  if (nch < (n + max_ch - 1) / max_ch) nch = (n + max_ch - 1) / max_ch;
-  if (nch > c->max_chunks) nch = c->max_chunks;
-  if (nch < 1) nch = 1;
-  if (c->force_chunks > 0) nch = c->force_chunks < n ? c->force_chunks : n;
   const int CH = (n + nch - 1) / nch;
-  if (CH > max_ch || nch > c->max_chunks) return TR_ERR_UNSUPPORTED;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
   const int grid = BH * nch;
+  const bool prof_was = c->prof_on;
+  c->prof_on = prof_was && prof_ok;
+  tr_status st = TR_OK;
   {
     TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
     if (L.D == 64)
-      hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
-                         c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp);
+      hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch, stride,
+                         kscale, q, mode, part, out, c->hq, c->grp);
     else
-      hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch,
-                         c->max_chunks, kscale, q, mode, c->partials, out, c->hq, c->grp);
-    TR_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch, stride,
+                         kscale, q, mode, part, out, c->hq, c->grp);
+    if (hipGetLastError() != hipSuccess) st = TR_ERR_HIP;
   }
-  if (nch > 1) {
+  if (st == TR_OK && nch > 1) {
     TrProfScope prof(c, TR_PROF_DECODE_COMBINE, stream);
     if (L.D == 64)
-      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, c->max_chunks, mode,
-                         c->partials, out);
+      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, stride, mode, part, out);
     else
-      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, t, window, CH, c->max_chunks, mode,
-                         c->partials, out);
-    TR_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, t, window, CH, stride, mode, part, out);
+    if (hipGetLastError() != hipSuccess) st = TR_ERR_HIP;
   }
+  c->prof_on = prof_was;
+  return st;
+}
+
+}  // namespace
+
+tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
+                           uint16_t* out, hipStream_t stream) {
+  const int n = c->len[layer];
+  const int nch = decode_chunks(c, n, c->lay.B * c->hq, c->max_chunks);
+  if (nch < 1) return TR_ERR_UNSUPPORTED;
+  return decode_run(c, layer, q, mode, window, out, nch, c->partials, c->max_chunks, true, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode without any allocation: the split-K partial results go to a file-scope device array
+// instead of the cache's scratch.  Every device the library runs on holds its own copy of the
+// array for the life of the process; host code reaches it only through the device address that
+// hipGetSymbolAddress returns on that device (the array's name on the host is a stand-in, not a
+// device address).
+
+#define TR_NOALLOC_SCRATCH_BYTES (8u << 20)
+static __device__ __align__(256) float scratch[TR_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];                  // device address of `scratch` on each device
+
+// Device address of this device's scratch, looked up once per device with it current.
+tr_status scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TR_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TR_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TR_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
   return TR_OK;
+}
+
+}  // namespace
+
+tr_status tr_decode_noalloc_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
+                                   uint16_t* out, hipStream_t stream) {
+  float* part = nullptr;
+  const tr_status st = scratch_of_current_device(&part);
+  if (st != TR_OK) return st;
+  const int BH = c->lay.B * c->hq;
+  const int64_t rec = (int64_t)(c->lay.D + 2) * sizeof(float);
+  const int64_t limit = (int64_t)TR_NOALLOC_SCRATCH_BYTES / rec / BH;    // partial records per pair
+  const int nch = decode_chunks(c, c->len[layer], BH, (int)(limit < (1 << 20) ? limit : (1 << 20)));
+  if (nch < 1) return TR_ERR_SCRATCH;
+  // every chunk writes its own record before the combine reads it: nothing needs clearing
+  return decode_run(c, layer, q, mode, window, out, nch, part, nch, false, stream);
 }

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     import mixed_precision_kv_tr_amd as tr
-    for code in range(8):
+    for code in range(9):
         s = tr.tr_status_str(code)
         assert s and s != "unknown status"
     assert tr.tr_status_str(99) == "unknown status"
