@@ -588,7 +588,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=10,
+    ap.add_argument("--cpu-reps", type=int, default=2,
                     help="decode oracle: timed repetitions of each sampled sequence's step")
     ap.add_argument("--only", choices=["decode", "prefill", "small", "gqa_decode", "gqa_prefill", "baselines",
                                        "controller", "moe"], default=None)

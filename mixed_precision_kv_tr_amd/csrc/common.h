@@ -48,12 +48,10 @@ struct tr_kv_cache {
 // Decode work items: at most TR_DECODE_ITEM_MAX positions (LDS score buffer) and at most
 // TR_DECODE_PG_MAX page ids per width class (LDS page list); the host never picks chunks below
 // TR_DECODE_MIN_CHUNK positions unless those limits force it.
-#define TR_DECODE_ITEM_MAX 512
-#define TR_DECODE_PG_MAX 34
-#ifndef TR_DECODE_MIN_CHUNK
+#define TR_DECODE_ITEM_MAX 544
+#define TR_DECODE_PG_MAX 36
 #ifndef TR_DECODE_MIN_CHUNK
 #define TR_DECODE_MIN_CHUNK 256
-#endif
 #endif
 
 // Partial-result slots per (seq, query head) of the decode split-K are at least this many, so a

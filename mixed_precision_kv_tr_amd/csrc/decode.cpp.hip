@@ -1,31 +1,31 @@
-// Decode routed attention over the mixed-width paged cache (TriRoute review page,
-// xllm-io.github.io: Eq. (2) modes read by a query; Eq. (4) codes written per token).
+// Decode routed attention over the mixed-width paged cache on the matrix cores (TriRoute review
+// page, xllm-io.github.io: Eq. (2) modes read by a query; Eq. (4) codes written per token).
 //
-// One query per (sequence, query head) at position t, reading the K/V of its KV head
-// (query head h reads KV head h / G with G query heads per KV head; G = 1 is plain multi-head
-// attention).  Its key set is the position window
-// [lo, t] (lo = 0 for full, max(0, t - w) for local; skip heads read nothing).  The window is
-// split into position chunks (split-K); every chunk maps, through the per-position class
-// prefix counts, to one contiguous slot range per width class, so out-of-window keys are
-// never read and each inner loop runs over a single width (wave-uniform unpacking).
+// Work item: one wavefront = one workgroup = (sequence, KV head, block of up to GB query heads of
+// that KV head, position chunk).  The block's query heads are the columns of the matrix products:
+// query head h reads KV head h / G, so with grouped-query attention (G > 1) the KV rows a block
+// reads serve all of its query heads at once; G = 1 is multi-head attention, one column.  The item
+// covers a chunk of the union of its columns' windows ([lo, t]: lo = 0 for full, max(0, t - w) for
+// local; skip columns read nothing); every chunk maps, through the per-position class prefix
+// counts, to one contiguous slot range per width class, so out-of-window keys are never read and
+// each inner loop runs over a single width.  A local column of a block that also holds a full
+// column sees only the slots at or after its window start (one more prefix row).
 //
-// k_decode: one wavefront = one workgroup = one (seq, query head, chunk) work item, with no
-// cross-wave synchronization, so every wave streams independently.
-//   prologue the chunk's page ids of every class and q -> LDS.
-//   phase 1  K codes -> scores in LDS.  Each lane takes a 16/32-byte slice of a key row;
-//            batches of keys are software-pipelined (the next batch is in flight while the
-//            current one is computed).  2- and 4-bit codes become bf16 (128 + c) by an OR
-//            into the mantissa and go through v_dot2_f32_bf16 with bf16 q pairs; 8-bit codes
-//            use byte converts and fp32 FMA; bf16 keys use v_dot2 directly.  Partial dots are
-//            reduced across the lanes of the key.  The zero point folds out as
-//            s * (q . c) + z * sum(q) (an exact identity of Eq. (4)'s reconstruction); scores
-//            are kept in the log2 domain.
-//   softmax  chunk max m, p = 2^(score - m), l = sum p (fp32).
-//   phase 2  V codes, pipelined the same way: each lane owns 32 fixed channels of a key, so
-//            all width classes accumulate into the same 32 fp32 registers:
-//            acc += (p * s_v) * c, plus sum(p * z_v) once per key.
-//   epilogue a one-chunk window writes bf16 out directly; otherwise the chunk writes
-//            (o[D], m, l).  Skip heads: chunk 0 writes zeros.
+// phase 1  S^T = Q K^T per 16 keys on v_mfma_f32_16x16x32_f16 (_bf16 for b = 16 keys).  The lane
+//          that owns a key's B column loads its slice of the key's code row and expands it in
+//          registers to exact fp16 values 1024 + c 2^(kf): code fields are ORed into fp16 1024's
+//          mantissa where they sit, and the field's power of two is folded into the query row (A),
+//          which is prescaled into fp16 range per column.  Eq. (4)'s reconstruction folds out
+//          exactly: q . (s c + z) = s (q . c) + z sum(q).  Scores (log2 domain) go to LDS, with
+//          per-column running maxima and the chunk's largest V scale per class.
+// phase 2  O^T = V^T P'^T per tile of keys.  The tile's raw V code rows are staged in LDS and read
+//          back transposed (ds_read_b64_tr_b4 / _b8 / _b16), so each lane holds one channel of 8 or
+//          16 keys, expanded to fp16 like the keys; P' = p s_V 2^-tau (p = 2^(score - max)) enters
+//          as an fp16 hi + lo pair (bf16 for b = 16 keys, whose values are bf16), and the zero
+//          points add sum(p z_V) per column.  2-bit tiles hold two channels per nibble: they
+//          accumulate apart and are added through LDS.
+// epilogue a one-chunk window writes bf16 out directly; otherwise the chunk writes (o[D], m, l)
+//          per column.  Columns whose mode is skip get zeros from chunk 0.
 // k_decode_combine: log-sum-exp merge of multi-chunk windows -> bf16.
 #include <math.h>
 
@@ -36,19 +36,25 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kItemMax = TR_DECODE_ITEM_MAX;
 constexpr int kPgMax = TR_DECODE_PG_MAX;
 constexpr int kMinChunk = TR_DECODE_MIN_CHUNK;
+constexpr uint32_t kF16K = 0x64006400u;            // the fp16 pair (1024, 1024)
+constexpr uint32_t kF16B = 0x64646464u;            // byte 0x64 (fp16 1024's high byte) everywhere
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
+// Positions per chunk the LDS score buffer holds, by columns per item.
+template <int GB>
+constexpr int chunk_cap() { return GB == 1 ? TR_DECODE_ITEM_MAX : 256; }
 
 // A constant hidden from the compiler in an SGPR / a VGPR, so that (x & m) | c is emitted as one
-// v_and_or_b32 (gfx9 VOP3 takes no literal operands; left visible, the compiler splits it into
-// an AND and an OR with literals).
+// v_and_or_b32 (VOP3 takes no literal operands; left visible, the compiler splits it in two).
 __device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
   __asm__("" : "+s"(x));
   return x;
@@ -58,35 +64,57 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
   return x;
 }
 
-// Class-0 (2-bit) keys as bf16 dot operands.  Pair k of a code word holds elements (k, k + 8) of
-// its 16 (bits 2k and 16 + 2k).  Fields 0-2 are masked in place, fields 3-5 after w >> 6, fields
-// 6-7 after w >> 12, and ORed into bf16 128.0's mantissa: pair k then reads 128 + c * 4^(k % 3),
-// exactly, with two shifts per word.  The q pair k is scaled by 4^-(k % 3) to match (exact in
-// bf16), so the dot is sum(c q) + 128 * sum(q 4^-(k % 3)).
-__device__ __forceinline__ float q_scale_k2(int k) { return k % 3 == 0 ? 1.0f : k % 3 == 1 ? 0.25f : 0.0625f; }
-
-template <int NP>
-__device__ __forceinline__ float dot_k2_word(uint32_t w, const uint32_t* qp, float acc, uint32_t m0, uint32_t m1,
-                                             uint32_t m2, uint32_t ob) {
-  const uint32_t w6 = w >> 6, w12 = w >> 12;
-  acc = dot2((w & m0) | ob, qp[0], acc);
-  acc = dot2((w & m1) | ob, qp[1], acc);
-  acc = dot2((w & m2) | ob, qp[2], acc);
-  acc = dot2((w6 & m0) | ob, qp[3], acc);
-  acc = dot2((w6 & m1) | ob, qp[4], acc);
-  acc = dot2((w6 & m2) | ob, qp[5], acc);
-  acc = dot2((w12 & m0) | ob, qp[6], acc);
-  acc = dot2((w12 & m1) | ob, qp[7], acc);
-  return acc;
+__device__ __forceinline__ f32x4 mma_f16(const uint32_t* a, const uint32_t* b, f32x4 acc) {
+  const u32x4 av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv), acc, 0,
+                                                0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16(const uint32_t* a, const uint32_t* b, f32x4 acc) {
+  const u32x4 av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc,
+                                                 0, 0, 0);
+}
+// K = 16: A / B hold 4 bf16 each (two words).
+__device__ __forceinline__ f32x4 mma_bf16_k16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 acc) {
+  const u32x2 av = {a0, a1}, bv = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av), __builtin_bit_cast(s16x4, bv), acc,
+                                                   0, 0, 0);
 }
 
-// bf16 bit pattern of a float that holds a bf16 value (q is bf16 on input, so this is exact).
-__device__ __forceinline__ uint32_t bf16_bits(float x) { return __float_as_uint(x) >> 16; }
+// Transposing LDS reads.  Each lane names 8 bytes; within every group of 16 lanes, lane L receives
+//   tr4:  nibble L of the 16 lanes' reads, in lane order (16 values);
+//   tr8:  byte L % 8 of the reads of lanes L / 8, L / 8 + 2, ..., L / 8 + 14 (8 values);
+//   tr16: element L % 4 of the reads of lanes L / 4, L / 4 + 4, L / 4 + 8, L / 4 + 12 (4 values).
+#define TR_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+__device__ __forceinline__ void tr4(const uint8_t* p, uint32_t& x0, uint32_t& x1) {
+  const i32x2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32(TR_LDS(i32x2, p));
+  x0 = (uint32_t)r[0];
+  x1 = (uint32_t)r[1];
+}
+__device__ __forceinline__ void tr8(const uint8_t* p, uint32_t& x0, uint32_t& x1) {
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TR_LDS(i32x2, p));
+  x0 = (uint32_t)r[0];
+  x1 = (uint32_t)r[1];
+}
+__device__ __forceinline__ void tr16(const uint8_t* p, uint32_t& x0, uint32_t& x1) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TR_LDS(s16x4, p));
+  const u32x2 w = __builtin_bit_cast(u32x2, r);
+  x0 = w[0];
+  x1 = w[1];
+}
 
-// Cross-lane sums and maxima without LDS: DPP inside rows of 16 lanes (quad_perm 1,0,3,2 and
-// 2,3,0,1; row_half_mirror; row_mirror; row_ror 4 and 8), v_permlane16_swap / v_permlane32_swap
-// across rows and halves.  Each swap hands every lane its partner's value (l ^ 16, l ^ 32) in one
-// of its two results, so combining both results gives the pairwise reduction in every lane.
+// Orders this wave's LDS accesses around it.  A workgroup here is a single wave, and LDS
+// instructions of a wave complete in the order they are issued, so no barrier is needed -- only
+// that the compiler moves no memory access across, and that earlier LDS accesses are done.  The
+// wave's global loads stay in flight (a barrier's workgroup fence would wait for them as well).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0); vmcnt and expcnt untouched
+  __asm__ volatile("" ::: "memory");
+}
+
+// Cross-lane sums and maxima without LDS: DPP inside rows of 16 lanes, v_permlane16_swap /
+// v_permlane32_swap across rows and halves (each swap hands every lane its partner's value in one
+// of its two results, so combining both results gives the pairwise reduction in every lane).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -107,438 +135,864 @@ __device__ __forceinline__ float max32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// Sum over each group of N adjacent lanes (N = 1, 2, 4, 8, 16), result in every lane of it.
-template <int N>
-__device__ __forceinline__ float sum_adjacent(float v) {
-  if constexpr (N >= 2) v += dpp_f<0xB1>(v);
-  if constexpr (N >= 4) v += dpp_f<0x4E>(v);
-  if constexpr (N >= 8) v += dpp_f<0x141>(v);
-  if constexpr (N >= 16) v += dpp_f<0x140>(v);
+// Sum / max over the 16 lanes of each row (result in every lane of the row).
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<0xB1>(v);                             // quad_perm 1,0,3,2
+  v += dpp_f<0x4E>(v);                             // quad_perm 2,3,0,1
+  v += dpp_f<0x141>(v);                            // row_half_mirror
+  v += dpp_f<0x140>(v);                            // row_mirror
   return v;
 }
-// Sum over the lanes l' = l mod S (S = 1, 2, 4, 8): all 64 / S lanes of one residue.
-template <int S>
-__device__ __forceinline__ float sum_strided(float v) {
-  if constexpr (S == 1) v = sum_adjacent<2>(v);
-  if constexpr (S <= 2) v += dpp_f<0x4E>(v);
-  if constexpr (S <= 4) v += dpp_f<0x124>(v);
-  v += dpp_f<0x128>(v);
-  return sum32(sum16(v));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
+__device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp_f<0xB1>(v));
   v = fmaxf(v, dpp_f<0x4E>(v));
   v = fmaxf(v, dpp_f<0x141>(v));
   v = fmaxf(v, dpp_f<0x140>(v));
-  return max32(max16(v));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) { return max32(max16(row_max(v))); }
+__device__ __forceinline__ float wave_sum(float v) { return sum32(sum16(row_sum(v))); }
+
+// ---- code expansion to fp16 operands ------------------------------------------------------------
+// Every expansion writes pairs (lo, hi) of fp16 values 1024 + (code field in place); the other
+// operand of the product carries the field's inverse power of two.
+
+// 16 two-bit codes of a word (element e at bits 2e) as 8 pairs: pair f (f = 0..4) holds elements
+// (f, 8 + f) times 4^f, pair 5 + f (f = 0..2) elements (5 + f, 13 + f) times 4^f.
+__device__ __forceinline__ void exp_k2(uint32_t w, uint32_t* p, uint32_t K, const uint32_t* m) {
+  p[0] = (w & m[0]) | K;
+  p[1] = (w & m[1]) | K;
+  p[2] = (w & m[2]) | K;
+  p[3] = (w & m[3]) | K;
+  p[4] = (w & m[4]) | K;
+  const uint32_t w10 = w >> 10;
+  p[5] = (w10 & m[0]) | K;
+  p[6] = (w10 & m[1]) | K;
+  p[7] = (w10 & m[2]) | K;
+}
+// 8 four-bit codes of a word (element e at bits 4e) as 4 pairs: (0, 4), (1, 5) x 16, (2, 6),
+// (3, 7) x 16.  The same expansion serves V: a tr4 word holds one channel of 8 keys.
+__device__ __forceinline__ void exp_k4(uint32_t w, uint32_t* p, uint32_t K, uint32_t m0, uint32_t m1) {
+  p[0] = (w & m0) | K;
+  p[1] = (w & m1) | K;
+  const uint32_t w8 = w >> 8;
+  p[2] = (w8 & m0) | K;
+  p[3] = (w8 & m1) | K;
+}
+// 4 byte codes of a word as 2 pairs (0, 1), (2, 3): the bytes with 0x64 above them.
+__device__ __forceinline__ void exp_k8(uint32_t w, uint32_t* p, uint32_t B) {
+  p[0] = __builtin_amdgcn_perm(B, w, 0x04010400u);
+  p[1] = __builtin_amdgcn_perm(B, w, 0x04030402u);
+}
+// A tr4 word of a 2-bit tile: nibble k = key k, the even channel's code in bits 0-1 and the odd
+// channel's in bits 2-3 (the caller shifts the word right by 2 for the odd channel).  Pairs
+// (k, k + 4): keys 0, 1, 2 in place (times 1, 16, 256), key 3 after a shift.
+__device__ __forceinline__ void exp_v2(uint32_t x, uint32_t* p, uint32_t K, uint32_t m0, uint32_t m1, uint32_t m2) {
+  p[0] = (x & m0) | K;
+  p[1] = (x & m1) | K;
+  p[2] = (x & m2) | K;
+  p[3] = ((x >> 12) & m0) | K;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return sum_strided<1>(v); }
-
-// Codes of b bits, element e of a little-endian packed slice, as floats, in groups that map to
-// byte converts: for b = 2 the mask (w >> 2k) & 0x03030303 holds elements 4i + k in byte i;
-// b = 4: (w >> 4k) & 0x0f0f0f0f holds 2i + k; b = 8: byte i is element i.
-template <int B, int NW>
-__device__ __forceinline__ void unpack_codes(const uint32_t* w, float* out) {
-#pragma unroll
-  for (int d = 0; d < NW; ++d) {
-    if constexpr (B == 2) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t m = (w[d] >> (2 * k)) & 0x03030303u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[16 * d + 4 * i + k] = (float)((m >> (8 * i)) & 0xffu);
-      }
-    } else if constexpr (B == 4) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t m = (w[d] >> (4 * k)) & 0x0f0f0f0fu;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[8 * d + 2 * i + k] = (float)((m >> (8 * i)) & 0xffu);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[4 * d + i] = (float)((w[d] >> (8 * i)) & 0xffu);
-    }
-  }
+// Factor on the P' operand of key k (0..7) of a tr4 word, undoing the expansion's field scale.
+template <int C>
+__device__ __forceinline__ float pfield(int k) {
+  if constexpr (C == 0) return (k & 3) == 1 ? 0.0625f : (k & 3) == 2 ? 0.00390625f : 1.0f;
+  else if constexpr (C == 1) return (k & 1) ? 0.0625f : 1.0f;
+  else return 1.0f;
 }
 
-// Codes of b = 2 or 4 bits as floats c * 4^k (b = 2, element 4i + k of a word) or c * 16^k
-// (b = 4, element 2i + k): each word is masked in place (one AND per field) and its bytes go
-// through v_cvt_f32_ubyte0..3; the caller scales its weights by 4^-k / 16^-k (exact).  The
-// masked word is hidden from the compiler, which would otherwise re-derive every element with
-// a bit-field extract of its own.
-template <int B, int NW>
-__device__ __forceinline__ void unpack_codes_scaled(const uint32_t* w, float* out) {
-#pragma unroll
-  for (int d = 0; d < NW; ++d) {
-    if constexpr (B == 2) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t m = w[d] & (0x03030303u << (2 * k));
-        __asm__("" : "+v"(m));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[16 * d + 4 * i + k] = (float)((m >> (8 * i)) & 0xffu);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        uint32_t m = w[d] & (0x0f0f0f0fu << (4 * k));
-        __asm__("" : "+v"(m));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[8 * d + 2 * i + k] = (float)((m >> (8 * i)) & 0xffu);
-      }
-    }
-  }
-}
-
-// Weight factor of element e of a scaled unpack: 4^-(e % 4) (b = 2) or 16^-(e % 2) (b = 4).
-template <int B>
-__device__ __forceinline__ float unpack_scale(int e) {
-  if constexpr (B == 2) return e % 4 == 0 ? 1.0f : e % 4 == 1 ? 0.25f : e % 4 == 2 ? 0.0625f : 0.015625f;
-  else return e % 2 == 0 ? 1.0f : 0.0625f;
-}
-
-template <int NW>
-__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
-  if constexpr (NW == 1) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (NW == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
-    w[0] = t.x; w[1] = t.y;
-  } else {
-#pragma unroll
-    for (int x = 0; x < NW / 4; ++x) {
-      const uint4 t = reinterpret_cast<const uint4*>(p)[x];
-      w[4 * x] = t.x; w[4 * x + 1] = t.y; w[4 * x + 2] = t.z; w[4 * x + 3] = t.w;
-    }
-  }
-}
-
-// One batch of U keys (one sub-iteration of KPW keys per u) of class C: codes and (s, z).
-template <int U, int NW, bool SIDE>
-struct Batch {
-  uint32_t w[U][NW];
-  float2 sz[U];
+// Per-class constants (D channels, class C: b = 2 << C).
+template <int D, int C>
+struct Cls {
+  static constexpr int b = 2 << C;
+  static constexpr int RB = D * b / 8;             // code row bytes of one (token, head)
+  static constexpr int NWK = RB / 16;              // words per lane in phase 1 (a quarter row)
+  static constexpr int TK = C <= 1 ? 64 : C == 2 ? 32 : 16;   // keys per phase-2 tile
+  static constexpr int RS = RB + 16;               // LDS row stride of a staged tile
+  static constexpr int PPR = RB / 16;              // 16-byte pieces per row
+  static constexpr int NP = TK * PPR;              // pieces per tile
+  static constexpr int NPL = (NP + 63) / 64;       // pieces per lane
+  // phase-1 groups of 16 keys per batch: 4 KB of codes per wave (2 KB for D = 64's 2- and 4-bit
+  // classes, whose chunks hold fewer bytes), and the side-data slots that cover them (64 keys each)
+  static constexpr int U = (D == 128) ? (C == 0 ? 8 : C == 1 ? 4 : C == 2 ? 2 : 1) : (C <= 2 ? 4 : 2);
+  static constexpr int NS = (16 * U + 63) / 64;
 };
 
-template <int U, int NW, bool SIDE, int LPK>
-__device__ __forceinline__ void load_batch(Batch<U, NW, SIDE>& bt, const CacheLayout& c, const int32_t* pg, int first,
-                                           int lp, int pm, int base, int e, int kslot, int64_t code_off,
-                                           int64_t side_off, int rowb) {
-  constexpr int KPW = kWave / LPK;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = min(base + u * KPW + kslot, e - 1);    // clamped: loads never branch
-    const int page = pg[(j >> lp) - first];
-    const int slot = j & pm;
-    const uint8_t* pb = c.pool + (int64_t)page * c.page_bytes;
-    load_words<NW>(pb + code_off + (int64_t)slot * rowb, bt.w[u]);
-    if constexpr (SIDE) bt.sz[u] = reinterpret_cast<const float2*>(pb + side_off)[slot];
+// Shared state of a work item.
+template <int D, int GB>
+struct Smem {
+  static constexpr int SCAP = chunk_cap<GB>() + 32;   // per column: chunk + 8-padding per class
+  static constexpr int VT = D == 128 ? 5120 : 3072;   // one staged V tile (largest class)
+  alignas(16) uint8_t vt[VT];
+  alignas(16) float sc[GB * SCAP];                    // scores; q rows during the prologue
+  alignas(16) uint16_t qv[4][GB][D];                  // query rows as A operands, per class
+  alignas(16) uint16_t pb[GB + 1][2][64];             // P' hi / lo of a tile; column GB = zeros
+  alignas(16) float od[GB][D];                        // the 2-bit class's contribution
+  int32_t pg[TR_NCLASS][kPgMax];                      // page ids of the chunk, per class
+  float qoff[4][GB];                                  // 1024 * sum of each class's A row
+  float isig[GB], qsum[GB], cmax[GB];
+  int32_t lb[TR_NCLASS][GB];                          // first visible slot per class and column
+};
+
+// Channel of element j of step s, lane group g, in class C's query operand, and the factor that
+// undoes the code field's power of two (D / 4 channels per lane group).
+template <int D, int C>
+__device__ __forceinline__ void qchan(int s, int g, int j, int& ch, float& f) {
+  const int base = (D / 4) * g;
+  if constexpr (C == 0) {
+    const int fld = 4 * (s & 1) + (j >> 1);
+    ch = base + 16 * (s >> 1) + fld + 8 * (j & 1);
+    const int pw = fld < 5 ? fld : fld - 5;
+    f = pw == 0 ? 1.0f : pw == 1 ? 0.25f : pw == 2 ? 0.0625f : pw == 3 ? 0.015625f : 0.00390625f;
+  } else if constexpr (C == 1) {
+    ch = base + 8 * s + (j >> 1) + 4 * (j & 1);
+    f = ((j >> 1) & 1) ? 0.0625f : 1.0f;
+  } else {
+    ch = base + 8 * s + j;
+    f = 1.0f;
   }
 }
 
-// Phase 1 for width class C over class slots [a, e): scores into sc[off + (j - a)].
-// Lane slices: 16 bytes (b = 2, 4, 8) or 32 bytes (b = 16) of one key row.
-//   b = 2, 4: code pairs are ORed into bf16 mantissas (value 128 + c, exact) and dotted with
-//             bf16 q pairs by v_dot2_f32_bf16; the 128 * sum(q) offset is removed with the
-//             zero point: score = s * dot + (z - 128 s) * sum(q).
-//   b = 8:    byte converts and fp32 FMA.
-//   b = 16:   native bf16 pairs straight into v_dot2_f32_bf16.
-template <int D, int C>
-__device__ __forceinline__ void score_phase(const CacheLayout& c, const int32_t* pg, int first, int h, int a, int e,
-                                            int off, const float* qs, float sigma, float sig0, float kscale,
-                                            float* sc) {
-  constexpr int b = 2 << C;
-  constexpr int SB = (C == 3) ? 32 : 16;           // slice bytes per lane per key
-  constexpr int E = SB * 8 / b;                    // elements per lane
-  constexpr int LPK = D * b / 8 / SB;              // lanes per key
-  constexpr int KPW = kWave / LPK;                 // keys per wave sub-iteration
-  constexpr int NW = SB / 4;
-#ifndef TR_DECODE_U1
-#define TR_DECODE_U1 2
-#endif
-#ifndef TR_DECODE_UK3
-#define TR_DECODE_UK3 4                            // bf16 keys: 4 x 8 keys (8 KB) per batch
-#endif
-  constexpr int U = (C == 3) ? TR_DECODE_UK3 : TR_DECODE_U1;   // sub-iterations per batch
-  constexpr int NQ = (C == 2) ? 1 : E / 2;
-  const int lane = threadIdx.x;
-  const int part = lane % LPK, kslot = lane / LPK;
-  const float* qv = qs + part * E;
-  uint32_t qp[NQ];
-  float qf[(C == 2) ? E : 1];
+// Phase 1 for width class C over class slots [a, e): scores into sc[n * SCAP + off + (j - a)].
+template <int D, int GB, int C>
+__device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, int first, int h, int a, int e, int off,
+                                       int ncol, float kscale, float (&mrun)[(GB + 3) / 4], float& vmax) {
+  using K = Cls<D, C>;
+  constexpr int KS = D / 32;
+  constexpr int NCL = (GB + 3) / 4;
+  constexpr int SCAP = Smem<D, GB>::SCAP;
+  constexpr int U = K::U;
+  const int lane = threadIdx.x, kr = lane & 15, g = lane >> 4;
+  // A operand: query row n at MFMA row 4 (n % 4) + n / 4, zeros for rows without a column
+  uint32_t qa[KS][4];
+  {
+    const int n = 4 * (kr & 3) + (kr >> 2);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < ncol) v = *reinterpret_cast<const uint4*>(&sm.qv[C][n][(s * 4 + g) * 8]);
+      qa[s][0] = v.x; qa[s][1] = v.y; qa[s][2] = v.z; qa[s][3] = v.w;
+    }
+  }
+  // this lane's columns n = 4 i + g: score factors and first visible slot
+  float fs[NCL], fz[NCL], fo[NCL];
+  int lbn[NCL];
+  bool act[NCL];
+#pragma unroll
+  for (int i = 0; i < NCL; ++i) {
+    const int n = 4 * i + g;
+    act[i] = n < ncol && sm.lb[C][min(n, GB - 1)] >= 0;
+    const int nn = act[i] ? n : 0;
+    fs[i] = (C < 3 ? sm.isig[nn] : 1.0f) * kscale;
+    fz[i] = sm.qsum[nn] * kscale;
+    fo[i] = sm.qoff[C][nn];
+    lbn[i] = act[i] ? sm.lb[C][nn] : e;
+  }
+  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
+  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + g * (K::RB / 4);
+  const int64_t sk_off = c.sk_off[C] + (int64_t)h * P * 8, sv_off = c.sv_off[C] + (int64_t)h * P * 8;
+  const int32_t* pg = sm.pg[C];
+  const uint32_t KK = opaque_v(kF16K);
+  uint32_t mk[5] = {0, 0, 0, 0, 0};
   if constexpr (C == 0) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        qp[8 * d + k] = bf16_bits(qv[16 * d + k] * q_scale_k2(k)) | (bf16_bits(qv[16 * d + k + 8] * q_scale_k2(k)) << 16);
+    for (int f = 0; f < 5; ++f) mk[f] = opaque_s(0x00030003u << (2 * f));
   } else if constexpr (C == 1) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qp[4 * d + k] = bf16_bits(qv[8 * d + k]) | (bf16_bits(qv[8 * d + k + 4]) << 16);
-  } else if constexpr (C == 2) {
-#pragma unroll
-    for (int k = 0; k < E; ++k) qf[k] = qv[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < NQ; ++k) qp[k] = bf16_bits(qv[2 * k]) | (bf16_bits(qv[2 * k + 1]) << 16);
+    mk[0] = opaque_s(0x000f000fu);
+    mk[1] = opaque_s(0x00f000f0u);
   }
-  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1;
-  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + part * SB;
-  const int64_t side_off = c.sk_off[C] + (int64_t)h * c.ptok[C] * 8;
-  constexpr int RB = D * b / 8;
-  constexpr int STEP = KPW * U;
-  const uint32_t ob = opaque_v(0x43004300u);
-  const uint32_t m0 = opaque_s(C == 0 ? 0x00030003u : 0x000f000fu), m1 = opaque_s(0x000c000cu),
-                 m2 = opaque_s(0x00300030u);
-  Batch<U, NW, (C < 3)> cur, nxt;
-  load_batch<U, NW, (C < 3), LPK>(cur, c, pg, first, lp, pm, a, e, kslot, code_off, side_off, RB);
-  for (int base = a; base < e; base += STEP) {
-    if (base + STEP < e) load_batch<U, NW, (C < 3), LPK>(nxt, c, pg, first, lp, pm, base + STEP, e, kslot, code_off,
-                                                        side_off, RB);
+  const uint32_t BB = opaque_s(kF16B);
+
+  // A batch: the code words of U groups of 16 keys (lane: key kr of each group, quarter row g), and
+  // the K scale / zero and V scale of the batch's keys, one key per lane (key 64 i + lane in slot
+  // i), handed to the lanes that need them by a cross-lane permute.
+  struct Batch {
+    uint32_t w[U][K::NWK];
+    float sk[K::NS], zk[K::NS], sv[K::NS];
+  };
+  auto load = [&](Batch& bt, int base) {
+    if constexpr (C < 3) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (base + u * KPW >= e) break;              // past the class's last key: nothing to compute
-      float dot = 0.0f;
-      if constexpr (C == 0) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) dot = dot_k2_word<8>(cur.w[u][d], qp + 8 * d, dot, m0, m1, m2, ob);
-      } else if constexpr (C == 1) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) dot = dot2(((cur.w[u][d] >> (4 * k)) & m0) | ob, qp[4 * d + k], dot);
-      } else if constexpr (C == 2) {
-        float cf[E];
-        unpack_codes<8, NW>(cur.w[u], cf);
-#pragma unroll
-        for (int k = 0; k < E; ++k) dot = fmaf(qf[k], cf[k], dot);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) dot = dot2(cur.w[u][k], qp[k], dot);
-      }
-      dot = sum_adjacent<LPK>(dot);
-      const int j = base + u * KPW + kslot;
-      if (j < e && part == 0) {
-        float x;
-        if constexpr (C == 0) x = fmaf(cur.sz[u].x, dot, fmaf(-128.0f * cur.sz[u].x, sig0, cur.sz[u].y * sigma));
-        else if constexpr (C == 1) x = fmaf(cur.sz[u].x, dot, fmaf(-128.0f, cur.sz[u].x, cur.sz[u].y) * sigma);
-        else if constexpr (C == 2) x = fmaf(cur.sz[u].x, dot, cur.sz[u].y * sigma);
-        else x = dot;
-        sc[off + (j - a)] = x * kscale;
+      for (int i = 0; i < K::NS; ++i) {
+        const int j = min(base + 64 * i + lane, e - 1);      // clamped: loads never branch
+        const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
+        const int row = j & pm;
+        const u32x2 kz = *reinterpret_cast<const u32x2*>(pb + sk_off + (int64_t)row * 8);
+        bt.sk[i] = __uint_as_float(kz[0]);
+        bt.zk[i] = __uint_as_float(kz[1]);
+        bt.sv[i] = *reinterpret_cast<const float*>(pb + sv_off + (int64_t)row * 8);
       }
     }
-    cur = nxt;
-  }
-}
-
-// Phase 2 for width class C: acc[32] (channels 32*part ..) += p * v_hat.
-template <int D, int C>
-__device__ __forceinline__ void value_phase(const CacheLayout& c, const int32_t* pg, int first, int h, int a, int e,
-                                            int off, const float* pw, float* acc, float& zacc) {
-  constexpr int b = 2 << C;
-  constexpr int VLPK = D / 32;                     // lanes per key
-  constexpr int KPW = kWave / VLPK;
-  constexpr int NW = b;                            // 32 codes of b bits = b words
-#ifndef TR_DECODE_U2
-#define TR_DECODE_U2 2
-#endif
-#ifndef TR_DECODE_UV
-#define TR_DECODE_UV 1
-#endif
-#ifndef TR_DECODE_UV3
-#define TR_DECODE_UV3 1
-#endif
-  constexpr int U = (C == 0) ? TR_DECODE_U2 : (C == 3) ? TR_DECODE_UV3 : TR_DECODE_UV;
-  constexpr int RB = D * b / 8;
-  constexpr int STEP = KPW * U;
-  const int lane = threadIdx.x;
-  const int part = lane % VLPK, kslot = lane / VLPK;
-  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1;
-  const int64_t code_off = c.v_off[C] + (int64_t)h * c.cb + part * (4 * b);
-  const int64_t side_off = c.sv_off[C] + (int64_t)h * c.ptok[C] * 8;
-  Batch<U, NW, (C < 3)> cur, nxt;
-  load_batch<U, NW, (C < 3), VLPK>(cur, c, pg, first, lp, pm, a, e, kslot, code_off, side_off, RB);
-  for (int base = a; base < e; base += STEP) {
-    if (base + STEP < e) load_batch<U, NW, (C < 3), VLPK>(nxt, c, pg, first, lp, pm, base + STEP, e, kslot,
-                                                         code_off, side_off, RB);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (base + u * KPW >= e) break;              // past the class's last key
-      const int jr = base + u * KPW + kslot;
-      const float p = (jr < e) ? pw[off + (min(jr, e - 1) - a)] : 0.0f;
-      if constexpr (C < 2) {
-        const float ps = p * cur.sz[u].x;
-        if (part == 0) zacc = fmaf(p, cur.sz[u].y, zacc);
-        float cf[32];
-        unpack_codes_scaled<b, NW>(cur.w[u], cf);
-#pragma unroll
-        for (int k = 0; k < 32; ++k) acc[k] = fmaf(ps * unpack_scale<b>(k), cf[k], acc[k]);
-      } else if constexpr (C == 2) {
-        const float ps = p * cur.sz[u].x;
-        if (part == 0) zacc = fmaf(p, cur.sz[u].y, zacc);
-        float cf[32];
-        unpack_codes<b, NW>(cur.w[u], cf);
-#pragma unroll
-        for (int k = 0; k < 32; ++k) acc[k] = fmaf(ps, cf[k], acc[k]);
+      const int j = min(base + 16 * u + kr, e - 1);          // clamped: loads never branch
+      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
+      const int row = j & pm;
+      const uint8_t* src = pb + code_off + (int64_t)row * K::RB;
+      if constexpr (K::NWK == 1) {
+        bt.w[u][0] = *reinterpret_cast<const uint32_t*>(src);
+      } else if constexpr (K::NWK == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        bt.w[u][0] = v.x; bt.w[u][1] = v.y;
       } else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          acc[2 * k] = fmaf(p, tr_bf16_lo(cur.w[u][k]), acc[2 * k]);
-          acc[2 * k + 1] = fmaf(p, tr_bf16_hi(cur.w[u][k]), acc[2 * k + 1]);
+        for (int x = 0; x < K::NWK / 4; ++x) {
+          const u32x4 v = reinterpret_cast<const u32x4*>(src)[x];
+          bt.w[u][4 * x] = v[0]; bt.w[u][4 * x + 1] = v[1]; bt.w[u][4 * x + 2] = v[2]; bt.w[u][4 * x + 3] = v[3];
         }
       }
     }
+  };
+  // One batch: U groups of 16 keys from `base`; scores of the keys before e.
+  auto compute = [&](const Batch& cur, int base) {
+    if constexpr (C < 3) {
+#pragma unroll
+      for (int i = 0; i < K::NS; ++i)
+        if (base + 64 * i + lane < e) vmax = fmaxf(vmax, cur.sv[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + 16 * u >= e) break;               // past the class's last key (wave-uniform)
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint32_t bop[4];
+        if constexpr (C == 0) {
+          if ((s & 1) == 0) {
+            uint32_t p8[8];
+            exp_k2(cur.w[u][s >> 1], p8, KK, mk);
+            bop[0] = p8[0]; bop[1] = p8[1]; bop[2] = p8[2]; bop[3] = p8[3];
+            acc = mma_f16(qa[s], bop, acc);
+            bop[0] = p8[4]; bop[1] = p8[5]; bop[2] = p8[6]; bop[3] = p8[7];
+            acc = mma_f16(qa[s + 1], bop, acc);
+          }
+        } else if constexpr (C == 1) {
+          exp_k4(cur.w[u][s], bop, KK, mk[0], mk[1]);
+          acc = mma_f16(qa[s], bop, acc);
+        } else if constexpr (C == 2) {
+          exp_k8(cur.w[u][2 * s], bop, BB);
+          exp_k8(cur.w[u][2 * s + 1], bop + 2, BB);
+          acc = mma_f16(qa[s], bop, acc);
+        } else {
+          bop[0] = cur.w[u][4 * s]; bop[1] = cur.w[u][4 * s + 1];
+          bop[2] = cur.w[u][4 * s + 2]; bop[3] = cur.w[u][4 * s + 3];
+          acc = mma_bf16(qa[s], bop, acc);
+        }
+      }
+      // lane (key kr, group g) holds rows 4 g + i: columns n = 4 i + g
+      const int jr = base + 16 * u + kr;
+      float sk = 0.0f, zk = 0.0f;
+      if constexpr (C < 3) {                       // key 16 u + kr of the batch: slot u / 4
+        const int src = 4 * (16 * (u & 3) + kr);
+        sk = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur.sk[u >> 2])));
+        zk = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cur.zk[u >> 2])));
+      }
+#pragma unroll
+      for (int i = 0; i < NCL; ++i) {
+        if (!act[i] || jr >= e) continue;
+        float x;
+        if constexpr (C < 3) x = fmaf(sk * fs[i], acc[i] - fo[i], zk * fz[i]);
+        else x = acc[i] * fs[i];
+        x = jr >= lbn[i] ? x : -INFINITY;
+        mrun[i] = fmaxf(mrun[i], x);
+        sm.sc[(4 * i + g) * SCAP + off + (jr - a)] = x;
+      }
+    }
+  };
+  // The next batch's loads are always issued (clamped into the range) before the current one is
+  // computed, so they stay in flight during its products; the batches rotate by value (see
+  // phase 2).
+  Batch cur, nxt;
+  load(cur, a);
+  for (int base = a;;) {
+    load(nxt, base + 16 * U);
+    compute(cur, base);
+    base += 16 * U;
+    if (base >= e) break;
     cur = nxt;
   }
 }
 
-// Occupancy floor handed to the compiler.  With 4 it settles at 96 VGPRs for D = 128 (5 waves per
-// SIMD, no spills; a 1.3B-shaped decode has ~4100 items for 5120 wave slots) and at 120 for D = 64.
+// Phase 2 for width class C over class slots [a, e): acc += V^T P'^T in units of 2^tau.
+template <int D, int GB, int C>
+__device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, int first, int h, int a, int e, int off,
+                                       int ncol, float tsc, f32x4 (&acc)[D / 16], float (&lp)[GB], float (&zp)[GB],
+                                       float (&cp)[GB]) {
+  using K = Cls<D, C>;
+  constexpr int NT = D / 16;
+  constexpr int SCAP = Smem<D, GB>::SCAP;
+  constexpr int TK = K::TK, RS = K::RS;
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const int lpg = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
+  const int64_t code_off = c.v_off[C] + (int64_t)h * c.cb;
+  const int64_t sv_off = c.sv_off[C] + (int64_t)h * P * 8;
+  const int32_t* pg = sm.pg[C];
+  const uint32_t KK = opaque_v(kF16K);
+  const uint32_t m40 = opaque_s(0x000f000fu), m41 = opaque_s(0x00f000f0u);
+  const uint32_t m20 = opaque_s(0x00030003u), m21 = opaque_s(0x00300030u), m22 = opaque_s(0x03000300u);
+  const uint32_t BB = opaque_s(kF16B);
+  // this lane's B-operand column (P' rows of column n; the zero column for rows without one)
+  const int ncolB = (r < ncol) ? r : GB;
+  // tr read address of this lane within a tile (plus the channel-tile offset)
+  int tro;
+  if constexpr (C <= 1) tro = (16 * g + r) * RS;                            // tr4: row = key 16 g + r
+  else if constexpr (C == 2) tro = (8 * g + (r >> 1)) * RS + 8 * (r & 1);   // tr8: key 8 g + r / 2
+  else tro = (4 * g + (r >> 2)) * RS + 8 * (r & 3);                         // tr16: key 4 g + r / 4
+
+  struct Tile {
+    u32x4 pc[K::NPL];
+    float sz[2];
+  };
+  auto load = [&](Tile& tl, int tb) {
+#pragma unroll
+    for (int x = 0; x < K::NPL; ++x) {
+      const int pcx = lane + 64 * x;
+      const int key = min(pcx / K::PPR, TK - 1), part = pcx % K::PPR;
+      const int j = min(tb + key, e - 1);
+      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lpg) - first] * c.page_bytes;
+      tl.pc[x] = *reinterpret_cast<const u32x4*>(pb + code_off + (int64_t)(j & pm) * K::RB + 16 * part);
+    }
+    if constexpr (C < 3) {
+      const int j = min(tb + min(lane, TK - 1), e - 1);
+      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lpg) - first] * c.page_bytes;
+      const u32x2 w = *reinterpret_cast<const u32x2*>(pb + sv_off + (int64_t)(j & pm) * 8);
+      tl.sz[0] = __uint_as_float(w[0]);
+      tl.sz[1] = __uint_as_float(w[1]);
+    } else {
+      tl.sz[0] = 1.0f;
+      tl.sz[1] = 0.0f;
+    }
+  };
+  // One tile from tb, with its rows and V side data already in registers.
+  auto run = [&](const Tile& cur, int tb) {
+    // stage the tile's rows
+#pragma unroll
+    for (int x = 0; x < K::NPL; ++x) {
+      const int pcx = lane + 64 * x;
+      if (K::NP % 64 == 0 || pcx < K::NP)
+        *reinterpret_cast<u32x4*>(sm.vt + (pcx / K::PPR) * RS + 16 * (pcx % K::PPR)) = cur.pc[x];
+    }
+    const float2 szv = make_float2(cur.sz[0], cur.sz[1]);
+    // P' of the tile's keys for every column: key j = lane
+    if (lane < TK) {
+      const int jr = tb + lane;
+      int pos;                                      // element position in the B operand
+      float fld;
+      if constexpr (C <= 1) {
+        const int kk = lane & 7;
+        pos = (lane & ~7) + 2 * (kk & 3) + (kk >> 2);
+        fld = pfield<C>(kk);
+      } else {
+        pos = lane;
+        fld = 1.0f;
+      }
+#pragma unroll
+      for (int n = 0; n < GB; ++n) {
+        if (n >= ncol) break;
+        const float mx = sm.cmax[n];
+        float p = 0.0f;
+        if (jr < e && mx != -INFINITY) p = exp2f(sm.sc[n * SCAP + off + (jr - a)] - mx);
+        lp[n] += p;
+        uint16_t hi, lo;
+        if constexpr (C < 3) {
+          zp[n] = fmaf(p, szv.y, zp[n]);
+          const float v = p * szv.x * tsc * fld;
+          const _Float16 vh = (_Float16)v;
+          const _Float16 vl = (_Float16)(v - (float)vh);
+          cp[n] += 1024.0f * ((float)vh + (float)vl);   // the offset the fp16 codes carry
+          hi = __builtin_bit_cast(uint16_t, vh);
+          lo = __builtin_bit_cast(uint16_t, vl);
+        } else {
+          const float v = p * tsc;
+          hi = tr_f32_to_bf16(v);
+          lo = tr_f32_to_bf16(v - tr_bf16_lo(hi));
+        }
+        sm.pb[n][0][pos] = hi;
+        sm.pb[n][1][pos] = lo;
+      }
+    }
+    wave_lds_sync();
+    if constexpr (C <= 1) {
+      // B operands: keys 16 g + 8 hb .. + 7 (the two words of this lane group's tr4 rows)
+      uint32_t bh[2][4], bl[2][4];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint4 vh = *reinterpret_cast<const uint4*>(&sm.pb[ncolB][0][(2 * g + hb) * 8]);
+        const uint4 vl = *reinterpret_cast<const uint4*>(&sm.pb[ncolB][1][(2 * g + hb) * 8]);
+        bh[hb][0] = vh.x; bh[hb][1] = vh.y; bh[hb][2] = vh.z; bh[hb][3] = vh.w;
+        bl[hb][0] = vl.x; bl[hb][1] = vl.y; bl[hb][2] = vl.z; bl[hb][3] = vl.w;
+      }
+      if constexpr (C == 1) {
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+          uint32_t x0, x1, av[4];
+          tr4(sm.vt + tro + 8 * m, x0, x1);
+          exp_k4(x0, av, KK, m40, m41);
+          acc[m] = mma_f16(av, bh[0], acc[m]);
+          acc[m] = mma_f16(av, bl[0], acc[m]);
+          exp_k4(x1, av, KK, m40, m41);
+          acc[m] = mma_f16(av, bh[1], acc[m]);
+          acc[m] = mma_f16(av, bl[1], acc[m]);
+        }
+      } else {
+        // 32 channels per tr4 (two per nibble): even channels into tile 2 m, odd into 2 m + 1
+#pragma unroll
+        for (int m = 0; m < NT / 2; ++m) {
+          uint32_t x0, x1, av[4];
+          tr4(sm.vt + tro + 8 * m, x0, x1);
+          exp_v2(x0, av, KK, m20, m21, m22);
+          acc[2 * m] = mma_f16(av, bh[0], acc[2 * m]);
+          acc[2 * m] = mma_f16(av, bl[0], acc[2 * m]);
+          exp_v2(x0 >> 2, av, KK, m20, m21, m22);
+          acc[2 * m + 1] = mma_f16(av, bh[0], acc[2 * m + 1]);
+          acc[2 * m + 1] = mma_f16(av, bl[0], acc[2 * m + 1]);
+          exp_v2(x1, av, KK, m20, m21, m22);
+          acc[2 * m] = mma_f16(av, bh[1], acc[2 * m]);
+          acc[2 * m] = mma_f16(av, bl[1], acc[2 * m]);
+          exp_v2(x1 >> 2, av, KK, m20, m21, m22);
+          acc[2 * m + 1] = mma_f16(av, bh[1], acc[2 * m + 1]);
+          acc[2 * m + 1] = mma_f16(av, bl[1], acc[2 * m + 1]);
+        }
+      }
+    } else if constexpr (C == 2) {
+      uint32_t bh[4], bl[4];
+      {
+        const uint4 vh = *reinterpret_cast<const uint4*>(&sm.pb[ncolB][0][8 * g]);
+        const uint4 vl = *reinterpret_cast<const uint4*>(&sm.pb[ncolB][1][8 * g]);
+        bh[0] = vh.x; bh[1] = vh.y; bh[2] = vh.z; bh[3] = vh.w;
+        bl[0] = vl.x; bl[1] = vl.y; bl[2] = vl.z; bl[3] = vl.w;
+      }
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        uint32_t x0, x1, av[4];
+        tr8(sm.vt + tro + 16 * m, x0, x1);
+        exp_k8(x0, av, BB);
+        exp_k8(x1, av + 2, BB);
+        acc[m] = mma_f16(av, bh, acc[m]);
+        acc[m] = mma_f16(av, bl, acc[m]);
+      }
+    } else {
+      const uint2 vh = *reinterpret_cast<const uint2*>(&sm.pb[ncolB][0][4 * g]);
+      const uint2 vl = *reinterpret_cast<const uint2*>(&sm.pb[ncolB][1][4 * g]);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        uint32_t x0, x1;
+        tr16(sm.vt + tro + 32 * m, x0, x1);
+        acc[m] = mma_bf16_k16(x0, x1, vh.x, vh.y, acc[m]);
+        acc[m] = mma_bf16_k16(x0, x1, vl.x, vl.y, acc[m]);
+      }
+    }
+    wave_lds_sync();                               // the tile and P' are rewritten next
+  };
+  // The next tile's loads are always issued (clamped into the range) before the current one is
+  // staged and computed, so they stay in flight during its products.  The tiles rotate by value:
+  // two tiles used in turn through one loop body would be addressed through a pointer, which keeps
+  // them out of registers (in scratch memory, one more round trip per tile).
+  Tile cur, nxt;
+  load(cur, a);
+  for (int tb = a;;) {
+    load(nxt, tb + TK);
+    run(cur, tb);
+    tb += TK;
+    if (tb >= e) break;
+    cur = nxt;
+  }
+}
+
+// e with vmax <= 2^e (0 for vmax = 0): the P' normalization of a class set.
+__device__ __forceinline__ int scale_exp(float vmax) { return vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : 0; }
+
+// Occupancy floor handed to the compiler.
 #ifndef TR_DECODE_WAVES
 #define TR_DECODE_WAVES 4
 #endif
-template <int D>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_WAVES, 8))) void k_decode(CacheLayout c, int layer, int t, int window, int CH, int nch_grid,
-                                                  int max_chunks, float kscale, const uint16_t* __restrict__ q,
-                                                  const uint8_t* __restrict__ mode, float* __restrict__ part,
-                                                  uint16_t* __restrict__ out, int HQ, int G) {
-  __shared__ float qs[D];
-  __shared__ float sc[kItemMax];
-  __shared__ int32_t pg[TR_NCLASS][kPgMax];
+// Work items in launch order.  Each item is one chunk of one group (seq, KV head, block of query
+// heads); a group is "full" if any of its columns is, else "local" if any is, else "skip".  Rank r
+// (the block index) takes, in turn: the chunks of the full groups (chunk-major: chunk 0 of every
+// full group, then chunk 1, ...), the chunks of the local groups (chunk-major), one item per skip
+// group (it writes the zero rows), and nothing for the ranks left over.  So every item that
+// reads the cache is dispatched before any empty one -- mixed in, the short-lived empty waves make
+// the dispatcher pile long ones onto a few compute units -- and consecutive ranks, which go to
+// the XCDs in turn, spread each chunk index over all of them.
+//
+// Every wave ranks the groups itself: lane l holds groups [l P, l P + P) (P <= kRankPerLane; larger
+// batches fall back to chunk-major order over all groups), one bit each in a full and a local
+// mask; scans over the lanes place rank r.
+constexpr int kRankPerLane = 32;
+
+__device__ __forceinline__ bool item_of_rank(int r, const uint8_t* __restrict__ mode, int groups, int H, int HQ, int G,
+                                             int GB, int NB, int nchf, int nchl, int& k, int& grp) {
   const int lane = threadIdx.x;
-  const int k = blockIdx.x % nch_grid;
-  const int sh = blockIdx.x / nch_grid;             // (seq, query head)
-  const int s = sh / HQ, h = (sh % HQ) / G;         // sequence, KV head it reads
-  const int m = mode[sh];
-  uint16_t* o = out + (int64_t)sh * D;
-  if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) {
-    if (k == 0) {
+  const int P = (groups + kWave - 1) / kWave;
+  if (P > kRankPerLane) {
+    k = r / groups;
+    grp = r % groups;
+    return k < nchf;
+  }
+  uint32_t fb = 0, lb = 0, vb = 0;
+  for (int i0 = 0; i0 < P; i0 += 8) {
+    uint8_t m[8][4];
 #pragma unroll
-      for (int d = lane; d < D; d += kWave) o[d] = 0;
-      if (lane == 0 && m != TR_MODE_SKIP) atomicOr(c.err, TR_ERRF_BAD_MODE);
+    for (int i = 0; i < 8; ++i) {                    // every load issued before any is used
+      const int g = min(lane * P + i0 + i, groups - 1);
+      const int s = g / (H * NB), hb = g % (H * NB);
+      const int h0 = (hb / NB) * G + (hb % NB) * GB;
+      const int nc = min(GB, G - (hb % NB) * GB);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) m[i][n] = n < GB ? mode[(int64_t)s * HQ + h0 + min(n, nc - 1)] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int li = i0 + i;
+      if (li >= P || lane * P + li >= groups) continue;
+      bool full = false, loc = false;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        full = full || m[i][n] == TR_MODE_FULL;
+        loc = loc || m[i][n] == TR_MODE_LOCAL;
+      }
+      vb |= 1u << li;
+      fb |= (full ? 1u : 0u) << li;
+      lb |= (!full && loc ? 1u : 0u) << li;
+    }
+  }
+  const uint32_t sb = vb & ~(fb | lb);
+  // inclusive scans over the lanes of the three counts, packed 21 bits apiece
+  long long sc = (long long)__popc(fb) | ((long long)__popc(lb) << 21) | ((long long)__popc(sb) << 42);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const long long x = __shfl_up(sc, o);
+    if (lane >= o) sc += x;
+  }
+  const long long tot = __shfl(sc, kWave - 1);
+  const int NF = (int)__builtin_amdgcn_readfirstlane((int)(tot & 0x1fffff));
+  const int NL = (int)__builtin_amdgcn_readfirstlane((int)((tot >> 21) & 0x1fffff));
+  const int NS = (int)__builtin_amdgcn_readfirstlane((int)((tot >> 42) & 0x1fffff));
+  int which, j;
+  if (r < NF * nchf) {
+    which = 0;
+    k = r / NF;
+    j = r % NF;
+  } else if (r - NF * nchf < NL * nchl) {
+    which = 1;
+    k = (r - NF * nchf) / NL;
+    j = (r - NF * nchf) % NL;
+  } else if (r - NF * nchf - NL * nchl < NS) {
+    which = 2;
+    k = 0;
+    j = r - NF * nchf - NL * nchl;
+  } else {
+    return false;
+  }
+  const uint32_t bits = which == 0 ? fb : which == 1 ? lb : sb;
+  const int incl = (int)((sc >> (21 * which)) & 0x1fffff);
+  const int excl = incl - __popc(bits);
+  const uint64_t hit = __ballot(excl <= j && j < incl);
+  const int L = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : 0);
+  // the (j - excl)-th set bit of this lane's mask (meaningful in lane L only)
+  uint32_t b = bits;
+  const int drop = min(max(j - excl, 0), 31);
+  for (int x = 0; x < drop; ++x) b &= b - 1;
+  const int pos = b ? __builtin_ctz(b) : 0;
+  grp = __builtin_amdgcn_readlane(lane * P + pos, L);
+  return true;
+}
+
+template <int D, int GB>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_WAVES, 8))) void k_decode(
+    CacheLayout c, int layer, int t, int window, int CH, int stride, float kscale, const uint16_t* __restrict__ q,
+    const uint8_t* __restrict__ mode, float* __restrict__ part, uint16_t* __restrict__ out, int HQ, int G, int NB) {
+  constexpr int NT = D / 16, KS = D / 32, NCL = (GB + 3) / 4;
+  __shared__ Smem<D, GB> sm;
+  const int lane = threadIdx.x;
+  const int groups = c.B * c.H * NB;
+  int k, grp;
+  {
+    const int nchf = (t + 1 + CH - 1) / CH, nchl = (t + 1 - max(0, t - window) + CH - 1) / CH;
+    if (!item_of_rank(blockIdx.x, mode, groups, c.H, HQ, G, GB, NB, nchf, nchl, k, grp)) return;
+  }
+  const int s = grp / (c.H * NB), hb = grp % (c.H * NB);
+  const int hk = hb / NB, blk = hb % NB;
+  const int h0 = hk * G + blk * GB;                  // the block's first query head
+  const int ncol = min(GB, G - blk * GB);
+  const int64_t row0 = (int64_t)s * HQ + h0;         // (seq, query head) index of column 0
+
+  // Every load that needs nothing else goes out at once: the columns' modes, the query rows, and
+  // the class prefix rows of the chunk under both possible windows (any full column: [0, t];
+  // local columns only: [lo_loc, t]) plus that of lo_loc.  Page ids follow; phase 1 next.
+  const int lo_loc = max(0, t - window);
+  int cb[2][2];                                      // [window kind][p0, p1]; p0 > t: no chunk k
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const int lo = w == 0 ? 0 : lo_loc;
+    const int L = t + 1 - lo;
+    const int nch = (L + CH - 1) / CH;
+    const int per = (L + nch - 1) / nch;
+    cb[w][0] = k < nch ? lo + k * per : t + 1;
+    cb[w][1] = k < nch ? min(cb[w][0] + per, t + 1) : t + 1;
+  }
+  const int mval = lane < ncol ? (int)mode[row0 + lane] : 0;
+  constexpr int QPL = (GB * D + kWave - 1) / kWave;  // query values per lane
+  uint16_t qraw[QPL];
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int x = lane + kWave * i;
+    qraw[i] = x < ncol * D ? q[row0 * D + x] : (uint16_t)0;
+  }
+  const int4 paf = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[0][0]));
+  const int4 pef = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[0][1]));
+  const int4 pal = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[1][0]));
+  const int4 pel = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[1][1]));
+  const int4 pl = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, lo_loc));
+
+  // modes of the block's columns
+  const bool bad = lane < ncol && mval > TR_MODE_FULL;
+  const uint64_t fullm = __ballot(lane < ncol && mval == TR_MODE_FULL);
+  const uint64_t locm = __ballot(lane < ncol && mval == TR_MODE_LOCAL);
+  if (k == 0) {
+    if (bad) atomicOr(c.err, TR_ERRF_BAD_MODE);
+    // columns that attend to nothing get zeros
+    for (int n = 0; n < ncol; ++n) {
+      if (((fullm | locm) >> n) & 1) continue;
+      for (int d = lane; d < D; d += kWave) out[(row0 + n) * D + d] = 0;
+    }
+  }
+  if (!(fullm | locm)) return;
+  const int wk = fullm ? 0 : 1;
+  const int p0 = cb[wk][0];
+  if (p0 > t) return;                                // the union window has fewer chunks
+  const int lo = fullm ? 0 : lo_loc;
+  const int nch = (t + 1 - lo + CH - 1) / CH;
+  const bool mixed = fullm && locm;
+
+  // slot ranges of the chunk, and the first slot a local column sees
+  const int4 pa = fullm ? paf : pal, pe = fullm ? pef : pel;
+  const int a[4] = {pa.x, pa.y, pa.z, pa.w}, e[4] = {pe.x, pe.y, pe.z, pe.w};
+  const int4 plv = mixed ? pl : pa;
+  const int al[4] = {max(pa.x, plv.x), max(pa.y, plv.y), max(pa.z, plv.z), max(pa.w, plv.w)};
+  int first[4], off[4];
+  {
+    int o = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      first[x] = a[x] >> c.ptok_log2[x];
+      off[x] = o;
+      o += (e[x] - a[x] + 7) & ~7;
+    }
+  }
+  // page ids: at most kPgMax (< 64) per class, one per lane; the four classes' loads go out together
+  {
+    int32_t pv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int np = e[x] > a[x] ? ((e[x] - 1) >> c.ptok_log2[x]) - first[x] + 1 : 0;
+      pv[x] = lane < np ? tr_ptab(c, layer, s, x)[first[x] + lane] : -1;
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (lane < kPgMax) sm.pg[x][lane] = pv[x];
+  }
+  // per column: first visible slot per class (-1: the column attends to nothing)
+  if (lane < GB) {
+    const bool on = lane < ncol && (mval == TR_MODE_FULL || mval == TR_MODE_LOCAL);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) sm.lb[x][lane] = !on ? -1 : (mval == TR_MODE_LOCAL ? al[x] : a[x]);
+  }
+  // query rows in fp32 (in the score buffer), their sums and fp16 prescale
+  float* qf = sm.sc;
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int x = lane + kWave * i;
+    if (x < GB * D) qf[x] = x < ncol * D && (((fullm | locm) >> (x / D)) & 1) ? tr_bf16_lo((uint32_t)qraw[i]) : 0.0f;
+  }
+  wave_lds_sync();
+  for (int n = 0; n < ncol; ++n) {
+    float qs = 0.0f, qm = 0.0f;
+    for (int d = lane; d < D; d += kWave) {
+      const float v = qf[n * D + d];
+      qs += v;
+      qm = fmaxf(qm, fabsf(v));
+    }
+    qs = wave_sum(qs);
+    qm = wave_max(qm);
+    if (lane == 0) {
+      const int ex = qm > 0.0f ? __builtin_amdgcn_frexp_expf(qm) : 0;   // qm < 2^ex
+      sm.isig[n] = ldexpf(1.0f, ex - 15);                                // q' = q 2^(15 - ex) < 2^15
+      sm.qsum[n] = qs;
+    }
+  }
+  wave_lds_sync();
+  // A operands of every class: lane -> (class cl, step st, group gg), 8 values each; the fp16
+  // classes' 1024-offset sums per (class, column)
+  {
+    constexpr int GPC = KS * 4;                    // (step, group) pairs per class
+    const int cl = lane / GPC, sg = lane % GPC, st = sg / 4, gg = sg % 4;
+    for (int n = 0; n < ncol; ++n) {
+      const float pre = 1.0f / sm.isig[n];
+      float osum = 0.0f;
+      if (cl < 4) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          int ch0 = 0, ch1 = 0;
+          float f0 = 1.0f, f1 = 1.0f;
+          if (cl == 0) { qchan<D, 0>(st, gg, j, ch0, f0); qchan<D, 0>(st, gg, j + 1, ch1, f1); }
+          else if (cl == 1) { qchan<D, 1>(st, gg, j, ch0, f0); qchan<D, 1>(st, gg, j + 1, ch1, f1); }
+          else { qchan<D, 2>(st, gg, j, ch0, f0); qchan<D, 2>(st, gg, j + 1, ch1, f1); }
+          const float v0 = qf[n * D + ch0], v1 = qf[n * D + ch1];
+          if (cl < 3) {
+            const _Float16 h0v = (_Float16)(v0 * pre * f0), h1v = (_Float16)(v1 * pre * f1);
+            osum += (float)h0v + (float)h1v;
+            w[j / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0v) | ((uint32_t)__builtin_bit_cast(uint16_t, h1v) << 16);
+          } else {
+            w[j / 2] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);   // exact: q is bf16
+          }
+        }
+        *reinterpret_cast<uint4*>(&sm.qv[cl][n][sg * 8]) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      // sum over the GPC lanes of each class (rows of 16 lanes for D = 128; half rows for 64)
+      if constexpr (GPC == 16) {
+        osum = row_sum(osum);
+      } else {
+        osum += dpp_f<0xB1>(osum);
+        osum += dpp_f<0x4E>(osum);
+        osum += dpp_f<0x141>(osum);
+      }
+      if (sg == 0 && cl < 3) sm.qoff[cl][n] = 1024.0f * osum;
+    }
+  }
+  for (int i = lane; i < GB * D; i += kWave) (&sm.od[0][0])[i] = 0.0f;
+  for (int i = lane; i < 128; i += kWave) (&sm.pb[GB][0][0])[i] = 0;
+  wave_lds_sync();
+
+  // phase 1
+  float mrun[NCL];
+#pragma unroll
+  for (int i = 0; i < NCL; ++i) mrun[i] = -INFINITY;
+  float vm[3] = {0.0f, 0.0f, 0.0f};
+  float vdummy = 0.0f;
+  if (e[0] > a[0]) phase1<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, kscale, mrun, vm[0]);
+  if (e[1] > a[1]) phase1<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, kscale, mrun, vm[1]);
+  if (e[2] > a[2]) phase1<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, kscale, mrun, vm[2]);
+  if (e[3] > a[3]) phase1<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, kscale, mrun, vdummy);
+  // column maxima: lanes of group g hold columns 4 i + g
+#pragma unroll
+  for (int i = 0; i < NCL; ++i) {
+    const float mx = row_max(mrun[i]);
+    if ((lane & 15) == 0 && 4 * i + (lane >> 4) < GB) sm.cmax[4 * i + (lane >> 4)] = mx;
+  }
+  // P' scales: class 0 alone, classes 1-3 together (b = 16 keys count as scale 1)
+  const int e0 = scale_exp(wave_max(vm[0]));
+  const int em = scale_exp(fmaxf(wave_max(fmaxf(vm[1], vm[2])), e[3] > a[3] ? 1.0f : 0.0f));
+  wave_lds_sync();
+
+  // phase 2
+  f32x4 acc[NT];
+  float lp[GB], zp[GB], cp[GB];
+#pragma unroll
+  for (int n = 0; n < GB; ++n) lp[n] = zp[n] = cp[n] = 0.0f;
+  const int r = lane & 15, g = lane >> 4;
+  if (e[0] > a[0]) {
+#pragma unroll
+    for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    phase2<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, ldexpf(1.0f, -e0), acc, lp, zp, cp);
+    // add the 2-bit class into od: tile 2 m row L = channel 32 m + 2 L, tile 2 m + 1 the odd one
+    float cr = 0.0f;
+#pragma unroll
+    for (int n = 0; n < GB; ++n) {
+      const float cs = wave_sum(cp[n]);
+      cp[n] = 0.0f;
+      cr = r == n ? cs : cr;
+    }
+    const float s0 = ldexpf(1.0f, e0);
+    if (r < ncol) {
+#pragma unroll
+      for (int m = 0; m < NT / 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 32 * m + 2 * (4 * g + i);
+          sm.od[r][ch] = (acc[2 * m][i] - cr) * s0;
+          sm.od[r][ch + 1] = (acc[2 * m + 1][i] - cr) * s0;
+        }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float tm = ldexpf(1.0f, -em);
+  if (e[1] > a[1]) phase2<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, tm, acc, lp, zp, cp);
+  if (e[2] > a[2]) phase2<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, tm, acc, lp, zp, cp);
+  if (e[3] > a[3]) phase2<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, tm, acc, lp, zp, cp);
+  wave_lds_sync();
+
+  // epilogue: lane (column r, group g) holds channels 16 m + 4 g + i of column r
+  float lsum = 0.0f, zsum = 0.0f, corr = 0.0f;
+#pragma unroll
+  for (int n = 0; n < GB; ++n) {
+    const float ls = wave_sum(lp[n]), zs = wave_sum(zp[n]), cs = wave_sum(cp[n]);
+    if (r == n) {
+      lsum = ls;
+      zsum = zs;
+      corr = cs;
+    }
+  }
+  if (r >= ncol || !(((fullm | locm) >> r) & 1)) return;
+  const float sM = ldexpf(1.0f, em);
+  const float mx = sm.cmax[r];
+  const int64_t orow = row0 + r;
+  float o[NT][4];
+#pragma unroll
+  for (int m = 0; m < NT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[m][i] = (acc[m][i] - corr) * sM + sm.od[r][16 * m + 4 * g + i] + zsum;
+  if (nch == 1) {
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      uint2 w;
+      w.x = (uint32_t)tr_f32_to_bf16(o[m][0] * inv) | ((uint32_t)tr_f32_to_bf16(o[m][1] * inv) << 16);
+      w.y = (uint32_t)tr_f32_to_bf16(o[m][2] * inv) | ((uint32_t)tr_f32_to_bf16(o[m][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(out + orow * D + 16 * m + 4 * g) = w;
     }
     return;
   }
-  const int lo = (m == TR_MODE_FULL) ? 0 : max(0, t - window);
-  const int L = t + 1 - lo;
-  const int nch = (L + CH - 1) / CH;
-  if (k >= nch) return;
-  const int per = (L + nch - 1) / nch;
-  const int p0 = lo + k * per, p1 = min(p0 + per, t + 1);
-
-  const int32_t* pa = tr_prefix_row(c, layer, s, p0);
-  const int32_t* pe = tr_prefix_row(c, layer, s, p1);
-  int a[4], e[4], off[4], first[4];
-  int nk = 0;
+  float* dst = part + (orow * stride + k) * (D + 2);
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    a[x] = pa[x];
-    e[x] = pe[x];
-    off[x] = nk;
-    nk += e[x] - a[x];
-    first[x] = a[x] >> c.ptok_log2[x];
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    if (e[x] > a[x]) {
-      const int np = ((e[x] - 1) >> c.ptok_log2[x]) - first[x] + 1;
-      const int32_t* pt = tr_ptab(c, layer, s, x) + first[x];
-      for (int i = lane; i < np; i += kWave) pg[x][i] = pt[i];
-    }
-  }
-  float qpart = 0.0f, qpart0 = 0.0f;
-#pragma unroll
-  for (int d = lane; d < D; d += kWave) {
-    const float v = tr_bf16_lo((uint32_t)q[(int64_t)sh * D + d]);
-    qs[d] = v;
-    qpart += v;
-    qpart0 += v * q_scale_k2(d & 7);              // channel d sits in pair (d & 7) of its 16
-  }
-  const float sigma = wave_sum(qpart), sig0 = wave_sum(qpart0);
-  __syncthreads();
-
-  if (e[0] > a[0]) score_phase<D, 0>(c, pg[0], first[0], h, a[0], e[0], off[0], qs, sigma, sig0, kscale, sc);
-  if (e[1] > a[1]) score_phase<D, 1>(c, pg[1], first[1], h, a[1], e[1], off[1], qs, sigma, sig0, kscale, sc);
-  if (e[2] > a[2]) score_phase<D, 2>(c, pg[2], first[2], h, a[2], e[2], off[2], qs, sigma, sig0, kscale, sc);
-  if (e[3] > a[3]) score_phase<D, 3>(c, pg[3], first[3], h, a[3], e[3], off[3], qs, sigma, sig0, kscale, sc);
-  __syncthreads();
-
-  float mx = -INFINITY;
-  for (int i = lane; i < nk; i += kWave) mx = fmaxf(mx, sc[i]);
-  mx = wave_max(mx);
-  float lsum = 0.0f;
-  for (int i = lane; i < nk; i += kWave) {
-    const float p = exp2f(sc[i] - mx);
-    sc[i] = p;
-    lsum += p;
-  }
-  lsum = wave_sum(lsum);
-  __syncthreads();
-
-  float acc[32];
-#pragma unroll
-  for (int x = 0; x < 32; ++x) acc[x] = 0.0f;
-  float zacc = 0.0f;
-  if (e[0] > a[0]) value_phase<D, 0>(c, pg[0], first[0], h, a[0], e[0], off[0], sc, acc, zacc);
-  if (e[1] > a[1]) value_phase<D, 1>(c, pg[1], first[1], h, a[1], e[1], off[1], sc, acc, zacc);
-  if (e[2] > a[2]) value_phase<D, 2>(c, pg[2], first[2], h, a[2], e[2], off[2], sc, acc, zacc);
-  if (e[3] > a[3]) value_phase<D, 3>(c, pg[3], first[3], h, a[3], e[3], off[3], sc, acc, zacc);
-
-  // Sum over the key slots (lanes with the same channel group); lane p < VLPK then holds
-  // channels [32 p, 32 p + 32).
-  constexpr int VLPK = D / 32;
-#pragma unroll
-  for (int x = 0; x < 32; ++x) acc[x] = sum_strided<VLPK>(acc[x]);
-  zacc = wave_sum(zacc);
-  if (nch == 1) {                                  // whole window in this chunk
-    if (lane < VLPK) {
-      const float inv = 1.0f / lsum;
-      uint32_t pk[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        pk[x] = (uint32_t)tr_f32_to_bf16((acc[2 * x] + zacc) * inv) |
-                ((uint32_t)tr_f32_to_bf16((acc[2 * x + 1] + zacc) * inv) << 16);
-      uint4* dst = reinterpret_cast<uint4*>(o + 32 * lane);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) dst[x] = make_uint4(pk[4 * x], pk[4 * x + 1], pk[4 * x + 2], pk[4 * x + 3]);
-    }
-    return;
-  }
-  float* dst = part + ((int64_t)sh * max_chunks + k) * (D + 2);
-  if (lane < VLPK) {
-#pragma unroll
-    for (int x = 0; x < 32; ++x) dst[32 * lane + x] = acc[x] + zacc;
-  }
-  if (lane == 0) {
+  for (int m = 0; m < NT; ++m)
+    *reinterpret_cast<float4*>(dst + 16 * m + 4 * g) = make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
+  if (g == 0) {
     dst[D] = mx;
     dst[D + 1] = lsum;
   }
 }
 
 // Log-sum-exp merge of the chunks of windows that span more than one chunk: one workgroup per
-// (seq, head), thread d = channel d.  Chunks go in batches of 32: every load of a batch -- the
-// channel's 32 partial values and, in lane k of each wave, chunk k's (max, sum) -- is issued at
-// once (indices clamped into the window), then the batch folds into a running (max, num, den)
-// with the chunk weights broadcast from their lanes.
+// (seq, query head), thread d = channel d.  The chunks are those of the union window of the
+// head's block of query heads (a chunk outside the head's own window carries max -inf, weight 0).
+// Chunks go in batches of 32: every load of a batch -- the channel's 32 partial values and, in
+// lane k of each wave, chunk k's (max, sum) -- is issued at once (indices clamped into the window),
+// then the batch folds into a running (max, num, den) with the chunk weights broadcast from their
+// lanes.
 template <int D>
-__global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH, int max_chunks,
-                                                      const uint8_t* __restrict__ mode,
-                                                      const float* __restrict__ part, uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH, int stride,
+                                                      const uint8_t* __restrict__ mode, const float* __restrict__ part,
+                                                      uint16_t* __restrict__ out, int HQ, int G, int GB) {
   constexpr int KB = 32;
   const int sh = blockIdx.x;
   const int d = threadIdx.x, lane = d & 63;
   const int m = mode[sh];
   if (m != TR_MODE_LOCAL && m != TR_MODE_FULL) return;
-  const int lo = (m == TR_MODE_FULL) ? 0 : max(0, t - window);
+  // the union window of the head's block
+  const int hq = sh % HQ;
+  const int b0 = (hq / G) * G + ((hq % G) / GB) * GB;
+  const int nb = min(GB, (hq / G) * G + G - b0);
+  bool anyfull = false;
+  for (int n = 0; n < nb; ++n) anyfull |= mode[sh - hq + b0 + n] == TR_MODE_FULL;
+  const int lo = anyfull ? 0 : max(0, t - window);
   const int L = t + 1 - lo;
   const int nch = (L + CH - 1) / CH;
   if (nch == 1) return;                            // written by k_decode
-  const float* base = part + (int64_t)sh * max_chunks * (D + 2);
+  const float* base = part + (int64_t)sh * stride * (D + 2);
   float M = -INFINITY, num = 0.0f, den = 0.0f;
   for (int k0 = 0; k0 < nch; k0 += KB) {
     float v[KB];
@@ -551,30 +1005,34 @@ __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH,
     const float lk = pk[D + 1];
     const float Mn = fmaxf(M, wave_max(mk));
     const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
-    const float wk = own ? exp2f(mk - Mn) : 0.0f;
+    const float wk = (own && mk != -INFINITY) ? exp2f(mk - Mn) : 0.0f;
     den = den * a + wave_sum(wk * lk);
-    float nb = 0.0f;
+    float nb2 = 0.0f;
 #pragma unroll
     for (int x = 0; x < KB; ++x)
-      nb = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), x)), v[x], nb);
-    num = num * a + nb;
+      nb2 = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), x)), v[x], nb2);
+    num = num * a + nb2;
     M = Mn;
   }
   out[(int64_t)sh * D + d] = tr_f32_to_bf16(num / den);
 }
 
-}  // namespace
+// Columns per item: the query heads of one KV head, up to 4 per item.
+int block_cols(int G) { return G == 1 ? 1 : 4; }
 
-namespace {
-
-// Chunks per window for a decode over n positions of BH (seq, query head) pairs with room for
-// `limit` partial records per pair: about 8192 work items if every head were full (a few times
-// the waves the chip holds at once), but no chunk below kMinChunk positions and none above the
-// work item's limit; 0 if `limit` cannot hold the chunks a full window needs.
-int decode_chunks(const tr_kv_cache* c, int n, int BH, int limit) {
-  const int max_ch = tr_decode_max_chunk(c->lay);
+// Chunks per window for a decode over n positions with room for `limit` partial records per
+// (seq, query head): about 8192 work items if every head were full (a few times the waves the chip
+// holds at once), but no chunk below kMinChunk positions and none above the work item's limits;
+// 0 if `limit` cannot hold the chunks a full window needs.
+int decode_chunks(const tr_kv_cache* c, int n, int limit) {
+  const int GB = block_cols(c->grp);
+  const int NB = (c->grp + GB - 1) / GB;
+  const int items = c->lay.B * c->lay.H * NB;       // (seq, KV head, block) groups
+  int max_ch = tr_decode_max_chunk(c->lay);
+  const int cap = GB == 1 ? chunk_cap<1>() : chunk_cap<4>();
+  if (max_ch > cap) max_ch = cap;
   const int need = (n + max_ch - 1) / max_ch;      // fewest chunks a full window allows
-  int nch = (8192 + BH - 1) / BH;
+  int nch = (8192 + items - 1) / items;
   if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
   if (nch < need) nch = need;
   if (nch > limit) nch = limit;
@@ -591,29 +1049,39 @@ tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t
   const CacheLayout& L = c->lay;
   const int t = c->len[layer] - 1;
   const int n = t + 1;
+  const int G = c->grp;
+  const int GB = block_cols(G);
+  const int NB = (G + GB - 1) / GB;
   const int BH = L.B * c->hq;                       // (seq, query head) pairs
   const int CH = (n + nch - 1) / nch;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
-  const int grid = BH * nch;
+  const int grid = L.B * L.H * NB * nch;
   const bool prof_was = c->prof_on;
   c->prof_on = prof_was && prof_ok;
   tr_status st = TR_OK;
   {
     TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
-    if (L.D == 64)
-      hipLaunchKernelGGL(k_decode<64>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch, stride,
-                         kscale, q, mode, part, out, c->hq, c->grp);
-    else
-      hipLaunchKernelGGL(k_decode<128>, dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, nch, stride,
-                         kscale, q, mode, part, out, c->hq, c->grp);
+#define TR_DECODE_LAUNCH(DD, GG)                                                                             \
+  hipLaunchKernelGGL((k_decode<DD, GG>), dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, stride, \
+                     kscale, q, mode, part, out, c->hq, G, NB)
+    if (L.D == 64) {
+      if (GB == 1) TR_DECODE_LAUNCH(64, 1);
+      else TR_DECODE_LAUNCH(64, 4);
+    } else {
+      if (GB == 1) TR_DECODE_LAUNCH(128, 1);
+      else TR_DECODE_LAUNCH(128, 4);
+    }
+#undef TR_DECODE_LAUNCH
     if (hipGetLastError() != hipSuccess) st = TR_ERR_HIP;
   }
   if (st == TR_OK && nch > 1) {
     TrProfScope prof(c, TR_PROF_DECODE_COMBINE, stream);
     if (L.D == 64)
-      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, stride, mode, part, out);
+      hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, stride, mode, part, out,
+                         c->hq, G, GB);
     else
-      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, t, window, CH, stride, mode, part, out);
+      hipLaunchKernelGGL(k_decode_combine<128>, dim3(BH), dim3(128), 0, stream, t, window, CH, stride, mode, part,
+                         out, c->hq, G, GB);
     if (hipGetLastError() != hipSuccess) st = TR_ERR_HIP;
   }
   c->prof_on = prof_was;
@@ -624,8 +1092,7 @@ tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t
 
 tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window,
                            uint16_t* out, hipStream_t stream) {
-  const int n = c->len[layer];
-  const int nch = decode_chunks(c, n, c->lay.B * c->hq, c->max_chunks);
+  const int nch = decode_chunks(c, c->len[layer], c->max_chunks);
   if (nch < 1) return TR_ERR_UNSUPPORTED;
   return decode_run(c, layer, q, mode, window, out, nch, c->partials, c->max_chunks, true, stream);
 }
@@ -671,7 +1138,7 @@ tr_status tr_decode_noalloc_launch(tr_kv_cache* c, int layer, const uint16_t* q,
   const int BH = c->lay.B * c->hq;
   const int64_t rec = (int64_t)(c->lay.D + 2) * sizeof(float);
   const int64_t limit = (int64_t)TR_NOALLOC_SCRATCH_BYTES / rec / BH;    // partial records per pair
-  const int nch = decode_chunks(c, c->len[layer], BH, (int)(limit < (1 << 20) ? limit : (1 << 20)));
+  const int nch = decode_chunks(c, c->len[layer], (int)(limit < (1 << 20) ? limit : (1 << 20)));
   if (nch < 1) return TR_ERR_SCRATCH;
   // every chunk writes its own record before the combine reads it: nothing needs clearing
   return decode_run(c, layer, q, mode, window, out, nch, part, nch, false, stream);

@@ -121,19 +121,24 @@ def test_decode_config4_full_size(tr):
 
 
 def test_decode_chunking_and_paging_invariance(tr):
-    """Page sizes leave the output bit-identical; every forced split-K chunk count matches the
-    oracle: 5 and 8 chunks (one combine batch), 40 and 64 chunks (merges of more than 32 chunks,
-    i.e. two combine batches), a single chunk over a whole window of up to 512 positions, and a
-    single chunk over a longer window is refused."""
+    """With the chunk count fixed, page sizes leave the output bit-identical; every forced split-K
+    chunk count matches the oracle: 5 and 8 chunks (one combine batch), 40 and 64 chunks (merges of more than 32 chunks,
+    i.e. two combine batches), a single chunk over a whole window of the largest item (544
+    positions), and a single chunk over a longer window is refused."""
     say("decode: split-K chunk counts and page sizes agree")
     case = random_case(2, 2500, 4, 128, window=700, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
                        mode_weights={"local": 0.5, "full": 0.5}, seed=77, device="cuda", n_queries=1)
     case["q"], case["mode"] = case["q"][:, 0].contiguous(), case["mode"][:, 0].contiguous()
-    base, _ = run_decode(tr, case, 700)
+    # pages of 1024 code bytes hold 4 bf16 tokens at head_dim 128, which caps a chunk at 136
+    # positions; with the chunk count fixed (20 chunks of 125) the page size must not matter
+    base, _ = run_decode(tr, case, 700, chunks=20)
     for pcb in (1024, 16384):
-        other, _ = run_decode(tr, case, 700, page_code_bytes=pcb)
+        other, _ = run_decode(tr, case, 700, page_code_bytes=pcb, chunks=20)
         assert torch.equal(base, other), f"page_code_bytes={pcb} changed the output"
     refs = oracle_decode(case, 700, range(2))
+    got = bf16_to_f64(base)
+    for s in range(2):
+        compare_out(got[s], refs[s], f"nch=20 seq {s}")
     for nch in (5, 8, 40, 64):
         out, status = run_decode(tr, case, 700, chunks=nch)
         assert status == 0
@@ -142,12 +147,12 @@ def test_decode_chunking_and_paging_invariance(tr):
             compare_out(got[s], refs[s], f"nch={nch} seq {s}")
     with pytest.raises(tr.TriRouteError):
         run_decode(tr, case, 700, chunks=1)               # 2500 positions in one item: refused
-    short = random_case(2, 512, 4, 128, window=100, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+    short = random_case(2, 544, 4, 128, window=100, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
                         mode_weights={"local": 0.5, "full": 0.5}, seed=78, device="cuda", n_queries=1)
     short["q"], short["mode"] = short["q"][:, 0].contiguous(), short["mode"][:, 0].contiguous()
     out, status = run_decode(tr, short, 100, chunks=1)
     assert status == 0
-    check(short, out, 100, range(2), "nch=1, 512-position window")
+    check(short, out, 100, range(2), "nch=1, 544-position window")
 
 def test_decode_bad_mode_is_flagged(tr):
     case = random_case(1, 20, 2, 64, window=3, bit_weights={4: 1.0}, mode_weights={"full": 1.0},
