@@ -51,7 +51,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Positions per chunk the LDS score buffer holds, by columns per item.
 template <int GB>
-constexpr int chunk_cap() { return GB == 1 ? TR_DECODE_ITEM_MAX : 256; }
+constexpr int chunk_cap() { return GB == 1 ? TR_DECODE_ITEM_MAX : 352; }
 
 // A constant hidden from the compiler in an SGPR / a VGPR, so that (x & m) | c is emitted as one
 // v_and_or_b32 (VOP3 takes no literal operands; left visible, the compiler splits it in two).
@@ -194,6 +194,15 @@ __device__ __forceinline__ void exp_v2(uint32_t x, uint32_t* p, uint32_t K, uint
   p[3] = ((x >> 12) & m0) | K;
 }
 
+// 8 two-bit fields (element e at bits 2e of the low 16 bits, or of the high 16 bits for hi) into
+// 8 four-bit slots (element e at bits 4e): a 2-bit code row restaged with the 4-bit row layout.
+__device__ __forceinline__ uint32_t spread2(uint32_t w, bool hi) {
+  uint32_t x = __builtin_amdgcn_perm(0u, w, hi ? 0x0c030c02u : 0x0c010c00u);   // bytes b, 0, b', 0
+  x = (x | (x << 4)) & 0x0f0f0f0fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return x;
+}
+
 // Factor on the P' operand of key k (0..7) of a tr4 word, undoing the expansion's field scale.
 template <int C>
 __device__ __forceinline__ float pfield(int k) {
@@ -224,35 +233,59 @@ template <int D, int GB>
 struct Smem {
   static constexpr int SCAP = chunk_cap<GB>() + 32;   // per column: chunk + 8-padding per class
   static constexpr int VT = D == 128 ? 5120 : 3072;   // one staged V tile (largest class)
-  alignas(16) uint8_t vt[VT];
+  // The 2-bit class's contribution waits in LDS (one column) or in registers (blocks of query
+  // heads, whose LDS is the tighter budget; it passes through the dead score buffer at the end).
+  static constexpr bool kOdLds = GB == 1;
+  union {                                             // phase 1 reads qv, phase 2 stages vt
+    alignas(16) uint8_t vt[VT];                       // one staged V tile
+    alignas(16) uint16_t qv[4][GB][D];                // query rows as A operands, per class
+  };
   alignas(16) float sc[GB * SCAP];                    // scores; q rows during the prologue
-  alignas(16) uint16_t qv[4][GB][D];                  // query rows as A operands, per class
   alignas(16) uint16_t pb[GB + 1][2][64];             // P' hi / lo of a tile; column GB = zeros
-  alignas(16) float od[GB][D];                        // the 2-bit class's contribution
+  alignas(16) float od[kOdLds ? GB : 1][kOdLds ? D : 1];
   int32_t pg[TR_NCLASS][kPgMax];                      // page ids of the chunk, per class
   float qoff[4][GB];                                  // 1024 * sum of each class's A row
   float isig[GB], qsum[GB], cmax[GB];
   int32_t lb[TR_NCLASS][GB];                          // first visible slot per class and column
 };
 
-// Channel of element j of step s, lane group g, in class C's query operand, and the factor that
-// undoes the code field's power of two (D / 4 channels per lane group).
-template <int D, int C>
-__device__ __forceinline__ void qchan(int s, int g, int j, int& ch, float& f) {
-  const int base = (D / 4) * g;
-  if constexpr (C == 0) {
-    const int fld = 4 * (s & 1) + (j >> 1);
-    ch = base + 16 * (s >> 1) + fld + 8 * (j & 1);
-    const int pw = fld < 5 ? fld : fld - 5;
-    f = pw == 0 ? 1.0f : pw == 1 ? 0.25f : pw == 2 ? 0.0625f : pw == 3 ? 0.015625f : 0.00390625f;
-  } else if constexpr (C == 1) {
-    ch = base + 8 * s + (j >> 1) + 4 * (j & 1);
-    f = ((j >> 1) & 1) ? 0.0625f : 1.0f;
-  } else {
-    ch = base + 8 * s + j;
-    f = 1.0f;
+// The query operand's channel map.  Lane l builds 8 elements of the A operand of class
+// cl = l / (D / 8) (classes 0, 1, 2 fp16, class 3 bf16) for MFMA step s and lane group g
+// ((s, g) = ((l % (D / 8)) / 4, l % 4)): element j is channel ch[l][j] of the query row, times
+// 2^-fx[l][j], the inverse of the power of two at which the key expansion leaves that channel's
+// code field (D / 4 channels per lane group).  A compile-time table: every item reads its two
+// 8-byte rows instead of recomputing the map.
+struct QMap {
+  uint8_t ch[kWave][8];
+  uint8_t fx[kWave][8];
+};
+template <int D>
+constexpr QMap make_qmap() {
+  QMap t{};
+  constexpr int GPC = (D / 32) * 4;
+  for (int lane = 0; lane < kWave; ++lane) {
+    const int cl = lane / GPC, sg = lane % GPC, s = sg / 4, g = sg % 4;
+    const int base = (D / 4) * g;
+    for (int j = 0; j < 8; ++j) {
+      int ch = 0, fx = 0;
+      if (cl == 0) {                               // 2-bit: pairs (f, 8 + f) of field f in 0..4
+        const int fld = 4 * (s & 1) + (j >> 1);
+        ch = base + 16 * (s >> 1) + fld + 8 * (j & 1);
+        fx = 2 * (fld < 5 ? fld : fld - 5);
+      } else if (cl == 1) {                        // 4-bit: pairs (0, 4), (1, 5) x 16, ...
+        ch = base + 8 * s + (j >> 1) + 4 * (j & 1);
+        fx = ((j >> 1) & 1) ? 4 : 0;
+      } else if (cl < 4) {                         // 8-bit and bf16: in order
+        ch = base + 8 * s + j;
+      }
+      t.ch[lane][j] = (uint8_t)ch;
+      t.fx[lane][j] = (uint8_t)fx;
+    }
   }
+  return t;
 }
+__constant__ QMap kQmap64 = make_qmap<64>();
+__constant__ QMap kQmap128 = make_qmap<128>();
 
 // Phase 1 for width class C over class slots [a, e): scores into sc[n * SCAP + off + (j - a)].
 template <int D, int GB, int C>
@@ -422,7 +455,10 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
   using K = Cls<D, C>;
   constexpr int NT = D / 16;
   constexpr int SCAP = Smem<D, GB>::SCAP;
-  constexpr int TK = K::TK, RS = K::RS;
+  // SP: the 2-bit class restaged with each code in a 4-bit slot (blocks of query heads), so that
+  // its products land in the same accumulator layout as the other classes
+  constexpr bool SP = C == 0 && !Smem<D, GB>::kOdLds;
+  constexpr int TK = K::TK, RS = SP ? 2 * K::RB + 16 : K::RS;
   const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
   const int lpg = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
   const int64_t code_off = c.v_off[C] + (int64_t)h * c.cb;
@@ -470,8 +506,18 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
 #pragma unroll
     for (int x = 0; x < K::NPL; ++x) {
       const int pcx = lane + 64 * x;
-      if (K::NP % 64 == 0 || pcx < K::NP)
-        *reinterpret_cast<u32x4*>(sm.vt + (pcx / K::PPR) * RS + 16 * (pcx % K::PPR)) = cur.pc[x];
+      if (K::NP % 64 == 0 || pcx < K::NP) {
+        if constexpr (SP) {
+          const u32x4 v = cur.pc[x];
+          const u32x4 lo = {spread2(v[0], false), spread2(v[0], true), spread2(v[1], false), spread2(v[1], true)};
+          const u32x4 hi = {spread2(v[2], false), spread2(v[2], true), spread2(v[3], false), spread2(v[3], true)};
+          uint8_t* dst = sm.vt + (pcx / K::PPR) * RS + 32 * (pcx % K::PPR);
+          *reinterpret_cast<u32x4*>(dst) = lo;
+          *reinterpret_cast<u32x4*>(dst + 16) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(sm.vt + (pcx / K::PPR) * RS + 16 * (pcx % K::PPR)) = cur.pc[x];
+        }
+      }
     }
     const float2 szv = make_float2(cur.sz[0], cur.sz[1]);
     // P' of the tile's keys for every column: key j = lane
@@ -482,7 +528,7 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
       if constexpr (C <= 1) {
         const int kk = lane & 7;
         pos = (lane & ~7) + 2 * (kk & 3) + (kk >> 2);
-        fld = pfield<C>(kk);
+        fld = pfield<SP ? 1 : C>(kk);
       } else {
         pos = lane;
         fld = 1.0f;
@@ -523,7 +569,7 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
         bh[hb][0] = vh.x; bh[hb][1] = vh.y; bh[hb][2] = vh.z; bh[hb][3] = vh.w;
         bl[hb][0] = vl.x; bl[hb][1] = vl.y; bl[hb][2] = vl.z; bl[hb][3] = vl.w;
       }
-      if constexpr (C == 1) {
+      if constexpr (C == 1 || SP) {
 #pragma unroll
         for (int m = 0; m < NT; ++m) {
           uint32_t x0, x1, av[4];
@@ -636,11 +682,17 @@ __device__ __forceinline__ bool item_of_rank(int r, const uint8_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {                    // every load issued before any is used
       const int g = min(lane * P + i0 + i, groups - 1);
-      const int s = g / (H * NB), hb = g % (H * NB);
-      const int h0 = (hb / NB) * G + (hb % NB) * GB;
-      const int nc = min(GB, G - (hb % NB) * GB);
+      if (NB == 1) {
+        // one block per KV head: group g's G columns are query heads g G .. g G + G - 1
 #pragma unroll
-      for (int n = 0; n < 4; ++n) m[i][n] = n < GB ? mode[(int64_t)s * HQ + h0 + min(n, nc - 1)] : 0;
+        for (int n = 0; n < 4; ++n) m[i][n] = n < GB ? mode[(int64_t)g * G + min(n, G - 1)] : 0;
+      } else {
+        const int s = g / (H * NB), hb = g % (H * NB);
+        const int h0 = (hb / NB) * G + (hb % NB) * GB;
+        const int nc = min(GB, G - (hb % NB) * GB);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) m[i][n] = n < GB ? mode[(int64_t)s * HQ + h0 + min(n, nc - 1)] : 0;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -733,6 +785,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
     cb[w][1] = k < nch ? min(cb[w][0] + per, t + 1) : t + 1;
   }
   const int mval = lane < ncol ? (int)mode[row0 + lane] : 0;
+  const QMap& qmap = D == 128 ? kQmap128 : kQmap64;
+  const u32x2 qch = *reinterpret_cast<const u32x2*>(&qmap.ch[lane][0]);
+  const u32x2 qfx = *reinterpret_cast<const u32x2*>(&qmap.fx[lane][0]);
   constexpr int QPL = (GB * D + kWave - 1) / kWave;  // query values per lane
   uint16_t qraw[QPL];
 #pragma unroll
@@ -827,7 +882,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   // classes' 1024-offset sums per (class, column)
   {
     constexpr int GPC = KS * 4;                    // (step, group) pairs per class
-    const int cl = lane / GPC, sg = lane % GPC, st = sg / 4, gg = sg % 4;
+    const int cl = lane / GPC, sg = lane % GPC;
     for (int n = 0; n < ncol; ++n) {
       const float pre = 1.0f / sm.isig[n];
       float osum = 0.0f;
@@ -835,14 +890,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          int ch0 = 0, ch1 = 0;
-          float f0 = 1.0f, f1 = 1.0f;
-          if (cl == 0) { qchan<D, 0>(st, gg, j, ch0, f0); qchan<D, 0>(st, gg, j + 1, ch1, f1); }
-          else if (cl == 1) { qchan<D, 1>(st, gg, j, ch0, f0); qchan<D, 1>(st, gg, j + 1, ch1, f1); }
-          else { qchan<D, 2>(st, gg, j, ch0, f0); qchan<D, 2>(st, gg, j + 1, ch1, f1); }
+          const int ch0 = (qch[j >> 2] >> (8 * (j & 3))) & 0xff, ch1 = (qch[j >> 2] >> (8 * (j & 3) + 8)) & 0xff;
+          const int x0 = (qfx[j >> 2] >> (8 * (j & 3))) & 0xff, x1 = (qfx[j >> 2] >> (8 * (j & 3) + 8)) & 0xff;
           const float v0 = qf[n * D + ch0], v1 = qf[n * D + ch1];
           if (cl < 3) {
-            const _Float16 h0v = (_Float16)(v0 * pre * f0), h1v = (_Float16)(v1 * pre * f1);
+            const _Float16 h0v = (_Float16)ldexpf(v0 * pre, -x0), h1v = (_Float16)ldexpf(v1 * pre, -x1);
             osum += (float)h0v + (float)h1v;
             w[j / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0v) | ((uint32_t)__builtin_bit_cast(uint16_t, h1v) << 16);
           } else {
@@ -862,7 +914,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
       if (sg == 0 && cl < 3) sm.qoff[cl][n] = 1024.0f * osum;
     }
   }
-  for (int i = lane; i < GB * D; i += kWave) (&sm.od[0][0])[i] = 0.0f;
+  if constexpr (Smem<D, GB>::kOdLds)
+    for (int i = lane; i < GB * D; i += kWave) (&sm.od[0][0])[i] = 0.0f;
   for (int i = lane; i < 128; i += kWave) (&sm.pb[GB][0][0])[i] = 0;
   wave_lds_sync();
 
@@ -893,11 +946,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
 #pragma unroll
   for (int n = 0; n < GB; ++n) lp[n] = zp[n] = cp[n] = 0.0f;
   const int r = lane & 15, g = lane >> 4;
+  constexpr bool kOdLds = Smem<D, GB>::kOdLds;
   if (e[0] > a[0]) {
 #pragma unroll
     for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     phase2<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, ldexpf(1.0f, -e0), acc, lp, zp, cp);
-    // add the 2-bit class into od: tile 2 m row L = channel 32 m + 2 L, tile 2 m + 1 the odd one
     float cr = 0.0f;
 #pragma unroll
     for (int n = 0; n < GB; ++n) {
@@ -905,20 +958,33 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
       cp[n] = 0.0f;
       cr = r == n ? cs : cr;
     }
-    const float s0 = ldexpf(1.0f, e0);
-    if (r < ncol) {
+    if constexpr (kOdLds) {
+      // the 2-bit class into od: tile 2 m row L = channel 32 m + 2 L, tile 2 m + 1 the odd one
+      const float s0 = ldexpf(1.0f, e0);
+      if (r < ncol) {
 #pragma unroll
-      for (int m = 0; m < NT / 2; ++m)
+        for (int m = 0; m < NT / 2; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ch = 32 * m + 2 * (4 * g + i);
-          sm.od[r][ch] = (acc[2 * m][i] - cr) * s0;
-          sm.od[r][ch + 1] = (acc[2 * m + 1][i] - cr) * s0;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int ch = 32 * m + 2 * (4 * g + i);
+            sm.od[r][ch] = (acc[2 * m][i] - cr) * s0;
+            sm.od[r][ch + 1] = (acc[2 * m + 1][i] - cr) * s0;
+          }
+      }
+    } else {
+      // same layout as the other classes: the offsets out, then rescaled (exactly, by a power of
+      // two) to their P' scale, and the other classes accumulate on top
+      const float s0 = ldexpf(1.0f, e0 - em);
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][i] = (acc[m][i] - cr) * s0;
     }
   }
+  if (kOdLds || !(e[0] > a[0])) {
 #pragma unroll
-  for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   const float tm = ldexpf(1.0f, -em);
   if (e[1] > a[1]) phase2<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, tm, acc, lp, zp, cp);
   if (e[2] > a[2]) phase2<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, tm, acc, lp, zp, cp);
@@ -944,7 +1010,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
 #pragma unroll
   for (int m = 0; m < NT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[m][i] = (acc[m][i] - corr) * sM + sm.od[r][16 * m + 4 * g + i] + zsum;
+    for (int i = 0; i < 4; ++i)
+      o[m][i] = (acc[m][i] - corr) * sM + (kOdLds ? sm.od[r][16 * m + 4 * g + i] : 0.0f) + zsum;
   if (nch == 1) {
     const float inv = 1.0f / lsum;
 #pragma unroll
@@ -1020,10 +1087,34 @@ __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH,
 // Columns per item: the query heads of one KV head, up to 4 per item.
 int block_cols(int G) { return G == 1 ? 1 : 4; }
 
+// Waves of k_decode<D, GB> the device holds at once (occupancy x compute units), per device; 0 if
+// the runtime cannot tell.
+template <int D, int GB>
+int resident_waves() {
+  static std::mutex mu;
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_decode<D, GB>), kWave,
+                                                     0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+        cus < 1) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev] = per_cu * cus;
+  }
+  return cache[dev];
+}
+
 // Chunks per window for a decode over n positions with room for `limit` partial records per
-// (seq, query head): about 8192 work items if every head were full (a few times the waves the chip
-// holds at once), but no chunk below kMinChunk positions and none above the work item's limits;
-// 0 if `limit` cannot hold the chunks a full window needs.
+// (seq, query head).  The kernel dispatches the items that read the cache first, so the count
+// aims at as many items as the chip holds waves at once if every group were full (fewer, longer
+// items when the groups alone fill it), but no chunk below kMinChunk positions and none above
+// the work item's limits; 0 if `limit` cannot hold the chunks a full window needs.
 int decode_chunks(const tr_kv_cache* c, int n, int limit) {
   const int GB = block_cols(c->grp);
   const int NB = (c->grp + GB - 1) / GB;
@@ -1032,7 +1123,10 @@ int decode_chunks(const tr_kv_cache* c, int n, int limit) {
   const int cap = GB == 1 ? chunk_cap<1>() : chunk_cap<4>();
   if (max_ch > cap) max_ch = cap;
   const int need = (n + max_ch - 1) / max_ch;      // fewest chunks a full window allows
-  int nch = (8192 + items - 1) / items;
+  int waves = c->lay.D == 64 ? (GB == 1 ? resident_waves<64, 1>() : resident_waves<64, 4>())
+                             : (GB == 1 ? resident_waves<128, 1>() : resident_waves<128, 4>());
+  if (waves < 1) waves = 4096;
+  int nch = waves / items;
   if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
   if (nch < need) nch = need;
   if (nch > limit) nch = limit;
