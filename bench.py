@@ -27,6 +27,14 @@ the mode and width arrays, timed on one layer's tokens for the 160M and 1.3B pre
 Sixth object (``moe``): the expert FFN of Eq. 3 (8 SwiGLU experts plus the null expert, top-2),
 timed on one layer's tokens for the 160M and 1.3B shapes and a 1.3B decode step, random weights.
 
+Seventh object (``small``): the workloads whose whole step fits in the 256 MB last-level cache --
+the tiny prefill (T = 256, 4 heads), the 160M decode (8 sequences, 2048 cached, 12 heads) and
+the 1.3B long-context decode (1 sequence, 65536 cached) -- timed iteration by iteration with the
+last-level cache evicted before each (a 512 MB buffer rewritten), the median reported.
+
+The line also carries the seed of the inputs, the sha256 of the library's sources and the git
+revision (null where the tree has no .git).
+
 Accounting (algorithmic, from the realized seeded draws):
   decode bytes  = per attended (key, KV head): 2*D*b/8 codes + 16 B (s, z of K and V) for b < 16,
                   4*D for b = 16, counted once over the union of the windows of the query heads
@@ -38,7 +46,11 @@ Accounting (algorithmic, from the realized seeded draws):
 Timing: warmup steps, then K steps between HIP events on the launch stream (torch's current
 stream), synchronized on both sides.  A second pass of the same steps with the library's
 per-kernel event timing enabled gives each kernel's average launch duration (roofline).
-The CPU oracle is timed on a bounded sample of the same inputs, on this host.
+The CPU oracle (``cpu_baseline``) is timed on a bounded sample of the same inputs, on this host,
+in spawned worker processes (one BLAS thread each, up to 16): decode = all 32 sequences of layer
+0, each the step repeated --cpu-reps times (Eq. 4 on the new token, then Eq. 2 for its heads) on
+a cache quantized beforehand (untimed); prefill = the whole step, one job per (layer, sequence).
+Its value = the sample's algorithmic bytes (tokens) / (timed work / workers).
 """
 
 from __future__ import annotations
@@ -67,7 +79,39 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # lists the files the kernel is built from and their sha256 when the counters were taken: once
 # any of them changes the figures no longer describe the kernel and the bench reports traffic
 # as null.
-TRAFFIC = {}
+TRAFFIC = {
+    ("k_decode", "1.3b-decode-L24-B32-C8192-H16-D128"): {
+        "fetch_kib": 174292.1, "write_kib": 1837.1, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "profile": "profiles/k_decode_1.3b-decode-L24-B32-C8192-H16-D128.md",
+        "sources": {
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "46f894c6c8b61767384a41249f5a437b29f526a97f532e366ed0a06046f82b8c",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
+            "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
+            "include/triroute.h": "03f5904b8aab554fe8d9b402e8e084ae7581b75d53d74bb4e77b6dbfed859738",
+        },
+    },
+    ("k_decode", "1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128"): {
+        "fetch_kib": 89339.7, "write_kib": 4642.8, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "profile": "profiles/k_decode_1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128.md",
+        "sources": {
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "46f894c6c8b61767384a41249f5a437b29f526a97f532e366ed0a06046f82b8c",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
+            "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
+            "include/triroute.h": "03f5904b8aab554fe8d9b402e8e084ae7581b75d53d74bb4e77b6dbfed859738",
+        },
+    },
+    ("k_prefill_attn", "160m-prefill-L12-B4-T2048-H12-D64"): {
+        "fetch_kib": 19257.7, "write_kib": 19043.9, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "profile": "profiles/k_prefill_attn_160m-prefill-L12-B4-T2048-H12-D64.md",
+        "sources": {
+            "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip": "af4ba0a1ed87eba042bc59e7c0e7eb069b4e8043c4b5a0d229a4430e331ee717",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
+            "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
+            "mixed_precision_kv_tr_amd/csrc/kv_write.h": "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
+            "include/triroute.h": "03f5904b8aab554fe8d9b402e8e084ae7581b75d53d74bb4e77b6dbfed859738",
+        },
+    },
+}
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA, TFLOP/s
 METRIC = "mixed-bit KV decode GB/s (% HBM peak); routed prefill tokens/s (% MFMA peak)"
