@@ -165,6 +165,38 @@ __global__ __launch_bounds__(1024) void k_moe_lists(const int32_t* __restrict__ 
 
 // The tile a workgroup takes: tiles of kTile listed tokens over the (slot, expert) lists in order,
 // restricted to slots [s0, s1) and experts [e0, E]; returns false past the last tile.
+// Work item of workgroup `b` of a 1-D grid of n: consecutive workgroups go to the eight XCDs in
+// turn, so XCD x (= b % 8) gets the contiguous range of items [start_x, start_x + count_x) --
+// items listed weight block by weight block then share their block in that XCD's L2 instead of
+// every XCD fetching it.
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  constexpr int kXcd = 8;
+  const int x = b % kXcd, i = b / kXcd, q = n / kXcd, r = n % kXcd;
+  return x * q + min(x, r) + i;
+}
+
+// Token tile `id` of the up products, expert by expert and, within an expert, slot by slot (so the
+// tiles of both slots that read one expert's weights are listed together).
+template <int kTile>
+__device__ __forceinline__ bool find_tile_expert_major(const int32_t* counts, int E, int K, int id, int& slot, int& e,
+                                                       int& tile, int& cnt) {
+  for (int x = 1; x <= E; ++x) {
+    for (int s = 0; s < K; ++s) {
+      const int c = counts[s * (E + 1) + x];
+      const int nt = (c + kTile - 1) / kTile;
+      if (id < nt) {
+        slot = s;
+        e = x;
+        tile = id;
+        cnt = c;
+        return true;
+      }
+      id -= nt;
+    }
+  }
+  return false;
+}
+
 template <int kTile>
 __device__ __forceinline__ bool find_tile(const int32_t* counts, int E, int s0, int s1, int e0, int id, int& slot,
                                           int& e, int& tile, int& cnt) {
@@ -191,12 +223,16 @@ template <int kMB>
 __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, const int32_t* __restrict__ lists,
                                                 const int32_t* __restrict__ counts, const float* __restrict__ inv_rms,
                                                 const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                                uint16_t* __restrict__ hbuf, int d, int de, int E, int k, int cap) {
+                                                uint16_t* __restrict__ hbuf, int d, int de, int E, int k, int cap,
+                                                int ntiles) {
   constexpr int kTile = 32 * kMB;
   __shared__ int32_t tok[kTile];
   __shared__ float inv[kTile];
+  // work item: (block of 128 hidden units, token tile), unit block by unit block
+  const int item = xcd_item(blockIdx.x, (int)gridDim.x);
+  const int ublk = item / ntiles;
   int slot, e, tile, cnt;
-  if (!find_tile<kTile>(counts, E, 0, k, 1, blockIdx.x, slot, e, tile, cnt)) return;
+  if (!find_tile_expert_major<kTile>(counts, E, k, item % ntiles, slot, e, tile, cnt)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ntok = min(kTile, cnt - tile * kTile);
   const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kTile;
@@ -207,7 +243,7 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
   }
   __syncthreads();
   const int r = lane & 31, kh = lane >> 5;
-  const int n = blockIdx.y * kUnits + 32 * wave + r;  // hidden unit of this lane's B column
+  const int n = ublk * kUnits + 32 * wave + r;      // hidden unit of this lane's B column
   // The tile's token rows are shared by the four waves: each stage of kPS k-steps (kPS * 16
   // channels of every row) is loaded once per workgroup, one 16-byte piece per thread, into a
   // double-buffered LDS tile whose 16-byte-padded rows spread over the banks.  Each wave's own
@@ -285,13 +321,16 @@ template <int kMB>
 __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ lists,
                                                   const int32_t* __restrict__ counts, const float* __restrict__ wt,
                                                   const uint16_t* __restrict__ wd, float* __restrict__ y, int d, int de,
-                                                  int E, int k, int cap, int slot) {
+                                                  int E, int k, int cap, int slot, int ntiles) {
   constexpr int kTile = 32 * kMB;
   __shared__ int32_t tok[kTile];
   __shared__ float wgt[kTile];
+  // work item: (block of 128 output channels, token tile), channel block by channel block
+  const int item = xcd_item(blockIdx.x, (int)gridDim.x);
+  const int cblk = item / ntiles;
   int s_, e, tile, cnt;
   // slot 0 also takes the null expert's tiles (zeros); later slots skip it
-  if (!find_tile<kTile>(counts, E, slot, slot + 1, slot == 0 ? 0 : 1, blockIdx.x, s_, e, tile, cnt)) return;
+  if (!find_tile<kTile>(counts, E, slot, slot + 1, slot == 0 ? 0 : 1, item % ntiles, s_, e, tile, cnt)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ntok = min(kTile, cnt - tile * kTile);
   const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kTile;
@@ -302,7 +341,7 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
   }
   __syncthreads();
   const int r = lane & 31, kh = lane >> 5;
-  const int n = blockIdx.y * kUnits + 32 * wave + r;  // output channel of this lane's B column
+  const int n = cblk * kUnits + 32 * wave + r;      // output channel of this lane's B column
   f32x16 acc[kMB] = {};
   if (e > 0) {
     // hidden rows shared by the four waves through LDS, as in k_moe_up
@@ -443,13 +482,15 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
   // upper bounds on the tile counts (the workgroups past the real count exit at once)
   auto run = [&](auto mb) {
     constexpr int MB = decltype(mb)::value, T = 32 * MB;
+    // 1-D grids of (unit block, token tile) items, see xcd_item
     const int tiles_up = K * ((M + T - 1) / T) + K * E;
-    hipLaunchKernelGGL(k_moe_up<MB>, dim3(tiles_up, m->de / kUnits), dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                       m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d, m->de, E, K, m->max_tokens);
+    hipLaunchKernelGGL(k_moe_up<MB>, dim3(tiles_up * (m->de / kUnits)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d,
+                       m->de, E, K, m->max_tokens, tiles_up);
     const int tiles_dn = (M + T - 1) / T + E + 1;
     for (int s = 0; s < K; ++s)
-      hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn, m->d / kUnits), dim3(256), 0, st, m->hbuf, m->lists,
-                         m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s);
+      hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn * (m->d / kUnits)), dim3(256), 0, st, m->hbuf, m->lists,
+                         m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s, tiles_dn);
   };
   if (M > kSmallCall) run(std::integral_constant<int, 2>());
   else run(std::integral_constant<int, 1>());
