@@ -316,6 +316,177 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
   }
 }
 
+// Gate and up products on a tile of 256 listed tokens x 128 hidden units (large calls): 8 waves,
+// each 64 tokens x 64 units of both products.  Per stage of 64 input channels the workgroup loads
+// the tile's x rows (A, 16-byte-padded rows) and the two weight blocks (B, in their packed k-step
+// order) into double-buffered LDS, one 64-byte piece of each per thread, the next stage in
+// registers while the current one multiplies: every weight byte brought in serves 256 tokens and
+// every x byte 128 units, against 64 and 128 in k_moe_up.  Epilogue as in k_moe_up.
+constexpr int kTM = 256;                 // listed tokens per tile
+constexpr int kGY = 4;                   // unit blocks per group in the work order
+
+// Items of the tiled up products, expert by expert: for expert e with T_e token tiles (both slots)
+// and NY unit blocks, groups of kGY unit blocks, within a group token tile by token tile, within
+// a tile its kGY unit blocks.  The XCD ranges (xcd_item) then give each XCD about one expert, and
+// the ~32 workgroups it runs at once share kGY weight blocks and a few token tiles in its L2.
+// Returns the item count when id < 0.
+__device__ __forceinline__ int up_item(const int32_t* counts, int E, int K, int NY, int id, int& slot, int& e, int& tile,
+                                       int& cnt, int& y) {
+  int base = 0;
+  for (int x = 1; x <= E; ++x) {
+    int te = 0;
+    for (int s = 0; s < K; ++s) te += (counts[s * (E + 1) + x] + kTM - 1) / kTM;
+    const int ne = te * NY;
+    if (id >= base && id < base + ne) {
+      const int i = id - base, nfull = NY / kGY;
+      int t;
+      if (i < nfull * te * kGY) {
+        const int r2 = i % (te * kGY);
+        t = r2 / kGY;
+        y = (i / (te * kGY)) * kGY + r2 % kGY;
+      } else {
+        const int i2 = i - nfull * te * kGY, gs = NY - nfull * kGY;
+        t = i2 / gs;
+        y = nfull * kGY + i2 % gs;
+      }
+      for (int s = 0; s < K; ++s) {
+        const int c = counts[s * (E + 1) + x];
+        const int nt = (c + kTM - 1) / kTM;
+        if (t < nt) {
+          slot = s;
+          e = x;
+          tile = t;
+          cnt = c;
+          return 1;
+        }
+        t -= nt;
+      }
+      return 0;
+    }
+    base += ne;
+  }
+  return id < 0 ? base : 0;
+}
+constexpr int kTN = 128;                 // hidden units per tile
+constexpr int kAP = 144;                 // LDS bytes per A row: 64 channels + 16 bytes
+constexpr int kBS = 2 * 4 * kTN * 32;    // LDS bytes of one stage's B tiles: [gate, up][k-step][unit][16]
+
+__global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x, const int32_t* __restrict__ lists,
+                                                  const int32_t* __restrict__ counts,
+                                                  const float* __restrict__ inv_rms, const uint16_t* __restrict__ wg,
+                                                  const uint16_t* __restrict__ wu, uint16_t* __restrict__ hbuf, int d,
+                                                  int de, int E, int k, int cap) {
+  __shared__ int32_t tok[kTM];
+  __shared__ float inv[kTM];
+  __shared__ __align__(16) uint8_t As[2][kTM * kAP];
+  __shared__ __align__(16) uint8_t Bs[2][kBS];
+  int slot = 0, e = 0, tile = 0, cnt = 0, ublk = 0;
+  const int nitems = up_item(counts, E, k, de / kTN, -1, slot, e, tile, cnt, ublk);
+  if ((int)blockIdx.x >= nitems) return;
+  if (!up_item(counts, E, k, de / kTN, xcd_item(blockIdx.x, nitems), slot, e, tile, cnt, ublk)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ntok = min(kTM, cnt - tile * kTM);
+  const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kTM;
+  if (tid < kTM) {
+    const int t = lst[min(tid, ntok - 1)];         // rows past the list's end repeat its last token
+    tok[tid] = t;
+    inv[tid] = inv_rms[t];
+  }
+  __syncthreads();
+  // this thread's pieces of a stage g (channels 64 g .. 64 g + 63):
+  //   A: row tid / 2, channels 32 (tid % 2) .. + 31 of the stage
+  //   B: piece c = tid / 64 = (matrix c / 4, k-step 4 g + c % 4), units 2 (tid % 64) and + 1
+  const int arow = tid >> 1, ahalf = tid & 1;
+  const uint16_t* xa = x + (int64_t)tok[arow] * d + 32 * ahalf;
+  const int bc = tid >> 6, bn = 2 * (tid & 63);
+  const int64_t mat = (int64_t)de * d;
+  const uint16_t* wb = ((bc >> 2) ? wu : wg) + (int64_t)(e - 1) * mat + ((int64_t)(bc & 3) * de + ublk * kTN + bn) * 16;
+  const int64_t gstep = (int64_t)4 * de * 16;     // elements per stage of 4 k-steps
+  // two register sets, one and two stages ahead of the stage being multiplied
+  uint4 ra0[4], rb0[4], ra1[4], rb1[4];
+  auto gl = [&](int g, uint4 (&ra)[4], uint4 (&rb)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = gload16(xa + 64 * g + 8 * q);
+      rb[q] = gload16(wb + g * gstep + 8 * q);
+    }
+  };
+  auto st = [&](int b, const uint4 (&ra)[4], const uint4 (&rb)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<uint4*>(&As[b][arow * kAP + 64 * ahalf + 16 * q]) = ra[q];
+      // unit u's two 16-byte halves swap places when bit 3 of u is set (see compute)
+      const int u = bn + (q >> 1);
+      *reinterpret_cast<uint4*>(&Bs[b][(bc * kTN + u) * 32 + 16 * ((q & 1) ^ ((u >> 3) & 1))]) = rb[q];
+    }
+  };
+  const int r = lane & 31, kh = lane >> 5;
+  const int tw = wave & 3, uw = wave >> 2;          // this wave: tokens 64 tw .., units 64 uw ..
+  f32x16 acc[2][2][2] = {};                         // [gate, up][token block][unit block]
+  auto compute = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 av[2], bv[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        av[tb] = *reinterpret_cast<const uint4*>(&As[b][(64 * tw + 32 * tb + r) * kAP + 16 * j + 64 * kh]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub)
+        {
+          // units r and r + 8 of a 16-lane pass would share banks at a 32-byte pitch: the halves
+          // of every unit with bit 3 set are stored swapped
+          const int u = 64 * uw + 32 * ub + r;
+          bv[m][ub] = *reinterpret_cast<const uint4*>(&Bs[b][((4 * m + j) * kTN + u) * 32 + 16 * (kh ^ ((u >> 3) & 1))]);
+        }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int ub = 0; ub < 2; ++ub) acc[m][tb][ub] = mfma(av[tb], bv[m][ub], acc[m][tb][ub]);
+    }
+  };
+  const int ns = d / 64;                            // even: d is a multiple of 128
+  gl(0, ra0, rb0);
+  st(0, ra0, rb0);
+  __syncthreads();
+  gl(min(1, ns - 1), ra0, rb0);
+  gl(min(2, ns - 1), ra1, rb1);
+  // stage g sits in LDS buffer g & 1; the loop is unrolled by two so that each register set keeps
+  // its registers (set 0 holds the odd stages, set 1 the even ones); loads are clamped, never
+  // branched around
+  for (int g = 0; g < ns; g += 2) {
+    compute(0);
+    st(1, ra0, rb0);                                // stage g + 1
+    __syncthreads();
+    gl(min(g + 3, ns - 1), ra0, rb0);
+    compute(1);
+    st(0, ra1, rb1);                                // stage g + 2 (a repeat of the last one at the end)
+    __syncthreads();
+    gl(min(g + 4, ns - 1), ra1, rb1);
+  }
+  // D[token][unit]: lane (r, kh) holds unit r of its unit block for rows 8 (reg / 4) + 4 kh + reg % 4
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const int row = 64 * tw + 32 * tb + 8 * (reg >> 2) + 4 * kh + (reg & 3);
+        if (row < ntok) {
+          const int n = ublk * kTN + 64 * uw + 32 * ub + r;
+          const float gv = acc[0][tb][ub][reg] * inv[row], uv = acc[1][tb][ub][reg] * inv[row];
+          const float h = gv / (1.0f + expf(-gv)) * uv;
+          const uint16_t hi = tr_f32_to_bf16(h);
+          uint16_t* hr = hbuf + ((int64_t)tok[row] * k + slot) * 2 * de + n;
+          hr[0] = hi;
+          hr[de] = tr_f32_to_bf16(h - tr_bf16_lo(hi));
+        }
+      }
+}
+
 // Down product for one slot: 32 kMB tokens of one (slot, expert) list and 128 output channels.
 template <int kMB>
 __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ lists,
@@ -483,10 +654,16 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
   auto run = [&](auto mb) {
     constexpr int MB = decltype(mb)::value, T = 32 * MB;
     // 1-D grids of (unit block, token tile) items, see xcd_item
-    const int tiles_up = K * ((M + T - 1) / T) + K * E;
-    hipLaunchKernelGGL(k_moe_up<MB>, dim3(tiles_up * (m->de / kUnits)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d,
-                       m->de, E, K, m->max_tokens, tiles_up);
+    if (MB == 2) {
+      const int tiles_up = K * ((M + kTM - 1) / kTM) + K * E;
+      hipLaunchKernelGGL(k_moe_up_t, dim3(tiles_up * (m->de / kTN)), dim3(512), 0, st, static_cast<const uint16_t*>(x),
+                         m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d, m->de, E, K, m->max_tokens);
+    } else {
+      const int tiles_up = K * ((M + T - 1) / T) + K * E;
+      hipLaunchKernelGGL(k_moe_up<MB>, dim3(tiles_up * (m->de / kUnits)), dim3(256), 0, st,
+                         static_cast<const uint16_t*>(x), m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d,
+                         m->de, E, K, m->max_tokens, tiles_up);
+    }
     const int tiles_dn = (M + T - 1) / T + E + 1;
     for (int s = 0; s < K; ++s)
       hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn * (m->d / kUnits)), dim3(256), 0, st, m->hbuf, m->lists,
