@@ -212,7 +212,13 @@ tr_status tr_profile_read(tr_kv_cache* cache, int64_t* launches, double* total_m
  *   mu_a, sigma_a, mu_b, sigma_b  float [128]   Eq. (11) statistics, attention / bit axis
  *   w_a      float [128][3 * heads]     attention head, in x out; head h's logits are columns
  *                                       3h (skip), 3h + 1 (local), 3h + 2 (full)
- *   w_b      float [128][4]             bit head, in x out; columns b = 2, 4, 8, 16 */
+ *   w_b      float [128][4]             bit head, in x out; columns b = 2, 4, 8, 16
+ * workspace (optional): DEVICE scratch of workspace_bytes >= tr_controller_workspace_bytes(d),
+ * 16-byte aligned, caller owned, or NULL.  With it, calls of up to 256 tokens (a decode step)
+ * spread the first layer over (tokens / 32 rounded up) x 4 x ceil(d / 256) workgroups and finish
+ * each token in a workgroup of its own (two launches); without it, and for larger calls, one
+ * workgroup handles 32 tokens.  Calls that share a workspace must be ordered (one stream); its
+ * contents need no initialization and are not kept between calls. */
 typedef struct {
   int32_t d;                /* model width: a multiple of 64, 64 .. 16384 */
   int32_t d_side;           /* side features per token, 0 .. 32 */
@@ -229,7 +235,13 @@ typedef struct {
   const float* sigma_b;
   const float* w_a;
   const float* w_b;
+  void* workspace;
+  int64_t workspace_bytes;
 } tr_controller_weights;
+
+/* Bytes of the optional controller workspace for model width d (a multiple of 64, 64 .. 16384;
+ * -1 otherwise): 4 * 8 * ceil(d / 256) * 32 * 129.  Host only; no device call. */
+int64_t tr_controller_workspace_bytes(int32_t d);
 
 /* Pack the controller's first-layer weights (bf16 [128][d], out x in, row-major, device) into
  * the operand order tr_controller_route reads: w1_packed (bf16, d * 128 values, device, caller
@@ -245,8 +257,10 @@ tr_status tr_controller_pack_w1(const void* w1, void* w1_packed, int32_t d, void
  *   mode: uint8 [n_tokens, heads]  argmax of each head's 3 logits (TR_MODE_*)
  *   bits: uint8 [n_tokens]         (2, 4, 8, 16)[argmax of the 4 width logits]
  * Ties go to the lowest index.  The trunk's first layer runs on the matrix cores with the bf16
- * x and w1 as exact operands and fp32 accumulation; everything after it is fp32.  n_tokens = 0
- * is a no-op. */
+ * x and w1 as exact operands and fp32 accumulation; everything after it is fp32 (the order of
+ * the fp32 sums differs between the one- and two-launch forms).  n_tokens = 0 is a no-op.
+ * TR_ERR_INVALID_ARG for a workspace smaller than tr_controller_workspace_bytes(d) or not
+ * 16-byte aligned. */
 tr_status tr_controller_route(const tr_controller_weights* w, const void* x, const float* side,
                               int64_t n_tokens, uint8_t* mode, uint8_t* bits, void* stream);
 

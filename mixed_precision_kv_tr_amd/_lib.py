@@ -32,7 +32,8 @@ class _Desc(ctypes.Structure):
 
 class _CtlWeights(ctypes.Structure):
     _fields_ = [("d", _i32), ("d_side", _i32), ("d_r", _i32), ("heads", _i32)] + [
-        (n, _vp) for n in ("w1", "w1_side", "b1", "w2", "b2", "mu_a", "sigma_a", "mu_b", "sigma_b", "w_a", "w_b")]
+        (n, _vp) for n in ("w1", "w1_side", "b1", "w2", "b2", "mu_a", "sigma_a", "mu_b", "sigma_b", "w_a", "w_b")] + [
+        ("workspace", _vp), ("workspace_bytes", _i64)]
 
 
 class _MoeDesc(ctypes.Structure):
@@ -60,6 +61,7 @@ _pages = _sig("tr_kv_cache_pages_used", _i64, _vp, _vp)
 _status_str = _sig("tr_status_str", ctypes.c_char_p, ctypes.c_int)
 _truncate = _sig("tr_kv_cache_truncate", ctypes.c_int, _vp, _i32, _i32)
 _ctl_pack = _sig("tr_controller_pack_w1", ctypes.c_int, _vp, _vp, _i32, _vp)
+_ctl_ws_bytes = _sig("tr_controller_workspace_bytes", _i64, _i32)
 _ctl_route = _sig("tr_controller_route", ctypes.c_int, ctypes.POINTER(_CtlWeights), _vp, _vp, _i64, _vp, _vp, _vp)
 _moe_alloc = _sig("tr_moe_alloc", ctypes.c_int, ctypes.POINTER(_MoeDesc), ctypes.POINTER(_vp))
 _moe_free = _sig("tr_moe_free", ctypes.c_int, _vp)
@@ -203,11 +205,13 @@ def tr_kv_cache_truncate(cache: KVCache, layer: int, new_len: int):
 
 class ControllerWeights:
     """The C struct tr_controller_weights built once from a dict of device tensors (and holding
-    them alive, with w1 packed by tr_controller_pack_w1), so that a call passes one pointer."""
+    them alive, with w1 packed by tr_controller_pack_w1), so that a call passes one pointer.
+    With workspace=True (the default) it also owns the optional workspace that lets calls of up
+    to 256 tokens spread over many workgroups."""
 
     NAMES = ("w1", "w1_side", "b1", "w2", "b2", "mu_a", "sigma_a", "mu_b", "sigma_b", "w_a", "w_b")
 
-    def __init__(self, weights: dict, stream=None):
+    def __init__(self, weights: dict, stream=None, workspace: bool = True):
         import torch
         d_r, d = weights["w1"].shape
         side = weights.get("w1_side")
@@ -218,9 +222,16 @@ class ControllerWeights:
         self.tensors["w1"] = torch.empty_like(weights["w1"])
         _check(_ctl_pack(_ptr(weights["w1"]), _ptr(self.tensors["w1"]), int(d), _stream(stream)),
                "tr_controller_pack_w1")
+        ws, ws_bytes = None, 0
+        if workspace:
+            ws_bytes = int(_ctl_ws_bytes(int(d)))
+            if ws_bytes < 0:
+                raise ValueError(f"tr_controller_workspace_bytes: unsupported d = {d}")
+            self.workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=weights["w1"].device)
+            ws = _ptr(self.workspace)
         self.struct = _CtlWeights(d, self.d_side, d_r, self.heads,
                                   *[_ptr(self.tensors[n]) if (n != "w1_side" or self.d_side) else None
-                                    for n in self.NAMES])
+                                    for n in self.NAMES], ws, ws_bytes)
 
 
 def tr_controller_route(weights, x, side, n_tokens: int, mode, bits, stream=None):

@@ -86,6 +86,8 @@ struct CtlSmem {
   float part[kSplit][kTok][kRow];
   float wts[kDr * kDr];
   float sd[kTok][kMaxSide];
+  float w1s[kDr][kMaxSide];       // layer 1's side-feature weights
+  float pu[6][kDr];               // per unit: b1, b2, mu_a, sigma_a, mu_b, sigma_b
   float ssp[kSplit][kTok];
   float inv2[kTok];
 };
@@ -106,9 +108,29 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
   float4 w2r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) w2r[j] = reinterpret_cast<const float4*>(a.w2)[tid + j * kThreads];
+  // every other small parameter goes out now too, so that no later step waits on memory: the side
+  // features and their weights, the per-unit vectors, and the heads' weights when they fit LDS
+  // (held in registers until W2 is done)
   for (int i = tid; i < kTok * a.d_side; i += kThreads) {
     const int t = i / a.d_side, s = i % a.d_side;
     sm.sd[t][s] = t < ntok ? side[(tok0 + t) * a.d_side + s] : 0.0f;
+  }
+  for (int i = tid; i < kDr * a.d_side; i += kThreads) sm.w1s[i / a.d_side][i % a.d_side] = a.w1_side[i];
+  if (tid < 6 * kDr) {
+    const int v = tid / kDr, n = tid % kDr;
+    const float* src = v == 0 ? a.b1 : v == 1 ? a.b2 : v == 2 ? a.mu_a : v == 3 ? a.sigma_a : v == 4 ? a.mu_b : a.sigma_b;
+    sm.pu[v][n] = src[n];
+  }
+  const int na = 3 * a.heads, no = na + 4;
+  const bool wl = no * kDr <= kDr * kDr;
+  constexpr int kHW = (3 * 40 + 4) * kDr / kThreads + 1;   // head weights per thread (up to 40 heads)
+  float hw[kHW];
+  if (wl) {
+#pragma unroll
+    for (int q = 0; q < kHW; ++q) {
+      const int i = tid + q * kThreads;
+      hw[q] = i < kDr * na ? a.w_a[i] : i < kDr * no ? a.w_b[i - kDr * na] : 0.0f;
+    }
   }
 
   // ---- layer 1 on the matrix cores: wave (unit block ub, k-split ks) computes
@@ -128,31 +150,29 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
     const int64_t wstep = (int64_t)kDr * 16;        // packed W1: one k-step of all units
     f32x16 acc = {};
     float ss = 0.0f;
-    if (g0 < g1) {
-      uint4 xa[4], wb[4];
+    // The wave's channel groups in chunks of kCG: every load of a chunk is issued before any of
+    // its products, so a split of up to kCG groups (d <= 2048) costs one memory round trip.
+    // Indices are clamped (loads never branch); groups past the split's end are not multiplied.
+    constexpr int kCG = 8;
+    for (int c0 = g0; c0 < g1; c0 += kCG) {
+      uint4 xa[kCG][4], wb[kCG][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xa[j] = gload16(xr + 64 * g0 + 8 * j);
-        wb[j] = gload16(wr + (4 * g0 + j) * wstep);
+      for (int q = 0; q < kCG; ++q) {
+        const int g = min(c0 + q, g1 - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xa[q][j] = gload16(xr + 64 * g + 8 * j);
+          wb[q][j] = gload16(wr + (4 * g + j) * wstep);
+        }
       }
-      for (int g = g0; g < g1; ++g) {
-        const int gn = min(g + 1, g1 - 1);          // clamped: the loads never branch
-        uint4 xn[4], wn[4];
+#pragma unroll
+      for (int q = 0; q < kCG; ++q) {
+        if (c0 + q >= g1) break;                    // wave-uniform
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          xn[j] = gload16(xr + 64 * gn + 8 * j);
-          wn[j] = gload16(wr + (4 * gn + j) * wstep);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[j]),
-                                                        __builtin_bit_cast(bf16x8, wb[j]), acc, 0, 0, 0);
-          ss += sq8(xa[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xa[j] = xn[j];
-          wb[j] = wn[j];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[q][j]),
+                                                        __builtin_bit_cast(bf16x8, wb[q][j]), acc, 0, 0, 0);
+          ss += sq8(xa[q][j]);
         }
       }
     }
@@ -168,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
   // ---- reduce the splits, RMSNorm(x) as a per-token scale, side features, bias, SiLU ----
   {
     const int n = tid & (kDr - 1), p = tid >> 7;    // tokens p, p + 8, p + 16, p + 24
-    const float b1 = a.b1[n];
+    const float b1 = sm.pu[0][n];
 #pragma unroll
     for (int m = 0; m < kTok / 8; ++m) {
       const int t = p + 8 * m;
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
         sq += sm.ssp[k][t];
       }
       float v = fmaf(sum, 1.0f / sqrtf(sq / (float)a.d + 1e-6f), b1);
-      for (int s = 0; s < a.d_side; ++s) v = fmaf(sm.sd[t][s], a.w1_side[n * a.d_side + s], v);
+      for (int s = 0; s < a.d_side; ++s) v = fmaf(sm.sd[t][s], sm.w1s[n][s], v);
       hs[t][n] = v / (1.0f + expf(-v));
     }
   }
@@ -188,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
   {
     const int n = tid & (kDr - 1), p = tid >> 7;
     float acc[kTok / 8];
-    const float b2 = a.b2[n];
+    const float b2 = sm.pu[1][n];
 #pragma unroll
     for (int m = 0; m < kTok / 8; ++m) acc[m] = b2;
     for (int k = 0; k < kDr; k += 4) {
@@ -207,12 +227,13 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
     for (int m = 0; m < kTok / 8; ++m) h2s[p + 8 * m][n] = acc[m];
   }
   __syncthreads();
-  // the heads' weights replace W2 in LDS when they fit (up to 40 heads): one round of loads
-  const int na = 3 * a.heads, no = na + 4;
-  const bool wl = no * kDr <= kDr * kDr;
+  // the heads' weights replace W2 in LDS when they fit (up to 40 heads), from registers
   if (wl) {
-    for (int i = tid; i < kDr * na; i += kThreads) sm.wts[i] = a.w_a[i];
-    for (int i = tid; i < kDr * 4; i += kThreads) sm.wts[kDr * na + i] = a.w_b[i];
+#pragma unroll
+    for (int q = 0; q < kHW; ++q) {
+      const int i = tid + q * kThreads;
+      if (i < kDr * no) sm.wts[i] = hw[q];
+    }
   }
   if (tid < kTok) {
     float s = 0.0f;
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
   // ---- RMSNorm and Eq. (11) per axis: hhat^a -> hs, hhat^b -> h2s ----
   {
     const int n = tid & (kDr - 1), p = tid >> 7;
-    const float mua = a.mu_a[n], sa = a.sigma_a[n] + 1e-5f, mub = a.mu_b[n], sb = a.sigma_b[n] + 1e-5f;
+    const float mua = sm.pu[2][n], sa = sm.pu[3][n] + 1e-5f, mub = sm.pu[4][n], sb = sm.pu[5][n] + 1e-5f;
 #pragma unroll
     for (int m = 0; m < kTok / 8; ++m) {
       const int t = p + 8 * m;
@@ -283,6 +304,227 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
   }
 }
 
+// ---- split path for small calls (up to kSplitMaxTok tokens) ----
+// A decode step routes a few dozen tokens: one workgroup per 32 tokens would leave the chip idle
+// and pull all of W1 through one CU.  Instead two launches:
+//   k_ctl_l1   workgroup (token block, channel slice ks, unit block us): 4 waves, wave w takes
+//              channel group 4 ks + w (64 channels, 4 k-steps) for 32 tokens x 32 units on the
+//              matrix cores; the 4 waves are summed in LDS and the partial goes to the workspace
+//              (with the slice's sums of squares of x, from the us = 0 workgroups).
+//   k_ctl_tok  one workgroup (8 waves) per token: sums the slices, and runs RMSNorm(x), the side
+//              term, SiLU, layer 2, RMSNorm, Eq. (11) and the heads for that token, with every
+//              weight it needs requested at its start.
+constexpr int kSplitMaxTok = 256;
+constexpr int kFinThreads = 512;
+
+__host__ __device__ constexpr int ctl_slices(int d) { return (d / 64 + 3) / 4; }
+int64_t ctl_ws_floats(int d) { return (int64_t)(kSplitMaxTok / kTok) * ctl_slices(d) * kTok * (kDr + 1); }
+
+__global__ __launch_bounds__(256) void k_ctl_l1(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1p, int d,
+                                                int64_t M, int KS, float* __restrict__ part, float* __restrict__ ssp) {
+  __shared__ float red[4][kTok][33];
+  __shared__ float ssr[4][kTok];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x, us = b & 3, ks = (b >> 2) % KS, blk = (b >> 2) / KS;
+  const int64_t tok0 = (int64_t)blk * kTok;
+  const int ntok = (int)min<int64_t>(kTok, M - tok0);
+  const int g = 4 * ks + wave, r = lane & 31, kh = lane >> 5;
+  f32x16 acc = {};
+  float ss = 0.0f;
+  if (g < d / 64) {                                 // wave-uniform
+    // rows past the last token repeat it (their partials are never read)
+    const uint16_t* xr = x + (tok0 + min(r, ntok - 1)) * d + 64 * g + 32 * kh;
+    const uint16_t* wr = w1p + ((int64_t)(4 * g) * kDr + 32 * us + r) * 16 + 8 * kh;
+    uint4 xa[4], wb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xa[j] = gload16(xr + 8 * j);
+      wb[j] = gload16(wr + (int64_t)j * kDr * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[j]), __builtin_bit_cast(bf16x8, wb[j]),
+                                                    acc, 0, 0, 0);
+      ss += sq8(xa[j]);
+    }
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+  if (lane < kTok) ssr[wave][lane] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+#pragma unroll
+  for (int reg = 0; reg < 16; ++reg) red[wave][8 * (reg >> 2) + 4 * kh + (reg & 3)][r] = acc[reg];
+  __syncthreads();
+  float* dst = part + ((int64_t)blk * KS + ks) * kTok * kDr + 32 * us;
+  const int u = tid & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = (tid >> 5) + 8 * i;
+    dst[t * kDr + u] = (red[0][t][u] + red[1][t][u]) + (red[2][t][u] + red[3][t][u]);
+  }
+  if (us == 0 && tid < kTok)
+    ssp[((int64_t)blk * KS + ks) * kTok + tid] = (ssr[0][tid] + ssr[1][tid]) + (ssr[2][tid] + ssr[3][tid]);
+}
+
+__device__ __forceinline__ float gload_f(const float* p) { return *(const __attribute__((address_space(1))) float*)(p); }
+__device__ __forceinline__ float4 gload_f4(const float* p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f v = *(const __attribute__((address_space(1))) v4f*)(p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// PER: layer-1 slices per thread (KS <= 4 PER); TPO: threads per head output, the largest power
+// of two with TPO (3 heads + 4) <= 512, so that each thread holds 128 / TPO weights of its output.
+template <int PER, int TPO>
+__global__ __launch_bounds__(kFinThreads) void k_ctl_tok(CtlArgs a, const float* __restrict__ side, int KS,
+                                                          const float* __restrict__ part, const float* __restrict__ ssp,
+                                                          uint8_t* __restrict__ mode, uint8_t* __restrict__ bits) {
+  __shared__ float r1[4][kDr];
+  __shared__ float w1s[kMaxSide][kDr];
+  __shared__ float sds[kMaxSide];
+  __shared__ float hs[kDr];
+  __shared__ float r2[16][kDr];
+  __shared__ float hab[2][kDr];
+  __shared__ float zl[kMaxOut];
+  __shared__ float sq[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t m = blockIdx.x;
+  const int64_t blk = m / kTok;
+  const int row = (int)(m % kTok);
+  // ---- every load goes out first (none waits on another) ----
+  const int n = tid & (kDr - 1), kq = tid >> 7;     // layer-1 slices kq, kq + 4, ...
+  // side features: W1's side columns (at most 32 x 128 = 8 per thread) and the token's row
+  float wsr[kMaxSide * kDr / kFinThreads];
+#pragma unroll
+  for (int j = 0; j < kMaxSide * kDr / kFinThreads; ++j) {
+    const int i = tid + j * kFinThreads;
+    wsr[j] = i < kDr * a.d_side ? gload_f(a.w1_side + i) : 0.0f;
+  }
+  const float sdv = tid < a.d_side ? gload_f(side + m * a.d_side + tid) : 0.0f;
+  // W2 (in x out): thread (unit quad q, k-group kg) holds W2[8 kg .. 8 kg + 7][4 q .. 4 q + 3]
+  const int q = tid & 31, kg = tid >> 5;
+  float4 w2v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w2v[i] = gload_f4(a.w2 + (8 * kg + i) * kDr + 4 * q);
+  // heads: TPO adjacent threads per output, each over kper = 128 / TPO inputs
+  const int na = 3 * a.heads, no = na + 4;
+  constexpr int kper = kDr / TPO;
+  const int o = tid / TPO, hp = tid % TPO;
+  const bool oa = o < no;
+  float hw[kper];
+  {
+    // (threads past the last output read the last column; their sums are never stored)
+    const bool att = o < na;
+    const float* wcol = att ? a.w_a + min(o, na - 1) : a.w_b + min(o - na, 3);
+    const int ws = att ? na : 4;
+#pragma unroll
+    for (int j = 0; j < kper; ++j) hw[j] = gload_f(wcol + (hp * kper + j) * ws);
+  }
+  const float b1 = gload_f(a.b1 + n), b2 = gload_f(a.b2 + n);
+  const float mua = gload_f(a.mu_a + n), sa = gload_f(a.sigma_a + n) + 1e-5f;
+  const float mub = gload_f(a.mu_b + n), sb = gload_f(a.sigma_b + n) + 1e-5f;
+  // the layer-1 partials of this token (at most 64 slices: 16 per thread) and the slices' sums
+  // of squares of x (one per lane of wave 0).  The loads are unconditional, from indices clamped
+  // to the last slice, and the extras multiplied by 0 afterwards (the partials are finite): a
+  // load under a condition, or a select of it, ends up in a branch that waits for it (and for
+  // every load before it) on the spot.
+  const float* pp = part + (blk * KS * kTok + row) * kDr + n;
+  float pv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) pv[j] = gload_f(pp + (int64_t)min(kq + 4 * j, KS - 1) * kTok * kDr);
+  float sqx = gload_f(ssp + (blk * KS + min(lane, KS - 1)) * kTok + row);
+  float s1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) s1 = fmaf(pv[j], kq + 4 * j < KS ? 1.0f : 0.0f, s1);
+  sqx *= (wave == 0 && lane < KS) ? 1.0f : 0.0f;
+
+  // ---- layer 1: sum of the slices, RMSNorm(x) as a scale, side term, bias, SiLU ----
+  r1[kq][n] = s1;
+  const int dsd = max(a.d_side, 1);
+#pragma unroll
+  for (int j = 0; j < kMaxSide * kDr / kFinThreads; ++j) {
+    const int i = tid + j * kFinThreads;
+    if (i < kDr * a.d_side) w1s[i % dsd][i / dsd] = wsr[j];
+  }
+  if (tid < a.d_side) sds[tid] = sdv;
+  if (wave == 0) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sqx += __shfl_xor(sqx, off);
+    if (lane == 0) sq[0] = sqx;
+  }
+  __syncthreads();
+  if (tid < kDr) {
+    const float sum = (r1[0][n] + r1[1][n]) + (r1[2][n] + r1[3][n]);
+    float v = fmaf(sum, 1.0f / sqrtf(sq[0] / (float)a.d + 1e-6f), b1);
+    for (int s = 0; s < a.d_side; ++s) v = fmaf(sds[s], w1s[s][n], v);
+    hs[n] = v / (1.0f + expf(-v));
+  }
+  __syncthreads();
+  // ---- layer 2 ----
+  {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float h = hs[8 * kg + i];
+      acc.x = fmaf(h, w2v[i].x, acc.x);
+      acc.y = fmaf(h, w2v[i].y, acc.y);
+      acc.z = fmaf(h, w2v[i].z, acc.z);
+      acc.w = fmaf(h, w2v[i].w, acc.w);
+    }
+    *reinterpret_cast<float4*>(&r2[kg][4 * q]) = acc;
+  }
+  __syncthreads();
+  float h2 = 0.0f;
+  if (tid < kDr) {
+    float s = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) s += r2[g][n];
+    h2 = b2 + s;
+    float e = h2 * h2;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
+    if (lane == 0) sq[1 + wave] = e;
+  }
+  __syncthreads();
+  // ---- RMSNorm and Eq. (11) per axis ----
+  if (tid < kDr) {
+    const float hh = h2 * (1.0f / sqrtf((sq[1] + sq[2]) / (float)kDr + 1e-6f));
+    hab[0][n] = (hh - mua) / sa;
+    hab[1][n] = (hh - mub) / sb;
+  }
+  __syncthreads();
+  // ---- heads: the TPO lanes of an output are adjacent and within one wave ----
+  {
+    const float* src = &hab[o < na ? 0 : 1][hp * kper];
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kper; ++j) z = fmaf(src[j], hw[j], z);
+#pragma unroll
+    for (int off = TPO >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    if (oa && hp == 0) zl[o] = z;
+  }
+  __syncthreads();
+  // ---- hard argmax (first maximum on ties) ----
+  if (tid < a.heads) {
+    const float z0 = zl[3 * tid], z1 = zl[3 * tid + 1], z2 = zl[3 * tid + 2];
+    int idx = 0;
+    float best = z0;
+    if (z1 > best) { idx = 1; best = z1; }
+    if (z2 > best) idx = 2;
+    mode[m * a.heads + tid] = (uint8_t)idx;
+  } else if (tid == kFinThreads - 1) {
+    int idx = 0;
+    float best = zl[na];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      if (zl[na + j] > best) {
+        idx = j;
+        best = zl[na + j];
+      }
+    }
+    bits[m] = (uint8_t)(2 << idx);
+  }
+}
+
 // Packed W1: element [s][n][16] for k-step s = 4 g + j and unit n holds channels
 // 64 g + 8 j .. + 7 (first 8) and 64 g + 32 + 8 j .. + 7 (last 8) of row n.  One thread per
 // (k-step, unit, half): a 16-byte copy.
@@ -309,6 +551,11 @@ tr_status tr_controller_pack_w1(const void* w1, void* w1_packed, int32_t d, void
   return TR_OK;
 }
 
+int64_t tr_controller_workspace_bytes(int32_t d) {
+  if (d < 64 || d > 16384 || d % 64 != 0) return -1;
+  return (int64_t)sizeof(float) * ctl_ws_floats(d);
+}
+
 tr_status tr_controller_route(const tr_controller_weights* w, const void* x, const float* side, int64_t n_tokens,
                               uint8_t* mode, uint8_t* bits, void* stream) {
   if (!w || n_tokens < 0) return TR_ERR_INVALID_ARG;
@@ -323,6 +570,45 @@ tr_status tr_controller_route(const tr_controller_weights* w, const void* x, con
   if (blocks > 0x7fffffffLL) return TR_ERR_UNSUPPORTED;
   CtlArgs a{w->d, w->d_side, w->heads, static_cast<const uint16_t*>(w->w1), w->w1_side, w->b1, w->w2, w->b2,
             w->mu_a, w->sigma_a, w->mu_b, w->sigma_b, w->w_a, w->w_b};
+  if (w->workspace) {
+    if (w->workspace_bytes < (int64_t)sizeof(float) * ctl_ws_floats(w->d) ||
+        reinterpret_cast<uintptr_t>(w->workspace) % 16 != 0)
+      return TR_ERR_INVALID_ARG;
+    if (n_tokens <= kSplitMaxTok) {
+      const int KS = ctl_slices(w->d);
+      float* part = static_cast<float*>(w->workspace);
+      float* ssp = part + (int64_t)(kSplitMaxTok / kTok) * KS * kTok * kDr;
+      hipStream_t st = static_cast<hipStream_t>(stream);
+      hipLaunchKernelGGL(k_ctl_l1, dim3((unsigned)(blocks * KS * 4)), dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w->w1), w->d, n_tokens, KS, part, ssp);
+      TR_LAUNCH_CHECK();
+      const int no = 3 * w->heads + 4;
+      int tpo = 64;
+      while (tpo * no > kFinThreads) tpo >>= 1;
+      const float* cp = part;
+      const float* cs = ssp;
+      const dim3 grid((unsigned)n_tokens), blk(kFinThreads);
+#define TR_CTL_TOK(PER, TPO) hipLaunchKernelGGL((k_ctl_tok<PER, TPO>), grid, blk, 0, st, a, side, KS, cp, cs, mode, bits)
+#define TR_CTL_TOK_T(PER)             \
+  switch (tpo) {                      \
+    case 64: TR_CTL_TOK(PER, 64); break; \
+    case 32: TR_CTL_TOK(PER, 32); break; \
+    case 16: TR_CTL_TOK(PER, 16); break; \
+    case 8: TR_CTL_TOK(PER, 8); break;   \
+    case 4: TR_CTL_TOK(PER, 4); break;   \
+    default: TR_CTL_TOK(PER, 2); break;  \
+  }
+      if (KS <= 8) {
+        TR_CTL_TOK_T(2)
+      } else {
+        TR_CTL_TOK_T(16)
+      }
+#undef TR_CTL_TOK_T
+#undef TR_CTL_TOK
+      TR_LAUNCH_CHECK();
+      return TR_OK;
+    }
+  }
   hipLaunchKernelGGL(k_controller, dim3((unsigned)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a,
                      static_cast<const uint16_t*>(x), side, n_tokens, mode, bits);
   TR_LAUNCH_CHECK();

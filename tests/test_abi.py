@@ -94,6 +94,24 @@ def test_controller_host_validation_without_gpu():
     assert _ctl_route(None, fake, None, 5, fake, fake, None) == 1
 
 
+def test_controller_workspace_host_checks_without_gpu():
+    from mixed_precision_kv_tr_amd._lib import _CtlWeights, _ctl_route, _ctl_ws_bytes
+
+    # 4 bytes x 8 token blocks x ceil(d / 256) channel slices x 32 tokens x (128 units + 1)
+    for d, slices in ((64, 1), (256, 1), (320, 2), (768, 3), (2048, 8), (16384, 64)):
+        assert _ctl_ws_bytes(d) == 4 * 8 * slices * 32 * 129, d
+    for d in (0, 32, 100, 16448):
+        assert _ctl_ws_bytes(d) == -1
+    fake = 0x1000                                    # never dereferenced: every call fails first
+    need = _ctl_ws_bytes(2048)
+    w = _CtlWeights(2048, 0, 128, 4, *([fake] * 11), fake, need - 4)
+    route = lambda w, n: _ctl_route(ctypes.byref(w), fake, None, n, fake, fake, None)
+    assert route(w, 5) == 1                          # one float short
+    assert route(w, 1000) == 1                       # checked for large calls too
+    w.workspace_bytes, w.workspace = need, fake + 4  # not 16-byte aligned
+    assert route(w, 5) == 1
+
+
 def test_controller_pack_host_validation_without_gpu():
     from mixed_precision_kv_tr_amd._lib import _ctl_pack
     a, b = 0x1000, 0x2000                            # never dereferenced: every call fails first

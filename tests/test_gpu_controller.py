@@ -24,11 +24,12 @@ def tr():
     return tr
 
 
-def run(tr, c):
+def run(tr, c, workspace=True):
     M, H = c["x"].shape[0], c["w"]["w_a"].shape[1] // 3
     mode = torch.full((M, H), 255, dtype=torch.uint8, device="cuda")
     bits = torch.full((M,), 255, dtype=torch.uint8, device="cuda")
-    tr.tr_controller_route(c["w"], c["x"], c["side"] if c["side"].shape[1] else None, M, mode, bits)
+    cw = tr.ControllerWeights(c["w"], workspace=workspace)
+    tr.tr_controller_route(cw, c["x"], c["side"] if c["side"].shape[1] else None, M, mode, bits)
     torch.cuda.synchronize()
     return mode.cpu().numpy(), bits.cpu().numpy()
 
@@ -65,6 +66,39 @@ def test_controller_matches_oracle(tr, M, d, H, d_side):
     gmode, gbits = run(tr, c)
     omode, obits, za, zb = oracle_of(c)
     check(gmode, gbits, omode, obits, za, zb, f"M={M} d={d} H={H}")
+
+
+@pytest.mark.parametrize("M,d,H,d_side", [(1, 2048, 16, 8), (31, 768, 12, 8), (33, 320, 5, 1), (256, 4096, 64, 32),
+                                          (257, 2048, 16, 8), (200, 16384, 7, 0)])
+def test_controller_split_and_single_workgroup_forms(tr, M, d, H, d_side):
+    """Up to 256 tokens the call spreads the first layer over channel slices (the workspace
+    form); with no workspace, or beyond 256 tokens, one workgroup takes 32 tokens.  Both forms
+    against the oracle, on the same inputs: ragged token blocks, a channel slice of fewer than
+    4 groups (d = 320), the most heads and side features, the widest model."""
+    say(f"controller forms M={M} d={d} H={H} d_side={d_side}")
+    c = controller_case(M, d, H, d_side=d_side, seed=3 * M + d, device="cuda")
+    omode, obits, za, zb = oracle_of(c)
+    for ws in (True, False):
+        gmode, gbits = run(tr, c, workspace=ws)
+        check(gmode, gbits, omode, obits, za, zb, f"M={M} d={d} H={H} workspace={ws}")
+
+
+def test_controller_workspace_reuse_across_calls(tr):
+    """One workspace serves calls of different sizes in a row (nothing carried over).  The cases
+    share the seed, so their weights are the same and one ControllerWeights serves all three."""
+    cw = None
+    for M in (256, 3, 100):
+        c = controller_case(M, 2048, 16, d_side=8, seed=11, device="cuda")
+        if cw is None:
+            cw = tr.ControllerWeights(c["w"])
+        assert torch.equal(cw.tensors["w2"], c["w"]["w2"]) and torch.equal(cw.tensors["w_a"], c["w"]["w_a"])
+        H = 16
+        mode = torch.full((M, H), 255, dtype=torch.uint8, device="cuda")
+        bits = torch.full((M,), 255, dtype=torch.uint8, device="cuda")
+        tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits)
+        torch.cuda.synchronize()
+        omode, obits, za, zb = oracle_of(c)
+        check(mode.cpu().numpy(), bits.cpu().numpy(), omode, obits, za, zb, f"reuse M={M}")
 
 
 def test_controller_full_size_prefill_layer(tr):
