@@ -66,6 +66,18 @@ __device__ __forceinline__ uint4 gload16(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Every kernel argument in scalar registers at this point: the argument loads then go out
+// together and are waited for once, instead of one wait per argument at its first use.
+template <typename T>
+__device__ __forceinline__ void pin_sreg(T& v) {
+  asm volatile("" : "+s"(v));
+}
+__device__ __forceinline__ void pin_args(CtlArgs& a) {
+  pin_sreg(a.d), pin_sreg(a.d_side), pin_sreg(a.heads), pin_sreg(a.w1), pin_sreg(a.w1_side), pin_sreg(a.b1);
+  pin_sreg(a.w2), pin_sreg(a.b2), pin_sreg(a.mu_a), pin_sreg(a.sigma_a), pin_sreg(a.mu_b), pin_sreg(a.sigma_b);
+  pin_sreg(a.w_a), pin_sreg(a.w_b);
+}
+
 __device__ __forceinline__ float sq8(uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float s = 0.0f;
@@ -324,6 +336,7 @@ __global__ __launch_bounds__(256) void k_ctl_l1(const uint16_t* __restrict__ x, 
                                                 int64_t M, int KS, float* __restrict__ part, float* __restrict__ ssp) {
   __shared__ float red[4][kTok][33];
   __shared__ float ssr[4][kTok];
+  pin_sreg(x), pin_sreg(w1p), pin_sreg(d), pin_sreg(M), pin_sreg(KS), pin_sreg(part), pin_sreg(ssp);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = blockIdx.x, us = b & 3, ks = (b >> 2) % KS, blk = (b >> 2) / KS;
   const int64_t tok0 = (int64_t)blk * kTok;
@@ -341,6 +354,7 @@ __global__ __launch_bounds__(256) void k_ctl_l1(const uint16_t* __restrict__ x, 
       xa[j] = gload16(xr + 8 * j);
       wb[j] = gload16(wr + (int64_t)j * kDr * 16);
     }
+    __builtin_amdgcn_sched_barrier(0);              // all eight loads issued before the first wait
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[j]), __builtin_bit_cast(bf16x8, wb[j]),
@@ -371,9 +385,11 @@ __device__ __forceinline__ float4 gload_f4(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-// PER: layer-1 slices per thread (KS <= 4 PER); TPO: threads per head output, the largest power
-// of two with TPO (3 heads + 4) <= 512, so that each thread holds 128 / TPO weights of its output.
-template <int PER, int TPO>
+// PER: layer-1 slices per thread (KS <= 4 PER); OPW: head outputs per row of threads (64, 128 or
+// 256, >= 3 heads + 4).  Thread (output o = tid % OPW, input group hp = tid / OPW) holds the
+// weights of o for inputs hp kper .. hp kper + kper - 1, kper = 128 OPW / 512: a wave's lanes
+// are consecutive outputs of one input row, so every weight load is a contiguous row segment.
+template <int PER, int OPW>
 __global__ __launch_bounds__(kFinThreads) void k_ctl_tok(CtlArgs a, const float* __restrict__ side, int KS,
                                                           const float* __restrict__ part, const float* __restrict__ ssp,
                                                           uint8_t* __restrict__ mode, uint8_t* __restrict__ bits) {
@@ -383,8 +399,10 @@ __global__ __launch_bounds__(kFinThreads) void k_ctl_tok(CtlArgs a, const float*
   __shared__ float hs[kDr];
   __shared__ float r2[16][kDr];
   __shared__ float hab[2][kDr];
-  __shared__ float zl[kMaxOut];
+  __shared__ float zp[kFinThreads];
   __shared__ float sq[4];
+  pin_args(a);
+  pin_sreg(side), pin_sreg(KS), pin_sreg(part), pin_sreg(ssp), pin_sreg(mode), pin_sreg(bits);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t m = blockIdx.x;
   const int64_t blk = m / kTok;
@@ -405,14 +423,13 @@ __global__ __launch_bounds__(kFinThreads) void k_ctl_tok(CtlArgs a, const float*
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     w2v[i] = gload_f4(a.w2 + (8 * kg + i) * kDr + 4 * q);
-  // heads: TPO adjacent threads per output, each over kper = 128 / TPO inputs
+  // heads
   const int na = 3 * a.heads, no = na + 4;
-  constexpr int kper = kDr / TPO;
-  const int o = tid / TPO, hp = tid % TPO;
-  const bool oa = o < no;
+  constexpr int kper = kDr * OPW / kFinThreads;
+  const int o = tid % OPW, hp = tid / OPW;
   float hw[kper];
   {
-    // (threads past the last output read the last column; their sums are never stored)
+    // (threads past the last output read the last column; their sums are never used)
     const bool att = o < na;
     const float* wcol = att ? a.w_a + min(o, na - 1) : a.w_b + min(o - na, 3);
     const int ws = att ? na : 4;
@@ -492,20 +509,25 @@ __global__ __launch_bounds__(kFinThreads) void k_ctl_tok(CtlArgs a, const float*
     hab[1][n] = (hh - mub) / sb;
   }
   __syncthreads();
-  // ---- heads: the TPO lanes of an output are adjacent and within one wave ----
+  // ---- heads: partial logits per input group, summed in a fixed order by the argmax ----
   {
     const float* src = &hab[o < na ? 0 : 1][hp * kper];
     float z = 0.0f;
 #pragma unroll
     for (int j = 0; j < kper; ++j) z = fmaf(src[j], hw[j], z);
-#pragma unroll
-    for (int off = TPO >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-    if (oa && hp == 0) zl[o] = z;
+    zp[tid] = z;
   }
   __syncthreads();
+  constexpr int kGroups = kFinThreads / OPW;
+  const auto zl = [&](int oo) {
+    float z = zp[oo];
+#pragma unroll
+    for (int g = 1; g < kGroups; ++g) z += zp[g * OPW + oo];
+    return z;
+  };
   // ---- hard argmax (first maximum on ties) ----
   if (tid < a.heads) {
-    const float z0 = zl[3 * tid], z1 = zl[3 * tid + 1], z2 = zl[3 * tid + 2];
+    const float z0 = zl(3 * tid), z1 = zl(3 * tid + 1), z2 = zl(3 * tid + 2);
     int idx = 0;
     float best = z0;
     if (z1 > best) { idx = 1; best = z1; }
@@ -513,12 +535,13 @@ __global__ __launch_bounds__(kFinThreads) void k_ctl_tok(CtlArgs a, const float*
     mode[m * a.heads + tid] = (uint8_t)idx;
   } else if (tid == kFinThreads - 1) {
     int idx = 0;
-    float best = zl[na];
+    float best = zl(na);
 #pragma unroll
     for (int j = 1; j < 4; ++j) {
-      if (zl[na + j] > best) {
+      const float zj = zl(na + j);
+      if (zj > best) {
         idx = j;
-        best = zl[na + j];
+        best = zj;
       }
     }
     bits[m] = (uint8_t)(2 << idx);
@@ -583,20 +606,16 @@ tr_status tr_controller_route(const tr_controller_weights* w, const void* x, con
                          static_cast<const uint16_t*>(w->w1), w->d, n_tokens, KS, part, ssp);
       TR_LAUNCH_CHECK();
       const int no = 3 * w->heads + 4;
-      int tpo = 64;
-      while (tpo * no > kFinThreads) tpo >>= 1;
+      const int opw = no <= 64 ? 64 : no <= 128 ? 128 : 256;
       const float* cp = part;
       const float* cs = ssp;
       const dim3 grid((unsigned)n_tokens), blk(kFinThreads);
-#define TR_CTL_TOK(PER, TPO) hipLaunchKernelGGL((k_ctl_tok<PER, TPO>), grid, blk, 0, st, a, side, KS, cp, cs, mode, bits)
-#define TR_CTL_TOK_T(PER)             \
-  switch (tpo) {                      \
-    case 64: TR_CTL_TOK(PER, 64); break; \
-    case 32: TR_CTL_TOK(PER, 32); break; \
-    case 16: TR_CTL_TOK(PER, 16); break; \
-    case 8: TR_CTL_TOK(PER, 8); break;   \
-    case 4: TR_CTL_TOK(PER, 4); break;   \
-    default: TR_CTL_TOK(PER, 2); break;  \
+#define TR_CTL_TOK(PER, OPW) hipLaunchKernelGGL((k_ctl_tok<PER, OPW>), grid, blk, 0, st, a, side, KS, cp, cs, mode, bits)
+#define TR_CTL_TOK_T(PER)                \
+  switch (opw) {                         \
+    case 64: TR_CTL_TOK(PER, 64); break;   \
+    case 128: TR_CTL_TOK(PER, 128); break; \
+    default: TR_CTL_TOK(PER, 256); break;  \
   }
       if (KS <= 8) {
         TR_CTL_TOK_T(2)
