@@ -226,6 +226,32 @@ def copy_calibration(mib: int, reps: int = 5):
     del src, dst
 
 
+def time_graph(step, calls: int, replays: int = 10) -> float:
+    """ms per call of `step` captured `calls` times in one HIP graph (torch.cuda.graph) and
+    replayed `replays` times between HIP events: the device time of back-to-back calls without
+    the host's per-call launch cost, as a serving loop that replays a captured step sees it.
+    `step` takes the capture stream's handle."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(s.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream().cuda_stream
+        for _ in range(calls):
+            step(st)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * calls)
+
+
 def time_steps(step, K: int) -> float:
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -570,7 +596,10 @@ def bench_controller(tr, args):
     prefill layer (4 x 2048 tokens, d = 768, 12 heads), a 1.3B-shaped one (d = 2048, 16 heads) and
     a 1.3B decode step (32 tokens).  Random weights (no trained controller exists); 8 side features.
     Bytes: x (2 d per token) + decisions (heads + 1 per token) + the weights once; FLOP: the trunk
-    and heads, 2 * (d + 8) * 128 + 2 * 128 * 128 + 2 * 128 * (3 heads + 4) per token."""
+    and heads, 2 * (d + 8) * 128 + 2 * 128 * 128 + 2 * 128 * (3 heads + 4) per token.
+    us_per_call: 50 calls captured in a HIP graph and replayed (device time, no per-call host
+    launch cost); eager_us_per_call: the same calls launched one by one from Python, which for
+    the small decode call measures the host's launch rate rather than the kernels."""
     from workloads import controller_case
     out = {}
     for name, M, d, H in (("prefill_160m", 8192, 768, 12), ("prefill_1.3b", 8192, 2048, 16), ("decode_1.3b", 32, 2048, 16)):
@@ -582,12 +611,13 @@ def bench_controller(tr, args):
         call = lambda: tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits, stream)
         for _ in range(5):
             call()
-        reps = 200
-        ms = time_steps(call, reps)
+        ms_eager = time_steps(call, 200)
+        ms = time_graph(lambda st: tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits, st), 50)
         wbytes = sum(v.numel() * v.element_size() for v in c["w"].values())
         nbytes = M * (2 * d + 4 * 8 + H + 1) + wbytes
         flops = M * (2 * (d + 8) * 128 + 2 * 128 * 128 + 2 * 128 * (3 * H + 4))
         out[name] = {"tokens": M, "d": d, "heads": H, "us_per_call": round(ms * 1e3, 2),
+                     "eager_us_per_call": round(ms_eager * 1e3, 2),
                      "tokens_per_s": round(M / (ms * 1e-3), 1), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}

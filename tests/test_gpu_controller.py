@@ -101,6 +101,36 @@ def test_controller_workspace_reuse_across_calls(tr):
         check(mode.cpu().numpy(), bits.cpu().numpy(), omode, obits, za, zb, f"reuse M={M}")
 
 
+def test_controller_graph_replays_match_eager(tr):
+    """The decode-step call (split form, 32 tokens) and a 300-token call (one-workgroup form)
+    captured in a HIP graph: every replay, with eager work and synchronizations in between,
+    writes exactly the eager decisions."""
+    for M in (32, 300):
+        c = controller_case(M, 2048, 16, d_side=8, seed=5, device="cuda")
+        cw = tr.ControllerWeights(c["w"])
+        mode = torch.full((M, 16), 255, dtype=torch.uint8, device="cuda")
+        bits = torch.full((M,), 255, dtype=torch.uint8, device="cuda")
+        tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits)
+        torch.cuda.synchronize()
+        emode, ebits = mode.clone(), bits.clone()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits, s.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits, torch.cuda.current_stream().cuda_stream)
+        for rep in range(4):
+            mode.fill_(255)
+            bits.fill_(255)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(mode, emode) and torch.equal(bits, ebits), f"M={M} replay {rep}"
+            tr.tr_controller_route(cw, c["x"], c["side"], M, mode, bits)   # eager work in between
+            torch.cuda.synchronize()
+
+
 def test_controller_full_size_prefill_layer(tr):
     """One 160M-shaped prefill layer's tokens (4 x 2048, d = 768, 12 heads) and one 1.3B decode
     step (32 tokens, d = 2048, 16 heads)."""
