@@ -423,29 +423,39 @@ __global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x
   const int r = lane & 31, kh = lane >> 5;
   const int tw = wave & 3, uw = wave >> 2;          // this wave: tokens 64 tw .., units 64 uw ..
   f32x16 acc[2][2][2] = {};                         // [gate, up][token block][unit block]
+  // operands of k-step j of buffer b
+  auto rd = [&](int b, int j, uint4 (&av)[2], uint4 (&bv)[2][2]) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+      av[tb] = *reinterpret_cast<const uint4*>(&As[b][(64 * tw + 32 * tb + r) * kAP + 16 * j + 64 * kh]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ub = 0; ub < 2; ++ub) {
+        // units r and r + 8 of a 16-lane pass would share banks at a 32-byte pitch: the halves
+        // of every unit with bit 3 set are stored swapped
+        const int u = 64 * uw + 32 * ub + r;
+        bv[m][ub] = *reinterpret_cast<const uint4*>(&Bs[b][((4 * m + j) * kTN + u) * 32 + 16 * (kh ^ ((u >> 3) & 1))]);
+      }
+  };
+  // the 4 k-steps of a stage, each k-step's LDS reads issued before the previous one's products
+  // (scheduling barriers keep the order), so the reads' latency hides behind 8 products
   auto compute = [&](int b) {
+    uint4 av0[2], bv0[2][2], av1[2], bv1[2][2];
+    rd(b, 0, av0, bv0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint4 av[2], bv[2][2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        av[tb] = *reinterpret_cast<const uint4*>(&As[b][(64 * tw + 32 * tb + r) * kAP + 16 * j + 64 * kh]);
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub)
-        {
-          // units r and r + 8 of a 16-lane pass would share banks at a 32-byte pitch: the halves
-          // of every unit with bit 3 set are stored swapped
-          const int u = 64 * uw + 32 * ub + r;
-          bv[m][ub] = *reinterpret_cast<const uint4*>(&Bs[b][((4 * m + j) * kTN + u) * 32 + 16 * (kh ^ ((u >> 3) & 1))]);
-        }
+      uint4(&av)[2] = (j & 1) ? av1 : av0;
+      uint4(&bv)[2][2] = (j & 1) ? bv1 : bv0;
+      if (j < 3) rd(b, j + 1, (j & 1) ? av0 : av1, (j & 1) ? bv0 : bv1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int ub = 0; ub < 2; ++ub) acc[m][tb][ub] = mfma(av[tb], bv[m][ub], acc[m][tb][ub]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   const int ns = d / 64;                            // even: d is a multiple of 128
@@ -576,6 +586,164 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
   }
 }
 
+// Down product of one slot on a tile of 128 listed tokens x 256 output channels (large calls, d a
+// multiple of 256): 8 waves, each 64 tokens x 64 channels.  Per stage of 64 hidden channels the
+// workgroup loads the tile's hidden rows (hi and lo planes, 16-byte-padded rows) and the weight
+// block (in its packed k-step order) into double-buffered LDS, one 64-byte piece of each per
+// thread, the next two stages in registers: every weight byte brought in serves 128 tokens and
+// every hidden byte 256 channels, against 64 and 128 in k_moe_down.  Both planes multiply the
+// same weights into one accumulator.  Epilogue as in k_moe_down.
+constexpr int kDM = 128;                 // listed tokens per tile
+constexpr int kDN = 256;                 // output channels per tile
+constexpr int kDBS = 4 * kDN * 32;       // LDS bytes of one stage's B tile: [k-step][channel][16]
+
+// Items of the tiled down product of one slot, expert by expert (the null expert first in slot 0:
+// its tiles only write zeros): for expert e with T_e token tiles and NY channel blocks, groups of
+// kGY channel blocks, within a group token tile by token tile, within a tile its kGY blocks, as
+// in up_item.  Returns the item count when id < 0.
+__device__ __forceinline__ int down_item(const int32_t* counts, int E, int slot, int NY, int id, int& e, int& tile,
+                                         int& cnt, int& y) {
+  int base = 0;
+  for (int x = slot == 0 ? 0 : 1; x <= E; ++x) {
+    const int c = counts[slot * (E + 1) + x];
+    const int te = (c + kDM - 1) / kDM;
+    const int ne = te * NY;
+    if (id >= base && id < base + ne) {
+      const int i = id - base, nfull = NY / kGY;
+      if (i < nfull * te * kGY) {
+        const int r2 = i % (te * kGY);
+        tile = r2 / kGY;
+        y = (i / (te * kGY)) * kGY + r2 % kGY;
+      } else {
+        const int i2 = i - nfull * te * kGY, gs = NY - nfull * kGY;
+        tile = i2 / gs;
+        y = nfull * kGY + i2 % gs;
+      }
+      e = x;
+      cnt = c;
+      return 1;
+    }
+    base += ne;
+  }
+  return id < 0 ? base : 0;
+}
+
+__global__ __launch_bounds__(512) void k_moe_down_t(const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ lists,
+                                                    const int32_t* __restrict__ counts, const float* __restrict__ wt,
+                                                    const uint16_t* __restrict__ wd, float* __restrict__ y, int d, int de,
+                                                    int E, int k, int cap, int slot) {
+  __shared__ int32_t tok[kDM];
+  __shared__ float wgt[kDM];
+  __shared__ __align__(16) uint8_t As[2][2][kDM * kAP];      // [buffer][hi, lo][row]
+  __shared__ __align__(16) uint8_t Bs[2][kDBS];
+  int e = 0, tile = 0, cnt = 0, cblk = 0;
+  const int nitems = down_item(counts, E, slot, d / kDN, -1, e, tile, cnt, cblk);
+  if ((int)blockIdx.x >= nitems) return;
+  if (!down_item(counts, E, slot, d / kDN, xcd_item(blockIdx.x, nitems), e, tile, cnt, cblk)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ntok = min(kDM, cnt - tile * kDM);
+  const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kDM;
+  if (tid < kDM) {
+    const int t = lst[min(tid, ntok - 1)];         // rows past the list's end repeat its last token
+    tok[tid] = t;
+    wgt[tid] = wt[t * k + slot];
+  }
+  __syncthreads();
+  const int r = lane & 31, kh = lane >> 5;
+  const int tw = wave & 1, uw = wave >> 1;          // this wave: tokens 64 tw .., channels 64 uw ..
+  f32x16 acc[2][2] = {};                            // [token block][channel block]
+  if (e > 0) {
+    // this thread's pieces of a stage g (hidden channels 64 g .. 64 g + 63):
+    //   A: row tid / 4, plane (tid / 2) % 2, channels 32 (tid % 2) .. + 31 of the stage
+    //   B: k-step 4 g + tid / 128, channels 2 (tid % 128) and + 1 of the block
+    const int arow = tid >> 2, aplane = (tid >> 1) & 1, ahalf = tid & 1;
+    const uint16_t* ha = hbuf + ((int64_t)tok[arow] * k + slot) * 2 * de + aplane * de + 32 * ahalf;
+    const int bc = tid >> 7, bn = 2 * (tid & 127);
+    const uint16_t* wb = wd + (int64_t)(e - 1) * d * de + ((int64_t)bc * d + cblk * kDN + bn) * 16;
+    const int64_t gstep = (int64_t)4 * d * 16;      // elements per stage of 4 k-steps
+    uint4 ra0[4], rb0[4], ra1[4], rb1[4];
+    auto gl = [&](int g, uint4 (&ra)[4], uint4 (&rb)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ra[q] = gload16(ha + 64 * g + 8 * q);
+        rb[q] = gload16(wb + g * gstep + 8 * q);
+      }
+    };
+    auto st = [&](int b, const uint4 (&ra)[4], const uint4 (&rb)[4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<uint4*>(&As[b][aplane][arow * kAP + 64 * ahalf + 16 * q]) = ra[q];
+        // channel u's two 16-byte halves swap places when bit 3 of u is set (see compute)
+        const int u = bn + (q >> 1);
+        *reinterpret_cast<uint4*>(&Bs[b][(bc * kDN + u) * 32 + 16 * ((q & 1) ^ ((u >> 3) & 1))]) = rb[q];
+      }
+    };
+    auto rd = [&](int b, int j, uint4 (&av)[2][2], uint4 (&bv)[2]) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+          av[tb][pl] = *reinterpret_cast<const uint4*>(&As[b][pl][(64 * tw + 32 * tb + r) * kAP + 16 * j + 64 * kh]);
+#pragma unroll
+      for (int ub = 0; ub < 2; ++ub) {
+        const int u = 64 * uw + 32 * ub + r;
+        bv[ub] = *reinterpret_cast<const uint4*>(&Bs[b][(j * kDN + u) * 32 + 16 * (kh ^ ((u >> 3) & 1))]);
+      }
+    };
+    // as in k_moe_up_t: each k-step's reads go out before the previous k-step's products
+    auto compute = [&](int b) {
+      uint4 av0[2][2], bv0[2], av1[2][2], bv1[2];
+      rd(b, 0, av0, bv0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint4(&av)[2][2] = (j & 1) ? av1 : av0;
+        uint4(&bv)[2] = (j & 1) ? bv1 : bv0;
+        if (j < 3) rd(b, j + 1, (j & 1) ? av0 : av1, (j & 1) ? bv0 : bv1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int ub = 0; ub < 2; ++ub) {
+            acc[tb][ub] = mfma(av[tb][0], bv[ub], acc[tb][ub]);
+            acc[tb][ub] = mfma(av[tb][1], bv[ub], acc[tb][ub]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    const int ns = de / 64;                         // even: de is a multiple of 128
+    gl(0, ra0, rb0);
+    st(0, ra0, rb0);
+    __syncthreads();
+    gl(min(1, ns - 1), ra0, rb0);
+    gl(min(2, ns - 1), ra1, rb1);
+    for (int g = 0; g < ns; g += 2) {
+      compute(0);
+      st(1, ra0, rb0);                              // stage g + 1
+      __syncthreads();
+      gl(min(g + 3, ns - 1), ra0, rb0);
+      compute(1);
+      st(0, ra1, rb1);                              // stage g + 2 (a repeat of the last one at the end)
+      __syncthreads();
+      gl(min(g + 4, ns - 1), ra1, rb1);
+    }
+  }
+  // D[token][channel]: lane (r, kh) holds channel r of its block for rows 8 (reg / 4) + 4 kh + reg % 4
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const int row = 64 * tw + 32 * tb + 8 * (reg >> 2) + 4 * kh + (reg & 3);
+        if (row < ntok) {
+          float* dst = y + (int64_t)tok[row] * d + cblk * kDN + 64 * uw + 32 * ub + r;
+          const float v = e > 0 ? acc[tb][ub][reg] * wgt[row] : 0.0f;
+          if (slot == 0) *dst = v;
+          else *dst += v;
+        }
+      }
+}
+
 }  // namespace
 
 extern "C" {
@@ -664,10 +832,17 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
                          static_cast<const uint16_t*>(x), m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d,
                          m->de, E, K, m->max_tokens, tiles_up);
     }
-    const int tiles_dn = (M + T - 1) / T + E + 1;
-    for (int s = 0; s < K; ++s)
-      hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn * (m->d / kUnits)), dim3(256), 0, st, m->hbuf, m->lists,
-                         m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s, tiles_dn);
+    if (MB == 2 && m->d % kDN == 0) {
+      const int tiles_dn = (M + kDM - 1) / kDM + E + 1;
+      for (int s = 0; s < K; ++s)
+        hipLaunchKernelGGL(k_moe_down_t, dim3(tiles_dn * (m->d / kDN)), dim3(512), 0, st, m->hbuf, m->lists, m->counts,
+                           m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s);
+    } else {
+      const int tiles_dn = (M + T - 1) / T + E + 1;
+      for (int s = 0; s < K; ++s)
+        hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn * (m->d / kUnits)), dim3(256), 0, st, m->hbuf, m->lists,
+                           m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s, tiles_dn);
+    }
   };
   if (M > kSmallCall) run(std::integral_constant<int, 2>());
   else run(std::integral_constant<int, 1>());

@@ -76,8 +76,11 @@ def compare_with_ties(c, k, rows, y, where):
     say(f"  {where}: {int((~unique).sum())} tokens with tied top-{k} sets")
 
 
+# calls above 512 tokens take the tiled products (the down product only when d is a multiple of
+# 256: (600, 640, ...) takes the other one)
 @pytest.mark.parametrize("M,d,de,E,k", [(100, 128, 128, 4, 2), (1000, 768, 1024, 8, 2), (33, 256, 384, 3, 1),
-                                        (1, 128, 128, 1, 2), (77, 384, 256, 16, 1)])
+                                        (1, 128, 128, 1, 2), (77, 384, 256, 16, 1), (700, 512, 256, 5, 2),
+                                        (600, 640, 256, 4, 2), (513, 256, 384, 3, 1)])
 def test_moe_matches_oracle(tr, M, d, de, E, k):
     say(f"moe M={M} d={d} d_e={de} E={E} k={k}")
     c = moe_case(M, d, de, E, seed=M + E, device="cuda")
@@ -90,15 +93,15 @@ def test_moe_matches_oracle(tr, M, d, de, E, k):
 def test_moe_null_expert_heavy(tr):
     """Most tokens pick the null expert first: their outputs are exactly zero (k = 1) or the other
     expert's weighted output (k = 2)."""
-    for k in (1, 2):
-        c = moe_case(300, 256, 256, 4, seed=9, device="cuda", null_bias=2.0)
+    for M, k in ((300, 1), (300, 2), (800, 1), (800, 2)):
+        c = moe_case(M, 256, 256, 4, seed=9, device="cuda", null_bias=2.0)
         y = run(tr, c, k)
-        _, sel, _ = reference(c, k, np.arange(300))
+        _, sel, _ = reference(c, k, np.arange(M))
         if k == 1:
             z = c["z"].cpu().numpy()
-            alone = [i for i in range(300) if sel[i, 0] == 0 and len(tied_sets(z[i].astype(np.float64), 1)) == 1]
+            alone = [i for i in range(M) if sel[i, 0] == 0 and len(tied_sets(z[i].astype(np.float64), 1)) == 1]
             assert np.all(y[alone] == 0.0)
-        compare_with_ties(c, k, np.arange(300), y, f"null-heavy k={k}")
+        compare_with_ties(c, k, np.arange(M), y, f"null-heavy M={M} k={k}")
 
 
 def test_moe_partial_call_and_full_size_sample(tr):
