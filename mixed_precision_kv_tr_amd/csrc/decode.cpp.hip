@@ -757,6 +757,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
     const uint8_t* __restrict__ mode, float* __restrict__ part, uint16_t* __restrict__ out, int HQ, int G, int NB) {
   constexpr int NT = D / 16, KS = D / 32, NCL = (GB + 3) / 4;
   __shared__ Smem<D, GB> sm;
+  // one column per item only without grouping (G = 1, so one block per KV head)
+  if constexpr (GB == 1) {
+    G = 1;
+    NB = 1;
+  }
   const int lane = threadIdx.x;
   const int groups = c.B * c.H * NB;
   int k, grp;
@@ -793,13 +798,20 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
 #pragma unroll
   for (int i = 0; i < QPL; ++i) {
     const int x = lane + kWave * i;
-    qraw[i] = x < ncol * D ? q[row0 * D + x] : (uint16_t)0;
+    // unconditional (clamped) loads: one under a condition would wait on the spot; the values
+    // past the block's columns are never used
+    qraw[i] = q[row0 * D + min(x, ncol * D - 1)];
   }
   const int4 paf = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[0][0]));
   const int4 pef = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[0][1]));
   const int4 pal = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[1][0]));
   const int4 pel = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, cb[1][1]));
   const int4 pl = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, lo_loc));
+  // the prefix rows arrive here, together with the modes and query rows issued above (otherwise
+  // the compiler issues them only after the modes are used, one more memory round trip)
+  asm volatile("" ::"s"(paf.x), "s"(paf.y), "s"(paf.z), "s"(paf.w), "s"(pef.x), "s"(pef.y), "s"(pef.z), "s"(pef.w));
+  asm volatile("" ::"s"(pal.x), "s"(pal.y), "s"(pal.z), "s"(pal.w), "s"(pel.x), "s"(pel.y), "s"(pel.z), "s"(pel.w));
+  asm volatile("" ::"s"(pl.x), "s"(pl.y), "s"(pl.z), "s"(pl.w));
 
   // modes of the block's columns
   const bool bad = lane < ncol && mval > TR_MODE_FULL;
