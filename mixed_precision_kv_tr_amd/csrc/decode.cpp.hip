@@ -931,6 +931,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   for (int i = lane; i < 128; i += kWave) (&sm.pb[GB][0][0])[i] = 0;
   wave_lds_sync();
 
+  // Issue priority by progress: the items of a launch are alike in size and all resident at once,
+  // and among waves of equal priority a SIMD issues for the oldest first, so the items would
+  // finish in start order, several microseconds apart, the last ones alone at the end.  A wave
+  // steps its priority down as it gets through its item (3, 2, 1, 0 at about a quarter, half and
+  // three quarters of the work), so that waves behind are issued first and the items finish
+  // together.
+  __builtin_amdgcn_s_setprio(3);
   // phase 1
   float mrun[NCL];
 #pragma unroll
@@ -939,6 +946,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   float vdummy = 0.0f;
   if (e[0] > a[0]) phase1<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, kscale, mrun, vm[0]);
   if (e[1] > a[1]) phase1<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, kscale, mrun, vm[1]);
+  __builtin_amdgcn_s_setprio(2);
   if (e[2] > a[2]) phase1<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, kscale, mrun, vm[2]);
   if (e[3] > a[3]) phase1<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, kscale, mrun, vdummy);
   // column maxima: lanes of group g hold columns 4 i + g
@@ -953,6 +961,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   wave_lds_sync();
 
   // phase 2
+  __builtin_amdgcn_s_setprio(1);
   f32x4 acc[NT];
   float lp[GB], zp[GB], cp[GB];
 #pragma unroll
@@ -999,6 +1008,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   }
   const float tm = ldexpf(1.0f, -em);
   if (e[1] > a[1]) phase2<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, tm, acc, lp, zp, cp);
+  __builtin_amdgcn_s_setprio(0);
   if (e[2] > a[2]) phase2<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, tm, acc, lp, zp, cp);
   if (e[3] > a[3]) phase2<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, tm, acc, lp, zp, cp);
   wave_lds_sync();
