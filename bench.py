@@ -81,34 +81,34 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # as null.
 TRAFFIC = {
     ("k_decode", "1.3b-decode-L24-B32-C8192-H16-D128"): {
-        "fetch_kib": 174292.1, "write_kib": 1837.1, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "fetch_kib": 174254.2, "write_kib": 1837.4, "fetch_per_byte": 0.500101, "write_per_byte": 1.0,
         "profile": "profiles/k_decode_1.3b-decode-L24-B32-C8192-H16-D128.md",
         "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "46f894c6c8b61767384a41249f5a437b29f526a97f532e366ed0a06046f82b8c",
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "41ea5a27866581555dfade95440ce58e82e22a2fa4c9041f417ff4e4a8c9769c",
             "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
-            "include/triroute.h": "03f5904b8aab554fe8d9b402e8e084ae7581b75d53d74bb4e77b6dbfed859738",
+            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
         },
     },
     ("k_decode", "1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128"): {
-        "fetch_kib": 89339.7, "write_kib": 4642.8, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "fetch_kib": 89341.7, "write_kib": 4642.3, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
         "profile": "profiles/k_decode_1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128.md",
         "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "46f894c6c8b61767384a41249f5a437b29f526a97f532e366ed0a06046f82b8c",
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "41ea5a27866581555dfade95440ce58e82e22a2fa4c9041f417ff4e4a8c9769c",
             "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
-            "include/triroute.h": "03f5904b8aab554fe8d9b402e8e084ae7581b75d53d74bb4e77b6dbfed859738",
+            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
         },
     },
     ("k_prefill_attn", "160m-prefill-L12-B4-T2048-H12-D64"): {
-        "fetch_kib": 19257.7, "write_kib": 19043.9, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "fetch_kib": 19429.1, "write_kib": 19048.0, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
         "profile": "profiles/k_prefill_attn_160m-prefill-L12-B4-T2048-H12-D64.md",
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip": "af4ba0a1ed87eba042bc59e7c0e7eb069b4e8043c4b5a0d229a4430e331ee717",
             "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
             "mixed_precision_kv_tr_amd/csrc/kv_write.h": "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
-            "include/triroute.h": "03f5904b8aab554fe8d9b402e8e084ae7581b75d53d74bb4e77b6dbfed859738",
+            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
         },
     },
 }
