@@ -77,9 +77,14 @@ __global__ __launch_bounds__(kBlock) void k_write_small(CacheLayout c, int layer
   for (int x = 0; x < NPF; ++x) raw[x] = *reinterpret_cast<const uint4*>(src_of(x * GPI + tid / LPG));
 
   if (tid < 64) {
+    // the widths and the prefix row go out together (the width load unconditional, clamped: a
+    // load under a condition would be waited for on the spot, before the prefix row is issued)
+    const int bw = bits[(int64_t)s * n + min(lane, n - 1)];
+    const int4 pre0 = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, p0));
+    asm volatile("" ::"v"(bw), "v"(pre0.x), "v"(pre0.y), "v"(pre0.z), "v"(pre0.w));
     int cls = 3;
     if (lane < n) {
-      cls = tr_class_of_bits(bits[(int64_t)s * n + lane]);
+      cls = tr_class_of_bits(bw);
       if (cls < 0) {
         atomicOr(c.err, TR_ERRF_BAD_BITS);
         cls = 3;
@@ -90,7 +95,6 @@ __global__ __launch_bounds__(kBlock) void k_write_small(CacheLayout c, int layer
       if (cls == 0) a = 1u; else if (cls == 1) a = 1u << 16; else if (cls == 2) b = 1u; else b = 1u << 16;
     }
     const uint32_t ia = tr_wave_incl_scan(a), ib = tr_wave_incl_scan(b);
-    const int4 pre0 = *reinterpret_cast<const int4*>(tr_prefix_row(c, layer, s, p0));
     const int n0[4] = {pre0.x, pre0.y, pre0.z, pre0.w};
     const int inc[4] = {(int)(ia & 0xffffu), (int)(ia >> 16), (int)(ib & 0xffffu), (int)(ib >> 16)};
     if (lane < n) {
