@@ -849,16 +849,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
     }
   }
   // page ids: at most kPgMax (< 64) per class, one per lane; the four classes' loads go out together
+  // and land in LDS only at the end of the prologue, so their round trip overlaps the query work
+  int32_t pv[4];
   {
-    int32_t pv[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int np = e[x] > a[x] ? ((e[x] - 1) >> c.ptok_log2[x]) - first[x] + 1 : 0;
-      pv[x] = lane < np ? tr_ptab(c, layer, s, x)[first[x] + lane] : -1;
+      // unconditional (index clamped into the class's page table): a load under a condition
+      // makes the compiler's wait counts conservative, and the query rows' wait below would then
+      // wait for these too
+      const int32_t v = tr_ptab(c, layer, s, x)[min(first[x] + min(lane, max(np - 1, 0)), c.maxp[x] - 1)];
+      pv[x] = lane < np ? v : -1;
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      if (lane < kPgMax) sm.pg[x][lane] = pv[x];
   }
   // per column: first visible slot per class (-1: the column attends to nothing)
   if (lane < GB) {
@@ -929,6 +931,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   if constexpr (Smem<D, GB>::kOdLds)
     for (int i = lane; i < GB * D; i += kWave) (&sm.od[0][0])[i] = 0.0f;
   for (int i = lane; i < 128; i += kWave) (&sm.pb[GB][0][0])[i] = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    if (lane < kPgMax) sm.pg[x][lane] = pv[x];
   wave_lds_sync();
 
   // Issue priority by progress: the items of a launch are alike in size and all resident at once,
