@@ -81,20 +81,20 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # as null.
 TRAFFIC = {
     ("k_decode", "1.3b-decode-L24-B32-C8192-H16-D128"): {
-        "fetch_kib": 174254.2, "write_kib": 1837.4, "fetch_per_byte": 0.500101, "write_per_byte": 1.0,
+        "fetch_kib": 174243.3, "write_kib": 1837.3, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
         "profile": "profiles/k_decode_1.3b-decode-L24-B32-C8192-H16-D128.md",
         "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "41ea5a27866581555dfade95440ce58e82e22a2fa4c9041f417ff4e4a8c9769c",
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "d4f07c52198361e83487d672f4c8977788447255e96689e694a235d2f0bb19f6",
             "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
             "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
         },
     },
     ("k_decode", "1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128"): {
-        "fetch_kib": 89341.7, "write_kib": 4642.3, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "fetch_kib": 89340.9, "write_kib": 4642.3, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
         "profile": "profiles/k_decode_1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128.md",
         "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "41ea5a27866581555dfade95440ce58e82e22a2fa4c9041f417ff4e4a8c9769c",
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "d4f07c52198361e83487d672f4c8977788447255e96689e694a235d2f0bb19f6",
             "mixed_precision_kv_tr_amd/csrc/common.h": "2962d26cfbabf5b0a32bca69b1e9f5201e2009316f929a68fed2d31664059005",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
             "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
