@@ -16,11 +16,12 @@
 //             comes from the same A operands), then the side-feature term, the bias and SiLU,
 //             in fp32.  (Splitting the channels gives a 32-token decode step 16 waves instead of
 //             4, and shortens each wave's chain of dependent loads 4x.)
-//   layer 2   fp32 FMAs: thread (unit n, tokens n8 + 8 m) runs over the 128 inputs, weights from
-//             LDS (W2's loads are issued at the start and overlap layer 1) and activations
-//             broadcast from LDS.  The heads' weights then replace W2 in LDS (up to 40 heads;
-//             beyond that they are read from global memory).
-//   RMSNorm, whitening of both axes, the heads (fp32) and the argmaxes, all from LDS.
+//   layer 2   on the matrix cores with fp32 operands (v_mfma_f32_16x16x4f32): wave w takes a
+//             16-token x 16-unit block over the 128 inputs, weights from LDS (W2's loads are
+//             issued at the start and overlap layer 1).  The heads' weights then replace W2 in
+//             LDS (up to 40 heads; beyond that they are read from global memory).
+//   RMSNorm (sums of squares over 32-lane groups), whitening of both axes, the heads (fp32
+//   matrix cores again, 16 x 16 blocks of tokens x outputs) and the argmaxes, all from LDS.
 // The controller is < 1% of a layer's FLOPs on the page; the kernel streams x once (2 d bytes
 // per token) and re-reads the 0.25-4 MB of weights from L2.
 #include <math.h>
@@ -216,27 +217,22 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
     }
   }
   __syncthreads();
-  // ---- layer 2: h2 = h W2 + b2, thread (unit n, tokens p + 8 m) ----
+  // ---- layer 2 on the matrix cores (v_mfma_f32_16x16x4f32, fp32 operands): wave w computes
+  //      tokens 16 (w >> 3) .. + 15 x units 16 (w & 7) .. + 15 over all 128 inputs; lane l
+  //      supplies h[row l % 16][k + l / 16] and W2[k + l / 16][col l % 16] and ends with
+  //      D[4 (l / 16) + r][l % 16] ----
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int r16 = lane & 15, q16 = lane >> 4;
   {
-    const int n = tid & (kDr - 1), p = tid >> 7;
-    float acc[kTok / 8];
-    const float b2 = sm.pu[1][n];
+    const int tb = wave >> 3, ub = wave & 7;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float* arow = &hs[16 * tb + r16][q16];
+    const float* bcol = &sm.wts[q16 * kDr + 16 * ub + r16];
+#pragma unroll 8
+    for (int k = 0; k < kDr; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[k], bcol[k * kDr], acc, 0, 0, 0);
+    const float b2 = sm.pu[1][16 * ub + r16];
 #pragma unroll
-    for (int m = 0; m < kTok / 8; ++m) acc[m] = b2;
-    for (int k = 0; k < kDr; k += 4) {
-      const float w0 = sm.wts[(k + 0) * kDr + n], w1 = sm.wts[(k + 1) * kDr + n];
-      const float w2 = sm.wts[(k + 2) * kDr + n], w3 = sm.wts[(k + 3) * kDr + n];
-#pragma unroll
-      for (int m = 0; m < kTok / 8; ++m) {
-        const float4 hv = *reinterpret_cast<const float4*>(&hs[p + 8 * m][k]);
-        acc[m] = fmaf(hv.x, w0, acc[m]);
-        acc[m] = fmaf(hv.y, w1, acc[m]);
-        acc[m] = fmaf(hv.z, w2, acc[m]);
-        acc[m] = fmaf(hv.w, w3, acc[m]);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < kTok / 8; ++m) h2s[p + 8 * m][n] = acc[m];
+    for (int r = 0; r < 4; ++r) h2s[16 * tb + 4 * q16 + r][16 * ub + r16] = acc[r] + b2;
   }
   __syncthreads();
   // the heads' weights replace W2 in LDS when they fit (up to 40 heads), from registers
@@ -247,10 +243,14 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
       if (i < kDr * no) sm.wts[i] = hw[q];
     }
   }
-  if (tid < kTok) {
-    float s = 0.0f;
-    for (int k = 0; k < kDr; ++k) s = fmaf(h2s[tid][k], h2s[tid][k], s);
-    sm.inv2[tid] = 1.0f / sqrtf(s / (float)kDr + 1e-6f);
+  // sums of squares: thread (token tid / 32, units 4 (tid % 32) .. + 3), then over 32 lanes
+  {
+    const int t = tid >> 5, j4 = 4 * (tid & 31);
+    const float4 v = *reinterpret_cast<const float4*>(&h2s[t][j4]);
+    float e = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) e += __shfl_xor(e, off);
+    if ((tid & 31) == 0) sm.inv2[t] = 1.0f / sqrtf(e / (float)kDr + 1e-6f);
   }
   __syncthreads();
   // ---- RMSNorm and Eq. (11) per axis: hhat^a -> hs, hhat^b -> h2s ----
@@ -266,28 +266,31 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
     }
   }
   __syncthreads();
-  // ---- heads: column o of [W_a | W_b] for the tokens of thread group g ----
+  // ---- heads on the matrix cores: items (token block of 16, output block of 16) over the
+  //      attention head's ceil(3 H / 16) blocks (inputs hhat^a) and the bit head's one block
+  //      (inputs hhat^b); outputs past a head's columns multiply zeros ----
   {
-    const int groups = kThreads / no;               // >= 5 since no <= 196
-    const int o = tid % no, g = tid / no;
-    if (g < groups) {
-      const bool att = o < na;
-      const float* wa = wl ? sm.wts : a.w_a;
-      const float* wb = wl ? sm.wts + kDr * na : a.w_b;
-      const float* wcol = att ? wa + o : wb + (o - na);
+    const int nab = (na + 15) / 16, items = 2 * (nab + 1);
+    const float* wa = wl ? sm.wts : a.w_a;
+    const float* wb = wl ? sm.wts + kDr * na : a.w_b;
+    for (int it = wave; it < items; it += kThreads / 64) {
+      const int tb = it & 1, ob = it >> 1;
+      const bool att = ob < nab;
+      const int o = att ? 16 * ob + r16 : r16;      // column within its head
+      const bool live = att ? o < na : o < 4;
+      const float* src = att ? &hs[16 * tb + r16][q16] : &h2s[16 * tb + r16][q16];
+      const float* wcol = att ? wa + min(o, na - 1) : wb + min(o, 3);
       const int ws = att ? na : 4;
-      for (int t = g; t < kTok; t += groups) {
-        const float* src = att ? &hs[t][0] : &h2s[t][0];
-        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};       // four independent chains
-#pragma unroll 4
-        for (int k = 0; k < kDr; k += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(src + k);
-          z[0] = fmaf(v.x, wcol[(k + 0) * ws], z[0]);
-          z[1] = fmaf(v.y, wcol[(k + 1) * ws], z[1]);
-          z[2] = fmaf(v.z, wcol[(k + 2) * ws], z[2]);
-          z[3] = fmaf(v.w, wcol[(k + 3) * ws], z[3]);
-        }
-        zl[t][o] = (z[0] + z[1]) + (z[2] + z[3]);
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int k = 0; k < kDr; k += 4) {
+        const float w = live ? wcol[(k + q16) * ws] : 0.0f;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(src[k], w, acc, 0, 0, 0);
+      }
+      if (live) {
+        const int col = att ? o : na + o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zl[16 * tb + 4 * q16 + r][col] = acc[r];
       }
     }
   }
