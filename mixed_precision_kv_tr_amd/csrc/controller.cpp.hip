@@ -99,7 +99,7 @@ struct CtlSmem {
   float part[kSplit][kTok][kRow];
   float wts[kDr * kDr];
   float sd[kTok][kMaxSide];
-  float w1s[kDr][kMaxSide];       // layer 1's side-feature weights
+  float w1s[kMaxSide][kDr];       // layer 1's side-feature weights, transposed (unit-contiguous)
   float pu[6][kDr];               // per unit: b1, b2, mu_a, sigma_a, mu_b, sigma_b
   float ssp[kSplit][kTok];
   float inv2[kTok];
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
     const int t = i / a.d_side, s = i % a.d_side;
     sm.sd[t][s] = t < ntok ? side[(tok0 + t) * a.d_side + s] : 0.0f;
   }
-  for (int i = tid; i < kDr * a.d_side; i += kThreads) sm.w1s[i / a.d_side][i % a.d_side] = a.w1_side[i];
+  for (int i = tid; i < kDr * a.d_side; i += kThreads) sm.w1s[i % a.d_side][i / a.d_side] = a.w1_side[i];
   if (tid < 6 * kDr) {
     const int v = tid / kDr, n = tid % kDr;
     const float* src = v == 0 ? a.b1 : v == 1 ? a.b2 : v == 2 ? a.mu_a : v == 3 ? a.sigma_a : v == 4 ? a.mu_b : a.sigma_b;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_controller(CtlArgs a, const uint16
         sq += sm.ssp[k][t];
       }
       float v = fmaf(sum, 1.0f / sqrtf(sq / (float)a.d + 1e-6f), b1);
-      for (int s = 0; s < a.d_side; ++s) v = fmaf(sm.sd[t][s], sm.w1s[n][s], v);
+      for (int s = 0; s < a.d_side; ++s) v = fmaf(sm.sd[t][s], sm.w1s[s][n], v);
       hs[t][n] = v / (1.0f + expf(-v));
     }
   }
