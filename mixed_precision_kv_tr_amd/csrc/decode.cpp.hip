@@ -287,10 +287,66 @@ constexpr QMap make_qmap() {
 __constant__ QMap kQmap64 = make_qmap<64>();
 __constant__ QMap kQmap128 = make_qmap<128>();
 
+// A phase-1 batch: the code words of U groups of 16 keys (lane: key kr of each group, quarter row g),
+// and the K scale / zero and V scale of the batch's keys, one key per lane (key 64 i + lane in slot
+// i), handed to the lanes that need them by a cross-lane permute.
+template <int D, int C>
+struct P1Batch {
+  uint32_t w[Cls<D, C>::U][Cls<D, C>::NWK];
+  float sk[Cls<D, C>::NS], zk[Cls<D, C>::NS], sv[Cls<D, C>::NS];
+};
+
+// Issues the loads of the phase-1 batch of class C that starts at class slot `base` (of the slots
+// [., e) whose pages are listed in sm.pg[C] from page `first` on).  Indices are clamped into the
+// range, so the loads never branch.
+template <int D, int GB, int C>
+__device__ __forceinline__ void p1_load(const CacheLayout& c, const Smem<D, GB>& sm, int first, int h, int e, int base,
+                                        P1Batch<D, C>& bt) {
+  using K = Cls<D, C>;
+  const int lane = threadIdx.x, kr = lane & 15, g = lane >> 4;
+  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
+  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + g * (K::RB / 4);
+  const int64_t sk_off = c.sk_off[C] + (int64_t)h * P * 8, sv_off = c.sv_off[C] + (int64_t)h * P * 8;
+  const int32_t* pg = sm.pg[C];
+  if constexpr (C < 3) {
+#pragma unroll
+    for (int i = 0; i < K::NS; ++i) {
+      const int j = min(base + 64 * i + lane, e - 1);
+      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
+      const int row = j & pm;
+      const u32x2 kz = *reinterpret_cast<const u32x2*>(pb + sk_off + (int64_t)row * 8);
+      bt.sk[i] = __uint_as_float(kz[0]);
+      bt.zk[i] = __uint_as_float(kz[1]);
+      bt.sv[i] = *reinterpret_cast<const float*>(pb + sv_off + (int64_t)row * 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < K::U; ++u) {
+    const int j = min(base + 16 * u + kr, e - 1);
+    const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
+    const int row = j & pm;
+    const uint8_t* src = pb + code_off + (int64_t)row * K::RB;
+    if constexpr (K::NWK == 1) {
+      bt.w[u][0] = *reinterpret_cast<const uint32_t*>(src);
+    } else if constexpr (K::NWK == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      bt.w[u][0] = v.x; bt.w[u][1] = v.y;
+    } else {
+#pragma unroll
+      for (int x = 0; x < K::NWK / 4; ++x) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(src)[x];
+        bt.w[u][4 * x] = v[0]; bt.w[u][4 * x + 1] = v[1]; bt.w[u][4 * x + 2] = v[2]; bt.w[u][4 * x + 3] = v[3];
+      }
+    }
+  }
+}
+
 // Phase 1 for width class C over class slots [a, e): scores into sc[n * SCAP + off + (j - a)].
+// `cur` holds the loads of the first batch (slots from a), issued by the caller.
 template <int D, int GB, int C>
 __device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, int first, int h, int a, int e, int off,
-                                       int ncol, float kscale, float (&mrun)[(GB + 3) / 4], float& vmax) {
+                                       int ncol, float kscale, float (&mrun)[(GB + 3) / 4], float& vmax,
+                                       P1Batch<D, C> cur) {
   using K = Cls<D, C>;
   constexpr int KS = D / 32;
   constexpr int NCL = (GB + 3) / 4;
@@ -322,10 +378,6 @@ __device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, in
     fo[i] = sm.qoff[C][nn];
     lbn[i] = act[i] ? sm.lb[C][nn] : e;
   }
-  const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
-  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + g * (K::RB / 4);
-  const int64_t sk_off = c.sk_off[C] + (int64_t)h * P * 8, sv_off = c.sv_off[C] + (int64_t)h * P * 8;
-  const int32_t* pg = sm.pg[C];
   const uint32_t KK = opaque_v(kF16K);
   uint32_t mk[5] = {0, 0, 0, 0, 0};
   if constexpr (C == 0) {
@@ -337,48 +389,8 @@ __device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, in
   }
   const uint32_t BB = opaque_s(kF16B);
 
-  // A batch: the code words of U groups of 16 keys (lane: key kr of each group, quarter row g), and
-  // the K scale / zero and V scale of the batch's keys, one key per lane (key 64 i + lane in slot
-  // i), handed to the lanes that need them by a cross-lane permute.
-  struct Batch {
-    uint32_t w[U][K::NWK];
-    float sk[K::NS], zk[K::NS], sv[K::NS];
-  };
-  auto load = [&](Batch& bt, int base) {
-    if constexpr (C < 3) {
-#pragma unroll
-      for (int i = 0; i < K::NS; ++i) {
-        const int j = min(base + 64 * i + lane, e - 1);      // clamped: loads never branch
-        const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
-        const int row = j & pm;
-        const u32x2 kz = *reinterpret_cast<const u32x2*>(pb + sk_off + (int64_t)row * 8);
-        bt.sk[i] = __uint_as_float(kz[0]);
-        bt.zk[i] = __uint_as_float(kz[1]);
-        bt.sv[i] = *reinterpret_cast<const float*>(pb + sv_off + (int64_t)row * 8);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = min(base + 16 * u + kr, e - 1);          // clamped: loads never branch
-      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
-      const int row = j & pm;
-      const uint8_t* src = pb + code_off + (int64_t)row * K::RB;
-      if constexpr (K::NWK == 1) {
-        bt.w[u][0] = *reinterpret_cast<const uint32_t*>(src);
-      } else if constexpr (K::NWK == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        bt.w[u][0] = v.x; bt.w[u][1] = v.y;
-      } else {
-#pragma unroll
-        for (int x = 0; x < K::NWK / 4; ++x) {
-          const u32x4 v = reinterpret_cast<const u32x4*>(src)[x];
-          bt.w[u][4 * x] = v[0]; bt.w[u][4 * x + 1] = v[1]; bt.w[u][4 * x + 2] = v[2]; bt.w[u][4 * x + 3] = v[3];
-        }
-      }
-    }
-  };
   // One batch: U groups of 16 keys from `base`; scores of the keys before e.
-  auto compute = [&](const Batch& cur, int base) {
+  auto compute = [&](const P1Batch<D, C>& cur, int base) {
     if constexpr (C < 3) {
 #pragma unroll
       for (int i = 0; i < K::NS; ++i)
@@ -436,10 +448,9 @@ __device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, in
   // The next batch's loads are always issued (clamped into the range) before the current one is
   // computed, so they stay in flight during its products; the batches rotate by value (see
   // phase 2).
-  Batch cur, nxt;
-  load(cur, a);
+  P1Batch<D, C> nxt;
   for (int base = a;;) {
-    load(nxt, base + 16 * U);
+    p1_load<D, GB, C>(c, sm, first, h, e, base + 16 * U, nxt);
     compute(cur, base);
     base += 16 * U;
     if (base >= e) break;
@@ -811,7 +822,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   // the compiler issues them only after the modes are used, one more memory round trip)
   asm volatile("" ::"s"(paf.x), "s"(paf.y), "s"(paf.z), "s"(paf.w), "s"(pef.x), "s"(pef.y), "s"(pef.z), "s"(pef.w));
   asm volatile("" ::"s"(pal.x), "s"(pal.y), "s"(pal.z), "s"(pal.w), "s"(pel.x), "s"(pel.y), "s"(pel.z), "s"(pel.w));
-  asm volatile("" ::"s"(pl.x), "s"(pl.y), "s"(pl.z), "s"(pl.w));
+  asm volatile("" ::"s"(pl.x), "s"(pl.y), "s"(pl.z), "s"(pl.w), "v"(qch[0]), "v"(qch[1]), "v"(qfx[0]), "v"(qfx[1]));
 
   // modes of the block's columns
   const bool bad = lane < ncol && mval > TR_MODE_FULL;
@@ -849,7 +860,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
     }
   }
   // page ids: at most kPgMax (< 64) per class, one per lane; the four classes' loads go out together
-  // and land in LDS only at the end of the prologue, so their round trip overlaps the query work
+  // and land in LDS after the query rows' sums, so their round trip overlaps that work
   int32_t pv[4];
   {
 #pragma unroll
@@ -891,7 +902,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
       sm.qsum[n] = qs;
     }
   }
+  // The page ids land in LDS, and the first phase-1 batch of class 0 (and of class 1 with one
+  // column, whose registers allow it) goes out: its round trip overlaps the rest of the query work,
+  // so the cache reads start as early as the page ids allow.
+  constexpr bool kEarly1 = GB == 1;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    if (lane < kPgMax) sm.pg[x][lane] = pv[x];
   wave_lds_sync();
+  P1Batch<D, 0> b0;
+  P1Batch<D, 1> b1;
+  if (e[0] > a[0]) p1_load<D, GB, 0>(c, sm, first[0], hk, e[0], a[0], b0);
+  if (kEarly1 && e[1] > a[1]) p1_load<D, GB, 1>(c, sm, first[1], hk, e[1], a[1], b1);
   // A operands of every class: lane -> (class cl, step st, group gg), 8 values each; the fp16
   // classes' 1024-offset sums per (class, column)
   {
@@ -931,9 +953,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   if constexpr (Smem<D, GB>::kOdLds)
     for (int i = lane; i < GB * D; i += kWave) (&sm.od[0][0])[i] = 0.0f;
   for (int i = lane; i < 128; i += kWave) (&sm.pb[GB][0][0])[i] = 0;
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-    if (lane < kPgMax) sm.pg[x][lane] = pv[x];
   wave_lds_sync();
 
   // Issue priority by progress: the items of a launch are alike in size and all resident at once,
@@ -949,11 +968,22 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   for (int i = 0; i < NCL; ++i) mrun[i] = -INFINITY;
   float vm[3] = {0.0f, 0.0f, 0.0f};
   float vdummy = 0.0f;
-  if (e[0] > a[0]) phase1<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, kscale, mrun, vm[0]);
-  if (e[1] > a[1]) phase1<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, kscale, mrun, vm[1]);
+  if (e[0] > a[0]) phase1<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, kscale, mrun, vm[0], b0);
+  if (e[1] > a[1]) {
+    if (!kEarly1) p1_load<D, GB, 1>(c, sm, first[1], hk, e[1], a[1], b1);
+    phase1<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, kscale, mrun, vm[1], b1);
+  }
   __builtin_amdgcn_s_setprio(2);
-  if (e[2] > a[2]) phase1<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, kscale, mrun, vm[2]);
-  if (e[3] > a[3]) phase1<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, kscale, mrun, vdummy);
+  if (e[2] > a[2]) {
+    P1Batch<D, 2> b2;
+    p1_load<D, GB, 2>(c, sm, first[2], hk, e[2], a[2], b2);
+    phase1<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, kscale, mrun, vm[2], b2);
+  }
+  if (e[3] > a[3]) {
+    P1Batch<D, 3> b3;
+    p1_load<D, GB, 3>(c, sm, first[3], hk, e[3], a[3], b3);
+    phase1<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, kscale, mrun, vdummy, b3);
+  }
   // column maxima: lanes of group g hold columns 4 i + g
 #pragma unroll
   for (int i = 0; i < NCL; ++i) {
