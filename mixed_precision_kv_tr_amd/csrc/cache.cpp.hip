@@ -274,6 +274,7 @@ static void free_all(tr_kv_cache* c) {
   (void)hipFree(c->lay.next_page);
   (void)hipFree(c->lay.err);
   (void)hipFree(c->partials);
+  (void)hipFree(c->merge_cnt);
   (void)hipFree(c->rows);
   (void)hipFree(c->row_counts);
   (void)hipFree(c->dk);
@@ -302,6 +303,7 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   tr_kv_cache* c = new tr_kv_cache();
   memset(&c->lay, 0, sizeof(c->lay));
   c->partials = nullptr;
+  c->merge_cnt = nullptr;
   c->rows = c->row_counts = nullptr;
   c->dk = c->dv = nullptr;
   c->dkf = nullptr;
@@ -360,6 +362,8 @@ tr_status tr_kv_cache_alloc(const tr_kv_cache_desc* d, tr_kv_cache** out) {
   ok = ok && hipMalloc((void**)&L.err, sizeof(uint32_t)) == hipSuccess;
   ok = ok && hipMalloc((void**)&c->partials,
                        sizeof(float) * (size_t)L.B * hq * c->max_chunks * (L.D + 2)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&c->merge_cnt, sizeof(int32_t) * (size_t)L.B * hq) == hipSuccess;
+  ok = ok && hipMemset(c->merge_cnt, 0, sizeof(int32_t) * (size_t)L.B * hq) == hipSuccess;
   c->np = (L.pfN + 63) / 64 * 64;
   c->pf_uph = L.pfN ? tr_prefill_units_per_head(L.pfN) : 0;
   if (L.pfN > 0) {                                 // prefill scratch, sized by its capacity

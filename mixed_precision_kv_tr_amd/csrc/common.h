@@ -18,6 +18,9 @@ struct tr_kv_cache {
   // decode split-K partials: [B][HQ][max_chunks][D + 2] floats (o[D], m, l)
   float* partials;
   int32_t max_chunks;
+  // decode merge counters, one per (seq, query head) (at least one per (seq, KV head, block)):
+  // zero between calls
+  int32_t* merge_cnt;
   int32_t force_chunks;           // tr_kv_cache_set_decode_chunks: 0 = automatic
   // prefill scratch: compacted query rows per (seq, query head) [B][HQ][N] and counts [B][HQ][4]
   int32_t* rows;

@@ -26,7 +26,9 @@
 //          accumulate apart and are added through LDS.
 // epilogue a one-chunk window writes bf16 out directly; otherwise the chunk writes (o[D], m, l)
 //          per column.  Columns whose mode is skip get zeros from chunk 0.
-// k_decode_combine: log-sum-exp merge of multi-chunk windows -> bf16.
+// merge    with one column per item, the wave that finishes a window's last chunk merges the
+//          window's chunk records (log-sum-exp) into bf16; with blocks of query heads,
+//          k_decode_combine does it in a launch of its own.
 #include <math.h>
 
 #include <mutex>
@@ -660,6 +662,71 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
 // e with vmax <= 2^e (0 for vmax = 0): the P' normalization of a class set.
 __device__ __forceinline__ int scale_exp(float vmax) { return vmax > 0.0f ? __builtin_amdgcn_frexp_expf(vmax) : 0; }
 
+// Agent-coherent (sc1) vector memory accesses for the split-K records: a record written by a wave
+// on one XCD is read by a wave of the same launch on another, so it must not wait in either XCD's
+// L2.  The base and size of a (seq, query head)'s records sit in a buffer resource.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kSc1 = 16;                            // cache policy bits: sc1 (agent scope)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const float* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Log-sum-exp merge of one (seq, query head)'s nch chunk records (o[D], m, l) into bf16 `dst`, by a
+// single wave: lane l holds channels D / 64 * l .. + D / 64 - 1.  Records go in batches of 32: every
+// load of a batch (the lane's channels of 32 records and, in lane k, record k's (m, l)) is issued
+// at once, indices clamped into the window, then the batch folds into a running (max, num, den)
+// with the chunk weights broadcast from their lanes.
+template <int D>
+__device__ __forceinline__ void merge_records(__amdgpu_buffer_rsrc_t rs, int nch, uint16_t* __restrict__ dst) {
+  constexpr int KB = 32, CPL = D / 64, REC = (D + 2) * 4;
+  const int lane = threadIdx.x;
+  float M = -INFINITY, den = 0.0f, num[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) num[i] = 0.0f;
+  for (int k0 = 0; k0 < nch; k0 += KB) {
+    float v[KB][CPL];
+#pragma unroll
+    for (int x = 0; x < KB; ++x) {
+      const int off = min(k0 + x, nch - 1) * REC + 4 * CPL * lane;
+      if constexpr (CPL == 2) {
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kSc1));
+        v[x][0] = __uint_as_float(w[0]);
+        v[x][1] = __uint_as_float(w[1]);
+      } else {
+        v[x][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kSc1));
+      }
+    }
+    const int kk = k0 + (lane & (KB - 1));
+    const u32x2 ml =
+        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, min(kk, nch - 1) * REC + 4 * D, 0, kSc1));
+    const bool own = kk < nch && lane < KB;         // lanes KB..63 repeat lanes 0..KB-1
+    const float mk = own ? __uint_as_float(ml[0]) : -INFINITY;
+    const float lk = __uint_as_float(ml[1]);
+    const float Mn = fmaxf(M, wave_max(mk));
+    const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+    const float wk = (own && mk != -INFINITY) ? exp2f(mk - Mn) : 0.0f;
+    den = den * a + wave_sum(wk * lk);
+    float nb[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) nb[i] = 0.0f;
+#pragma unroll
+    for (int x = 0; x < KB; ++x) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), x));
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) nb[i] = fmaf(w, v[x][i], nb[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) num[i] = num[i] * a + nb[i];
+    M = Mn;
+  }
+  if constexpr (CPL == 2) {
+    const uint32_t w = (uint32_t)tr_f32_to_bf16(num[0] / den) | ((uint32_t)tr_f32_to_bf16(num[1] / den) << 16);
+    *reinterpret_cast<uint32_t*>(dst + 2 * lane) = w;
+  } else {
+    dst[lane] = tr_f32_to_bf16(num[0] / den);
+  }
+}
+
 // Occupancy floor handed to the compiler.
 #ifndef TR_DECODE_WAVES
 #define TR_DECODE_WAVES 4
@@ -765,7 +832,8 @@ __device__ __forceinline__ bool item_of_rank(int r, const uint8_t* __restrict__ 
 template <int D, int GB>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE_WAVES, 8))) void k_decode(
     CacheLayout c, int layer, int t, int window, int CH, int stride, float kscale, const uint16_t* __restrict__ q,
-    const uint8_t* __restrict__ mode, float* __restrict__ part, uint16_t* __restrict__ out, int HQ, int G, int NB) {
+    const uint8_t* __restrict__ mode, float* __restrict__ part, uint16_t* __restrict__ out, int HQ, int G, int NB,
+    int32_t* __restrict__ cnt) {
   constexpr int NT = D / 16, KS = D / 32, NCL = (GB + 3) / 4;
   __shared__ Smem<D, GB> sm;
   // one column per item only without grouping (G = 1, so one block per KV head)
@@ -1059,34 +1127,65 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
       corr = cs;
     }
   }
-  if (r >= ncol || !(((fullm | locm) >> r) & 1)) return;
-  const float sM = ldexpf(1.0f, em);
-  const float mx = sm.cmax[r];
+  const bool own = r < ncol && (((fullm | locm) >> r) & 1);
   const int64_t orow = row0 + r;
-  float o[NT][4];
+  if (own) {
+    const float sM = ldexpf(1.0f, em);
+    const float mx = sm.cmax[r];
+    float o[NT][4];
 #pragma unroll
-  for (int m = 0; m < NT; ++m)
+    for (int m = 0; m < NT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[m][i] = (acc[m][i] - corr) * sM + (kOdLds ? sm.od[r][16 * m + 4 * g + i] : 0.0f) + zsum;
-  if (nch == 1) {
-    const float inv = 1.0f / lsum;
+      for (int i = 0; i < 4; ++i)
+        o[m][i] = (acc[m][i] - corr) * sM + (kOdLds ? sm.od[r][16 * m + 4 * g + i] : 0.0f) + zsum;
+    if (nch == 1) {
+      const float inv = 1.0f / lsum;
 #pragma unroll
-    for (int m = 0; m < NT; ++m) {
-      uint2 w;
-      w.x = (uint32_t)tr_f32_to_bf16(o[m][0] * inv) | ((uint32_t)tr_f32_to_bf16(o[m][1] * inv) << 16);
-      w.y = (uint32_t)tr_f32_to_bf16(o[m][2] * inv) | ((uint32_t)tr_f32_to_bf16(o[m][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(out + orow * D + 16 * m + 4 * g) = w;
+      for (int m = 0; m < NT; ++m) {
+        uint2 w;
+        w.x = (uint32_t)tr_f32_to_bf16(o[m][0] * inv) | ((uint32_t)tr_f32_to_bf16(o[m][1] * inv) << 16);
+        w.y = (uint32_t)tr_f32_to_bf16(o[m][2] * inv) | ((uint32_t)tr_f32_to_bf16(o[m][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(out + orow * D + 16 * m + 4 * g) = w;
+      }
+    } else if (GB == 1 && cnt) {
+      // the chunk's record (o[D], m, l), agent-coherent: a wave of this launch merges it
+      const __amdgpu_buffer_rsrc_t rs = rec_rsrc(part + orow * stride * (D + 2), (uint32_t)(stride * (D + 2) * 4));
+      const int rec = k * (D + 2) * 4;
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const u32x4 w = {__float_as_uint(o[m][0]), __float_as_uint(o[m][1]), __float_as_uint(o[m][2]),
+                         __float_as_uint(o[m][3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rs, rec + 4 * (16 * m + 4 * g), 0, kSc1);
+      }
+      if (g == 0) {
+        const u32x2 w = {__float_as_uint(mx), __float_as_uint(lsum)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rs, rec + 4 * D, 0, kSc1);
+      }
+    } else {
+      // the chunk's record, merged by k_decode_combine
+      float* dst = part + (orow * stride + k) * (D + 2);
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+        *reinterpret_cast<float4*>(dst + 16 * m + 4 * g) = make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
+      if (g == 0) {
+        dst[D] = mx;
+        dst[D + 1] = lsum;
+      }
     }
-    return;
   }
-  float* dst = part + (orow * stride + k) * (D + 2);
-#pragma unroll
-  for (int m = 0; m < NT; ++m)
-    *reinterpret_cast<float4*>(dst + 16 * m + 4 * g) = make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
-  if (g == 0) {
-    dst[D] = mx;
-    dst[D + 1] = lsum;
+  if (nch == 1 || !cnt) return;
+  // With one column per item, the wave that completes a group's last chunk merges the group's
+  // records itself: each wave's records are performed at agent scope before it counts its chunk
+  // in the group's counter, and the wave that brings the count to nch reads them all back with
+  // agent-coherent loads and returns the counter to zero for the next call.
+  if constexpr (GB == 1) {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(cnt + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != nch - 1) return;
+    if (lane == 0) __hip_atomic_store(cnt + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_records<D>(rec_rsrc(part + row0 * stride * (D + 2), (uint32_t)(stride * (D + 2) * 4)), nch, out + row0 * D);
   }
 }
 
@@ -1195,8 +1294,11 @@ int decode_chunks(const tr_kv_cache* c, int n, int limit) {
 
 // The decode kernels with the split-K partial results in `part` (records of D + 2 floats,
 // `stride` records per (seq, query head)).
+// With one column per item and a counter per (seq, KV head) in `cnt` (zero on entry, left zero),
+// k_decode merges the chunks itself; otherwise (blocks of query heads, or no counters) the merge is
+// a launch of its own.
 tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t* mode, int window, uint16_t* out,
-                     int nch, float* part, int stride, bool prof_ok, hipStream_t stream) {
+                     int nch, float* part, int stride, int32_t* cnt, bool prof_ok, hipStream_t stream) {
   const CacheLayout& L = c->lay;
   const int t = c->len[layer] - 1;
   const int n = t + 1;
@@ -1207,6 +1309,7 @@ tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t
   const int CH = (n + nch - 1) / nch;
   const float kscale = (float)(1.4426950408889634 / sqrt((double)L.D));
   const int grid = L.B * L.H * NB * nch;
+  if (GB != 1) cnt = nullptr;
   const bool prof_was = c->prof_on;
   c->prof_on = prof_was && prof_ok;
   tr_status st = TR_OK;
@@ -1214,7 +1317,7 @@ tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t
     TrProfScope prof(c, TR_PROF_DECODE_SPLIT, stream);
 #define TR_DECODE_LAUNCH(DD, GG)                                                                             \
   hipLaunchKernelGGL((k_decode<DD, GG>), dim3(grid), dim3(kWave), 0, stream, L, layer, t, window, CH, stride, \
-                     kscale, q, mode, part, out, c->hq, G, NB)
+                     kscale, q, mode, part, out, c->hq, G, NB, cnt)
     if (L.D == 64) {
       if (GB == 1) TR_DECODE_LAUNCH(64, 1);
       else TR_DECODE_LAUNCH(64, 4);
@@ -1225,7 +1328,7 @@ tr_status decode_run(tr_kv_cache* c, int layer, const uint16_t* q, const uint8_t
 #undef TR_DECODE_LAUNCH
     if (hipGetLastError() != hipSuccess) st = TR_ERR_HIP;
   }
-  if (st == TR_OK && nch > 1) {
+  if (st == TR_OK && nch > 1 && !cnt) {
     TrProfScope prof(c, TR_PROF_DECODE_COMBINE, stream);
     if (L.D == 64)
       hipLaunchKernelGGL(k_decode_combine<64>, dim3(BH), dim3(64), 0, stream, t, window, CH, stride, mode, part, out,
@@ -1245,7 +1348,7 @@ tr_status tr_decode_launch(tr_kv_cache* c, int layer, const uint16_t* q, const u
                            uint16_t* out, hipStream_t stream) {
   const int nch = decode_chunks(c, c->len[layer], c->max_chunks);
   if (nch < 1) return TR_ERR_UNSUPPORTED;
-  return decode_run(c, layer, q, mode, window, out, nch, c->partials, c->max_chunks, true, stream);
+  return decode_run(c, layer, q, mode, window, out, nch, c->partials, c->max_chunks, c->merge_cnt, true, stream);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1291,6 +1394,7 @@ tr_status tr_decode_noalloc_launch(tr_kv_cache* c, int layer, const uint16_t* q,
   const int64_t limit = (int64_t)TR_NOALLOC_SCRATCH_BYTES / rec / BH;    // partial records per pair
   const int nch = decode_chunks(c, c->len[layer], (int)(limit < (1 << 20) ? limit : (1 << 20)));
   if (nch < 1) return TR_ERR_SCRATCH;
-  // every chunk writes its own record before the combine reads it: nothing needs clearing
-  return decode_run(c, layer, q, mode, window, out, nch, part, nch, false, stream);
+  // every chunk writes its own record before the merge reads it, which here is always a launch of
+  // its own (an in-kernel merge would need counters that start at zero): nothing needs clearing
+  return decode_run(c, layer, q, mode, window, out, nch, part, nch, nullptr, false, stream);
 }

@@ -154,6 +154,42 @@ def test_decode_chunking_and_paging_invariance(tr):
     assert status == 0
     check(short, out, 100, range(2), "nch=1, 544-position window")
 
+def test_decode_repeated_calls_on_one_cache(tr):
+    """Calls in a row on one cache, with multi-chunk windows (merged by the wave that finishes a
+    window's last chunk, through per-window counters that each call must leave at zero) between
+    one-chunk ones: every call matches the oracle and repeating a call repeats its output bit for
+    bit, for both head sizes and a chunk count above one merge batch (32 chunks)."""
+    for D in (64, 128):
+        say(f"decode: repeated calls on one cache, D={D}")
+        case = random_case(3, 1800, 4, D, window=300, bit_weights={2: 0.3, 4: 0.3, 8: 0.2, 16: 0.2},
+                           mode_weights={"skip": 0.1, "local": 0.45, "full": 0.45}, seed=90 + D, device="cuda",
+                           n_queries=1)
+        q, mode = case["q"][:, 0].contiguous(), case["mode"][:, 0].contiguous()
+        B, T, H, _ = case["k"].shape
+        cache = tr.tr_kv_cache_alloc(1, B, H, D, T)
+        try:
+            tr.tr_kv_quantize_write(cache, 0, case["k"], case["v"], case["bits"])
+            refs = oracle_decode({**case, "q": q, "mode": mode}, 300, range(B))
+            first = {}
+            for chunks in (0, 7, 1, 40, 7, 0, 40):
+                if chunks == 1:
+                    continue                                 # 1800 positions exceed one item
+                out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+                tr.tr_kv_cache_set_decode_chunks(cache, chunks)
+                tr.tr_routed_attn_decode(cache, 0, q, mode, 300, out)
+                torch.cuda.synchronize()
+                assert tr.tr_kv_cache_status(cache) == 0
+                if chunks in first:
+                    assert torch.equal(first[chunks], out), f"D={D}: a repeated call with {chunks} chunks differs"
+                else:
+                    first[chunks] = out
+                    got = bf16_to_f64(out)
+                    for s in range(B):
+                        compare_out(got[s], refs[s], f"D={D} chunks={chunks} seq {s}")
+        finally:
+            cache.close()
+
+
 def test_decode_bad_mode_is_flagged(tr):
     case = random_case(1, 20, 2, 64, window=3, bit_weights={4: 1.0}, mode_weights={"full": 1.0},
                        seed=2, device="cuda", n_queries=1)
