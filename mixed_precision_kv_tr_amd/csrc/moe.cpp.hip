@@ -322,6 +322,18 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
 // order) into double-buffered LDS, one 64-byte piece of each per thread, the next stage in
 // registers while the current one multiplies: every weight byte brought in serves 256 tokens and
 // every x byte 128 units, against 64 and 128 in k_moe_up.  Epilogue as in k_moe_up.
+// Workgroup barrier for the stage pipelines that orders LDS only: the wave's LDS accesses
+// complete, then s_barrier.  __syncthreads() also carries a workgroup-scope memory fence, which
+// waits for every global load of the wave, including the next stage's, issued a stage earlier to
+// stay in flight across the barrier.  The empty asm statements keep the compiler from moving
+// memory accesses across (the barrier builtin itself does not).
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 constexpr int kTM = 256;                 // listed tokens per tile
 constexpr int kGY = 4;                   // unit blocks per group in the work order
 
@@ -462,7 +474,11 @@ __global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x
   gl(0, ra0, rb0);
   st(0, ra0, rb0);
   __syncthreads();
+  // stage 1's loads strictly before stage 2's, as in the loop: the wait before each stage's LDS
+  // stores then leaves the later stage's loads in flight (with the two sets issued the other way
+  // round here, the compiler's wait at the loop head, valid for both orders, is a full drain)
   gl(min(1, ns - 1), ra0, rb0);
+  __builtin_amdgcn_sched_barrier(0);
   gl(min(2, ns - 1), ra1, rb1);
   // stage g sits in LDS buffer g & 1; the loop is unrolled by two so that each register set keeps
   // its registers (set 0 holds the odd stages, set 1 the even ones); loads are clamped, never
@@ -470,11 +486,11 @@ __global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x
   for (int g = 0; g < ns; g += 2) {
     compute(0);
     st(1, ra0, rb0);                                // stage g + 1
-    __syncthreads();
+    lds_barrier();
     gl(min(g + 3, ns - 1), ra0, rb0);
     compute(1);
     st(0, ra1, rb1);                                // stage g + 2 (a repeat of the last one at the end)
-    __syncthreads();
+    lds_barrier();
     gl(min(g + 4, ns - 1), ra1, rb1);
   }
   // D[token][unit]: lane (r, kh) holds unit r of its unit block for rows 8 (reg / 4) + 4 kh + reg % 4
@@ -714,16 +730,17 @@ __global__ __launch_bounds__(512) void k_moe_down_t(const uint16_t* __restrict__
     gl(0, ra0, rb0);
     st(0, ra0, rb0);
     __syncthreads();
-    gl(min(1, ns - 1), ra0, rb0);
+    gl(min(1, ns - 1), ra0, rb0);                  // in order, as in k_moe_up_t
+    __builtin_amdgcn_sched_barrier(0);
     gl(min(2, ns - 1), ra1, rb1);
     for (int g = 0; g < ns; g += 2) {
       compute(0);
       st(1, ra0, rb0);                              // stage g + 1
-      __syncthreads();
+      lds_barrier();
       gl(min(g + 3, ns - 1), ra0, rb0);
       compute(1);
       st(0, ra1, rb1);                              // stage g + 2 (a repeat of the last one at the end)
-      __syncthreads();
+      lds_barrier();
       gl(min(g + 4, ns - 1), ra1, rb1);
     }
   }
