@@ -66,6 +66,30 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
   return x;
 }
 
+// Address of row `row` (of `rb` bytes) of pool page `pg`, from `base` = the pool plus the offset of
+// the row region inside a page: two unsigned 32 x 32 -> 64-bit multiply-adds (v_mad_u64_u32), with
+// no sign extension and no zero-extended 64-bit operand.  `rb` goes through an SGPR so that a
+// power of two stays a multiply (a 64-bit shift would need the row zero-extended first), and the
+// result is a global-memory pointer (a generic one would make the loads flat loads, which also
+// count against the LDS wait counter).
+typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
+__device__ __forceinline__ gbytes_t page_row(uint64_t base, uint32_t page_bytes, int32_t pg, int row, uint32_t rb) {
+  return (gbytes_t)((uint64_t)(uint32_t)row * opaque_s(rb) + ((uint64_t)(uint32_t)pg * page_bytes + base));
+}
+// Page id of class slot j from the chunk's page list `pg` (whose entry 0 is page `first` of the class):
+// the list's LDS byte address minus 4 * first is a wave-uniform base, so the lookup costs a shift
+// and one v_lshl_add_u32 per lane.
+__device__ __forceinline__ uint32_t pg_base(const int32_t* pg, int first) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int32_t*)pg - 4u * (uint32_t)first;
+}
+__device__ __forceinline__ int32_t page_of(uint32_t pgb, int j, int lp) {
+  return *(const __attribute__((address_space(3))) int32_t*)(uintptr_t)((((uint32_t)j >> lp) << 2) + pgb);
+}
+template <typename T>
+__device__ __forceinline__ T gload(gbytes_t p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
 __device__ __forceinline__ f32x4 mma_f16(const uint32_t* a, const uint32_t* b, f32x4 acc) {
   const u32x4 av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv), acc, 0,
@@ -307,36 +331,35 @@ __device__ __forceinline__ void p1_load(const CacheLayout& c, const Smem<D, GB>&
   using K = Cls<D, C>;
   const int lane = threadIdx.x, kr = lane & 15, g = lane >> 4;
   const int lp = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
-  const int64_t code_off = c.k_off[C] + (int64_t)h * c.cb + g * (K::RB / 4);
-  const int64_t sk_off = c.sk_off[C] + (int64_t)h * P * 8, sv_off = c.sv_off[C] + (int64_t)h * P * 8;
-  const int32_t* pg = sm.pg[C];
+  const uint64_t pool = (uint64_t)c.pool;
+  const uint32_t pbytes = (uint32_t)c.page_bytes;
+  const uint64_t code_base = pool + (uint32_t)(c.k_off[C] + h * c.cb + g * (K::RB / 4));
+  const uint64_t sk_base = pool + (uint32_t)(c.sk_off[C] + h * P * 8), sv_base = pool + (uint32_t)(c.sv_off[C] + h * P * 8);
+  const uint32_t pgb = pg_base(sm.pg[C], first);
   if constexpr (C < 3) {
 #pragma unroll
     for (int i = 0; i < K::NS; ++i) {
       const int j = min(base + 64 * i + lane, e - 1);
-      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
-      const int row = j & pm;
-      const u32x2 kz = *reinterpret_cast<const u32x2*>(pb + sk_off + (int64_t)row * 8);
+      const int32_t page = page_of(pgb, j, lp);
+      const u32x2 kz = gload<u32x2>(page_row(sk_base, pbytes, page, j & pm, 8u));
       bt.sk[i] = __uint_as_float(kz[0]);
       bt.zk[i] = __uint_as_float(kz[1]);
-      bt.sv[i] = *reinterpret_cast<const float*>(pb + sv_off + (int64_t)row * 8);
+      bt.sv[i] = gload<float>(page_row(sv_base, pbytes, page, j & pm, 8u));
     }
   }
 #pragma unroll
   for (int u = 0; u < K::U; ++u) {
     const int j = min(base + 16 * u + kr, e - 1);
-    const uint8_t* pb = c.pool + (int64_t)pg[(j >> lp) - first] * c.page_bytes;
-    const int row = j & pm;
-    const uint8_t* src = pb + code_off + (int64_t)row * K::RB;
+    const gbytes_t src = page_row(code_base, pbytes, page_of(pgb, j, lp), j & pm, (uint32_t)K::RB);
     if constexpr (K::NWK == 1) {
-      bt.w[u][0] = *reinterpret_cast<const uint32_t*>(src);
+      bt.w[u][0] = gload<uint32_t>(src);
     } else if constexpr (K::NWK == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(src);
-      bt.w[u][0] = v.x; bt.w[u][1] = v.y;
+      const u32x2 v = gload<u32x2>(src);
+      bt.w[u][0] = v[0]; bt.w[u][1] = v[1];
     } else {
 #pragma unroll
       for (int x = 0; x < K::NWK / 4; ++x) {
-        const u32x4 v = reinterpret_cast<const u32x4*>(src)[x];
+        const u32x4 v = gload<u32x4>(src + 16 * x);
         bt.w[u][4 * x] = v[0]; bt.w[u][4 * x + 1] = v[1]; bt.w[u][4 * x + 2] = v[2]; bt.w[u][4 * x + 3] = v[3];
       }
     }
@@ -345,10 +368,10 @@ __device__ __forceinline__ void p1_load(const CacheLayout& c, const Smem<D, GB>&
 
 // Phase 1 for width class C over class slots [a, e): scores into sc[n * SCAP + off + (j - a)].
 // `cur` holds the loads of the first batch (slots from a), issued by the caller.
-template <int D, int GB, int C>
+template <int D, int GB, int C, typename Next>
 __device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, int first, int h, int a, int e, int off,
                                        int ncol, float kscale, float (&mrun)[(GB + 3) / 4], float& vmax,
-                                       P1Batch<D, C> cur) {
+                                       P1Batch<D, C> cur, Next&& next) {
   using K = Cls<D, C>;
   constexpr int KS = D / 32;
   constexpr int NCL = (GB + 3) / 4;
@@ -447,24 +470,67 @@ __device__ __forceinline__ void phase1(const CacheLayout& c, Smem<D, GB>& sm, in
       }
     }
   };
-  // The next batch's loads are always issued (clamped into the range) before the current one is
-  // computed, so they stay in flight during its products; the batches rotate by value (see
-  // phase 2).
+  // The next batch's loads are issued before the current one is computed, so they stay in flight
+  // during its products; the last batch is peeled off and runs with `next()`'s loads in flight (the
+  // first loads of the next class or phase).  The batches rotate by value (see phase 2).
   P1Batch<D, C> nxt;
-  for (int base = a;;) {
+  int base = a;
+  for (; base + 16 * U < e; base += 16 * U) {
     p1_load<D, GB, C>(c, sm, first, h, e, base + 16 * U, nxt);
     compute(cur, base);
-    base += 16 * U;
-    if (base >= e) break;
     cur = nxt;
+  }
+  next();
+  compute(cur, base);
+}
+
+// A phase-2 tile: the 16-byte code pieces of TK keys' V rows (NPL per lane) and, in lane j, key j's
+// V scale and zero.
+template <int D, int C>
+struct P2Tile {
+  u32x4 pc[Cls<D, C>::NPL];
+  float sz[2];
+};
+
+// Issues the loads of the phase-2 tile of class C that starts at class slot tb (of the slots
+// [., e) whose pages are listed in sm.pg[C] from page `first` on), indices clamped into the range.
+template <int D, int GB, int C>
+__device__ __forceinline__ void p2_load(const CacheLayout& c, const Smem<D, GB>& sm, int first, int h, int e, int tb,
+                                        P2Tile<D, C>& tl) {
+  using K = Cls<D, C>;
+  constexpr int TK = K::TK;
+  const int lane = threadIdx.x;
+  const int lpg = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
+  const uint64_t pool = (uint64_t)c.pool;
+  const uint32_t pbytes = (uint32_t)c.page_bytes;
+  const uint32_t pgb = pg_base(sm.pg[C], first);
+#pragma unroll
+  for (int x = 0; x < K::NPL; ++x) {
+    const int pcx = lane + 64 * x;
+    const int key = min(pcx / K::PPR, TK - 1), part = pcx % K::PPR;
+    const int j = min(tb + key, e - 1);
+    const uint64_t code_base = pool + (uint32_t)(c.v_off[C] + h * c.cb + 16 * part);
+    tl.pc[x] = gload<u32x4>(page_row(code_base, pbytes, page_of(pgb, j, lpg), j & pm, (uint32_t)K::RB));
+  }
+  if constexpr (C < 3) {
+    const uint64_t sv_base = pool + (uint32_t)(c.sv_off[C] + h * P * 8);
+    const int j = min(tb + min(lane, TK - 1), e - 1);
+    const u32x2 w = gload<u32x2>(page_row(sv_base, pbytes, page_of(pgb, j, lpg), j & pm, 8u));
+    tl.sz[0] = __uint_as_float(w[0]);
+    tl.sz[1] = __uint_as_float(w[1]);
+  } else {
+    tl.sz[0] = 1.0f;
+    tl.sz[1] = 0.0f;
   }
 }
 
-// Phase 2 for width class C over class slots [a, e): acc += V^T P'^T in units of 2^tau.
-template <int D, int GB, int C>
+// Phase 2 for width class C over class slots [a, e): acc += V^T P'^T in units of 2^tau.  `cur` holds
+// the loads of the first tile (slots from a), issued by the caller; the last tile's products run
+// with `next()`'s loads in flight (the first tile of the next class) instead of another tile's.
+template <int D, int GB, int C, typename Next>
 __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, int first, int h, int a, int e, int off,
                                        int ncol, float tsc, f32x4 (&acc)[D / 16], float (&lp)[GB], float (&zp)[GB],
-                                       float (&cp)[GB]) {
+                                       float (&cp)[GB], P2Tile<D, C> cur, Next&& next) {
   using K = Cls<D, C>;
   constexpr int NT = D / 16;
   constexpr int SCAP = Smem<D, GB>::SCAP;
@@ -473,10 +539,6 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
   constexpr bool SP = C == 0 && !Smem<D, GB>::kOdLds;
   constexpr int TK = K::TK, RS = SP ? 2 * K::RB + 16 : K::RS;
   const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
-  const int lpg = c.ptok_log2[C], pm = c.ptok[C] - 1, P = c.ptok[C];
-  const int64_t code_off = c.v_off[C] + (int64_t)h * c.cb;
-  const int64_t sv_off = c.sv_off[C] + (int64_t)h * P * 8;
-  const int32_t* pg = sm.pg[C];
   const uint32_t KK = opaque_v(kF16K);
   const uint32_t m40 = opaque_s(0x000f000fu), m41 = opaque_s(0x00f000f0u);
   const uint32_t m20 = opaque_s(0x00030003u), m21 = opaque_s(0x00300030u), m22 = opaque_s(0x03000300u);
@@ -489,30 +551,7 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
   else if constexpr (C == 2) tro = (8 * g + (r >> 1)) * RS + 8 * (r & 1);   // tr8: key 8 g + r / 2
   else tro = (4 * g + (r >> 2)) * RS + 8 * (r & 3);                         // tr16: key 4 g + r / 4
 
-  struct Tile {
-    u32x4 pc[K::NPL];
-    float sz[2];
-  };
-  auto load = [&](Tile& tl, int tb) {
-#pragma unroll
-    for (int x = 0; x < K::NPL; ++x) {
-      const int pcx = lane + 64 * x;
-      const int key = min(pcx / K::PPR, TK - 1), part = pcx % K::PPR;
-      const int j = min(tb + key, e - 1);
-      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lpg) - first] * c.page_bytes;
-      tl.pc[x] = *reinterpret_cast<const u32x4*>(pb + code_off + (int64_t)(j & pm) * K::RB + 16 * part);
-    }
-    if constexpr (C < 3) {
-      const int j = min(tb + min(lane, TK - 1), e - 1);
-      const uint8_t* pb = c.pool + (int64_t)pg[(j >> lpg) - first] * c.page_bytes;
-      const u32x2 w = *reinterpret_cast<const u32x2*>(pb + sv_off + (int64_t)(j & pm) * 8);
-      tl.sz[0] = __uint_as_float(w[0]);
-      tl.sz[1] = __uint_as_float(w[1]);
-    } else {
-      tl.sz[0] = 1.0f;
-      tl.sz[1] = 0.0f;
-    }
-  };
+  using Tile = P2Tile<D, C>;
   // One tile from tb, with its rows and V side data already in registers.
   auto run = [&](const Tile& cur, int tb) {
     // stage the tile's rows
@@ -644,19 +683,21 @@ __device__ __forceinline__ void phase2(const CacheLayout& c, Smem<D, GB>& sm, in
     }
     wave_lds_sync();                               // the tile and P' are rewritten next
   };
-  // The next tile's loads are always issued (clamped into the range) before the current one is
-  // staged and computed, so they stay in flight during its products.  The tiles rotate by value:
-  // two tiles used in turn through one loop body would be addressed through a pointer, which keeps
-  // them out of registers (in scratch memory, one more round trip per tile).
-  Tile cur, nxt;
-  load(cur, a);
-  for (int tb = a;;) {
-    load(nxt, tb + TK);
+  // The next tile's loads are issued before the current one is staged and computed, so they stay
+  // in flight during its products; the last tile is peeled off, and the next class's first loads
+  // go out in its place (a branch between the two kinds of loads in one body would make the wait
+  // counts of every tile assume the smaller of the two).  The tiles rotate by value: two tiles
+  // used in turn through one loop body would be addressed through a pointer, which keeps them out
+  // of registers (in scratch memory, one more round trip per tile).
+  Tile nxt;
+  int tb = a;
+  for (; tb + TK < e; tb += TK) {
+    p2_load<D, GB, C>(c, sm, first, h, e, tb + TK, nxt);
     run(cur, tb);
-    tb += TK;
-    if (tb >= e) break;
     cur = nxt;
   }
+  next();
+  run(cur, tb);
 }
 
 // e with vmax <= 2^e (0 for vmax = 0): the P' normalization of a class set.
@@ -1036,21 +1077,49 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   for (int i = 0; i < NCL; ++i) mrun[i] = -INFINITY;
   float vm[3] = {0.0f, 0.0f, 0.0f};
   float vdummy = 0.0f;
-  if (e[0] > a[0]) phase1<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, kscale, mrun, vm[0], b0);
-  if (e[1] > a[1]) {
+  // One load pipeline across the classes and the two phases (one column per item): the last batch
+  // (tile) of a class is computed with the first loads of the next non-empty class in flight -- of
+  // phase 2's first class after phase 1's last -- so only a class that follows an empty one starts
+  // cold.  Blocks of query heads load each class's first batch on entry: their registers would
+  // not hold both (184 instead of 164, two waves per SIMD instead of three).
+  constexpr bool kChain = GB == 1;
+  const bool nz[4] = {e[0] > a[0], e[1] > a[1], e[2] > a[2], e[3] > a[3]};
+  const int lastnz = nz[3] ? 3 : nz[2] ? 2 : nz[1] ? 1 : 0;
+  P1Batch<D, 2> b2;
+  P1Batch<D, 3> b3;
+  P2Tile<D, 0> t0;
+  P2Tile<D, 1> t1;
+  P2Tile<D, 2> t2;
+  P2Tile<D, 3> t3;
+  auto load_t0 = [&] {
+    if (kChain && nz[0]) p2_load<D, GB, 0>(c, sm, first[0], hk, e[0], a[0], t0);
+  };
+  if (nz[0])
+    phase1<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, kscale, mrun, vm[0], b0, [&] {
+      if (!nz[1] && lastnz == 0) load_t0();          // (class 1's first batch went out with class 0's)
+    });
+  if (nz[1]) {
     if (!kEarly1) p1_load<D, GB, 1>(c, sm, first[1], hk, e[1], a[1], b1);
-    phase1<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, kscale, mrun, vm[1], b1);
+    phase1<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, kscale, mrun, vm[1], b1, [&] {
+      if constexpr (kChain) {
+        if (nz[2]) p1_load<D, GB, 2>(c, sm, first[2], hk, e[2], a[2], b2);
+        else if (lastnz == 1) load_t0();
+      }
+    });
   }
   __builtin_amdgcn_s_setprio(2);
-  if (e[2] > a[2]) {
-    P1Batch<D, 2> b2;
-    p1_load<D, GB, 2>(c, sm, first[2], hk, e[2], a[2], b2);
-    phase1<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, kscale, mrun, vm[2], b2);
+  if (nz[2]) {
+    if (!(kChain && nz[1])) p1_load<D, GB, 2>(c, sm, first[2], hk, e[2], a[2], b2);
+    phase1<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, kscale, mrun, vm[2], b2, [&] {
+      if constexpr (kChain) {
+        if (nz[3]) p1_load<D, GB, 3>(c, sm, first[3], hk, e[3], a[3], b3);
+        else load_t0();
+      }
+    });
   }
-  if (e[3] > a[3]) {
-    P1Batch<D, 3> b3;
-    p1_load<D, GB, 3>(c, sm, first[3], hk, e[3], a[3], b3);
-    phase1<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, kscale, mrun, vdummy, b3);
+  if (nz[3]) {
+    if (!(kChain && nz[2])) p1_load<D, GB, 3>(c, sm, first[3], hk, e[3], a[3], b3);
+    phase1<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, kscale, mrun, vdummy, b3, load_t0);
   }
   // column maxima: lanes of group g hold columns 4 i + g
 #pragma unroll
@@ -1074,7 +1143,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   if (e[0] > a[0]) {
 #pragma unroll
     for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    phase2<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, ldexpf(1.0f, -e0), acc, lp, zp, cp);
+    if constexpr (!kChain) p2_load<D, GB, 0>(c, sm, first[0], hk, e[0], a[0], t0);
+    phase2<D, GB, 0>(c, sm, first[0], hk, a[0], e[0], off[0], ncol, ldexpf(1.0f, -e0), acc, lp, zp, cp, t0, [&] {
+      if (kChain && nz[1]) p2_load<D, GB, 1>(c, sm, first[1], hk, e[1], a[1], t1);
+    });
     float cr = 0.0f;
 #pragma unroll
     for (int n = 0; n < GB; ++n) {
@@ -1110,10 +1182,23 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
     for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   const float tm = ldexpf(1.0f, -em);
-  if (e[1] > a[1]) phase2<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, tm, acc, lp, zp, cp);
+  if (nz[1]) {
+    if (!(kChain && nz[0])) p2_load<D, GB, 1>(c, sm, first[1], hk, e[1], a[1], t1);
+    phase2<D, GB, 1>(c, sm, first[1], hk, a[1], e[1], off[1], ncol, tm, acc, lp, zp, cp, t1, [&] {
+      if (kChain && nz[2]) p2_load<D, GB, 2>(c, sm, first[2], hk, e[2], a[2], t2);
+    });
+  }
   __builtin_amdgcn_s_setprio(0);
-  if (e[2] > a[2]) phase2<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, tm, acc, lp, zp, cp);
-  if (e[3] > a[3]) phase2<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, tm, acc, lp, zp, cp);
+  if (nz[2]) {
+    if (!(kChain && nz[1])) p2_load<D, GB, 2>(c, sm, first[2], hk, e[2], a[2], t2);
+    phase2<D, GB, 2>(c, sm, first[2], hk, a[2], e[2], off[2], ncol, tm, acc, lp, zp, cp, t2, [&] {
+      if (kChain && nz[3]) p2_load<D, GB, 3>(c, sm, first[3], hk, e[3], a[3], t3);
+    });
+  }
+  if (nz[3]) {
+    if (!(kChain && nz[2])) p2_load<D, GB, 3>(c, sm, first[3], hk, e[3], a[3], t3);
+    phase2<D, GB, 3>(c, sm, first[3], hk, a[3], e[3], off[3], ncol, tm, acc, lp, zp, cp, t3, [] {});
+  }
   wave_lds_sync();
 
   // epilogue: lane (column r, group g) holds channels 16 m + 4 g + i of column r
@@ -1177,7 +1262,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(TR_DECODE
   // With one column per item, the wave that completes a group's last chunk merges the group's
   // records itself: each wave's records are performed at agent scope before it counts its chunk
   // in the group's counter, and the wave that brings the count to nch reads them all back with
-  // agent-coherent loads and returns the counter to zero for the next call.
+  // agent-coherent loads and returns the counter to zero for the next call.  (Blocks of query
+  // heads merge in a launch of their own: one wave merging a block's columns one after another
+  // ended the launch later than that launch takes.)
   if constexpr (GB == 1) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     int prev = 0;
