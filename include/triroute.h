@@ -53,7 +53,7 @@ typedef enum {
   TR_ERR_HIP = 4,           /* a HIP runtime call failed (allocation, launch, copy) */
   TR_ERR_UNSUPPORTED = 5,   /* a valid but unsupported shape (head_dim not 64/128, ...) */
   TR_ERR_BAD_VALUE = 6,     /* sticky: a bits or mode element outside its domain was seen */
-  TR_ERR_RANGE = 7,         /* sticky: prefill met a stored V value with |v_hat| >= 65504 */
+  TR_ERR_RANGE = 7,         /* sticky: a value outside fp16's range (prefill's v_hat, the expert FFN) */
   TR_ERR_SCRATCH = 8        /* tr_routed_attn_decode_noalloc: the call needs more scratch than
                                its fixed array holds (nothing launched) */
 } tr_status;
@@ -268,10 +268,13 @@ tr_status tr_controller_route(const tr_controller_weights* w, const void* x, con
  *   FFN_t = sum_{j in S_t} p_tj / sum_{j' in S_t} p_tj' * f_j(RMSNorm(x_t)),  p_t = softmax(z_t),
  * over E experts plus the null expert f_0 = 0 (gate index 0), S_t the top_k largest p_t (ties to
  * the lower index), each expert a SwiGLU FFN f(u) = W2 (silu(W1 u) * (W3 u)) with no biases.
- * Products run on the matrix cores with bf16 operands and fp32 accumulation: x and the weights
- * exactly (the RMSNorm scale applied to the fp32 sums), the hidden activation as a bf16 pair
- * hi + lo (about 16 significant bits).   The gate logits come from the caller (e.g. an expert head
- * of the controller, Eq. (5)).  A handle owns the packed weights and the scratch of calls up to
+ * Products run on the matrix cores with fp32 accumulation: the gate and up products on bf16 x and
+ * W1, W3 exactly (the RMSNorm scale applied to the fp32 sums); the down product on fp16 operands,
+ * W2 rounded to fp16 once (exact for bf16 weights of magnitude 2^-14 .. 65504) and the hidden
+ * activation rounded to fp16 (11 significant bits).  A weight of W2 or a hidden value beyond fp16's
+ * range (|v| > 65504) sets the sticky TR_ERR_RANGE flag (tr_moe_status) and leaves the output
+ * unspecified.  The gate logits come from the caller (e.g. an expert head of the controller,
+ * Eq. (5)).  A handle owns the packed weights and the scratch of calls up to
  * max_tokens tokens. */
 typedef struct {
   int32_t d;                /* model width: a multiple of 128, 128 .. 16384 */
@@ -302,6 +305,11 @@ tr_status tr_moe_set_weights(tr_moe* moe, const void* w_gate, const void* w_up, 
  *   y:           float [n_tokens, d] receives FFN_t (a token whose choices are all the null
  *                expert gets zeros).  Deterministic: no atomics. */
 tr_status tr_moe_ffn(tr_moe* moe, const void* x, const float* gate_logits, int32_t n_tokens, float* y, void* stream);
+
+/* Sticky device flags of the handle, after synchronizing `stream`: TR_ERR_RANGE if a set_weights
+ * or ffn call met a value outside fp16's range (see above), else TR_OK.  The flags persist for the
+ * handle's lifetime. */
+tr_status tr_moe_status(tr_moe* moe, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* tr_status_str(tr_status status);

@@ -14,7 +14,7 @@ _EXPORTS = (
     "tr_kv_cache_status", "tr_kv_cache_pages_used", "tr_status_str", "tr_kv_cache_truncate",
     "tr_kv_cache_set_decode_chunks", "tr_routed_attn_decode_noalloc",
     "tr_profile_enable", "tr_profile_read", "PROFILE_FAMILIES", "tr_controller_route",
-    "ControllerWeights", "MoE", "tr_moe_alloc", "tr_moe_set_weights", "tr_moe_ffn",
+    "ControllerWeights", "MoE", "tr_moe_alloc", "tr_moe_set_weights", "tr_moe_ffn", "tr_moe_status",
 )
 
 __all__ = list(_EXPORTS)

@@ -67,6 +67,7 @@ _moe_alloc = _sig("tr_moe_alloc", ctypes.c_int, ctypes.POINTER(_MoeDesc), ctypes
 _moe_free = _sig("tr_moe_free", ctypes.c_int, _vp)
 _moe_set = _sig("tr_moe_set_weights", ctypes.c_int, _vp, _vp, _vp, _vp, _vp)
 _moe_ffn = _sig("tr_moe_ffn", ctypes.c_int, _vp, _vp, _vp, _i32, _vp, _vp)
+_moe_status = _sig("tr_moe_status", ctypes.c_int, _vp, _vp)
 _set_chunks = _sig("tr_kv_cache_set_decode_chunks", ctypes.c_int, _vp, _i32)
 _prof_enable = _sig("tr_profile_enable", ctypes.c_int, _vp, _i32)
 _prof_read = _sig("tr_profile_read", ctypes.c_int, _vp, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double))
@@ -277,6 +278,11 @@ def tr_moe_set_weights(moe: MoE, w_gate, w_up, w_down, stream=None):
 
 def tr_moe_ffn(moe: MoE, x, gate_logits, n_tokens: int, y, stream=None):
     _check(_moe_ffn(moe.handle, _ptr(x), _ptr(gate_logits), int(n_tokens), _ptr(y), _stream(stream)), "tr_moe_ffn")
+
+
+def tr_moe_status(moe: MoE, stream=None) -> int:
+    """Synchronizes and returns the handle's sticky status code (0 = ok); does not raise."""
+    return int(_moe_status(moe.handle, _stream(stream)))
 
 
 def tr_profile_enable(cache: KVCache, enable: bool = True):

@@ -11,11 +11,11 @@
 //   k_moe_up      one workgroup per (slot, expert, 32 or 64 listed tokens, 128 hidden units): the gate
 //                 and up products on the matrix cores (x rows gathered from the list, bf16 x and
 //                 packed bf16 W1 / W3 as exact operands, fp32 accumulation), then the RMSNorm
-//                 scale, silu(g) * u, stored into the hidden buffer as a bf16 pair: hi = bf16(h)
-//                 and lo = bf16(h - hi), together h to about 2^-16 relative.
+//                 scale, silu(g) * u, stored into the hidden buffer in fp16 (11 significant bits;
+//                 an |h| beyond fp16's range sets the sticky TR_ERRF_RANGE flag).
 //   k_moe_down    per slot, in slot order: one workgroup per (expert, 32 or 64 listed tokens, 128 output
-//                 channels): the down product of the gathered hidden rows (hi and lo halves
-//                 against the same weights, both on the matrix cores), times the token's
+//                 channels): the down product of the gathered fp16 hidden rows against the fp16
+//                 copy of W2 (packed once; exact for bf16 weights in fp16's range), times the token's
 //                 weight, stored (slot 0; the null expert stores zeros) or added (slot 1) into the
 //                 fp32 output -- no atomics, so the result does not depend on scheduling.
 // Weight matrices are packed once (tr_moe_set_weights) into the operand order of the matrix-core
@@ -41,13 +41,15 @@ struct tr_moe {
   float* inv_rms;    // [max_tokens]
   int32_t* lists;    // [k][E + 1][max_tokens] tokens per (slot, expert), in token order
   int32_t* counts;   // [k][E + 1]
-  uint16_t* hbuf;    // [max_tokens * k][2][de] bf16 hidden rows (row t * k + slot): hi, then lo
+  uint16_t* hbuf;    // [max_tokens * k][de] fp16 hidden rows (row t * k + slot)
+  uint32_t* err;     // sticky TR_ERRF_* flags
   bool weights_set;
 };
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Token tiles of 32 * MB listed tokens: each wave computes its 32 units for MB 32-token blocks,
@@ -65,14 +67,29 @@ __device__ __forceinline__ uint4 gload16(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// fp16 bits of x (round to nearest even); an |x| beyond fp16's range (an infinity after rounding,
+// or a NaN) sets TR_ERRF_RANGE in *err.
+__device__ __forceinline__ uint16_t f16_checked(float x, uint32_t* err) {
+  const _Float16 v = (_Float16)x;
+  if (!(fabsf((float)v) <= 65504.0f)) atomicOr(err, TR_ERRF_RANGE);
+  return __builtin_bit_cast(uint16_t, v);
+}
+
+__device__ __forceinline__ f32x16 mfma_f16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
 __device__ __forceinline__ f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
 }
 
 // Pack E matrices [units][K] (out x in) into the k-step operand order [K / 16][units][16].
+// to_f16: the packed copy holds the fp16 rounding of each bf16 weight (exact in fp16's normal
+// range; a weight beyond fp16's range sets TR_ERRF_RANGE).
 __global__ __launch_bounds__(256) void k_moe_pack(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                  int units, int K, int E) {
+                                                  int units, int K, int E, int to_f16, uint32_t* __restrict__ err) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per = (int64_t)(K / 16) * units * 2;
   if (i >= per * E) return;
@@ -81,8 +98,15 @@ __global__ __launch_bounds__(256) void k_moe_pack(const uint16_t* __restrict__ s
   const int h = (int)(r & 1), n = (int)((r >> 1) % units), s = (int)((r >> 1) / units);
   const int g = s >> 2, j = s & 3;
   const int64_t mat = (int64_t)units * K;
-  *reinterpret_cast<uint4*>(dst + e * mat + ((int64_t)s * units + n) * 16 + 8 * h) =
-      *reinterpret_cast<const uint4*>(src + e * mat + (int64_t)n * K + 64 * g + 32 * h + 8 * j);
+  uint4 v = *reinterpret_cast<const uint4*>(src + e * mat + (int64_t)n * K + 64 * g + 32 * h + 8 * j);
+  if (to_f16) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)f16_checked(tr_bf16_lo(w[q]), err) | ((uint32_t)f16_checked(tr_bf16_hi(w[q]), err) << 16);
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  *reinterpret_cast<uint4*>(dst + e * mat + ((int64_t)s * units + n) * 16 + 8 * h) = v;
 }
 
 // One wave per token.
@@ -224,7 +248,7 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
                                                 const int32_t* __restrict__ counts, const float* __restrict__ inv_rms,
                                                 const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
                                                 uint16_t* __restrict__ hbuf, int d, int de, int E, int k, int cap,
-                                                int ntiles) {
+                                                int ntiles, uint32_t* __restrict__ err) {
   constexpr int kTile = 32 * kMB;
   __shared__ int32_t tok[kTile];
   __shared__ float inv[kTile];
@@ -307,10 +331,7 @@ __global__ __launch_bounds__(256) void k_moe_up(const uint16_t* __restrict__ x, 
       if (row < ntok) {
         const float gv = ag[mb][reg] * inv[row], uv = au[mb][reg] * inv[row];
         const float h = gv / (1.0f + expf(-gv)) * uv;
-        const uint16_t hi = tr_f32_to_bf16(h);
-        uint16_t* hr = hbuf + ((int64_t)tok[row] * k + slot) * 2 * de + n;
-        hr[0] = hi;
-        hr[de] = tr_f32_to_bf16(h - tr_bf16_lo(hi));
+        hbuf[((int64_t)tok[row] * k + slot) * de + n] = f16_checked(h, err);
       }
     }
   }
@@ -387,7 +408,7 @@ __global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x
                                                   const int32_t* __restrict__ counts,
                                                   const float* __restrict__ inv_rms, const uint16_t* __restrict__ wg,
                                                   const uint16_t* __restrict__ wu, uint16_t* __restrict__ hbuf, int d,
-                                                  int de, int E, int k, int cap) {
+                                                  int de, int E, int k, int cap, uint32_t* __restrict__ err) {
   __shared__ int32_t tok[kTM];
   __shared__ float inv[kTM];
   __shared__ __align__(16) uint8_t As[2][kTM * kAP];
@@ -505,10 +526,7 @@ __global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x
           const int n = ublk * kTN + 64 * uw + 32 * ub + r;
           const float gv = acc[0][tb][ub][reg] * inv[row], uv = acc[1][tb][ub][reg] * inv[row];
           const float h = gv / (1.0f + expf(-gv)) * uv;
-          const uint16_t hi = tr_f32_to_bf16(h);
-          uint16_t* hr = hbuf + ((int64_t)tok[row] * k + slot) * 2 * de + n;
-          hr[0] = hi;
-          hr[de] = tr_f32_to_bf16(h - tr_bf16_lo(hi));
+          hbuf[((int64_t)tok[row] * k + slot) * de + n] = f16_checked(h, err);
         }
       }
 }
@@ -546,9 +564,8 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
     constexpr int PR = 2 * kPS;
     static_assert(kTile * PR == 256, "one piece per thread per stage");
     __shared__ uint4 hs[2][kTile][PR + 1];
-    __shared__ uint4 hl[2][kTile][PR + 1];        // the lo halves
     const int prow = tid / PR, pp = tid % PR;
-    const uint16_t* hrow = hbuf + ((int64_t)tok[prow] * k + slot) * 2 * de + 32 * (pp & 1);
+    const uint16_t* hrow = hbuf + ((int64_t)tok[prow] * k + slot) * de + 32 * (pp & 1);
     auto haddr = [&](int st) {
       const int s = st + (pp >> 1);
       return hrow + 64 * (s >> 2) + 8 * (s & 3);
@@ -562,25 +579,21 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
       for (int q = 0; q < kPS; ++q) wv[q] = gload16(dr + (st + q) * wstep);
     };
     hs[0][prow][pp] = gload16(haddr(0));
-    hl[0][prow][pp] = gload16(haddr(0) + de);
     wload(0, wa);
     __syncthreads();
     int buf = 0;
     for (int st = 0; st < ns; st += kPS) {
       const int nx = min(st + kPS, ns - kPS);
       const uint4 hn = gload16(haddr(nx));
-      const uint4 hln = gload16(haddr(nx) + de);
       uint4 wn[kPS];
       wload(nx, wn);
 #pragma unroll
       for (int q = 0; q < kPS; ++q)
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-          acc[mb] = mfma(hs[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
-          acc[mb] = mfma(hl[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
+          acc[mb] = mfma_f16(hs[buf][32 * mb + r][2 * q + kh], wa[q], acc[mb]);
         }
       hs[buf ^ 1][prow][pp] = hn;
-      hl[buf ^ 1][prow][pp] = hln;
 #pragma unroll
       for (int q = 0; q < kPS; ++q) wa[q] = wn[q];
       buf ^= 1;
@@ -604,11 +617,10 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
 
 // Down product of one slot on a tile of 128 listed tokens x 256 output channels (large calls, d a
 // multiple of 256): 8 waves, each 64 tokens x 64 channels.  Per stage of 64 hidden channels the
-// workgroup loads the tile's hidden rows (hi and lo planes, 16-byte-padded rows) and the weight
-// block (in its packed k-step order) into double-buffered LDS, one 64-byte piece of each per
-// thread, the next two stages in registers: every weight byte brought in serves 128 tokens and
-// every hidden byte 256 channels, against 64 and 128 in k_moe_down.  Both planes multiply the
-// same weights into one accumulator.  Epilogue as in k_moe_down.
+// workgroup loads the tile's fp16 hidden rows (16-byte-padded rows; 32 bytes per thread) and the
+// fp16 weight block (in its packed k-step order; 64 bytes per thread) into double-buffered LDS,
+// the next two stages in registers: every weight byte brought in serves 128 tokens and every
+// hidden byte 256 channels, against 64 and 128 in k_moe_down.  Epilogue as in k_moe_down.
 constexpr int kDM = 128;                 // listed tokens per tile
 constexpr int kDN = 256;                 // output channels per tile
 constexpr int kDBS = 4 * kDN * 32;       // LDS bytes of one stage's B tile: [k-step][channel][16]
@@ -650,7 +662,7 @@ __global__ __launch_bounds__(512) void k_moe_down_t(const uint16_t* __restrict__
                                                     int E, int k, int cap, int slot) {
   __shared__ int32_t tok[kDM];
   __shared__ float wgt[kDM];
-  __shared__ __align__(16) uint8_t As[2][2][kDM * kAP];      // [buffer][hi, lo][row]
+  __shared__ __align__(16) uint8_t As[2][kDM * kAP];         // [buffer][row]
   __shared__ __align__(16) uint8_t Bs[2][kDBS];
   int e = 0, tile = 0, cnt = 0, cblk = 0;
   const int nitems = down_item(counts, E, slot, d / kDN, -1, e, tile, cnt, cblk);
@@ -670,36 +682,34 @@ __global__ __launch_bounds__(512) void k_moe_down_t(const uint16_t* __restrict__
   f32x16 acc[2][2] = {};                            // [token block][channel block]
   if (e > 0) {
     // this thread's pieces of a stage g (hidden channels 64 g .. 64 g + 63):
-    //   A: row tid / 4, plane (tid / 2) % 2, channels 32 (tid % 2) .. + 31 of the stage
+    //   A: row tid / 4, channels 16 (tid % 4) .. + 15 of the stage
     //   B: k-step 4 g + tid / 128, channels 2 (tid % 128) and + 1 of the block
-    const int arow = tid >> 2, aplane = (tid >> 1) & 1, ahalf = tid & 1;
-    const uint16_t* ha = hbuf + ((int64_t)tok[arow] * k + slot) * 2 * de + aplane * de + 32 * ahalf;
+    const int arow = tid >> 2, aq = tid & 3;
+    const uint16_t* ha = hbuf + ((int64_t)tok[arow] * k + slot) * de + 16 * aq;
     const int bc = tid >> 7, bn = 2 * (tid & 127);
     const uint16_t* wb = wd + (int64_t)(e - 1) * d * de + ((int64_t)bc * d + cblk * kDN + bn) * 16;
     const int64_t gstep = (int64_t)4 * d * 16;      // elements per stage of 4 k-steps
-    uint4 ra0[4], rb0[4], ra1[4], rb1[4];
-    auto gl = [&](int g, uint4 (&ra)[4], uint4 (&rb)[4]) {
+    uint4 ra0[2], rb0[4], ra1[2], rb1[4];
+    auto gl = [&](int g, uint4 (&ra)[2], uint4 (&rb)[4]) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ra[q] = gload16(ha + 64 * g + 8 * q);
-        rb[q] = gload16(wb + g * gstep + 8 * q);
-      }
+      for (int q = 0; q < 2; ++q) ra[q] = gload16(ha + 64 * g + 8 * q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rb[q] = gload16(wb + g * gstep + 8 * q);
     };
-    auto st = [&](int b, const uint4 (&ra)[4], const uint4 (&rb)[4]) {
+    auto st = [&](int b, const uint4 (&ra)[2], const uint4 (&rb)[4]) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(&As[b][arow * kAP + 32 * aq + 16 * q]) = ra[q];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<uint4*>(&As[b][aplane][arow * kAP + 64 * ahalf + 16 * q]) = ra[q];
         // channel u's two 16-byte halves swap places when bit 3 of u is set (see compute)
         const int u = bn + (q >> 1);
         *reinterpret_cast<uint4*>(&Bs[b][(bc * kDN + u) * 32 + 16 * ((q & 1) ^ ((u >> 3) & 1))]) = rb[q];
       }
     };
-    auto rd = [&](int b, int j, uint4 (&av)[2][2], uint4 (&bv)[2]) {
+    auto rd = [&](int b, int j, uint4 (&av)[2], uint4 (&bv)[2]) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-          av[tb][pl] = *reinterpret_cast<const uint4*>(&As[b][pl][(64 * tw + 32 * tb + r) * kAP + 16 * j + 64 * kh]);
+        av[tb] = *reinterpret_cast<const uint4*>(&As[b][(64 * tw + 32 * tb + r) * kAP + 16 * j + 64 * kh]);
 #pragma unroll
       for (int ub = 0; ub < 2; ++ub) {
         const int u = 64 * uw + 32 * ub + r;
@@ -708,21 +718,18 @@ __global__ __launch_bounds__(512) void k_moe_down_t(const uint16_t* __restrict__
     };
     // as in k_moe_up_t: each k-step's reads go out before the previous k-step's products
     auto compute = [&](int b) {
-      uint4 av0[2][2], bv0[2], av1[2][2], bv1[2];
+      uint4 av0[2], bv0[2], av1[2], bv1[2];
       rd(b, 0, av0, bv0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint4(&av)[2][2] = (j & 1) ? av1 : av0;
+        uint4(&av)[2] = (j & 1) ? av1 : av0;
         uint4(&bv)[2] = (j & 1) ? bv1 : bv0;
         if (j < 3) rd(b, j + 1, (j & 1) ? av0 : av1, (j & 1) ? bv0 : bv1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int ub = 0; ub < 2; ++ub) {
-            acc[tb][ub] = mfma(av[tb][0], bv[ub], acc[tb][ub]);
-            acc[tb][ub] = mfma(av[tb][1], bv[ub], acc[tb][ub]);
-          }
+          for (int ub = 0; ub < 2; ++ub) acc[tb][ub] = mfma_f16(av[tb], bv[ub], acc[tb][ub]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -790,7 +797,9 @@ tr_status tr_moe_alloc(const tr_moe_desc* desc, tr_moe** out) {
   ok = ok && hipMalloc((void**)&m->inv_rms, sizeof(float) * M) == hipSuccess;
   ok = ok && hipMalloc((void**)&m->lists, sizeof(int32_t) * K * E1 * M) == hipSuccess;
   ok = ok && hipMalloc((void**)&m->counts, sizeof(int32_t) * K * E1) == hipSuccess;
-  ok = ok && hipMalloc((void**)&m->hbuf, 2 * 2 * M * K * q.d_expert) == hipSuccess;
+  ok = ok && hipMalloc((void**)&m->hbuf, 2 * M * K * q.d_expert) == hipSuccess;
+  ok = ok && hipMalloc((void**)&m->err, sizeof(uint32_t)) == hipSuccess;
+  ok = ok && hipMemset(m->err, 0, sizeof(uint32_t)) == hipSuccess;
   if (!ok) {
     tr_moe_free(m);
     return TR_ERR_HIP;
@@ -803,7 +812,7 @@ tr_status tr_moe_free(tr_moe* m) {
   if (!m) return TR_OK;
   (void)hipDeviceSynchronize();
   for (void* p : {(void*)m->wg, (void*)m->wu, (void*)m->wd, (void*)m->sel, (void*)m->wt, (void*)m->inv_rms,
-                  (void*)m->lists, (void*)m->counts, (void*)m->hbuf})
+                  (void*)m->lists, (void*)m->counts, (void*)m->hbuf, (void*)m->err})
     if (p) (void)hipFree(p);
   delete m;
   return TR_OK;
@@ -815,11 +824,11 @@ tr_status tr_moe_set_weights(tr_moe* m, const void* w_gate, const void* w_up, co
   const int64_t per_up = (int64_t)(m->d / 16) * m->de * 2, per_dn = (int64_t)(m->de / 16) * m->d * 2;
   const unsigned gu = (unsigned)((per_up * m->E + 255) / 256), gd = (unsigned)((per_dn * m->E + 255) / 256);
   hipLaunchKernelGGL(k_moe_pack, dim3(gu), dim3(256), 0, st, static_cast<const uint16_t*>(w_gate), m->wg, m->de, m->d,
-                     m->E);
+                     m->E, 0, m->err);
   hipLaunchKernelGGL(k_moe_pack, dim3(gu), dim3(256), 0, st, static_cast<const uint16_t*>(w_up), m->wu, m->de, m->d,
-                     m->E);
+                     m->E, 0, m->err);
   hipLaunchKernelGGL(k_moe_pack, dim3(gd), dim3(256), 0, st, static_cast<const uint16_t*>(w_down), m->wd, m->d, m->de,
-                     m->E);
+                     m->E, 1, m->err);
   TR_LAUNCH_CHECK();
   m->weights_set = true;
   return TR_OK;
@@ -842,12 +851,13 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
     if (MB == 2) {
       const int tiles_up = K * ((M + kTM - 1) / kTM) + K * E;
       hipLaunchKernelGGL(k_moe_up_t, dim3(tiles_up * (m->de / kTN)), dim3(512), 0, st, static_cast<const uint16_t*>(x),
-                         m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d, m->de, E, K, m->max_tokens);
+                         m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d, m->de, E, K, m->max_tokens,
+                         m->err);
     } else {
       const int tiles_up = K * ((M + T - 1) / T) + K * E;
       hipLaunchKernelGGL(k_moe_up<MB>, dim3(tiles_up * (m->de / kUnits)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(x), m->lists, m->counts, m->inv_rms, m->wg, m->wu, m->hbuf, m->d,
-                         m->de, E, K, m->max_tokens, tiles_up);
+                         m->de, E, K, m->max_tokens, tiles_up, m->err);
     }
     if (MB == 2 && m->d % kDN == 0) {
       const int tiles_dn = (M + kDM - 1) / kDM + E + 1;
@@ -865,6 +875,14 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
   else run(std::integral_constant<int, 1>());
   TR_LAUNCH_CHECK();
   return TR_OK;
+}
+
+tr_status tr_moe_status(tr_moe* m, void* stream) {
+  if (!m) return TR_ERR_INVALID_ARG;
+  uint32_t flags = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TR_ERR_HIP;
+  if (hipMemcpy(&flags, m->err, sizeof(flags), hipMemcpyDeviceToHost) != hipSuccess) return TR_ERR_HIP;
+  return (flags & TR_ERRF_RANGE) ? TR_ERR_RANGE : TR_OK;
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@ def run(tr, c, k, n=None):
     y = torch.full((M, d), float("nan"), dtype=torch.float32, device="cuda")
     tr.tr_moe_ffn(moe, c["x"], c["z"], n, y)
     torch.cuda.synchronize()
+    assert tr.tr_moe_status(moe) == 0, "fp16 range flag set on ordinary inputs"
     moe.close()
     return y.cpu().numpy()
 
@@ -113,3 +114,26 @@ def test_moe_partial_call_and_full_size_sample(tr):
     compare_with_ties(c, 2, rows, y[rows], "1.3B-shaped, sampled tokens")
     y2 = run(tr, c, 2, n=1000)
     assert np.array_equal(y2[:1000], y[:1000]) and np.all(np.isnan(y2[1000:]))
+
+
+def test_moe_fp16_range_is_flagged(tr):
+    """The down product runs on fp16 operands: a W2 weight or a hidden value beyond fp16's range
+    (|v| > 65504) sets the handle's sticky TR_ERR_RANGE flag instead of passing silently."""
+    M, d, de, E = 64, 256, 256, 4
+    c = moe_case(M, d, de, E, seed=21, device="cuda")
+    y = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    # a W2 weight of 2^17
+    w_down = c["w_down"].clone()
+    w_down[1, 5, 7] = 131072.0
+    moe = tr.tr_moe_alloc(d, de, E, 2, M)
+    tr.tr_moe_set_weights(moe, c["w_gate"], c["w_up"], w_down)
+    assert tr.tr_moe_status(moe) == 7                                   # TR_ERR_RANGE
+    moe.close()
+    # hidden values beyond fp16's range: gate and up weights 400x larger, so silu(g) * u ~ 1e5
+    moe = tr.tr_moe_alloc(d, de, E, 2, M)
+    tr.tr_moe_set_weights(moe, (c["w_gate"].float() * 400).to(torch.bfloat16),
+                          (c["w_up"].float() * 400).to(torch.bfloat16), c["w_down"])
+    assert tr.tr_moe_status(moe) == 0
+    tr.tr_moe_ffn(moe, c["x"], c["z"], M, y)
+    assert tr.tr_moe_status(moe) == 7
+    moe.close()
