@@ -567,7 +567,8 @@ def bench_small(tr, args):
 
 # The pages' baselines as configurations of the same kernels: dense (every token stored as
 # bf16, every head attending fully), KV-quantization only (one width for every token, every
-# head full: KIVI-style), routing only (bf16 cache, routed modes) and TriRoute (both).  Same
+# head full; per-token groups like the rest of the cache, not KIVI's per-channel keys), routing
+# only (bf16 cache, routed modes) and TriRoute (both).  Same
 # shapes, windows and seeded q/k/v as the workload; only the width and mode draws change.
 BASELINE_VARIANTS = (
     ("dense_bf16", {16: 1.0}, {"full": 1.0}),

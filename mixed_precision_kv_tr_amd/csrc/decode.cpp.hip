@@ -40,6 +40,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kPgMax = TR_DECODE_PG_MAX;
 constexpr int kMinChunk = TR_DECODE_MIN_CHUNK;
+constexpr int kMergeBatch = 32;                    // chunk records a merge folds per round trip
 constexpr uint32_t kF16K = 0x64006400u;            // the fp16 pair (1024, 1024)
 constexpr uint32_t kF16B = 0x64646464u;            // byte 0x64 (fp16 1024's high byte) everywhere
 
@@ -719,7 +720,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const float* p, uint3
 // with the chunk weights broadcast from their lanes.
 template <int D>
 __device__ __forceinline__ void merge_records(__amdgpu_buffer_rsrc_t rs, int nch, uint16_t* __restrict__ dst) {
-  constexpr int KB = 32, CPL = D / 64, REC = (D + 2) * 4;
+  constexpr int KB = kMergeBatch, CPL = D / 64, REC = (D + 2) * 4;
   const int lane = threadIdx.x;
   float M = -INFINITY, den = 0.0f, num[CPL];
 #pragma unroll
@@ -1287,7 +1288,7 @@ template <int D>
 __global__ __launch_bounds__(D) void k_decode_combine(int t, int window, int CH, int stride,
                                                       const uint8_t* __restrict__ mode, const float* __restrict__ part,
                                                       uint16_t* __restrict__ out, int HQ, int G, int GB) {
-  constexpr int KB = 32;
+  constexpr int KB = kMergeBatch;
   const int sh = blockIdx.x;
   const int d = threadIdx.x, lane = d & 63;
   const int m = mode[sh];
@@ -1357,7 +1358,10 @@ int resident_waves() {
 // (seq, query head).  The kernel dispatches the items that read the cache first, so the count
 // aims at as many items as the chip holds waves at once if every group were full (fewer, longer
 // items when the groups alone fill it), but no chunk below kMinChunk positions and none above
-// the work item's limits; 0 if `limit` cannot hold the chunks a full window needs.
+// the work item's limits, and no more merge batches (kMergeBatch records each, one round trip
+// apiece at the end of the window's last chunk) than the fewest chunks need: on a 65537-position
+// window of 16 heads, 256 chunks took 65 us per launch and 128 took 47.  0 if `limit` cannot
+// hold the chunks a full window needs.
 int decode_chunks(const tr_kv_cache* c, int n, int limit) {
   const int GB = block_cols(c->grp);
   const int NB = (c->grp + GB - 1) / GB;
@@ -1372,6 +1376,8 @@ int decode_chunks(const tr_kv_cache* c, int n, int limit) {
   int nch = waves / items;
   if (nch > (n + kMinChunk - 1) / kMinChunk) nch = (n + kMinChunk - 1) / kMinChunk;
   if (nch < need) nch = need;
+  const int by_merge = (need + kMergeBatch - 1) / kMergeBatch * kMergeBatch;
+  if (nch > by_merge) nch = by_merge;
   if (nch > limit) nch = limit;
   if (nch < 1) nch = 1;
   if (c->force_chunks > 0) nch = c->force_chunks < n ? c->force_chunks : n;
