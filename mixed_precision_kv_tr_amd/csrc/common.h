@@ -54,7 +54,7 @@ struct tr_kv_cache {
 #define TR_DECODE_ITEM_MAX 544
 #define TR_DECODE_PG_MAX 36
 #ifndef TR_DECODE_MIN_CHUNK
-#define TR_DECODE_MIN_CHUNK 256
+#define TR_DECODE_MIN_CHUNK 128
 #endif
 
 // Partial-result slots per (seq, query head) of the decode split-K are at least this many, so a
