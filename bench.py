@@ -81,45 +81,45 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 # as null.
 TRAFFIC = {
     ("k_decode", "1.3b-decode-L24-B32-C8192-H16-D128"): {
-        "fetch_kib": 175697.6, "write_kib": 2623.0, "fetch_per_byte": 0.5001, "write_per_byte": 1.0,
+        "fetch_kib": 175694.5, "write_kib": 2623.0, "fetch_per_byte": 0.500101, "write_per_byte": 1.0,
         "profile": "profiles/k_decode_1.3b-decode-L24-B32-C8192-H16-D128.md",
         "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "94cbdce07060fee5acc3c97c42d00d63eab64a5177f4e97a99c8a86f8d548258",
-            "mixed_precision_kv_tr_amd/csrc/common.h": "006c98642b9ce2f9bed609af523adddc638cf3aac5df2e2f4c9c316c74258d9f",
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "a45df512c8053dd187f88531bde9651dc0672ced2f92470d335e88e354bc64ae",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "ff7f42e41c0f7a910aa65712bb1a08697c255e0874e1a77bccd1b967ce083556",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
-            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
+            "include/triroute.h": "a878c5fe6a6d6f81c3e4f878b7ce714770ac11b44a59e099e3ba3d3b5428bee2",
         },
     },
     ("k_decode", "1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128"): {
-        "fetch_kib": 89435.4, "write_kib": 4640.6, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "fetch_kib": 89435.0, "write_kib": 4640.3, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
         "profile": "profiles/k_decode_1.3b-gqa-decode-L24-B32-C8192-H16-KV4-D128.md",
         "sources": {
-            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "94cbdce07060fee5acc3c97c42d00d63eab64a5177f4e97a99c8a86f8d548258",
-            "mixed_precision_kv_tr_amd/csrc/common.h": "006c98642b9ce2f9bed609af523adddc638cf3aac5df2e2f4c9c316c74258d9f",
+            "mixed_precision_kv_tr_amd/csrc/decode.cpp.hip": "a45df512c8053dd187f88531bde9651dc0672ced2f92470d335e88e354bc64ae",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "ff7f42e41c0f7a910aa65712bb1a08697c255e0874e1a77bccd1b967ce083556",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
-            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
+            "include/triroute.h": "a878c5fe6a6d6f81c3e4f878b7ce714770ac11b44a59e099e3ba3d3b5428bee2",
         },
     },
     ("k_prefill_attn", "160m-prefill-L12-B4-T2048-H12-D64"): {
-        "fetch_kib": 19258.6, "write_kib": 19043.7, "fetch_per_byte": 0.500101, "write_per_byte": 1.0,
+        "fetch_kib": 19258.2, "write_kib": 19043.9, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
         "profile": "profiles/k_prefill_attn_160m-prefill-L12-B4-T2048-H12-D64.md",
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip": "af4ba0a1ed87eba042bc59e7c0e7eb069b4e8043c4b5a0d229a4430e331ee717",
-            "mixed_precision_kv_tr_amd/csrc/common.h": "006c98642b9ce2f9bed609af523adddc638cf3aac5df2e2f4c9c316c74258d9f",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "ff7f42e41c0f7a910aa65712bb1a08697c255e0874e1a77bccd1b967ce083556",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
             "mixed_precision_kv_tr_amd/csrc/kv_write.h": "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
-            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
+            "include/triroute.h": "a878c5fe6a6d6f81c3e4f878b7ce714770ac11b44a59e099e3ba3d3b5428bee2",
         },
     },
     ("k_prefill_attn", "160m-gqa-prefill-L12-B4-T2048-H12-KV3-D64"): {
-        "fetch_kib": 19114.8, "write_kib": 19052.2, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
+        "fetch_kib": 19111.8, "write_kib": 19052.2, "fetch_per_byte": 0.500103, "write_per_byte": 1.0,
         "profile": "profiles/k_prefill_attn_160m-gqa-prefill-L12-B4-T2048-H12-KV3-D64.md",
         "sources": {
             "mixed_precision_kv_tr_amd/csrc/prefill.cpp.hip": "af4ba0a1ed87eba042bc59e7c0e7eb069b4e8043c4b5a0d229a4430e331ee717",
-            "mixed_precision_kv_tr_amd/csrc/common.h": "006c98642b9ce2f9bed609af523adddc638cf3aac5df2e2f4c9c316c74258d9f",
+            "mixed_precision_kv_tr_amd/csrc/common.h": "ff7f42e41c0f7a910aa65712bb1a08697c255e0874e1a77bccd1b967ce083556",
             "mixed_precision_kv_tr_amd/csrc/layout.h": "68327b740f988dfc84020652ed95c482ff0a871587eefe9dfba27d8ca782d454",
             "mixed_precision_kv_tr_amd/csrc/kv_write.h": "e9bf3bbc3fdaf24942e01dc74f503c5dda652b9b89b312eb428744f02eef8ca8",
-            "include/triroute.h": "e713e996d04d0fa2ba40434ce6b3fffb6c857a57f3254d5894a69d061021de2d",
+            "include/triroute.h": "a878c5fe6a6d6f81c3e4f878b7ce714770ac11b44a59e099e3ba3d3b5428bee2",
         },
     },
 }
