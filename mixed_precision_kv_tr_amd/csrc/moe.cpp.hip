@@ -43,6 +43,7 @@ struct tr_moe {
   int32_t* counts;   // [k][E + 1]
   uint16_t* hbuf;    // [max_tokens * k][de] fp16 hidden rows (row t * k + slot)
   uint32_t* err;     // sticky TR_ERRF_* flags
+  float* ys;         // [k][kDownSplit][kSmallCall][d] partial down-product rows of calls of <= kSmallCall tokens
   bool weights_set;
 };
 
@@ -221,6 +222,29 @@ __device__ __forceinline__ bool find_tile_expert_major(const int32_t* counts, in
   return false;
 }
 
+constexpr int kDownSplit = 2;     // hidden-channel halves of the small calls' down product
+
+// Tiles of every slot, expert by expert (the null expert first), the slots of an expert side by
+// side, so that the workgroups reading one expert's weights run close together.
+template <int kTile>
+__device__ __forceinline__ bool find_tile_all(const int32_t* counts, int E, int K, int id, int& slot, int& e, int& tile,
+                                              int& cnt) {
+  for (int x = 0; x <= E; ++x) {
+    for (int s = 0; s < K; ++s) {
+      const int c = counts[s * (E + 1) + x];
+      const int nt = (c + kTile - 1) / kTile;
+      if (id < nt) {
+        slot = s;
+        e = x;
+        tile = id;
+        cnt = c;
+        return true;
+      }
+      id -= nt;
+    }
+  }
+  return false;
+}
 template <int kTile>
 __device__ __forceinline__ bool find_tile(const int32_t* counts, int E, int s0, int s1, int e0, int id, int& slot,
                                           int& e, int& tile, int& cnt) {
@@ -531,21 +555,31 @@ __global__ __launch_bounds__(512) void k_moe_up_t(const uint16_t* __restrict__ x
       }
 }
 
-// Down product for one slot: 32 kMB tokens of one (slot, expert) list and 128 output channels.
+// Down product: 32 kMB tokens of one (slot, expert) list and 128 output channels.  With ys null,
+// the tiles of one slot, stored into y (slot 0) or added to it (later slots); otherwise the tiles
+// of every slot in one launch, each also split into kDownSplit halves of the hidden channels,
+// each (token, slot, half) row stored into ys[slot][half][token] (kSmallCall rows each), the null
+// expert's as zeros, for k_moe_ysum to add in a fixed order.
 template <int kMB>
 __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ hbuf, const int32_t* __restrict__ lists,
                                                   const int32_t* __restrict__ counts, const float* __restrict__ wt,
                                                   const uint16_t* __restrict__ wd, float* __restrict__ y, int d, int de,
-                                                  int E, int k, int cap, int slot, int ntiles) {
+                                                  int E, int k, int cap, int slot_arg, int ntiles,
+                                                  float* __restrict__ ys) {
   constexpr int kTile = 32 * kMB;
   __shared__ int32_t tok[kTile];
   __shared__ float wgt[kTile];
   // work item: (block of 128 output channels, token tile), channel block by channel block
-  const int item = xcd_item(blockIdx.x, (int)gridDim.x);
+  const int item0 = xcd_item(blockIdx.x, (int)gridDim.x);
+  const int half = ys ? item0 % kDownSplit : 0;    // the halves of a tile run side by side
+  const int item = ys ? item0 / kDownSplit : item0;
   const int cblk = item / ntiles;
-  int s_, e, tile, cnt;
+  int slot, e, tile, cnt;
   // slot 0 also takes the null expert's tiles (zeros); later slots skip it
-  if (!find_tile<kTile>(counts, E, slot, slot + 1, slot == 0 ? 0 : 1, item % ntiles, s_, e, tile, cnt)) return;
+  if (ys ? !find_tile_all<kTile>(counts, E, k, item % ntiles, slot, e, tile, cnt)
+         : !find_tile<kTile>(counts, E, slot_arg, slot_arg + 1, slot_arg == 0 ? 0 : 1, item % ntiles, slot, e, tile,
+                             cnt))
+    return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ntok = min(kTile, cnt - tile * kTile);
   const int32_t* lst = lists + (int64_t)(slot * (E + 1) + e) * cap + tile * kTile;
@@ -578,12 +612,14 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
 #pragma unroll
       for (int q = 0; q < kPS; ++q) wv[q] = gload16(dr + (st + q) * wstep);
     };
-    hs[0][prow][pp] = gload16(haddr(0));
-    wload(0, wa);
+    // this workgroup's k-steps: all of them, or one half (ns is a multiple of 8, a half of 4)
+    const int s0 = ys ? half * (ns / kDownSplit) : 0, s1 = ys ? s0 + ns / kDownSplit : ns;
+    hs[0][prow][pp] = gload16(haddr(s0));
+    wload(s0, wa);
     __syncthreads();
     int buf = 0;
-    for (int st = 0; st < ns; st += kPS) {
-      const int nx = min(st + kPS, ns - kPS);
+    for (int st = s0; st < s1; st += kPS) {
+      const int nx = min(st + kPS, s1 - kPS);
       const uint4 hn = gload16(haddr(nx));
       uint4 wn[kPS];
       wload(nx, wn);
@@ -606,13 +642,35 @@ __global__ __launch_bounds__(256) void k_moe_down(const uint16_t* __restrict__ h
     for (int reg = 0; reg < 16; ++reg) {
       const int row = 32 * mb + 8 * (reg >> 2) + 4 * kh + (reg & 3);
       if (row < ntok) {
-        float* dst = y + (int64_t)tok[row] * d + n;
         const float v = e > 0 ? acc[mb][reg] * wgt[row] : 0.0f;
-        if (slot == 0) *dst = v;
-        else *dst += v;
+        if (ys) {
+          ys[((int64_t)(slot * kDownSplit + half) * kSmallCall + tok[row]) * d + n] = v;
+        } else {
+          float* dst = y + (int64_t)tok[row] * d + n;
+          if (slot == 0) *dst = v;
+          else *dst += v;
+        }
       }
     }
   }
+}
+
+// y = the sum of the (slot, half) rows k_moe_down stored in ys, slot by slot and half by half
+// (a fixed order, so the result does not depend on scheduling).
+__global__ __launch_bounds__(256) void k_moe_ysum(const float* __restrict__ ys, float* __restrict__ y, int M, int d,
+                                                  int k) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;          // float4 index
+  if (i >= (int64_t)M * d / 4) return;
+  const int64_t t = i / (d / 4), c4 = i % (d / 4);
+  float4 acc = reinterpret_cast<const float4*>(ys + t * d)[c4];
+  for (int s = 1; s < k * kDownSplit; ++s) {
+    const float4 v = reinterpret_cast<const float4*>(ys + ((int64_t)s * kSmallCall + t) * d)[c4];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y + t * d)[c4] = acc;
 }
 
 // Down product of one slot on a tile of 128 listed tokens x 256 output channels (large calls, d a
@@ -799,6 +857,7 @@ tr_status tr_moe_alloc(const tr_moe_desc* desc, tr_moe** out) {
   ok = ok && hipMalloc((void**)&m->counts, sizeof(int32_t) * K * E1) == hipSuccess;
   ok = ok && hipMalloc((void**)&m->hbuf, 2 * M * K * q.d_expert) == hipSuccess;
   ok = ok && hipMalloc((void**)&m->err, sizeof(uint32_t)) == hipSuccess;
+  ok = ok && hipMalloc((void**)&m->ys, sizeof(float) * K * kDownSplit * kSmallCall * q.d) == hipSuccess;
   ok = ok && hipMemset(m->err, 0, sizeof(uint32_t)) == hipSuccess;
   if (!ok) {
     tr_moe_free(m);
@@ -812,7 +871,7 @@ tr_status tr_moe_free(tr_moe* m) {
   if (!m) return TR_OK;
   (void)hipDeviceSynchronize();
   for (void* p : {(void*)m->wg, (void*)m->wu, (void*)m->wd, (void*)m->sel, (void*)m->wt, (void*)m->inv_rms,
-                  (void*)m->lists, (void*)m->counts, (void*)m->hbuf, (void*)m->err})
+                  (void*)m->lists, (void*)m->counts, (void*)m->hbuf, (void*)m->err, (void*)m->ys})
     if (p) (void)hipFree(p);
   delete m;
   return TR_OK;
@@ -864,11 +923,21 @@ tr_status tr_moe_ffn(tr_moe* m, const void* x, const float* gate_logits, int32_t
       for (int s = 0; s < K; ++s)
         hipLaunchKernelGGL(k_moe_down_t, dim3(tiles_dn * (m->d / kDN)), dim3(512), 0, st, m->hbuf, m->lists, m->counts,
                            m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s);
+    } else if (MB == 1 && K > 1) {
+      // small calls: every slot's tiles in one launch, each split into halves of the hidden
+      // channels (four times the workgroups of a slot's launch, each expert's weights read by
+      // its slots' tiles together), then the sum
+      const int tiles_dn = K * ((M + T - 1) / T + E + 1);
+      hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn * (m->d / kUnits) * kDownSplit), dim3(256), 0, st, m->hbuf,
+                         m->lists, m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, 0, tiles_dn, m->ys);
+      hipLaunchKernelGGL(k_moe_ysum, dim3((unsigned)(((int64_t)M * m->d / 4 + 255) / 256)), dim3(256), 0, st, m->ys, y,
+                         M, m->d, K);
     } else {
       const int tiles_dn = (M + T - 1) / T + E + 1;
       for (int s = 0; s < K; ++s)
         hipLaunchKernelGGL(k_moe_down<MB>, dim3(tiles_dn * (m->d / kUnits)), dim3(256), 0, st, m->hbuf, m->lists,
-                           m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s, tiles_dn);
+                           m->counts, m->wt, m->wd, y, m->d, m->de, E, K, m->max_tokens, s, tiles_dn,
+                           static_cast<float*>(nullptr));
     }
   };
   if (M > kSmallCall) run(std::integral_constant<int, 2>());
