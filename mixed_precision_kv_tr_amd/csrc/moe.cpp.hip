@@ -3,7 +3,7 @@
 // E experts plus the null expert f_0 = 0, S_t the top-k; each expert a SwiGLU FFN
 // f(u) = W2 (silu(W1 u) * (W3 u)) with hidden width d_e.
 //
-// One call = four launches:
+// One call = four launches (five for calls of at most kSmallCall tokens with top-2):
 //   k_moe_route   one wave per token: 1 / rms(x_t), the top-k of the logits (ties to the lower
 //                 index) and the renormalized weights exp(z_j - z_max) / sum over S_t.
 //   k_moe_lists   one workgroup per (slot, expert, null included): the tokens whose slot-th
@@ -17,9 +17,13 @@
 //                 channels): the down product of the gathered fp16 hidden rows against the fp16
 //                 copy of W2 (packed once; exact for bf16 weights in fp16's range), times the token's
 //                 weight, stored (slot 0; the null expert stores zeros) or added (slot 1) into the
-//                 fp32 output -- no atomics, so the result does not depend on scheduling.
+//                 fp32 output -- no atomics, so the result does not depend on scheduling.  Calls of
+//                 at most kSmallCall tokens with top-2 run every slot in one launch, each tile split
+//                 into halves of the hidden channels, every (token, slot, half) row stored apart,
+//                 and k_moe_ysum adds them in a fixed order.  Calls above kSmallCall tokens take
+//                 the tiled forms k_moe_up_t / k_moe_down_t (below).
 // Weight matrices are packed once (tr_moe_set_weights) into the operand order of the matrix-core
-// k-loop: for k-step s = 4 g + j and output unit n, 16 bf16 holding input channels 64 g + 8 j ..
+// k-loop: for k-step s = 4 g + j and output unit n, 16 values (bf16 for W1 / W3, fp16 for W2) holding input channels 64 g + 8 j ..
 // + 7 and 64 g + 32 + 8 j .. + 7, so that the 32 units of a wave read one contiguous 1 KB per
 // k-step.  The gathered activation rows of a tile are shared by its four waves: each stage of
 // k-steps is loaded once per workgroup into double-buffered LDS (16-byte-padded rows), while each
