@@ -23,9 +23,9 @@
 //                 and k_moe_ysum adds them in a fixed order.  Calls above kSmallCall tokens take
 //                 the tiled forms k_moe_up_t / k_moe_down_t (below).
 // Weight matrices are packed once (tr_moe_set_weights) into the operand order of the matrix-core
-// k-loop: for k-step s = 4 g + j and output unit n, 16 values (bf16 for W1 / W3, fp16 for W2) holding input channels 64 g + 8 j ..
-// + 7 and 64 g + 32 + 8 j .. + 7, so that the 32 units of a wave read one contiguous 1 KB per
-// k-step.  The gathered activation rows of a tile are shared by its four waves: each stage of
+// k-loop: for k-step s = 4 g + j and output unit n, 16 values (bf16 for W1 / W3, fp16 for W2)
+// holding input channels 64 g + 8 j .. + 7 and 64 g + 32 + 8 j .. + 7, so that the 32 units of a
+// wave read one contiguous 1 KB per k-step.  The gathered activation rows of a tile are shared by its four waves: each stage of
 // k-steps is loaded once per workgroup into double-buffered LDS (16-byte-padded rows), while each
 // wave's weight columns come straight from memory into registers, the next stage in flight.
 #include <math.h>
