@@ -222,6 +222,15 @@ def git_sha():
         return None
 
 
+def built_from():
+    """The commit the library was built from, as recorded by the build (None if not recorded)."""
+    try:
+        with open(os.path.join(ROOT, "mixed_precision_kv_tr_amd", "_build", "REVISION")) as f:
+            return f.read().strip() or None
+    except OSError:
+        return None
+
+
 def copy_calibration(mib: int, reps: int = 5):
     """Plain device-to-device copies of a known size, for scaling the PMC byte counters.
 
@@ -715,7 +724,7 @@ def main():
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic",
-            "seed": args.seed, "source_sha256": source_digest(), "git_sha": git_sha()}
+            "seed": args.seed, "source_sha256": source_digest(), "git_sha": git_sha(), "library_built_from": built_from()}
     if dec:
         cfg = dec["cfg"]
         line.update({"value": round(dec["gbs"], 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 4),

@@ -61,7 +61,24 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp_lib, LIB)
+    _record_revision(tmp)
     return LIB
+
+
+def _record_revision(build_dir: str) -> None:
+    """Writes the git commit the library was built from (with "+dirty" if the tree had changes)
+    next to the objects, so that a copy of the tree without .git still names it."""
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        dirty = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+    except (OSError, subprocess.SubprocessError):
+        return
+    if head.returncode != 0 or not head.stdout.strip():
+        return
+    rev = head.stdout.strip() + ("+dirty" if dirty.returncode == 0 and dirty.stdout.strip() else "")
+    with open(os.path.join(build_dir, "REVISION"), "w") as f:
+        f.write(rev + "\n")
 
 
 if __name__ == "__main__":
